@@ -1,0 +1,198 @@
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+Default workload: the Llama-3.1-8B-shaped decode layer (32 query / 8 KV
+heads, head dim 128, batch 1, 32768 cached positions, bf16 K/V; keys 3-bit
+codes + 128-row QJL sketch, values 2-bit codes), over 32 distinct layer
+caches so that every decode reads HBM rather than the 256 MB Infinity Cache.
+
+A timed step is one decode pass over the 32 layer caches (one
+tq_decode_attention launch per layer).  `value` is the decode attention
+throughput in GB/s of algorithmic bytes: the packed K and V records of every
+attended position plus the query and output, divided by the step time.  The
+quantize-append half of the metric is measured in its own timed region: the
+32768-position prefill of each of the 32 layers, reported as tokens/s.
+
+Also printed: the roofline of the decode kernel (algorithmic bytes per launch
+over its mean launch duration, from HIP events on the launch stream), and the
+oracle's CPU throughput on a bounded sample (single-threaded).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_decode_bytes(w, cfg, tq, lens):
+    kb, vb = tq.cache_bytes(cfg)
+    slots = cfg.batch * cfg.n_kv_heads * ((cfg.max_ctx + 127) // 128) * 128
+    krec, vrec = kb // slots, vb // slots
+    recs = sum(lens) * cfg.n_kv_heads
+    qo = 2 * cfg.batch * cfg.n_q_heads * cfg.head_dim * 4
+    return recs * (krec + vrec) + qo, krec, vrec
+
+
+def cpu_baseline(w, seed):
+    """Oracle, single-threaded: quantise one layer's prefill (tokens/s) and
+    decode all query heads over it (GB/s of the same algorithmic bytes)."""
+    import numpy as np
+
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import oracle
+    from compressed_decode_attention_quantize_amd import synth
+
+    k, v = synth.make_kv(w, w.ctx, seed=seed)
+    q = synth.make_q(w, seed=seed + 1000).numpy()
+    kn = k.to("cpu").float().numpy()
+    vn = v.to("cpu").float().numpy()
+    codec = {synth.RAW_F32: 0, synth.POLAR: 1, synth.POLAR_QJL: 2, synth.Q8_BLOCK32: 3}
+    s = oracle.make_spec(d=w.d, n_q=w.n_q, n_kv=w.n_kv, batch=w.batch, max_ctx=w.ctx, k_codec=codec[w.k_codec],
+                         k_bits=w.k_bits, m=w.m, v_codec=codec[w.v_codec], v_bits=w.v_bits)
+    P = oracle.Params(s, 42, 0)
+    R = oracle.Records(s)
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        oracle.quantize_into(s, P, R, kn[b], vn[b], b, 0)
+    t_app = time.perf_counter() - t0
+    lens = np.full(w.batch, w.ctx, np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(s, P, R, lens, q)
+    t_dec = time.perf_counter() - t0
+    sz = oracle.spec_sizes(s)
+    rec = sz["k_record"] + sz["v_record"]
+    dec_bytes = w.batch * w.ctx * w.n_kv * rec + 2 * w.batch * w.n_q * w.d * 4
+    return {
+        "value": dec_bytes / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"one layer of {w.name}: oracle quantize of {w.batch * w.ctx} positions x {w.n_kv} KV heads "
+                   f"({t_app:.1f} s) then fp64 decode of all {w.n_q} query heads ({t_dec:.1f} s), "
+                   "single-threaded C on the host"),
+        "append_tokens_per_s": w.batch * w.ctx / t_app,
+        "seconds": t_app + t_dec,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_b1_ctx32k")
+    ap.add_argument("--layers", type=int, default=0, help="layer caches to cycle (0 = workload default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from compressed_decode_attention_quantize_amd import synth, tq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wi = synth.ORDER.index(args.workload)
+    w = synth.WORKLOADS[args.workload]
+    n_layers = args.layers or w.layers
+    data_seed = 1000 + wi
+
+    # ------------------------------------------------ inputs and layer caches
+    k, v = synth.make_kv(w, w.ctx, seed=data_seed, device=dev)
+    q = synth.make_q(w, seed=data_seed + 1000, device=dev)
+    layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l), dev, zero=False) for l in range(n_layers)]
+    torch.cuda.synchronize()
+
+    # ------------------------------------------ append: prefill of every layer
+    stream = torch.cuda.current_stream()
+    layers[0].append(k, v)          # warm-up launch (also fills layer 0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for L in layers[1:]:
+        L.append(k, v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_s = e0.elapsed_time(e1) / 1e3 / max(1, n_layers - 1)
+    append_tok_s = w.batch * w.ctx / append_s
+
+    # --------------------------------------------------------------- decode
+    lens = [w.ctx] * w.batch
+    cfg0 = layers[0].cfg
+    bytes_per_launch, krec, vrec = algorithmic_decode_bytes(w, cfg0, tq, lens)
+    outs = [torch.empty_like(q) for _ in layers]
+
+    def step(events=None):
+        for i, L in enumerate(layers):
+            if events is not None:
+                events[i][0].record(stream)
+            L.decode(q, out=outs[i])
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(args.steps):
+        step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = s0.elapsed_time(s1) / args.steps
+
+    # per-launch durations of the decode kernel (events on its stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+          for _ in range(args.steps)]
+    for st in range(args.steps):
+        step(ev[st])
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for row in ev for (a, b) in row]
+    launch_ms = sum(durs) / len(durs)
+
+    value = n_layers * bytes_per_launch / (step_ms / 1e3) / 1e9
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    result = {
+        "metric": "decode attention HBM GB/s on packed KV (% of peak); quantize-append tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "context": w.ctx, "n_q_heads": w.n_q,
+                   "n_kv_heads": w.n_kv, "head_dim": w.d, "k_codec": f"{w.k_codec} b{w.k_bits} m{w.m}",
+                   "v_codec": f"{w.v_codec} b{w.v_bits}", "k_dtype": w.dtype, "layers": n_layers,
+                   "record_bytes": {"k": krec, "v": vrec}},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "append_tokens_per_s": round(append_tok_s, 1),
+        "append_ms_per_layer": round(append_s * 1e3, 4),
+        "decode_us_per_layer": round(step_ms * 1e3 / n_layers, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "bytes_per_launch": bytes_per_launch,
+                     "launch_us": round(launch_ms * 1e3, 3)},
+        "wall_s_timed": round(wall, 4),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, data_seed)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,492 @@
+// tq_host.cpp -- host side of the C ABI declared in include/tq.h:
+// argument checks, sizes, per-layer parameter generation and kernel launches.
+//
+// Parameters (wis-web.com reader, TurboQuant article: the PolarQuant
+// paragraph's rotation "pour gaussianiser" and the angle law "connue a
+// l'avance"; leviatan.io, "Principe de quantification sans calibration": a
+// fixed, data-independent transform):
+//   * rotation signs D_K, D_V and the Gaussian sketch S come from
+//     counter-form SplitMix64 (Steele, Lea & Flood, OOPSLA 2014) keyed by
+//     (seed, layer, stream), with Box-Muller for the Gaussians;
+//   * the codebook is the Lloyd-Max quantiser of the coordinate law of a
+//     uniformly random unit vector scaled by sqrt(d), density proportional to
+//     (1 - t^2/d)^((d-3)/2); centroids are stored as fp16-exact values and
+//     the decision boundaries as the fp32 midpoints of adjacent centroids.
+// Integrals use composite 16-point Gauss-Legendre quadrature.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+using tq::kBlock;
+using tq::kD;
+using tq::kM;
+
+// ------------------------------------------------------------- checks
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+tq_status check_cfg(const tq_config* c) {
+  if (c == nullptr) return TQ_EINVAL;
+  if (c->abi_version != TQ_ABI_VERSION || c->reserved != 0) return TQ_EINVAL;
+  if (!is_pow2(c->head_dim) || c->head_dim < 16 || c->head_dim > 256) return TQ_EINVAL;
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads != 0) return TQ_EINVAL;
+  if (c->batch < 1 || c->max_ctx < 1) return TQ_EINVAL;
+  if (c->decode_chunk < 0 || c->decode_chunk % kBlock != 0) return TQ_EINVAL;
+  switch (c->k_codec) {
+    case TQ_CODEC_RAW_F32:
+      if (c->k_bits != 32 || c->qjl_m != 0) return TQ_EINVAL;
+      break;
+    case TQ_CODEC_POLAR:
+    case TQ_CODEC_POLAR_QJL:
+      if (c->k_bits < 1 || c->k_bits > 8) return TQ_EINVAL;
+      if (c->k_codec == TQ_CODEC_POLAR_QJL) {
+        if (c->qjl_m <= 0 || c->qjl_m % 64 != 0) return TQ_EINVAL;
+      } else if (c->qjl_m != 0) {
+        return TQ_EINVAL;
+      }
+      break;
+    case TQ_CODEC_Q8_BLOCK32:
+      if (c->k_bits != 8 || c->qjl_m != 0) return TQ_EINVAL;
+      break;
+    default:
+      return TQ_EINVAL;
+  }
+  switch (c->v_codec) {
+    case TQ_CODEC_RAW_F32:
+      if (c->v_bits != 32) return TQ_EINVAL;
+      break;
+    case TQ_CODEC_POLAR:
+      if (c->v_bits < 1 || c->v_bits > 8) return TQ_EINVAL;
+      break;
+    case TQ_CODEC_POLAR_QJL:
+    case TQ_CODEC_Q8_BLOCK32:
+      return TQ_EUNSUPPORTED;   // QJL corrects inner products: keys only; q8 is a key format
+    default:
+      return TQ_EINVAL;
+  }
+  // well formed; now what the kernels serve
+  if (c->head_dim != kD) return TQ_EUNSUPPORTED;
+  if (c->n_q_heads / c->n_kv_heads > tq::kMaxGroup) return TQ_EUNSUPPORTED;
+  if ((c->k_codec == TQ_CODEC_POLAR || c->k_codec == TQ_CODEC_POLAR_QJL) &&
+      (c->k_bits < 2 || c->k_bits > 4))
+    return TQ_EUNSUPPORTED;
+  if (c->k_codec == TQ_CODEC_POLAR_QJL && c->qjl_m != kM) return TQ_EUNSUPPORTED;
+  if (c->v_codec == TQ_CODEC_POLAR && (c->v_bits < 2 || c->v_bits > 4)) return TQ_EUNSUPPORTED;
+  return TQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int n_blocks(const tq_config* c) { return (c->max_ctx + kBlock - 1) / kBlock; }
+
+int64_t k_record_bytes(const tq_config* c) {
+  const int64_t d = c->head_dim;
+  switch (c->k_codec) {
+    case TQ_CODEC_RAW_F32: return 4 * d;
+    case TQ_CODEC_POLAR: return c->k_bits * d / 8 + 2;
+    case TQ_CODEC_POLAR_QJL: return c->k_bits * d / 8 + c->qjl_m / 8 + 4;
+    default: return d + 2 * (d / 32);
+  }
+}
+int64_t v_record_bytes(const tq_config* c) {
+  const int64_t d = c->head_dim;
+  return c->v_codec == TQ_CODEC_RAW_F32 ? 4 * d : c->v_bits * d / 8 + 2;
+}
+
+int qjl_rows(const tq_config* c) { return c->k_codec == TQ_CODEC_POLAR_QJL ? c->qjl_m : 0; }
+
+// --------------------------------------------------------------- PRNG
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ULL;
+
+uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+// Output k (0-based) of a SplitMix64 generator whose state starts at s.
+uint64_t splitmix_nth(uint64_t s, uint64_t k) { return mix64(s + (k + 1) * kGamma); }
+
+struct Stream {
+  uint64_t key;
+  Stream(uint64_t seed, int32_t layer, uint32_t id)
+      : key(splitmix_nth(seed, (static_cast<uint64_t>(static_cast<uint32_t>(layer)) << 8) + id)) {}
+  uint64_t operator()(uint64_t k) const { return splitmix_nth(key, k); }
+};
+
+void fill_signs(const Stream& st, int d, float* out) {
+  for (int i = 0; i < d; ++i) out[i] = (st(i) >> 63) ? -1.0f : 1.0f;
+}
+
+void fill_sketch(const Stream& st, int m, int d, float* S) {
+  const double two_pi = 6.283185307179586;
+  const double scale53 = 1.0 / 9007199254740992.0;
+  for (int j = 0; j < m; ++j) {
+    for (int i = 0; i < d; ++i) {
+      const uint64_t e = static_cast<uint64_t>(j) * d + i;
+      const double u1 = static_cast<double>((st(2 * e) >> 11) + 1) * scale53;
+      const double u2 = static_cast<double>(st(2 * e + 1) >> 11) * scale53;
+      S[static_cast<size_t>(j) * d + i] = static_cast<float>(std::sqrt(-2.0 * std::log(u1)) * std::cos(two_pi * u2));
+    }
+  }
+}
+
+// ------------------------------------------------------------ codebook
+
+struct GaussLegendre16 {
+  double x[16], w[16];
+  GaussLegendre16() {
+    const int n = 16;
+    for (int k = 0; k < n / 2; ++k) {
+      double z = std::cos(M_PI * (k + 0.75) / (n + 0.5));
+      double dp = 0.0;
+      for (int it = 0; it < 100; ++it) {
+        double p0 = 1.0, p1 = z;
+        for (int j = 2; j <= n; ++j) {
+          const double p2 = ((2.0 * j - 1.0) * z * p1 - (j - 1.0) * p0) / j;
+          p0 = p1;
+          p1 = p2;
+        }
+        dp = n * (z * p1 - p0) / (z * z - 1.0);
+        const double dz = p1 / dp;
+        z -= dz;
+        if (std::fabs(dz) < 1e-16) break;
+      }
+      x[k] = -z;
+      x[n - 1 - k] = z;
+      w[k] = w[n - 1 - k] = 2.0 / ((1.0 - z * z) * dp * dp);
+    }
+  }
+};
+
+struct Codebook {
+  float centroids[16];
+  float bounds[16];
+};
+
+// int_a^c t^moment (1 - t^2/d)^((d-3)/2) dt, 48 panels of 16-point Gauss-Legendre
+double law_integral(int d, double a, double c, int moment) {
+  static const GaussLegendre16 gl;
+  const int panels = 48;
+  const double hw = (c - a) / panels;
+  const double ex = 0.5 * (d - 3);
+  double total = 0.0;
+  for (int p = 0; p < panels; ++p) {
+    const double mid = a + (p + 0.5) * hw;
+    double s = 0.0;
+    for (int k = 0; k < 16; ++k) {
+      const double t = mid + 0.5 * hw * gl.x[k];
+      const double base = 1.0 - t * t / d;
+      if (base <= 0.0) continue;
+      double f = std::pow(base, ex);
+      if (moment == 1) f *= t;
+      s += gl.w[k] * f;
+    }
+    total += 0.5 * hw * s;
+  }
+  return total;
+}
+
+Codebook make_codebook(int d, int bits) {
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, Codebook> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({d, bits});
+  if (it != cache.end()) return it->second;
+
+  const int half = 1 << (bits - 1);
+  const double top = std::min(std::sqrt(static_cast<double>(d)), 16.0);
+  std::vector<double> c(half), edge(half + 1);
+  for (int k = 0; k < half; ++k) c[k] = 3.0 * (k + 0.5) / half;   // positive half; symmetric law
+  for (int round = 0; round < 100000; ++round) {
+    edge[0] = 0.0;
+    for (int k = 1; k < half; ++k) edge[k] = 0.5 * (c[k - 1] + c[k]);
+    edge[half] = top;
+    double moved = 0.0;
+    for (int k = 0; k < half; ++k) {
+      const double nc = law_integral(d, edge[k], edge[k + 1], 1) / law_integral(d, edge[k], edge[k + 1], 0);
+      moved = std::max(moved, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (moved <= 1e-13) break;
+  }
+  Codebook cb{};
+  const int levels = 2 * half;
+  for (int k = 0; k < half; ++k) {
+    const float pos = static_cast<float>(static_cast<_Float16>(c[k]));   // one RNE rounding to fp16
+    cb.centroids[half + k] = pos;
+    cb.centroids[half - 1 - k] = -pos;
+  }
+  for (int j = 0; j + 1 < levels; ++j) cb.bounds[j] = 0.5f * (cb.centroids[j] + cb.centroids[j + 1]);
+  cache[{d, bits}] = cb;
+  return cb;
+}
+
+// ------------------------------------------------------- params image
+
+void build_params(const tq_config* c, uint8_t* img) {
+  const int d = c->head_dim;
+  const int m = qjl_rows(c);
+  const tq::ParamsLayout L = tq::params_layout(d, m);
+  std::memset(img, 0, L.total);
+  fill_signs(Stream(c->seed, c->layer, 0), d, reinterpret_cast<float*>(img + L.dk));
+  fill_signs(Stream(c->seed, c->layer, 1), d, reinterpret_cast<float*>(img + L.dv));
+  if (m > 0) {
+    float* S = reinterpret_cast<float*>(img + L.s);
+    float* ST = reinterpret_cast<float*>(img + L.st);
+    fill_sketch(Stream(c->seed, c->layer, 2), m, d, S);
+    for (int j = 0; j < m; ++j)
+      for (int i = 0; i < d; ++i) ST[static_cast<size_t>(i) * m + j] = S[static_cast<size_t>(j) * d + i];
+  }
+  if (c->k_codec == TQ_CODEC_POLAR || c->k_codec == TQ_CODEC_POLAR_QJL) {
+    const Codebook cb = make_codebook(d, c->k_bits);
+    std::memcpy(img + L.ck, cb.centroids, 64);
+    std::memcpy(img + L.kb, cb.bounds, 64);
+  }
+  if (c->v_codec == TQ_CODEC_POLAR) {
+    const Codebook cb = make_codebook(d, c->v_bits);
+    std::memcpy(img + L.cv, cb.centroids, 64);
+    std::memcpy(img + L.vb, cb.bounds, 64);
+  }
+}
+
+tq::Tables tables(const tq_config* c, const void* params) {
+  const tq::ParamsLayout L = tq::params_layout(c->head_dim, qjl_rows(c));
+  const uint8_t* p = static_cast<const uint8_t*>(params);
+  tq::Tables t;
+  t.dk = reinterpret_cast<const float*>(p + L.dk);
+  t.dv = reinterpret_cast<const float*>(p + L.dv);
+  t.s = reinterpret_cast<const float*>(p + L.s);
+  t.st = reinterpret_cast<const float*>(p + L.st);
+  t.ck = reinterpret_cast<const float*>(p + L.ck);
+  t.kb = reinterpret_cast<const float*>(p + L.kb);
+  t.cv = reinterpret_cast<const float*>(p + L.cv);
+  t.vb = reinterpret_cast<const float*>(p + L.vb);
+  return t;
+}
+
+int decode_chunk_blocks(const tq_config* c, int32_t max_seq_len) {
+  const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
+  if (c->decode_chunk > 0) return c->decode_chunk / kBlock;
+  // aim for about 512 workgroups over the whole grid (2 per compute unit)
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int64_t want_splits = std::max<int64_t>(1, (512 + pairs - 1) / pairs);
+  return static_cast<int>(std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits));
+}
+
+int decode_splits(const tq_config* c, int32_t max_seq_len) {
+  const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
+  const int cb = decode_chunk_blocks(c, max_seq_len);
+  return (blocks + cb - 1) / cb;
+}
+
+// Largest split count of any call with lengths up to max_seq_len (the
+// automatic chunking is not monotonic in the length), for workspace sizing.
+int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
+  const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
+  if (c->decode_chunk > 0) return (blocks + c->decode_chunk / kBlock - 1) / (c->decode_chunk / kBlock);
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int64_t want_splits = std::max<int64_t>(1, (512 + pairs - 1) / pairs);
+  return static_cast<int>(std::min<int64_t>(blocks, want_splits));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_EUNSUPPORTED: return "unsupported configuration";
+    case TQ_ECAPACITY: return "append exceeds cache capacity";
+    case TQ_EWORKSPACE: return "buffer too small";
+    case TQ_EDEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+tq_status tq_cache_bytes(const tq_config* cfg, uint64_t* k_bytes, uint64_t* v_bytes) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (k_bytes == nullptr || v_bytes == nullptr) return TQ_EINVAL;
+  const uint64_t slots = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * n_blocks(cfg);
+  *k_bytes = slots * kBlock * k_record_bytes(cfg);
+  *v_bytes = slots * kBlock * v_record_bytes(cfg);
+  return TQ_OK;
+}
+
+tq_status tq_params_bytes(const tq_config* cfg, uint64_t* bytes) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (bytes == nullptr) return TQ_EINVAL;
+  *bytes = tq::params_layout(cfg->head_dim, qjl_rows(cfg)).total;
+  return TQ_OK;
+}
+
+tq_status tq_params_host(const tq_config* cfg, void* host_params, uint64_t bytes) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (host_params == nullptr || !aligned(host_params, 4)) return TQ_EINVAL;
+  if (bytes < tq::params_layout(cfg->head_dim, qjl_rows(cfg)).total) return TQ_EWORKSPACE;
+  build_params(cfg, static_cast<uint8_t*>(host_params));
+  return TQ_OK;
+}
+
+tq_status tq_init_params(const tq_config* cfg, void* params, uint64_t bytes, void* stream) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (params == nullptr || !aligned(params, 256)) return TQ_EINVAL;
+  const uint64_t need = tq::params_layout(cfg->head_dim, qjl_rows(cfg)).total;
+  if (bytes < need) return TQ_EWORKSPACE;
+  std::vector<uint8_t> img(need);
+  build_params(cfg, img.data());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(params, img.data(), need, hipMemcpyHostToDevice, s) != hipSuccess) return TQ_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return TQ_EDEVICE;
+  return TQ_OK;
+}
+
+tq_status tq_quantize_append(const tq_config* cfg, const void* params, void* k_cache, void* v_cache,
+                             const int32_t* seq_lens, int32_t max_seq_len, const void* k_new,
+                             const void* v_new, int32_t in_dtype, int32_t n_new, void* stream) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (n_new < 0 || max_seq_len < 0) return TQ_EINVAL;
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_EINVAL;
+  if (static_cast<int64_t>(max_seq_len) + n_new > cfg->max_ctx) return TQ_ECAPACITY;
+  if (n_new == 0) return TQ_OK;   // nothing to write; buffers are not examined
+  if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr ||
+      k_new == nullptr || v_new == nullptr)
+    return TQ_EINVAL;
+  if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
+      !aligned(k_new, in_dtype == TQ_F32 ? 4 : 2) || !aligned(v_new, in_dtype == TQ_F32 ? 4 : 2))
+    return TQ_EINVAL;
+  tq::QuantArgs a{};
+  a.tb = tables(cfg, params);
+  a.kc = static_cast<uint8_t*>(k_cache);
+  a.vc = static_cast<uint8_t*>(v_cache);
+  a.seq_lens = seq_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.in_dtype = in_dtype;
+  a.batch = cfg->batch;
+  a.n_kv = cfg->n_kv_heads;
+  a.max_ctx = cfg->max_ctx;
+  a.n_blocks = n_blocks(cfg);
+  a.n_new = n_new;
+  a.groups_per_seq = (n_new + 31) / 32 + 1;
+  a.k_codec = cfg->k_codec;
+  a.k_bits = cfg->k_bits;
+  a.v_codec = cfg->v_codec;
+  a.v_bits = cfg->v_bits;
+  a.k_block_bytes = kBlock * k_record_bytes(cfg);
+  a.v_block_bytes = kBlock * v_record_bytes(cfg);
+  return tq::launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EDEVICE;
+}
+
+tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, uint64_t* bytes) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (bytes == nullptr || max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
+  const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
+  const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * (kD + 2) * 4;
+  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * 4;
+  *bytes = ((partial + 255) & ~255ull) + ((counters + 255) & ~255ull);
+  return TQ_OK;
+}
+
+tq_status tq_decode_attention(const tq_config* cfg, const void* params, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens, int32_t max_seq_len,
+                              const float* q, float* out, float* logits, void* workspace,
+                              uint64_t workspace_bytes, void* stream) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr || q == nullptr ||
+      out == nullptr || workspace == nullptr)
+    return TQ_EINVAL;
+  if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
+      !aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256) || (logits && !aligned(logits, 4)))
+    return TQ_EINVAL;
+  if (max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
+  uint64_t need = 0;
+  tq_decode_workspace_bytes(cfg, max_seq_len, &need);
+  if (workspace_bytes < need) return TQ_EWORKSPACE;
+  const int splits = decode_splits(cfg, max_seq_len);
+  const uint64_t partial =
+      static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * decode_splits_bound(cfg, max_seq_len) * (kD + 2) * 4;
+  tq::DecodeArgs a{};
+  a.tb = tables(cfg, params);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.vc = static_cast<const uint8_t*>(v_cache);
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.out = out;
+  a.logits = logits;
+  a.partials = static_cast<float*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + ((partial + 255) & ~255ull));
+  a.batch = cfg->batch;
+  a.n_q = cfg->n_q_heads;
+  a.n_kv = cfg->n_kv_heads;
+  a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.max_ctx = cfg->max_ctx;
+  a.n_blocks = n_blocks(cfg);
+  a.chunk_blocks = decode_chunk_blocks(cfg, max_seq_len);
+  a.n_splits = splits;
+  a.k_codec = cfg->k_codec;
+  a.k_bits = cfg->k_bits;
+  a.v_codec = cfg->v_codec;
+  a.v_bits = cfg->v_bits;
+  a.k_block_bytes = kBlock * k_record_bytes(cfg);
+  a.v_block_bytes = kBlock * v_record_bytes(cfg);
+  return tq::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EDEVICE;
+}
+
+tq_status tq_dequantize(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
+                        int32_t b, int32_t start, int32_t count, float* k_out, float* v_out, uint32_t flags,
+                        void* stream) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (params == nullptr || !aligned(params, 256)) return TQ_EINVAL;
+  if (b < 0 || b >= cfg->batch || start < 0 || count < 0 ||
+      static_cast<int64_t>(start) + count > cfg->max_ctx)
+    return TQ_EINVAL;
+  if ((flags & ~TQ_DEQ_QJL) != 0) return TQ_EINVAL;
+  if (k_out != nullptr && (k_cache == nullptr || !aligned(k_cache, 16) || !aligned(k_out, 4))) return TQ_EINVAL;
+  if (v_out != nullptr && (v_cache == nullptr || !aligned(v_cache, 16) || !aligned(v_out, 4))) return TQ_EINVAL;
+  if (count == 0 || (k_out == nullptr && v_out == nullptr)) return TQ_OK;
+  tq::DequantArgs a{};
+  a.tb = tables(cfg, params);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.vc = static_cast<const uint8_t*>(v_cache);
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.b = b;
+  a.start = start;
+  a.count = count;
+  a.n_kv = cfg->n_kv_heads;
+  a.n_blocks = n_blocks(cfg);
+  a.k_codec = cfg->k_codec;
+  a.k_bits = cfg->k_bits;
+  a.v_codec = cfg->v_codec;
+  a.v_bits = cfg->v_bits;
+  a.qjl = (flags & TQ_DEQ_QJL) ? 1 : 0;
+  a.k_block_bytes = kBlock * k_record_bytes(cfg);
+  a.v_block_bytes = kBlock * v_record_bytes(cfg);
+  return tq::launch_dequantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EDEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// tq_internal.h -- shared declarations between the host part of the library
+// (tq_host.cpp) and its HIP kernels.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kD = 128;        // head_dim served by the kernels
+constexpr int kM = 128;        // QJL sketch rows served by the kernels
+constexpr int kBlock = 128;    // positions per cache block
+constexpr int kMaxGroup = 16;  // largest GQA group
+
+// Byte offsets inside the parameter image (all fp32 arrays).
+struct ParamsLayout {
+  uint64_t dk, dv;   // float[d] rotation signs (+/-1) for K and V
+  uint64_t s;        // float[m][d] Gaussian sketch (row j = sketch row)
+  uint64_t st;       // float[d][m] its transpose
+  uint64_t ck, kb;   // float[16] K centroids, float[16] K boundaries (2^b-1 used)
+  uint64_t cv, vb;   // same for V
+  uint64_t total;
+};
+
+inline ParamsLayout params_layout(int d, int m) {
+  ParamsLayout L{};
+  uint64_t o = 0;
+  L.dk = o; o += 4ull * d;
+  L.dv = o; o += 4ull * d;
+  L.s = o;  o += 4ull * m * d;
+  L.st = o; o += 4ull * m * d;
+  L.ck = o; o += 64;
+  L.kb = o; o += 64;
+  L.cv = o; o += 64;
+  L.vb = o; o += 64;
+  L.total = (o + 255) & ~255ull;
+  return L;
+}
+
+// Codec ids (mirror tq.h; kernels are compiled without it).
+enum { RAW_F32 = 0, POLAR = 1, POLAR_QJL = 2, Q8_BLOCK32 = 3 };
+enum { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
+
+struct Tables {
+  const float* dk;
+  const float* dv;
+  const float* s;    // [m][d]
+  const float* st;   // [d][m]
+  const float* ck;
+  const float* kb;
+  const float* cv;
+  const float* vb;
+};
+
+struct QuantArgs {
+  Tables tb;
+  uint8_t* kc;
+  uint8_t* vc;
+  const int32_t* seq_lens;
+  const void* k_new;
+  const void* v_new;
+  int32_t in_dtype;
+  int32_t batch, n_kv, max_ctx, n_blocks, n_new;
+  int32_t groups_per_seq;   // 32-position groups a sequence's append can touch
+  int32_t k_codec, k_bits, v_codec, v_bits;
+  int64_t k_block_bytes, v_block_bytes;
+};
+
+struct DecodeArgs {
+  Tables tb;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const int32_t* seq_lens;
+  const float* q;
+  float* out;
+  float* logits;      // may be null
+  float* partials;    // [batch][n_q][n_splits][d + 2]
+  uint32_t* counters; // [batch][n_kv]
+  int32_t batch, n_q, n_kv, group, max_ctx, n_blocks;
+  int32_t chunk_blocks, n_splits;
+  int32_t k_codec, k_bits, v_codec, v_bits;
+  int64_t k_block_bytes, v_block_bytes;
+};
+
+struct DequantArgs {
+  Tables tb;
+  const uint8_t* kc;
+  const uint8_t* vc;
+  float* k_out;
+  float* v_out;
+  int32_t b, start, count, n_kv, n_blocks;
+  int32_t k_codec, k_bits, v_codec, v_bits;
+  int32_t qjl;
+  int64_t k_block_bytes, v_block_bytes;
+};
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+
+}  // namespace tq

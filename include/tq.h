@@ -1,0 +1,175 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache library for MI355X (gfx950).
+ *
+ * The library implements the two data-parallel halves of the method the
+ * pages describe (wis-web.com reader, article on TurboQuant in a llama.cpp
+ * fork: the PolarQuant paragraph -- Walsh-Hadamard rotation, then radius +
+ * angle with the angle's law known in advance -- and the QJL paragraph -- a
+ * 1-bit corrector of the residual bias; leviatan.io, "TurboQuant : 6x moins
+ * de cache, jusqu'a 8x plus rapide", section "Principe de quantification
+ * sans calibration" -- a fixed, calibration-free transform):
+ *
+ *   tq_quantize_append   compress new K/V vectors into a packed block cache
+ *   tq_decode_attention  one-query-per-sequence attention read straight
+ *                        from the packed cache (flash-attention style,
+ *                        the article's "-fa on")
+ *   tq_dequantize        packed records back to fp32 (tests, inspection)
+ *
+ * Conventions
+ *  - Plain C types only.  "device" pointers are HIP device memory owned by
+ *    the caller; "host" pointers are ordinary host memory.  `stream` is a
+ *    hipStream_t (NULL = the default stream) passed as void*.
+ *  - The library never allocates, frees or synchronises device memory, with
+ *    one exception: tq_init_params copies a host image to the device and
+ *    waits for that copy.  It keeps no mutable global state apart from a
+ *    process-wide cache of codebooks, so calls on different streams may run
+ *    concurrently as long as they do not write the same buffers.
+ *  - Every argument check runs on the host before any HIP call and returns
+ *    a status; nothing aborts.  A failed kernel launch returns TQ_EDEVICE.
+ *    Non-finite inputs are not checked and give unspecified codes.
+ *  - Kernels exist for head_dim 128 and sketch size 128 (the shapes of the
+ *    model families the pages name); other powers of two are rejected with
+ *    TQ_EUNSUPPORTED.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1u
+#define TQ_BLOCK_TOKENS 128   /* positions per cache block */
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* malformed argument (null, misaligned, out of range) */
+  TQ_EUNSUPPORTED = 2,  /* well formed but no kernel for it (e.g. head_dim != 128) */
+  TQ_ECAPACITY = 3,     /* append would pass max_ctx */
+  TQ_EWORKSPACE = 4,    /* workspace or params buffer too small */
+  TQ_EDEVICE = 5        /* a HIP call or kernel launch failed */
+} tq_status;
+
+/* Per-tensor cache codecs.  K and V are chosen separately, as the article's
+ * llama-server example does with -ctk / -ctv. */
+typedef enum {
+  TQ_CODEC_RAW_F32 = 0,     /* bypass: fp32 copy (exact attention) */
+  TQ_CODEC_POLAR = 1,       /* rotation + fp16 radius + b-bit angle codes */
+  TQ_CODEC_POLAR_QJL = 2,   /* POLAR + 1-bit QJL sketch of the residual (K only) */
+  TQ_CODEC_Q8_BLOCK32 = 3   /* 8-bit symmetric per-32 block, fp16 scale, unrotated
+                               (the article's "K in q8_0"; K only) */
+} tq_codec;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* dequantize flags */
+#define TQ_DEQ_QJL 1u   /* keys: add the QJL correction (x_tilde) */
+
+typedef struct tq_config {
+  uint32_t abi_version;   /* must equal TQ_ABI_VERSION */
+  int32_t head_dim;       /* d: 128 */
+  int32_t n_q_heads;      /* query heads; a multiple of n_kv_heads (GQA group G = n_q/n_kv <= 16) */
+  int32_t n_kv_heads;     /* query head h reads KV head h / G */
+  int32_t batch;          /* sequences */
+  int32_t max_ctx;        /* capacity per sequence, in positions */
+  int32_t k_codec;        /* tq_codec */
+  int32_t k_bits;         /* POLAR*: 2..4; Q8: 8; RAW: 32 */
+  int32_t qjl_m;          /* POLAR_QJL: sketch rows (128); otherwise 0 */
+  int32_t v_codec;        /* TQ_CODEC_RAW_F32 or TQ_CODEC_POLAR */
+  int32_t v_bits;         /* POLAR: 2..4; RAW: 32 */
+  int32_t decode_chunk;   /* positions per split-K workgroup, a multiple of 128; 0 = automatic */
+  uint64_t seed;          /* rotation signs and sketch are drawn from (seed, layer) */
+  int32_t layer;
+  int32_t reserved;       /* must be 0 */
+} tq_config;
+
+/* Text for a status code (static storage). */
+const char* tq_status_string(tq_status s);
+
+/* Sizes in bytes of the K and V caches for cfg (host, pure).  Layout of one
+ * cache: [batch][n_kv][ceil(max_ctx/128)][block]; block = 128 positions of one
+ * (sequence, KV head):
+ *   K POLAR / POLAR_QJL (b bits, m rows): b code planes u32[d/32][128] (bit e
+ *     of word [j][t] = bit p of the code of coordinate 32j+e of position t),
+ *     then (QJL) the sign plane u32[m/32][128], then fp16 radius[128], then
+ *     (QJL) fp16 residual norm[128];
+ *   K Q8: int8[128][d] then fp16 scale[128][d/32];
+ *   V POLAR (b bits): b planes u32[4][d] (bit e of word [j][i] = bit p of the
+ *     code of coordinate i of position 32j+e), then fp16 radius[128];
+ *   RAW: fp32[128][d].
+ * Per position and head: K 3b+QJL 68 B, 4b+QJL 84 B, q8 136 B; V b bits
+ * 16b+2 B (d = 128). */
+tq_status tq_cache_bytes(const tq_config* cfg, uint64_t* k_bytes, uint64_t* v_bytes);
+
+/* Size of the per-layer parameter image (rotation signs, sketch, codebooks). */
+tq_status tq_params_bytes(const tq_config* cfg, uint64_t* bytes);
+
+/* Build the parameter image in host memory `host_params` (>= tq_params_bytes).
+ * Contents: signs D_K, D_V (+/-1, fp32[d]) drawn from counter-form SplitMix64
+ * keyed by (seed, layer); the Gaussian sketch S (fp32[m][d], Box-Muller) and
+ * its transpose; Lloyd-Max codebooks for the law of a rotated unit vector's
+ * coordinate (fp16-exact centroids, fp32 midpoint boundaries).  This is the
+ * "distribution known in advance" of the PolarQuant paragraph and the fixed
+ * transform of "Principe de quantification sans calibration".  Pure host. */
+tq_status tq_params_host(const tq_config* cfg, void* host_params, uint64_t bytes);
+
+/* Same image, copied to device memory `params` (>= tq_params_bytes) on
+ * `stream`; returns after the copy has completed. */
+tq_status tq_init_params(const tq_config* cfg, void* params, uint64_t bytes, void* stream);
+
+/* Quantise n_new new positions per sequence and store them at positions
+ * seq_lens[b] .. seq_lens[b]+n_new-1 of every sequence b.
+ *   params    device, from tq_init_params for the same cfg
+ *   k_cache, v_cache  device, tq_cache_bytes each, 16-byte aligned
+ *   seq_lens  device int32[batch]; read only (the caller advances it)
+ *   max_seq_len  host bound: every seq_lens[b] <= max_seq_len; the call
+ *             fails with TQ_ECAPACITY if max_seq_len + n_new > max_ctx
+ *   k_new, v_new  device [batch][n_new][n_kv][d] in in_dtype (tq_dtype)
+ * Per vector: y = H (D . x) (raw Walsh-Hadamard, fixed stage order), radius
+ * n = |x| -> fp16, angle codes = nearest codebook centroid of y/n (bit
+ * planes); keys with QJL add r = y - n16 C[code], its norm |r|/sqrt(d) ->
+ * fp16 and the m sign bits of S r.  Q8 keys and RAW tensors are stored as
+ * described at tq_cache_bytes.  Positions of a 32-position group that this
+ * call does not write keep their bits.  n_new == 0 is a no-op that does not
+ * examine the buffer pointers. */
+tq_status tq_quantize_append(const tq_config* cfg, const void* params, void* k_cache,
+                             void* v_cache, const int32_t* seq_lens, int32_t max_seq_len,
+                             const void* k_new, const void* v_new, int32_t in_dtype,
+                             int32_t n_new, void* stream);
+
+/* Workspace for tq_decode_attention with sequences up to max_seq_len. */
+tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, uint64_t* bytes);
+
+/* Decode attention: one query per sequence over positions [0, seq_lens[b]).
+ *   q        device fp32 [batch][n_q][d]
+ *   out      device fp32 [batch][n_q][d]
+ *   logits   device fp32 [batch][n_q][max_ctx] or NULL: pre-softmax scaled
+ *            logits of positions [0, seq_lens[b]) (others untouched)
+ *   workspace device, >= tq_decode_workspace_bytes(cfg, max_seq_len), and
+ *            zero-filled before its first use; every call leaves its
+ *            completion counters at zero again.
+ * Logit of position t (scale 1/sqrt(d)), for POLAR_QJL keys the
+ * QJL-corrected estimator <q, x_hat> + rho sqrt(pi/2)/m <S R q, sign(S r)>;
+ * softmax over all stored positions; output sum_t p_t v_hat_t.  An empty
+ * sequence gives a zero output.  Calls sharing a workspace must not overlap. */
+tq_status tq_decode_attention(const tq_config* cfg, const void* params, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens, int32_t max_seq_len,
+                              const float* q, float* out, float* logits, void* workspace,
+                              uint64_t workspace_bytes, void* stream);
+
+/* Dequantise positions [start, start+count) of sequence b.
+ *   k_out, v_out  device fp32 [count][n_kv][d]; either may be NULL
+ *   flags         TQ_DEQ_QJL: keys return x_tilde = x_hat + rho sqrt(pi/2)/m
+ *                 R^T S^T sign, whose inner product with q is the estimator
+ * Fails with TQ_EINVAL when start + count > max_ctx. */
+tq_status tq_dequantize(const tq_config* cfg, const void* params, const void* k_cache,
+                        const void* v_cache, int32_t b, int32_t start, int32_t count,
+                        float* k_out, float* v_out, uint32_t flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,0 +1,167 @@
+"""Host-only checks of the C ABI: the library loads and exports every
+declared symbol; size queries and host-built parameters agree with the
+oracle's independent implementation; argument checks return the documented
+status before any device call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    from compressed_decode_attention_quantize_amd import build_lib, tq
+    if not os.path.exists(build_lib.LIB):
+        build_lib.build()
+    tq.lib()
+    return tq
+
+
+def test_every_declared_symbol_is_exported(tq):
+    hdr = open(os.path.join(ROOT, "include", "tq.h")).read()
+    names = set(re.findall(r"^(?:tq_status|const char\*)\s+(tq_\w+)\(", hdr, re.M))
+    assert len(names) == 9
+    L = tq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_config_struct_layout(tq):
+    assert ctypes.sizeof(tq.Config) == 64
+    assert tq.Config.seed.offset == 48
+
+
+CFGS = [
+    dict(k_codec=2, k_bits=3, v_codec=1, v_bits=3),
+    dict(k_codec=2, k_bits=3, v_codec=1, v_bits=2),
+    dict(k_codec=2, k_bits=4, v_codec=1, v_bits=4),
+    dict(k_codec=3, k_bits=8, v_codec=1, v_bits=2),
+    dict(k_codec=1, k_bits=2, v_codec=0, v_bits=32),
+    dict(k_codec=0, k_bits=32, v_codec=0, v_bits=32),
+]
+
+
+@pytest.mark.parametrize("kw", CFGS)
+def test_sizes_match_oracle(tq, orc, kw):
+    cfg = tq.make_config(n_q_heads=32, n_kv_heads=8, batch=3, max_ctx=1000, **kw)
+    s = orc.make_spec(n_q=32, n_kv=8, batch=3, max_ctx=1000, k_codec=kw["k_codec"], k_bits=kw["k_bits"],
+                      v_codec=kw["v_codec"], v_bits=kw["v_bits"])
+    z = orc.spec_sizes(s)
+    assert tq.cache_bytes(cfg) == (z["k_cache"], z["v_cache"])
+
+
+@pytest.mark.parametrize("kw", CFGS[:5])
+@pytest.mark.parametrize("seed,layer", [(42, 0), (42, 31), (7, 5)])
+def test_params_match_oracle_tables(tq, orc, kw, seed, layer):
+    cfg = tq.make_config(seed=seed, layer=layer, **kw)
+    img = tq.params_host(cfg)
+    f = img.view(np.float32)
+    d = 128
+    s = orc.make_spec(k_codec=kw["k_codec"], k_bits=kw["k_bits"], v_codec=kw["v_codec"], v_bits=kw["v_bits"])
+    P = orc.Params(s, seed, layer)
+    m = 128 if kw["k_codec"] == 2 else 0
+    assert np.array_equal(f[0:d], P.DK) and np.array_equal(f[d:2 * d], P.DV)
+    off = 2 * d
+    if m:
+        S = f[off:off + m * d].reshape(m, d)
+        ST = f[off + m * d:off + 2 * m * d].reshape(d, m)
+        assert np.array_equal(S, P.S)
+        assert np.array_equal(ST, P.S.T)
+    off += 2 * m * d
+    ck, kb, cv, vb = (f[off + 16 * i: off + 16 * (i + 1)] for i in range(4))
+    if kw["k_codec"] in (1, 2):
+        L = 1 << kw["k_bits"]
+        assert np.array_equal(ck[:L], orc.f16_to_f32(P.ck16))
+        assert np.array_equal(kb[:L - 1], P.kbounds)
+    if kw["v_codec"] == 1:
+        L = 1 << kw["v_bits"]
+        assert np.array_equal(cv[:L], orc.f16_to_f32(P.cv16))
+        assert np.array_equal(vb[:L - 1], P.vbounds)
+
+
+def _cfg(tq, **kw):
+    return tq.make_config(**kw)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 2, 1), ("head_dim", 100, 1), ("head_dim", 64, 2), ("head_dim", 512, 1),
+    ("n_q_heads", 7, 1), ("n_kv_heads", 0, 1), ("batch", 0, 1), ("max_ctx", 0, 1),
+    ("k_bits", 9, 1), ("k_bits", 5, 2), ("qjl_m", 96, 1), ("qjl_m", 64, 2), ("v_codec", 2, 2),
+    ("v_codec", 3, 2), ("v_codec", 9, 1), ("k_codec", 7, 1), ("decode_chunk", 100, 1),
+    ("reserved", 1, 1), ("v_bits", 5, 2),
+])
+def test_config_validation(tq, field, value, status):
+    cfg = _cfg(tq)
+    setattr(cfg, field, value)
+    k, v = ctypes.c_uint64(), ctypes.c_uint64()
+    assert tq.lib().tq_cache_bytes(ctypes.byref(cfg), ctypes.byref(k), ctypes.byref(v)) == status
+
+
+def test_group_too_large_is_unsupported(tq):
+    cfg = _cfg(tq, n_q_heads=34, n_kv_heads=2)
+    n = ctypes.c_uint64()
+    assert tq.lib().tq_params_bytes(ctypes.byref(cfg), ctypes.byref(n)) == tq.EUNSUPPORTED
+
+
+FAKE = 1 << 20   # aligned, never dereferenced: every case below fails before a device call
+
+
+def test_append_argument_checks(tq):
+    L = tq.lib()
+    cfg = _cfg(tq, max_ctx=256)
+    p = ctypes.c_void_p
+    args = lambda **o: dict(dict(params=p(FAKE), kc=p(FAKE), vc=p(FAKE), lens=p(FAKE), maxlen=0, k=p(FAKE),
+                                 v=p(FAKE), dt=tq.F32, n=16), **o)
+
+    def call(a):
+        return L.tq_quantize_append(ctypes.byref(cfg), a["params"], a["kc"], a["vc"], a["lens"], a["maxlen"],
+                                    a["k"], a["v"], a["dt"], a["n"], None)
+    assert call(args(params=None)) == tq.EINVAL
+    assert call(args(kc=p(FAKE + 4))) == tq.EINVAL       # cache must be 16-byte aligned
+    assert call(args(dt=5)) == tq.EINVAL
+    assert call(args(n=-1)) == tq.EINVAL
+    assert call(args(maxlen=250, n=7)) == tq.ECAPACITY
+    assert call(args(maxlen=0, n=257)) == tq.ECAPACITY
+    assert call(args(n=0)) == tq.OK                      # no-op, no launch
+
+
+def test_decode_argument_checks(tq):
+    L = tq.lib()
+    cfg = _cfg(tq, max_ctx=4096)
+    need = tq.decode_workspace_bytes(cfg, 4096)
+    p = ctypes.c_void_p
+
+    def call(ws_bytes=need, maxlen=4096, q=p(FAKE), ws=p(FAKE)):
+        return L.tq_decode_attention(ctypes.byref(cfg), p(FAKE), p(FAKE), p(FAKE), p(FAKE), maxlen, q, p(FAKE),
+                                     None, ws, ws_bytes, None)
+    assert call(ws_bytes=need - 1) == tq.EWORKSPACE
+    assert call(maxlen=4097) == tq.EINVAL
+    assert call(q=None) == tq.EINVAL
+    assert call(ws=p(FAKE + 64)) == tq.EINVAL
+
+
+def test_workspace_bound_covers_every_shorter_length(tq):
+    for batch, kv in [(1, 8), (16, 8), (1, 2)]:
+        cfg = _cfg(tq, n_q_heads=4 * kv, n_kv_heads=kv, batch=batch, max_ctx=1 << 20)
+        top = tq.decode_workspace_bytes(cfg, 1 << 20)
+        for L_ in [1, 127, 128, 129, 5000, 8192, 32768, 65 * 128, 1 << 19, 1 << 20]:
+            assert tq.decode_workspace_bytes(cfg, L_) <= top
+
+
+def test_dequantize_argument_checks(tq):
+    L = tq.lib()
+    cfg = _cfg(tq, max_ctx=256)
+    p = ctypes.c_void_p
+    assert L.tq_dequantize(ctypes.byref(cfg), p(FAKE), p(FAKE), p(FAKE), 1, 0, 4, p(FAKE), None, 0, None) == tq.EINVAL
+    assert L.tq_dequantize(ctypes.byref(cfg), p(FAKE), p(FAKE), p(FAKE), 0, 250, 7, p(FAKE), None, 0, None) == tq.EINVAL
+    assert L.tq_dequantize(ctypes.byref(cfg), p(FAKE), p(FAKE), p(FAKE), 0, 0, 4, p(FAKE), None, 2, None) == tq.EINVAL
+    assert L.tq_dequantize(ctypes.byref(cfg), p(FAKE), p(FAKE), p(FAKE), 0, 0, 0, p(FAKE), None, 0, None) == tq.OK
+
+
+def test_status_strings(tq):
+    assert tq.status_string(tq.ECAPACITY) == "append exceeds cache capacity"
+    assert tq.status_string(99) == "unknown status"

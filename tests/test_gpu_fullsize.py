@@ -1,0 +1,99 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (one prefill append of the whole context, then decode), on
+sampled (sequence, KV head) pairs that the oracle recomputes from the same
+inputs: every record of the pair bit-exact (counted sign exceptions), the
+pair's query heads' logits and outputs to the bars."""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+from parity_util import (THREADS, check_logits, check_out, compare_records, oracle, oracle_quantize_threaded,
+                         spec_of, synth, tq, widen_np)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sub_records(cfg, layer, b, h, n):
+    """GPU records of one (sequence, KV head), unpacked by the oracle."""
+    sub = spec_of(cfg, batch=1, n_kv=1, n_q=cfg.n_q_heads // cfg.n_kv_heads)
+    nb = (cfg.max_ctx + 127) // 128
+    kb, vb = tq.cache_bytes(cfg)
+    kslot = kb // (cfg.batch * cfg.n_kv_heads)
+    vslot = vb // (cfg.batch * cfg.n_kv_heads)
+    idx = b * cfg.n_kv_heads + h
+    kc = layer.k_cache[idx * kslot:(idx + 1) * kslot].cpu().numpy()
+    vc = layer.v_cache[idx * vslot:(idx + 1) * vslot].cpu().numpy()
+    assert kslot == nb * 128 * oracle.spec_sizes(sub)["k_record"]
+    return sub, oracle.unpack_cache(sub, kc, vc, np.array([n], np.int32))
+
+
+def _oracle_decode_threaded(sub, P, R, n, qh):
+    G = qh.shape[0]
+    with cf.ThreadPoolExecutor(min(G, THREADS)) as ex:
+        futs = [ex.submit(oracle.decode, sub, P, R, [n], qh[None], [(0, g)], True) for g in range(G)]
+        res = [f.result() for f in futs]
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
+def _check_pair(cfg, layer, k, v, q, lg, out, b, h, n, label):
+    G = cfg.n_q_heads // cfg.n_kv_heads
+    sub, Gr = _sub_records(cfg, layer, b, h, n)
+    P = oracle.Params(sub, cfg.seed, cfg.layer)
+    kn = widen_np(k[b, :n, h])[:, None, :]
+    vn = widen_np(v[b, :n, h])[:, None, :]
+    R = oracle_quantize_threaded(sub, P, kn, vn, n)
+    st = compare_records(sub, P, Gr, R, [n], kn[None], label)
+    qh = q[b, h * G:(h + 1) * G].cpu().numpy()
+    ref_out, ref_lg = _oracle_decode_threaded(sub, P, R, n, qh)
+    skip = None
+    if sub.k_codec == oracle.POLAR_QJL:
+        differ = (Gr.signs[:n] != R.signs[:n]).any(axis=1)
+        skip = np.repeat(differ[None], G, axis=0)
+    worst = check_logits(lg[b, h * G:(h + 1) * G].cpu().numpy(), ref_lg, n, label, skip=skip)
+    err = check_out(out[b, h * G:(h + 1) * G].cpu().numpy(), ref_out, label)
+    print(f"{label}: records={st['records']} sign exceptions={st['sign_mismatch']}/{st['sign_total']} "
+          f"worst logit rel={worst:.2e} max out err={err:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("wi,wname", [(i, n) for i, n in enumerate(synth.ORDER) if n != "serving_b16_ctx8k"])
+def test_full_size_prefill_then_decode(wi, wname):
+    w = synth.WORKLOADS[wname]
+    print(f"[fullsize] {wname}", flush=True)
+    cfg = tq.config_for(w, seed=42, layer=0)
+    L = tq.KVLayer(cfg, DEV)
+    k, v = synth.make_kv(w, w.ctx, seed=1000 + wi, device=DEV)
+    q = synth.make_q(w, seed=2000 + wi, device=DEV)
+    L.append(k, v)
+    lg = torch.full((w.batch, w.n_q, w.ctx), float("nan"), device=DEV)
+    out = L.decode(q, logits=lg)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(wi)
+    h = int(rng.integers(0, w.n_kv))
+    _check_pair(cfg, L, k, v, q, lg, out, 0, h, w.ctx, f"{wname} kv={h}")
+
+
+def test_full_size_serving_steps():
+    """Batched serving: 16 x 8192 prefill, then 64 steps of one appended
+    position per sequence followed by decode; steps 0, 31 and 63 checked on
+    two sampled (sequence, KV head) pairs."""
+    wi, w = 2, synth.WORKLOADS["serving_b16_ctx8k"]
+    cfg = tq.config_for(w, seed=42, layer=0, max_ctx=w.ctx + w.steps)
+    L = tq.KVLayer(cfg, DEV)
+    n_tot = w.ctx + w.steps
+    k, v = synth.make_kv(w, n_tot, seed=1000 + wi, device=DEV)
+    L.append(k[:, :w.ctx].contiguous(), v[:, :w.ctx].contiguous())
+    pairs = [(3, 5), (11, 0)]
+    for step in range(w.steps):
+        L.append(k[:, w.ctx + step:w.ctx + step + 1].contiguous(), v[:, w.ctx + step:w.ctx + step + 1].contiguous())
+        q = synth.make_q(w, seed=5000 + step, device=DEV)
+        lg = torch.full((w.batch, w.n_q, cfg.max_ctx), float("nan"), device=DEV)
+        out = L.decode(q, logits=lg)
+        if step in (0, 31, 63):
+            torch.cuda.synchronize()
+            n = w.ctx + step + 1
+            for b, h in pairs:
+                _check_pair(cfg, L, k, v, q, lg, out, b, h, n, f"serving step {step} b={b} kv={h}")

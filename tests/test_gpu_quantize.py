@@ -1,0 +1,173 @@
+"""GPU parity of tq_quantize_append and tq_dequantize against the oracle,
+through the C ABI (binding = argument marshalling only)."""
+import numpy as np
+import pytest
+import torch
+
+from parity_util import (compare_records, gpu_records, oracle, oracle_quantize, spec_of, synth, tq,
+                         upload_cache, widen_np)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _layer(w, ctx, batch, layer_id=3, chunk=0):
+    ws = synth.with_ctx(w, ctx, batch=batch)
+    cfg = tq.config_for(ws, seed=42, layer=layer_id, decode_chunk=chunk)
+    return ws, cfg, tq.KVLayer(cfg, DEV)
+
+
+@pytest.mark.parametrize("wi,wname", list(enumerate(synth.ORDER)))
+def test_append_matches_oracle_ragged_chunks(wi, wname):
+    """Five appends of 1, 31, 33, 128 and 107 positions (block and group
+    boundaries, ragged tail) into two sequences."""
+    ws, cfg, L = _layer(synth.WORKLOADS[wname], 300, 2)
+    print(f"[append] {wname} cfg k={cfg.k_codec}/{cfg.k_bits} v={cfg.v_codec}/{cfg.v_bits}", flush=True)
+    k, v = synth.make_kv(ws, 300, seed=1000 + wi, batch=2)
+    pos = 0
+    for n in (1, 31, 33, 128, 107):
+        L.append(k[:, pos:pos + n].to(DEV).contiguous(), v[:, pos:pos + n].to(DEV).contiguous())
+        pos += n
+    torch.cuda.synchronize()
+    spec = spec_of(cfg)
+    P = oracle.Params(spec, 42, 3)
+    kn, vn = widen_np(k), widen_np(v)
+    R = oracle_quantize(spec, P, kn, vn, [300, 300])
+    G = gpu_records(spec, L.k_cache, L.v_cache, [300, 300])
+    st = compare_records(spec, P, G, R, [300, 300], kn, wname)
+    print(st)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_input_dtypes(dtype):
+    w = synth.WORKLOADS["tiny_b1_ctx1k_h8x2"]
+    ws, cfg, L = _layer(w, 256, 1)
+    k, v = synth.make_kv(ws, 256, seed=7)
+    k, v = k.to(dtype), v.to(dtype)
+    L.append(k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    spec = spec_of(cfg)
+    P = oracle.Params(spec, 42, 3)
+    kn, vn = widen_np(k), widen_np(v)
+    R = oracle_quantize(spec, P, kn, vn, [256])
+    compare_records(spec, P, gpu_records(spec, L.k_cache, L.v_cache, [256]), R, [256], kn, str(dtype))
+
+
+@pytest.mark.parametrize("wname", ["llama8b_b1_ctx32k", "cmdr104b_b1_ctx128k"])
+def test_offset_append_keeps_other_positions(wname):
+    """Sequences at different lengths; positions this call does not write keep
+    their bytes (value words are shared by 32 positions)."""
+    ws = synth.with_ctx(synth.WORKLOADS[wname], 300, batch=2)
+    cfg = tq.config_for(ws, seed=42, layer=1)
+    kb, vb = tq.cache_bytes(cfg)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    kc0 = torch.randint(0, 256, (kb,), generator=g, dtype=torch.uint8)
+    vc0 = torch.randint(0, 256, (vb,), generator=g, dtype=torch.uint8)
+    spec = spec_of(cfg)
+    # make the pre-existing fp16 fields finite: rewrite them through the oracle's own packer
+    pre = oracle.unpack_cache(spec, kc0.numpy(), vc0.numpy(), np.array([300, 300], np.int32))
+    for a in (pre.kn16, pre.rho16, pre.vn16, pre.s16):
+        if a.ndim and a.size > 1:
+            a &= 0x3bff
+    kc_np, vc_np = kc0.numpy().copy(), vc0.numpy().copy()
+    oracle.lib().or_pack_cache(oracle.ctypes.byref(spec), np.array([300, 300], np.int32),
+                               oracle.ctypes.byref(pre._k()), oracle.ctypes.byref(pre._v()),
+                               oracle._ptr(kc_np), oracle._ptr(vc_np))
+    k_cache, v_cache = upload_cache(kc_np, vc_np, DEV)
+    params = tq.init_params(cfg, DEV)
+    seq_lens = torch.tensor([0, 37], dtype=torch.int32, device=DEV)
+    k, v = synth.make_kv(ws, 200, seed=9, batch=2)
+    tq.quantize_append(cfg, params, k_cache, v_cache, seq_lens, 37, k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    G = gpu_records(spec, k_cache, v_cache, [300, 300])
+    P = oracle.Params(spec, 42, 1)
+    R = oracle.Records(spec)
+    kn, vn = widen_np(k), widen_np(v)
+    oracle.quantize_into(spec, P, R, kn[0], vn[0], 0, 0)
+    oracle.quantize_into(spec, P, R, kn[1], vn[1], 1, 37)
+    # written ranges
+    written = np.zeros(R.n, bool)
+    untouched = np.zeros(R.n, bool)
+    for b, (lo, hi) in enumerate([(0, 200), (37, 237)]):
+        for pos in range(300):
+            sl = slice((b * 300 + pos) * spec.n_kv, (b * 300 + pos + 1) * spec.n_kv)
+            (written if lo <= pos < hi else untouched)[sl] = True
+    for name in ("kcodes", "kn16", "rho16", "k8", "s16", "vcodes", "vn16"):
+        a_g, a_r, a_p = getattr(G, name), getattr(R, name), getattr(pre, name)
+        if a_g.shape[0] != R.n:
+            continue
+        assert np.array_equal(a_g[written], a_r[written]), name
+        assert np.array_equal(a_g[untouched], a_p[untouched]), f"{name} changed outside the append"
+    if spec.k_codec == oracle.POLAR_QJL:
+        assert np.array_equal(G.signs[untouched], pre.signs[untouched])
+        assert (G.signs[written] != R.signs[written]).mean() <= 1e-4
+
+
+def test_incremental_equals_one_shot():
+    w = synth.WORKLOADS["serving_b16_ctx8k"]
+    ws = synth.with_ctx(w, 520, batch=3)
+    cfg = tq.config_for(ws, seed=42, layer=0)
+    A, B = tq.KVLayer(cfg, DEV), tq.KVLayer(cfg, DEV)
+    k, v = synth.make_kv(ws, 520, seed=11, batch=3)
+    k, v = k.to(DEV), v.to(DEV)
+    A.append(k, v)
+    pos = 0
+    for n in (3, 29, 64, 1, 1, 200, 95, 127):
+        B.append(k[:, pos:pos + n].contiguous(), v[:, pos:pos + n].contiguous())
+        pos += n
+    torch.cuda.synchronize()
+    assert pos == 520
+    assert torch.equal(A.k_cache, B.k_cache) and torch.equal(A.v_cache, B.v_cache)
+
+
+def test_capacity_and_noop():
+    w = synth.WORKLOADS["tiny_b1_ctx1k_h8x2"]
+    ws, cfg, L = _layer(w, 300, 1)
+    k, v = synth.make_kv(ws, 300, seed=2)
+    before = L.k_cache.clone()
+    L.append(k[:, :0].to(DEV).contiguous(), v[:, :0].to(DEV).contiguous())   # n_new = 0
+    torch.cuda.synchronize()
+    assert torch.equal(before, L.k_cache)
+    L.append(k.to(DEV), v.to(DEV))                                            # fills to capacity
+    with pytest.raises(tq.TqError) as e:
+        L.append(k[:, :1].to(DEV).contiguous(), v[:, :1].to(DEV).contiguous())
+    assert e.value.status == tq.ECAPACITY
+
+
+@pytest.mark.parametrize("wname", synth.ORDER)
+@pytest.mark.parametrize("qjl", [False, True])
+def test_dequantize_matches_oracle(wname, qjl):
+    w = synth.WORKLOADS[wname]
+    if qjl and w.k_codec != synth.POLAR_QJL:
+        pytest.skip("QJL correction applies to QJL keys only")
+    ws = synth.with_ctx(w, 200, batch=2)
+    cfg = tq.config_for(ws, seed=42, layer=2)
+    spec = spec_of(cfg)
+    P = oracle.Params(spec, 42, 2)
+    k, v = synth.make_kv(ws, 200, seed=21, batch=2)
+    kn, vn = widen_np(k), widen_np(v)
+    R = oracle_quantize(spec, P, kn, vn, [200, 200])
+    kc, vc = oracle.pack_cache(spec, R, [200, 200])
+    k_cache, v_cache = upload_cache(kc, vc, DEV)
+    params = tq.init_params(cfg, DEV)
+    start, count = 57, 140
+    ko = torch.empty(count, cfg.n_kv_heads, 128, device=DEV)
+    vo = torch.empty(count, cfg.n_kv_heads, 128, device=DEV)
+    tq.dequantize(cfg, params, k_cache, v_cache, 1, start, count, ko, vo, qjl=qjl)
+    torch.cuda.synchronize()
+    ko, vo = ko.cpu().numpy(), vo.cpu().numpy()
+    for t in range(count):
+        for h in range(cfg.n_kv_heads):
+            i = R.rec_index(1, start + t, h)
+            if spec.k_codec == oracle.POLAR_QJL and qjl:
+                kr = oracle.dequant_polar_qjl(P.DK, P.ck16, P.S, R.kcodes[i], R.kn16[i], R.signs[i], R.rho16[i])
+            elif spec.k_codec in (oracle.POLAR, oracle.POLAR_QJL):
+                kr = oracle.dequant_polar(P.DK, P.ck16, R.kcodes[i], R.kn16[i])
+            elif spec.k_codec == oracle.Q8_BLOCK32:
+                kr = oracle.dequant_q8(R.k8[i], R.s16[i])
+            else:
+                kr = R.kraw[i].astype(np.float64)
+            vr = (oracle.dequant_polar(P.DV, P.cv16, R.vcodes[i], R.vn16[i]) if spec.v_codec == oracle.POLAR
+                  else R.vraw[i].astype(np.float64))
+            for got, ref in ((ko[t, h], kr), (vo[t, h], vr)):
+                assert np.max(np.abs(got - ref)) <= 1e-5 * max(np.linalg.norm(ref), 1e-30)
