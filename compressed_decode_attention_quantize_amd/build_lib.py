@@ -27,6 +27,7 @@ UNITS = [
     ("tq_host.cpp", []),
     ("tq_quant.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
+    ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
     ("tq_dequant.hip", []),
 ]
 

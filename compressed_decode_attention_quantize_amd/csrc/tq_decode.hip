@@ -27,6 +27,7 @@
 
 #include <hip/hip_fp16.h>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -45,23 +46,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
   return v;
-}
-
-// In-place raw FWHT over buf[G][128] (shared), all threads participate.
-__device__ void block_fwht(float* buf, int G) {
-  for (int h = 1; h < kD; h <<= 1) {
-    __syncthreads();
-    for (int k = threadIdx.x; k < G * (kD / 2); k += kThreads) {
-      const int g = k / (kD / 2);
-      const int r = k % (kD / 2);
-      const int lo = (r / h) * 2 * h + (r % h);
-      float* v = buf + g * kD;
-      const float x = v[lo], y = v[lo + h];
-      v[lo] = x + y;
-      v[lo + h] = x - y;
-    }
-  }
-  __syncthreads();
 }
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
@@ -97,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     m_run[tid] = -INFINITY;
     l_run[tid] = 0.0f;
   }
-  if (a.k_codec == POLAR || a.k_codec == POLAR_QJL) block_fwht(qv, G);   // q_raw = H D_K q
+  if (a.k_codec == POLAR || a.k_codec == POLAR_QJL) block_fwht128(qv, G, kThreads);   // q_raw = H D_K q
   __syncthreads();
   if (a.k_codec == POLAR_QJL) {
     for (int k = tid; k < G * kM; k += kThreads) {
@@ -147,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
             for (int p = 0; p < 4; ++p)
-              if (p < kbits) w[p] = planes[p * plane_words + j * kBlock + t];
+              if (p < kbits) w[p] = planes[p * plane_words + j * kBlock + slot_of(t)];
             for (int e = 0; e < 32; ++e) {
               int c = 0;
 #pragma unroll
@@ -166,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           if (a.k_codec == POLAR_QJL) {
             const uint32_t* sg = reinterpret_cast<const uint32_t*>(after);
             for (int j = 0; j < kM / 32; ++j) {
-              const uint32_t w = sg[j * kBlock + t];
+              const uint32_t w = sg[j * kBlock + slot_of(t)];
               for (int e = 0; e < 32; ++e) {
                 const bool pos = (w >> e) & 1u;
                 const int r = j * 32 + e;
@@ -181,9 +165,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
               }
             }
             after += 4 * (kM / 32) * kBlock;
-            rho = f16_to_f32(reinterpret_cast<const uint16_t*>(after + 2 * kBlock)[t]);
+            rho = f16_to_f32(reinterpret_cast<const uint16_t*>(after + 2 * kBlock)[slot_of(t)]);
           }
-          const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(after)[t]);
+          const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(after)[slot_of(t)]);
 #pragma unroll
           for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = alpha * n16 * cdot[u] + beta * rho * sdot[u];
         } else if (a.k_codec == Q8_BLOCK32) {
@@ -248,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       float vr0 = 1.0f, vr1 = 1.0f;
       if (a.v_codec == POLAR) {
         const uint16_t* vn = reinterpret_cast<const uint16_t*>(vb + 4 * vbits * 4 * kD);
-        vr0 = (lane < n_t) ? f16_to_f32(vn[lane]) : 0.0f;
-        vr1 = (lane + 64 < n_t) ? f16_to_f32(vn[lane + 64]) : 0.0f;
+        vr0 = (lane < n_t) ? f16_to_f32(vn[slot_of(lane)]) : 0.0f;
+        vr1 = (lane + 64 < n_t) ? f16_to_f32(vn[slot_of(lane + 64)]) : 0.0f;
       }
       pt[g * kBlock + lane] = p0 * vr0;
       pt[g * kBlock + lane + 64] = p1 * vr1;
@@ -304,57 +288,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   // --------------------------------------------------------- partials
-  const int64_t pstride = kD + 2;
+  const int64_t pstride = kPartialStride;
 #pragma unroll
   for (int u = 0; u < kMaxGroup / 2; ++u) {
     const int g = hpar + 2 * u;
     if (g < G) {
       float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + g) * a.n_splits + split) * pstride;
-      pp[ci] = acc[u];
+      store_coherent(pp + ci, acc[u]);
       if (ci == 0) {
-        pp[kD] = m_run[g];
-        pp[kD + 1] = l_run[g];
+        store_coherent(pp + kD, m_run[g]);
+        store_coherent(pp + kD + 1, l_run[g]);
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(a.counters + b * a.n_kv + h, 1u);
-    s_last = (prev == static_cast<uint32_t>(a.n_splits - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (!arrive_last(a.counters + b * a.n_kv + h, a.n_splits, &s_last)) return;
 
-  // ---------------------------------------------------------- combine
-  float* obuf = qv;   // reuse: [G][128]
-  for (int k = tid; k < G * kD; k += kThreads) {
-    const int g = k / kD, i = k % kD;
-    const float* pp = a.partials + (static_cast<int64_t>(b) * a.n_q + h * G + g) * a.n_splits * pstride;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, __builtin_nontemporal_load(pp + s * pstride + kD));
-    float L = 0.0f, A = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.n_splits; ++s) {
-        const float ms = __builtin_nontemporal_load(pp + s * pstride + kD);
-        if (ms == -INFINITY) continue;
-        const float w = __expf(ms - M);
-        L = fmaf(__builtin_nontemporal_load(pp + s * pstride + kD + 1), w, L);
-        A = fmaf(__builtin_nontemporal_load(pp + s * pstride + i), w, A);
-      }
-    }
-    obuf[k] = (L > 0.0f) ? A / L : 0.0f;
-  }
-  if (a.v_codec == POLAR) block_fwht(obuf, G);   // H acc; D_V and 1/d below
-  __syncthreads();
-  for (int k = tid; k < G * kD; k += kThreads) {
-    const int g = k / kD, i = k % kD;
-    float v = obuf[k];
-    if (a.v_codec == POLAR) v = v * a.tb.dv[i] * (1.0f / static_cast<float>(kD));
-    a.out[(static_cast<int64_t>(b) * a.n_q + h * G + g) * kD + i] = v;
-  }
-  if (tid == 0) a.counters[b * a.n_kv + h] = 0u;
+  combine_splits(a, b, h, qv, kThreads);
 }
 
 }  // namespace

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   const int k = item / a.n_kv;
   const int pos = a.start + k;
   const int t = pos % kBlock;
+  const int sl = slot_of(t);
   const int64_t slot = (static_cast<int64_t>(a.b) * a.n_kv + h) * a.n_blocks + pos / kBlock;
   const int64_t out_idx = (static_cast<int64_t>(k) * a.n_kv + h) * kD;
   const float inv_d = 1.0f / static_cast<float>(kD);
@@ -71,13 +72,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         if (p < a.k_bits) {
-          c_lo |= ((planes[p * plane_words + (lane >> 5) * kBlock + t] >> (lane & 31)) & 1u) << p;
-          c_hi |= ((planes[p * plane_words + (2 + (lane >> 5)) * kBlock + t] >> (lane & 31)) & 1u) << p;
+          c_lo |= ((planes[p * plane_words + (lane >> 5) * kBlock + sl] >> (lane & 31)) & 1u) << p;
+          c_hi |= ((planes[p * plane_words + (2 + (lane >> 5)) * kBlock + sl] >> (lane & 31)) & 1u) << p;
         }
       }
       const uint8_t* after = kb + 4 * a.k_bits * plane_words;
       const uint8_t* norms = after + ((a.k_codec == POLAR_QJL) ? 4 * (kM / 32) * kBlock : 0);
-      const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(norms)[t]);
+      const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(norms)[sl]);
       lo = n16 * a.tb.ck[c_lo];
       hi = n16 * a.tb.ck[c_hi];
       wave_fwht128(lo, hi, lane);
@@ -87,14 +88,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         const uint32_t* sg = reinterpret_cast<const uint32_t*>(after);
         float u_lo = 0.0f, u_hi = 0.0f;
         for (int j = 0; j < kM; ++j) {
-          const bool pos_sign = (sg[(j >> 5) * kBlock + t] >> (j & 31)) & 1u;
+          const bool pos_sign = (sg[(j >> 5) * kBlock + sl] >> (j & 31)) & 1u;
           const float s_lo = a.tb.s[j * kD + lane];
           const float s_hi = a.tb.s[j * kD + lane + 64];
           u_lo += pos_sign ? s_lo : -s_lo;
           u_hi += pos_sign ? s_hi : -s_hi;
         }
         wave_fwht128(u_lo, u_hi, lane);
-        const float rho = f16_to_f32(reinterpret_cast<const uint16_t*>(norms + 2 * kBlock)[t]);
+        const float rho = f16_to_f32(reinterpret_cast<const uint16_t*>(norms + 2 * kBlock)[sl]);
         const float kq = rho * 1.2533141373155003f / static_cast<float>(kM) * 0.08838834764831845f;
         lo += kq * a.tb.dk[lane] * u_lo;
         hi += kq * a.tb.dk[lane + 64] * u_hi;
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
           c_hi |= ((planes[p * 4 * kD + (t >> 5) * kD + lane + 64] >> (t & 31)) & 1u) << p;
         }
       }
-      const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(vb + 4 * a.v_bits * 4 * kD)[t]);
+      const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(vb + 4 * a.v_bits * 4 * kD)[sl]);
       lo = n16 * a.tb.cv[c_lo];
       hi = n16 * a.tb.cv[c_hi];
       wave_fwht128(lo, hi, lane);

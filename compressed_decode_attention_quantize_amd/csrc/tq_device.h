@@ -1,0 +1,131 @@
+// tq_device.h -- small device helpers shared by the decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+// In-place raw FWHT over buf[rows][128] in shared memory; every thread of the
+// block participates (contains barriers).
+__device__ inline void block_fwht128(float* buf, int rows, int nthreads) {
+  for (int h = 1; h < kD; h <<= 1) {
+    __syncthreads();
+    for (int k = threadIdx.x; k < rows * (kD / 2); k += nthreads) {
+      const int g = k / (kD / 2);
+      const int r = k % (kD / 2);
+      const int lo = (r / h) * 2 * h + (r % h);
+      float* v = buf + g * kD;
+      const float x = v[lo], y = v[lo + h];
+      v[lo] = x + y;
+      v[lo + h] = x - y;
+    }
+  }
+  __syncthreads();
+}
+
+// Partials travel between workgroups on different XCDs (each with its own L2)
+// as agent-scope atomic stores, which write through to the device-coherent
+// level, so the writers need no device-wide cache write-back (a
+// __threadfence).  A workgroup publishes its partials, waits for its stores
+// to complete, then bumps the (sequence, KV head) counter; the workgroup that
+// takes the counter to n_splits acquires (drops its own L2's stale lines) and
+// merges with ordinary vector loads.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Returns true in every thread of the workgroup that arrives last.
+__device__ inline bool arrive_last(uint32_t* counter, int n_splits, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (prev == static_cast<uint32_t>(n_splits - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Split-K merge done by the last workgroup of a (sequence, KV head): partials
+// hold, per query head and split, acc[128] (rotated frame for POLAR values),
+// the running max m (natural-log units) and the softmax denominator l.  Writes
+// out = D_V H (sum_s acc_s e^{m_s - M}) / (d sum_s l_s e^{m_s - M}) for POLAR
+// values, the same without the inverse rotation for RAW values.  obuf is a
+// shared buffer of G*128 floats.  One wavefront per query head; splits are
+// taken 32 at a time with every load of a chunk in flight together; lane
+// (half, i4) accumulates float4 i4 of the chunk's splits of parity half.
+__device__ inline void combine_splits(const DecodeArgs& a, int b, int h, float* obuf, int nthreads) {
+  // every split has arrived (counter); its write-through partials are visible
+  // once this workgroup drops stale lines from its own L2
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int G = a.group;
+  const int64_t pstride = kPartialStride;
+  const int lane = threadIdx.x & 63;
+  const int i4 = lane & 31;
+  const int half = lane >> 5;
+  const int nwaves = nthreads >> 6;
+  for (int g = threadIdx.x >> 6; g < G; g += nwaves) {
+    const float* pp = a.partials + (static_cast<int64_t>(b) * a.n_q + h * G + g) * a.n_splits * pstride;
+    float M = -INFINITY, L = 0.0f;
+    float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int c0 = 0; c0 < a.n_splits; c0 += 32) {
+      const int sm = c0 + i4;                       // split whose (m, l) this lane reads
+      float2 ml = make_float2(-INFINITY, 0.0f);
+      if (sm < a.n_splits) ml = *reinterpret_cast<const float2*>(pp + sm * pstride + kD);
+      float4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int s = c0 + half + 2 * u;
+        v[u] = (s < a.n_splits) ? *reinterpret_cast<const float4*>(pp + s * pstride + 4 * i4)
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+      float mc = ml.x;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) mc = fmaxf(mc, __shfl_xor(mc, off, 64));
+      const float Mn = fmaxf(M, mc);
+      const float fo = (M == -INFINITY) ? 0.0f : __expf(M - Mn);
+      M = Mn;
+      const float wgt = (ml.x == -INFINITY) ? 0.0f : __expf(ml.x - M);   // weight of split c0 + i4
+      float lw = ml.y * wgt;
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) lw += __shfl_xor(lw, off, 64);
+      L = L * fo + lw;
+      A.x *= fo;
+      A.y *= fo;
+      A.z *= fo;
+      A.w *= fo;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float ws = __shfl(wgt, half + 2 * u, 64);   // lane half + 2u holds split c0 + half + 2u
+        A.x = fmaf(v[u].x, ws, A.x);
+        A.y = fmaf(v[u].y, ws, A.y);
+        A.z = fmaf(v[u].z, ws, A.z);
+        A.w = fmaf(v[u].w, ws, A.w);
+      }
+    }
+    A.x += __shfl_xor(A.x, 32, 64);
+    A.y += __shfl_xor(A.y, 32, 64);
+    A.z += __shfl_xor(A.z, 32, 64);
+    A.w += __shfl_xor(A.w, 32, 64);
+    if (half == 0) {
+      const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+      obuf[g * kD + 4 * i4 + 0] = A.x * inv;
+      obuf[g * kD + 4 * i4 + 1] = A.y * inv;
+      obuf[g * kD + 4 * i4 + 2] = A.z * inv;
+      obuf[g * kD + 4 * i4 + 3] = A.w * inv;
+    }
+  }
+  if (a.v_codec == POLAR) block_fwht128(obuf, G, nthreads);   // H acc; D_V and 1/d below
+  __syncthreads();
+  for (int k = threadIdx.x; k < G * kD; k += nthreads) {
+    const int g = k / kD, i = k % kD;
+    float v = obuf[k];
+    if (a.v_codec == POLAR) v = v * a.tb.dv[i] * (1.0f / static_cast<float>(kD));
+    a.out[(static_cast<int64_t>(b) * a.n_q + h * G + g) * kD + i] = v;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + b * a.n_kv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace tq

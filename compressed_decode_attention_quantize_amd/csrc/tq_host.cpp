@@ -175,7 +175,29 @@ struct GaussLegendre16 {
 struct Codebook {
   float centroids[16];
   float bounds[16];
+  float coeffs[8];   // odd multilinear coefficients, see multilinear_coeffs
 };
+
+// A symmetric sorted codebook is an odd function of the code's bits read as
+// signs s_k = 2 bit_k - 1, so C[c] = sum_T a_T prod_{k in T} s_k over the odd
+// subsets T of the bit positions.  Order: singletons {0}..{b-1}, then (b = 3)
+// {0,1,2}, (b = 4) {0,1,2}, {0,1,3}, {0,2,3}, {1,2,3}.  a_T = 2^-b sum_c C[c]
+// prod_T s_k(c); with fp16-exact centroids these are exact in fp32.
+void multilinear_coeffs(int bits, const float* centroids, float* out) {
+  static const int triples[4][3] = {{0, 1, 2}, {0, 1, 3}, {0, 2, 3}, {1, 2, 3}};
+  const int levels = 1 << bits;
+  int n_terms = bits + (bits == 3 ? 1 : (bits == 4 ? 4 : 0));
+  for (int T = 0; T < 8; ++T) out[T] = 0.0f;
+  for (int T = 0; T < n_terms; ++T) {
+    double acc = 0.0;
+    for (int c = 0; c < levels; ++c) {
+      auto s = [&](int k) { return ((c >> k) & 1) ? 1.0 : -1.0; };
+      const double prod = (T < bits) ? s(T) : s(triples[T - bits][0]) * s(triples[T - bits][1]) * s(triples[T - bits][2]);
+      acc += centroids[c] * prod;
+    }
+    out[T] = static_cast<float>(acc / levels);
+  }
+}
 
 // int_a^c t^moment (1 - t^2/d)^((d-3)/2) dt, 48 panels of 16-point Gauss-Legendre
 double law_integral(int d, double a, double c, int moment) {
@@ -231,6 +253,7 @@ Codebook make_codebook(int d, int bits) {
     cb.centroids[half - 1 - k] = -pos;
   }
   for (int j = 0; j + 1 < levels; ++j) cb.bounds[j] = 0.5f * (cb.centroids[j] + cb.centroids[j + 1]);
+  if (bits >= 2 && bits <= 4) multilinear_coeffs(bits, cb.centroids, cb.coeffs);
   cache[{d, bits}] = cb;
   return cb;
 }
@@ -255,11 +278,13 @@ void build_params(const tq_config* c, uint8_t* img) {
     const Codebook cb = make_codebook(d, c->k_bits);
     std::memcpy(img + L.ck, cb.centroids, 64);
     std::memcpy(img + L.kb, cb.bounds, 64);
+    std::memcpy(img + L.ak, cb.coeffs, 32);
   }
   if (c->v_codec == TQ_CODEC_POLAR) {
     const Codebook cb = make_codebook(d, c->v_bits);
     std::memcpy(img + L.cv, cb.centroids, 64);
     std::memcpy(img + L.vb, cb.bounds, 64);
+    std::memcpy(img + L.av, cb.coeffs, 32);
   }
 }
 
@@ -275,6 +300,8 @@ tq::Tables tables(const tq_config* c, const void* params) {
   t.kb = reinterpret_cast<const float*>(p + L.kb);
   t.cv = reinterpret_cast<const float*>(p + L.cv);
   t.vb = reinterpret_cast<const float*>(p + L.vb);
+  t.ak = reinterpret_cast<const float*>(p + L.ak);
+  t.av = reinterpret_cast<const float*>(p + L.av);
   return t;
 }
 
@@ -403,7 +430,7 @@ tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, u
   if (st != TQ_OK) return st;
   if (bytes == nullptr || max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
   const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
-  const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * (kD + 2) * 4;
+  const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
   const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * 4;
   *bytes = ((partial + 255) & ~255ull) + ((counters + 255) & ~255ull);
   return TQ_OK;
@@ -427,7 +454,7 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
   if (workspace_bytes < need) return TQ_EWORKSPACE;
   const int splits = decode_splits(cfg, max_seq_len);
   const uint64_t partial =
-      static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * decode_splits_bound(cfg, max_seq_len) * (kD + 2) * 4;
+      static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * decode_splits_bound(cfg, max_seq_len) * tq::kPartialStride * 4;
   tq::DecodeArgs a{};
   a.tb = tables(cfg, params);
   a.kc = static_cast<const uint8_t*>(k_cache);
@@ -452,7 +479,9 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
   a.v_bits = cfg->v_bits;
   a.k_block_bytes = kBlock * k_record_bytes(cfg);
   a.v_block_bytes = kBlock * v_record_bytes(cfg);
-  return tq::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EDEVICE;
+  hipError_t e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
 
 tq_status tq_dequantize(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,

@@ -11,6 +11,16 @@ constexpr int kD = 128;        // head_dim served by the kernels
 constexpr int kM = 128;        // QJL sketch rows served by the kernels
 constexpr int kBlock = 128;    // positions per cache block
 constexpr int kMaxGroup = 16;  // largest GQA group
+constexpr int kPartialStride = kD + 4;  // floats per split partial: acc[128], m, l, 2 pad (16-byte rows)
+
+// Slot of position t inside its 128-position block for the per-position
+// fields of POLAR keys (code words, sign words, radius, residual norm) and
+// for the radius of POLAR values: a fixed permutation inside each group of
+// 32 positions, chosen so that the decode kernel's fp4 matrix operands and
+// its probability tiles line up with whole 8-byte loads.
+__host__ __device__ inline int slot_of(int t) { return 32 * (t >> 5) + 8 * (t & 3) + ((t & 31) >> 2); }
+// Inverse: the position stored in slot s.
+__host__ __device__ inline int pos_of_slot(int s) { return 32 * (s >> 5) + 4 * (s & 7) + ((s & 31) >> 3); }
 
 // Byte offsets inside the parameter image (all fp32 arrays).
 struct ParamsLayout {
@@ -19,6 +29,7 @@ struct ParamsLayout {
   uint64_t st;       // float[d][m] its transpose
   uint64_t ck, kb;   // float[16] K centroids, float[16] K boundaries (2^b-1 used)
   uint64_t cv, vb;   // same for V
+  uint64_t ak, av;   // float[8] odd multilinear coefficients of the K / V codebooks
   uint64_t total;
 };
 
@@ -33,6 +44,8 @@ inline ParamsLayout params_layout(int d, int m) {
   L.kb = o; o += 64;
   L.cv = o; o += 64;
   L.vb = o; o += 64;
+  L.ak = o; o += 32;
+  L.av = o; o += 32;
   L.total = (o + 255) & ~255ull;
   return L;
 }
@@ -50,6 +63,8 @@ struct Tables {
   const float* kb;
   const float* cv;
   const float* vb;
+  const float* ak;
+  const float* av;
 };
 
 struct QuantArgs {
@@ -74,7 +89,7 @@ struct DecodeArgs {
   const float* q;
   float* out;
   float* logits;      // may be null
-  float* partials;    // [batch][n_q][n_splits][d + 2]
+  float* partials;    // [batch][n_q][n_splits][kPartialStride]
   uint32_t* counters; // [batch][n_kv]
   int32_t batch, n_q, n_kv, group, max_ctx, n_blocks;
   int32_t chunk_blocks, n_splits;
@@ -96,6 +111,9 @@ struct DequantArgs {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Matrix-core decode for POLAR / POLAR_QJL keys with POLAR values and G <= 4;
+// returns hipErrorNotSupported for other configurations.
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 
 }  // namespace tq

@@ -18,7 +18,8 @@
 //   * sums of squares are fp64 pairwise trees (register pair, then xor
 //     butterflies 32..1), the tree the format fixes.
 //   * the b code bit-planes and the sign plane are wave ballots; key planes
-//     are token-major words, value planes accumulate one bit per position in
+//     are token-major words (at the position's slot inside its block), value
+//     planes accumulate one bit per position in
 //     coordinate-major words that the wavefront owns for the whole group
 //     (read-modify-write keeps bits of positions it does not write).
 //   * the sketch S r (m = 128 rows) reads S^T from LDS, one row pair per lane,
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
       for (int p = 0; p < a.k_bits; ++p) {
         const uint64_t mlo = __ballot((o.c_lo >> p) & 1);
         const uint64_t mhi = __ballot((o.c_hi >> p) & 1);
-        if (lane < 4) planes[p * plane_words + lane * kBlock + t] = pick_word(mlo, mhi, lane);
+        if (lane < 4) planes[p * plane_words + lane * kBlock + slot_of(t)] = pick_word(mlo, mhi, lane);
       }
       uint8_t* after = kblk + 4 * a.k_bits * plane_words;
       if (a.k_codec == POLAR_QJL) {
@@ -210,11 +211,11 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
         const uint64_t slo = __ballot(z_lo >= 0.0f);
         const uint64_t shi = __ballot(z_hi >= 0.0f);
         uint32_t* sgn = reinterpret_cast<uint32_t*>(after);
-        if (lane < 4) sgn[lane * kBlock + t] = pick_word(slo, shi, lane);
+        if (lane < 4) sgn[lane * kBlock + slot_of(t)] = pick_word(slo, shi, lane);
         after += 4 * (kM / 32) * kBlock;
-        if (lane == 0) reinterpret_cast<uint16_t*>(after + 2 * kBlock)[t] = norm_to_f16(rho);
+        if (lane == 0) reinterpret_cast<uint16_t*>(after + 2 * kBlock)[slot_of(t)] = norm_to_f16(rho);
       }
-      if (lane == 0) reinterpret_cast<uint16_t*>(after)[t] = o.n16;
+      if (lane == 0) reinterpret_cast<uint16_t*>(after)[slot_of(t)] = o.n16;
     }
 
     // ---------------------------------------------------------- values
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
         }
       }
       vmask |= bit;
-      if (lane == 0) reinterpret_cast<uint16_t*>(vblk + 4 * a.v_bits * 4 * kD)[t] = o.n16;
+      if (lane == 0) reinterpret_cast<uint16_t*>(vblk + 4 * a.v_bits * 4 * kD)[slot_of(t)] = o.n16;
     }
   }
 

@@ -93,13 +93,15 @@ const char* tq_status_string(tq_status s);
  * cache: [batch][n_kv][ceil(max_ctx/128)][block]; block = 128 positions of one
  * (sequence, KV head):
  *   K POLAR / POLAR_QJL (b bits, m rows): b code planes u32[d/32][128] (bit e
- *     of word [j][t] = bit p of the code of coordinate 32j+e of position t),
- *     then (QJL) the sign plane u32[m/32][128], then fp16 radius[128], then
- *     (QJL) fp16 residual norm[128];
- *   K Q8: int8[128][d] then fp16 scale[128][d/32];
+ *     of word [j][s(t)] = bit p of the code of coordinate 32j+e of position t),
+ *     then (QJL) the sign plane u32[m/32][128] (same slots), then fp16
+ *     radius[128], then (QJL) fp16 residual norm[128], both at slot s(t);
+ *   K Q8: int8[128][d] then fp16 scale[128][d/32] (natural order);
  *   V POLAR (b bits): b planes u32[4][d] (bit e of word [j][i] = bit p of the
- *     code of coordinate i of position 32j+e), then fp16 radius[128];
+ *     code of coordinate i of position 32j+e), then fp16 radius[128] at s(t);
  *   RAW: fp32[128][d].
+ * Here t is the position inside its block and s(t) = 32(t/32) + 8(t%4) +
+ * (t%32)/4, a fixed permutation inside each group of 32 positions.
  * Per position and head: K 3b+QJL 68 B, 4b+QJL 84 B, q8 136 B; V b bits
  * 16b+2 B (d = 128). */
 tq_status tq_cache_bytes(const tq_config* cfg, uint64_t* k_bytes, uint64_t* v_bytes);

@@ -435,18 +435,23 @@ void or_dequant_q8(int d, const int8_t* k8, const uint16_t* s16, double* out) {
  * Cache image: [batch][n_kv][n_blocks][block], n_blocks = ceil(max_ctx/128),
  * block = 128 consecutive positions of one (sequence, kv head).
  *
+ * Inside a block, the per-position fields of POLAR / POLAR_QJL keys (code
+ * words, sign words, radius, residual norm) and the radius of POLAR values
+ * sit at slot pi(t) = 32 (t/32) + 8 (t%4) + (t%32)/4 for position t (a
+ * fixed permutation inside each group of 32 positions).
+ *
  * K block, POLAR / POLAR_QJL with b bits, m sketch rows:
- *   plane p (p < b):  u32 word[d/32][128]; word[j][t] bit e = bit p of the
- *                     code of coordinate 32 j + e of token t
- *   sign plane (QJL): u32 word[m/32][128]; bit e of word[j][t] = sign bit of
- *                     sketch row 32 j + e of token t
- *   n16[128]  fp16;   rho16[128] fp16 (QJL)
+ *   plane p (p < b):  u32 word[d/32][128]; word[j][pi(t)] bit e = bit p of
+ *                     the code of coordinate 32 j + e of token t
+ *   sign plane (QJL): u32 word[m/32][128]; bit e of word[j][pi(t)] = sign bit
+ *                     of sketch row 32 j + e of token t
+ *   n16[128]  fp16;   rho16[128] fp16 (QJL), both at slot pi(t)
  * K block, Q8:   int8 k8[128][d], then fp16 s16[128][d/32]
  * K/V block RAW: fp32 [128][d]
  * V block, POLAR with b bits:
  *   plane p:          u32 word[4][d]; bit e of word[j][i] = bit p of the code
- *                     of coordinate i of token 32 j + e
- *   n16[128] fp16
+ *                     of coordinate i of token 32 j + e (natural order)
+ *   n16[128] fp16 at slot pi(t)
  */
 
 static int or_nblocks(const or_spec* s) { return (s->max_ctx + OR_BLOCK - 1) / OR_BLOCK; }
@@ -485,6 +490,8 @@ static uint8_t* or_vblock(const or_spec* s, int b, int pos, int h, uint8_t* vc) 
   return vc + blk * or_v_block_bytes(s);
 }
 
+static int or_slot(int t) { return 32 * (t / 32) + 8 * (t % 4) + (t % 32) / 4; }
+
 static void or_setbit(uint8_t* base, int64_t word, int bit, int v) {
   uint32_t w;
   memcpy(&w, base + 4 * word, 4);
@@ -512,22 +519,23 @@ void or_pack_k(const or_spec* s, int b, int pos, int h, const or_krec* r, int64_
     return;
   }
   int nb = s->k_bits;
+  int sl = or_slot(t);
   int64_t plane_words = (int64_t)(d / 32) * OR_BLOCK;
   for (int p = 0; p < nb; p++) {
     for (int i = 0; i < d; i++) {
       int bit = (r->codes[rec * d + i] >> p) & 1;
-      or_setbit(blk, p * plane_words + (int64_t)(i / 32) * OR_BLOCK + t, i % 32, bit);
+      or_setbit(blk, p * plane_words + (int64_t)(i / 32) * OR_BLOCK + sl, i % 32, bit);
     }
   }
   uint8_t* after = blk + 4 * nb * plane_words;
   if (s->k_codec == OR_POLAR_QJL) {
     for (int j = 0; j < s->m; j++) {
-      or_setbit(after, (int64_t)(j / 32) * OR_BLOCK + t, j % 32, r->signs[rec * s->m + j]);
+      or_setbit(after, (int64_t)(j / 32) * OR_BLOCK + sl, j % 32, r->signs[rec * s->m + j]);
     }
     after += 4 * (int64_t)(s->m / 32) * OR_BLOCK;
   }
-  memcpy(after + 2 * t, &r->n16[rec], 2);
-  if (s->k_codec == OR_POLAR_QJL) memcpy(after + 2 * OR_BLOCK + 2 * t, &r->rho16[rec], 2);
+  memcpy(after + 2 * sl, &r->n16[rec], 2);
+  if (s->k_codec == OR_POLAR_QJL) memcpy(after + 2 * OR_BLOCK + 2 * sl, &r->rho16[rec], 2);
 }
 
 void or_unpack_k(const or_spec* s, int b, int pos, int h, const uint8_t* kc, or_krec* r, int64_t rec) {
@@ -545,23 +553,24 @@ void or_unpack_k(const or_spec* s, int b, int pos, int h, const uint8_t* kc, or_
     return;
   }
   int nb = s->k_bits;
+  int sl = or_slot(t);
   int64_t plane_words = (int64_t)(d / 32) * OR_BLOCK;
   for (int i = 0; i < d; i++) {
     int c = 0;
     for (int p = 0; p < nb; p++) {
-      c |= or_getbit(blk, p * plane_words + (int64_t)(i / 32) * OR_BLOCK + t, i % 32) << p;
+      c |= or_getbit(blk, p * plane_words + (int64_t)(i / 32) * OR_BLOCK + sl, i % 32) << p;
     }
     r->codes[rec * d + i] = (uint8_t)c;
   }
   const uint8_t* after = blk + 4 * nb * plane_words;
   if (s->k_codec == OR_POLAR_QJL) {
     for (int j = 0; j < s->m; j++) {
-      r->signs[rec * s->m + j] = (uint8_t)or_getbit(after, (int64_t)(j / 32) * OR_BLOCK + t, j % 32);
+      r->signs[rec * s->m + j] = (uint8_t)or_getbit(after, (int64_t)(j / 32) * OR_BLOCK + sl, j % 32);
     }
     after += 4 * (int64_t)(s->m / 32) * OR_BLOCK;
   }
-  memcpy(&r->n16[rec], after + 2 * t, 2);
-  if (s->k_codec == OR_POLAR_QJL) memcpy(&r->rho16[rec], after + 2 * OR_BLOCK + 2 * t, 2);
+  memcpy(&r->n16[rec], after + 2 * sl, 2);
+  if (s->k_codec == OR_POLAR_QJL) memcpy(&r->rho16[rec], after + 2 * OR_BLOCK + 2 * sl, 2);
 }
 
 void or_pack_v(const or_spec* s, int b, int pos, int h, const or_vrec* r, int64_t rec, uint8_t* vc) {
@@ -580,7 +589,7 @@ void or_pack_v(const or_spec* s, int b, int pos, int h, const or_vrec* r, int64_
       or_setbit(blk, p * plane_words + (int64_t)(t / 32) * d + i, t % 32, bit);
     }
   }
-  memcpy(blk + 4 * nb * plane_words + 2 * t, &r->n16[rec], 2);
+  memcpy(blk + 4 * nb * plane_words + 2 * or_slot(t), &r->n16[rec], 2);
 }
 
 void or_unpack_v(const or_spec* s, int b, int pos, int h, const uint8_t* vc, or_vrec* r, int64_t rec) {
@@ -600,7 +609,7 @@ void or_unpack_v(const or_spec* s, int b, int pos, int h, const uint8_t* vc, or_
     }
     r->codes[rec * d + i] = (uint8_t)c;
   }
-  memcpy(&r->n16[rec], blk + 4 * nb * plane_words + 2 * t, 2);
+  memcpy(&r->n16[rec], blk + 4 * nb * plane_words + 2 * or_slot(t), 2);
 }
 
 /* ===================================================================== */

@@ -111,8 +111,11 @@ def test_split_count_invariance(codec):
         o, l, _ = _gpu_decode(cfg, kc, vc, lens, q)
         outs.append(o)
         lgs.append(l)
+    # the merge order changes with the split count, and so do the per-32-position
+    # exponents of the probability limbs (12 significant bits): results agree
+    # to well below the 2e-3 output bar
     for o, l in zip(outs[1:], lgs[1:]):
-        assert np.max(np.abs(o - outs[0])) <= 2e-6 * max(1.0, np.abs(outs[0]).max())
+        assert np.max(np.abs(o - outs[0])) <= 1e-4 * max(1.0, np.abs(outs[0]).max())
         assert np.array_equal(np.nan_to_num(l, nan=7.0), np.nan_to_num(lgs[0], nan=7.0))
 
 

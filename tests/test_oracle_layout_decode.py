@@ -83,6 +83,20 @@ def test_pack_unpack_round_trip(orc, kc, kb, vc, vb):
         assert np.array_equal(a, b)
 
 
+def test_slot_permutation_is_a_bijection_per_group(orc):
+    """pi(t) = 32(t/32) + 8(t%4) + (t%32)/4 permutes each group of 32 positions;
+    checked through the packer: one record per position lands on distinct slots."""
+    s = _spec(orc, batch=1, n_kv=1, n_q=4, max_ctx=128)
+    R = orc.Records(s)
+    for t in range(128):
+        R.kn16[R.rec_index(0, t, 0)] = 0x3c00 + t      # distinct radii
+    kc, _ = orc.pack_cache(s, R, np.array([128], np.int32))
+    n16 = kc[4 * 2048:4 * 2048 + 256].view(np.uint16)
+    pi = lambda t: 32 * (t // 32) + 8 * (t % 4) + (t % 32) // 4
+    assert sorted(pi(t) for t in range(128)) == list(range(128))
+    assert all(n16[pi(t)] == 0x3c00 + t for t in range(128))
+
+
 def test_bit_positions_of_one_record(orc):
     """Hand-computed byte offsets for one record in the documented layout."""
     s = _spec(orc, batch=1, n_kv=2, max_ctx=256)
@@ -99,19 +113,20 @@ def test_bit_positions_of_one_record(orc):
     kc, vc = orc.pack_cache(s, R, lens)
     kblk = 128 * 68
     base = ((0 * 2 + 1) * 2 + 1) * kblk         # (b, h, block) = (0, 1, 1)
-    word = lambda p, j, t: base + 4 * (p * 4 * 128 + j * 128 + t)
+    sl = 16                                     # token 2 of the block sits at slot 32*0 + 8*2 + 0
+    word = lambda p, j, s_: base + 4 * (p * 4 * 128 + j * 128 + s_)
     nz = np.flatnonzero(kc)
-    want = {word(0, 1, 2) + 0: 1 << 5, word(2, 1, 2) + 0: 1 << 5,   # coord 37 = word 1 bit 5
-            base + 3 * 2048 + 4 * (3 * 128 + 2) + 0: 1 << 4,        # sign row 100 = word 3 bit 4
-            base + 4 * 2048 + 2 * 2 + 1: 0x3c,                       # n16 high byte
-            base + 4 * 2048 + 256 + 2 * 2 + 1: 0x40}                 # rho16 high byte
+    want = {word(0, 1, sl) + 0: 1 << 5, word(2, 1, sl) + 0: 1 << 5,   # coord 37 = word 1 bit 5
+            base + 3 * 2048 + 4 * (3 * 128 + sl) + 0: 1 << 4,        # sign row 100 = word 3 bit 4
+            base + 4 * 2048 + 2 * sl + 1: 0x3c,                       # n16 high byte
+            base + 4 * 2048 + 256 + 2 * sl + 1: 0x40}                 # rho16 high byte
     assert {int(k): int(kc[k]) for k in nz} == want
     vblk = 128 * 50
     vbase = ((0 * 2 + 1) * 2 + 1) * vblk
     vword = lambda p, j, i_: vbase + 4 * (p * 4 * 128 + j * 128 + i_)
     nzv = np.flatnonzero(vc)
-    wantv = {vword(1, 0, 9) + 0: 1 << 2, vword(2, 0, 9) + 0: 1 << 2,   # token 2 of word j=0
-             vbase + 3 * 2048 + 2 * 2: 0x55, vbase + 3 * 2048 + 2 * 2 + 1: 0x35}
+    wantv = {vword(1, 0, 9) + 0: 1 << 2, vword(2, 0, 9) + 0: 1 << 2,   # token 2 = bit 2 of word j=0
+             vbase + 3 * 2048 + 2 * sl: 0x55, vbase + 3 * 2048 + 2 * sl + 1: 0x35}
     assert {int(k): int(vc[k]) for k in nzv} == wantv
 
 
