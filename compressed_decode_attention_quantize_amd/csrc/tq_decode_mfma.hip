@@ -31,14 +31,22 @@
 // the per-position key fields and value radii at slot_of(position), which makes
 // each lane's operands whole 8-byte loads.
 //
-// Mapping: grid (split, KV head, sequence); 4 waves per workgroup share each
-// 128-position block.  Wave w computes the logits of the block's positions in
-// k-slots [32w, 32w+32) (2 MFMA column groups), takes part in the block max
-// (shared memory), writes its fp8 limbs of p * radius, then computes the
-// weighted sum for coordinates [32w, 32w+32) over all 128 positions.  Loads
-// of the block after next are issued before the current one is processed.
+// Mapping: grid (split, KV head, sequence); a workgroup is eight waves in two
+// groups of four that take alternate 128-position blocks of the split's chunk
+// in lockstep.  Within a group, wave w computes the logits of the block's
+// positions in k-slots [32w, 32w+32) (2 MFMA column groups), the eight waves
+// share each step's maximum (shared memory), each group writes its fp8 limbs
+// of p * radius, and wave w then computes its group's weighted sum for
+// coordinates [32w, 32w+32) over the group's block.  Each group keeps four
+// blocks of loads in flight in registers; the query set-up (rotation, sketch,
+// limbs) is done once per workgroup while the first loads are outstanding.
+// The two groups' sums are added in shared memory and rotated back
+// (D_V H / d) before they leave the workgroup, so the workgroup that merges
+// the splits only forms a weighted average.
 
 #include <hip/hip_fp16.h>
+
+#include <algorithm>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -49,8 +57,9 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;   // two groups of four
+constexpr int kRing = 4;    // blocks in flight per group (3 for 4-bit keys with 4-bit values: registers)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -142,49 +151,148 @@ struct BlockRegs {
   uint32_t vw[2][VB];   // value words for coordinates 32w + 16r + t, positions 32 g4 ..
 };
 
+// Buffer resource over one (sequence, KV head)'s blocks [0, n_valid): loads at
+// offsets past the end return zero without touching memory (raw buffer,
+// stride 0; the range check covers the per-lane offset), so blocks past a
+// split's chunk need no branch around their loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t block_bytes, int n_valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0),
+                                           static_cast<int>(block_bytes * n_valid), 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint2 ld64(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(x[0], x[1]);
+}
+
+// Loads the operands of one block at byte offsets kofs / vofs of the K / V
+// resources; w is the wave within its group.
 template <int KB, bool QJL, int VB>
-__device__ __forceinline__ void load_block(BlockRegs<KB, VB>& R, const uint8_t* kbp, const uint8_t* vbp, int w,
-                                           int t, int g4) {
-  const uint32_t* kw = reinterpret_cast<const uint32_t*>(kbp);
-  const int so = g4 * kBlock + 32 * w + 2 * t;
+__device__ __forceinline__ void load_block(BlockRegs<KB, VB>& R, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           int kofs, int vofs, int w, int t, int g4) {
+  const int so = 4 * (g4 * kBlock + 32 * w + 2 * t);
 #pragma unroll
-  for (int p = 0; p < KB; ++p) R.kp[p] = *reinterpret_cast<const uint2*>(kw + p * 4 * kBlock + so);
-  const uint8_t* after = kbp + 4 * KB * 4 * kBlock;
+  for (int p = 0; p < KB; ++p) R.kp[p] = ld64(rk, kofs + p * 16 * kBlock + so);
+  int after = kofs + 16 * KB * kBlock;
   if (QJL) {
-    R.ks = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(after) + so);
-    after += 4 * 4 * kBlock;
-    R.kr = *reinterpret_cast<const uint32_t*>(after + 2 * kBlock + 2 * (32 * w + 2 * t));
+    R.ks = ld64(rk, after + so);
+    after += 16 * kBlock;
+    R.kr = ld32(rk, after + 2 * kBlock + 2 * (32 * w + 2 * t));
   } else {
     R.ks = make_uint2(0u, 0u);
     R.kr = 0u;
   }
-  R.kn = *reinterpret_cast<const uint32_t*>(after + 2 * (32 * w + 2 * t));
-  R.vn = *reinterpret_cast<const uint32_t*>(vbp + 4 * VB * 4 * kD + 2 * (32 * w + 2 * t));
-  const uint32_t* vwp = reinterpret_cast<const uint32_t*>(vbp);
+  R.kn = ld32(rk, after + 2 * (32 * w + 2 * t));
+  R.vn = ld32(rv, vofs + 16 * VB * kD + 2 * (32 * w + 2 * t));
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int p = 0; p < VB; ++p) R.vw[r][p] = vwp[p * 4 * kD + g4 * kD + 32 * w + 16 * r + t];
+    for (int p = 0; p < VB; ++p) R.vw[r][p] = ld32(rv, vofs + 4 * (p * 4 * kD + g4 * kD + 32 * w + 16 * r + t));
+}
+
+// Max / sum over the 32 lanes of each half-wave (rows via DPP, then the
+// swizzle that swaps 16-lane halves within 32 lanes).
+__device__ __forceinline__ float half_max32(float x) {
+  x = row_max16(x);
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
+}
+__device__ __forceinline__ float half_sum32(float x) {
+  x = row_sum16(x);
+  return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// Merge of the split partials by the workgroup that arrives last: partial s
+// of query head g holds o_s = D_V H acc_s / d (already in the original frame),
+// its running max m_s (natural-log units) and denominator l_s; the output is
+// sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.  Wave g merges head g; splits
+// are taken 32 at a time with every load of a round in flight together; lane
+// (half, i4) accumulates float4 i4 of the round's splits of parity half.
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int h, int w, int lane) {
+  // every split has arrived (counter); the partials were written through to
+  // the device-coherent level and are read back with device-scope coherent
+  // loads (sc1), so no cache invalidation is needed
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  constexpr int kCoherent = 16;   // sc1
+  const int G = a.group;
+  if (w < G) {
+    const int pstride = kPartialStride;
+    const int i4 = lane & 31;
+    const int half = lane >> 5;
+    const float* pp = a.partials + (static_cast<int64_t>(b) * a.n_q + h * G + w) * a.n_splits * kPartialStride;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(pp), static_cast<short>(0), a.n_splits * pstride * 4, 0x00020000);
+    float M = -INFINITY, L = 0.0f;
+    float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int c0 = 0; c0 < a.n_splits; c0 += 32) {
+      // splits past n_splits read as zero (out of the resource's range):
+      // m = 0, l = 0, acc = 0, weight forced to zero below
+      const int sm = c0 + i4;
+      const v2u mlv = __builtin_amdgcn_raw_buffer_load_b64(rp, (sm * pstride + kD) * 4, 0, kCoherent);
+      v4u v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rp, ((c0 + half + 2 * u) * pstride + 4 * i4) * 4, 0, kCoherent);
+      const float mx = (sm < a.n_splits) ? __uint_as_float(mlv[0]) : -INFINITY;
+      const float mc = half_max32(mx);
+      const float Mn = fmaxf(M, mc);
+      const float fo = (M == -INFINITY) ? 0.0f : __expf(M - Mn);
+      M = Mn;
+      const float wgt = (mx == -INFINITY) ? 0.0f : __expf(mx - M);
+      const float lw = half_sum32(__uint_as_float(mlv[1]) * wgt);
+      L = L * fo + lw;
+      A.x *= fo;
+      A.y *= fo;
+      A.z *= fo;
+      A.w *= fo;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float ws = __shfl(wgt, half + 2 * u, 64);   // lane half + 2u holds split c0 + half + 2u
+        A.x = fmaf(__uint_as_float(v[u][0]), ws, A.x);
+        A.y = fmaf(__uint_as_float(v[u][1]), ws, A.y);
+        A.z = fmaf(__uint_as_float(v[u][2]), ws, A.z);
+        A.w = fmaf(__uint_as_float(v[u][3]), ws, A.w);
+      }
+    }
+    A.x += __shfl_xor(A.x, 32, 64);
+    A.y += __shfl_xor(A.y, 32, 64);
+    A.z += __shfl_xor(A.z, 32, 64);
+    A.w += __shfl_xor(A.w, 32, 64);
+    if (half == 0) {
+      const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+      *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.n_q + h * G + w) * kD + 4 * i4) =
+          make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + b * a.n_kv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int KB, bool QJL, int VB>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NTK = NTerms<KB>::n;
   constexpr int NTV = NTerms<VB>::n;
+  constexpr int kR = (KB + VB >= 8) ? kRing - 1 : kRing;
   __shared__ float qr[4 * kD];              // q_raw = H D_K q per head (zero rows past G)
   __shared__ float sqs[4 * kM];             // S q_raw / sqrt d
-  __shared__ __attribute__((aligned(16))) uint8_t alimb[2][16 * 128];  // fp8 limbs [row = 4g + j][k]
+  __shared__ __attribute__((aligned(16))) uint8_t alimb[2][16 * 128];  // fp8 limbs [set][row = 4g + j][k]
   __shared__ uint8_t aexp[2][4][16];        // E8M0 scale [set][k / 32][row]
-  __shared__ __attribute__((aligned(16))) uint8_t plimb[16 * 128];     // fp8 limbs of p * radius [col][k]
-  __shared__ __attribute__((aligned(4))) uint8_t pexp[4][16];          // [k / 32][col]
+  __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * 128];  // per group: limbs of p * radius [col][k]
+  __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];       // per group: [k / 32][col]
   __shared__ float wred[kWaves][4];
-  __shared__ float hmax[3][kWaves];         // per-head max |value| for the limb exponents
-  __shared__ __attribute__((aligned(16))) float sred[8][4 * kM];   // partial sketch sums
+  __shared__ float hmax[2][kWaves];         // per-wave max |value| for the limb exponents
+  __shared__ float mrun[4];                 // running max per head at the end (log2 units)
+  __shared__ __attribute__((aligned(16))) float sred[16][4 * kM];   // partial sketch sums
+  __shared__ __attribute__((aligned(16))) float obuf[2][4][kD];     // per group: weighted sums
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int gr = w >> 2;   // group: blocks blk0 + gr, blk0 + gr + 2, ...
+  const int wl = w & 3;    // wave within the group
   const int t = lane & 15;
   const int g4 = lane >> 4;
   const int split = blockIdx.x;
@@ -195,145 +303,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
   const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
+  const int n_iter = max(0, (blk1 - blk0 + 1) / 2);   // steps of two blocks
   const int64_t slot0 = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
-
-  // loads of the first two blocks, the query rows and the sketch rows go out
-  // before any set-up arithmetic
-  BlockRegs<KB, VB> cur, nx1;
-  if (blk0 < blk1)
-    load_block<KB, QJL, VB>(cur, a.kc + (slot0 + blk0) * a.k_block_bytes, a.vc + (slot0 + blk0) * a.v_block_bytes,
-                            w, t, g4);
-  if (blk0 + 1 < blk1)
-    load_block<KB, QJL, VB>(nx1, a.kc + (slot0 + blk0 + 1) * a.k_block_bytes,
-                            a.vc + (slot0 + blk0 + 1) * a.v_block_bytes, w, t, g4);
   const float inv_sqrt_d = 0.08838834764831845f;
-  const int jq = tid & 31, ic = tid >> 5;   // sketch rows 4jq..4jq+3, coordinates 16ic..16ic+15
-  float4 st4[16];
-  if (QJL) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) st4[u] = *reinterpret_cast<const float4*>(a.tb.st + (16 * ic + u) * kM + 4 * jq);
-  }
-  float q_lo = 0.0f, q_hi = 0.0f;
-  if (w < G) {
-    const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + h * G + w) * kD;
-    q_lo = qp[lane] * a.tb.dk[lane];
-    q_hi = qp[lane + 64] * a.tb.dk[lane + 64];
-  }
 
-  // ------------------------------------------------------------- set-up
-  // wave w rotates the query of head w in registers: q_raw = H D_K q
-  wave_fwht128(q_lo, q_hi, lane);
-  qr[w * kD + lane] = q_lo;
-  qr[w * kD + lane + 64] = q_hi;
-  {
-    float qm = fmaxf(fabsf(q_lo), fabsf(q_hi));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) qm = fmaxf(qm, __shfl_xor(qm, off, 64));
-    if (lane == 0) hmax[0][w] = qm;
-  }
-  __syncthreads();
-  if (QJL) {
-    // sq = S q_raw / sqrt d: partial sums over 16 coordinates per thread, then over the 8 partials
-    float acc[4][4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[g][jj] = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float qv = qr[g * kD + 16 * ic + u];
-        acc[g][0] = fmaf(st4[u].x, qv, acc[g][0]);
-        acc[g][1] = fmaf(st4[u].y, qv, acc[g][1]);
-        acc[g][2] = fmaf(st4[u].z, qv, acc[g][2]);
-        acc[g][3] = fmaf(st4[u].w, qv, acc[g][3]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *reinterpret_cast<float4*>(&sred[ic][g * kM + 4 * jq]) = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
-    __syncthreads();
-    // thread tid owns outputs tid (head tid/128) and tid + 256 (head 2 + tid/128)
-    float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int k = tid + 256 * r;
-      float sum = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) sum += sred[c][k];
-      sum *= inv_sqrt_d;
-      sqs[k] = sum;
-      if (r == 0) m0 = fabsf(sum); else m1 = fabsf(sum);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      m0 = fmaxf(m0, __shfl_xor(m0, off, 64));
-      m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
-    }
-    if (lane == 0) {
-      hmax[1][w] = m0;   // waves 2g, 2g+1 cover head g (g < 2)
-      hmax[2][w] = m1;   // ... and head g + 2
-    }
-    __syncthreads();
-  }
-  {
-    // fp8 limbs of q_raw (set 0) and sq (set 1), one E8M0 exponent per (set,
-    // head): item (set, head, k-slot), k-slot k holding coordinate pos_of_slot(k)
-    const int n_items = (QJL ? 2 : 1) * 4 * 128;
-    for (int it = tid; it < n_items; it += kThreads) {
-      const int k = it & 127;
-      const int g = (it >> 7) & 3;
-      const int set = it >> 9;
-      const int coord = pos_of_slot(k);
-      const float u = set == 0 ? qr[g * kD + coord] : sqs[g * kM + coord];
-      float m;
-      if (set == 0) {
-        m = hmax[0][g];
-      } else {
-        const int row = g < 2 ? 1 : 2;
-        const int w0 = 2 * (g & 1);
-        m = fmaxf(hmax[row][w0], hmax[row][w0 + 1]);
-      }
-      const int s0 = (m >= 1e-30f) ? exponent_of(m) - 7 : 0;
-      float res = u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sj = s0 - 4 * j;
-        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(res, -sj), 0.0f, 0, false);
-        res -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), sj);
-        alimb[set][(4 * g + j) * 128 + k] = static_cast<uint8_t>(pk & 0xff);
-        if ((k & 31) == 0) aexp[set][k >> 5][4 * g + j] = static_cast<uint8_t>(min(max(sj + 127, 1), 254));
-      }
-    }
-  }
-  __syncthreads();
-  v8i Aq, Asq;
-  int scq, scsq = 127;
-  {
-    const uint4 lo = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 16 * g4]);
-    const uint4 hi = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 64 + 16 * g4]);
-    Aq = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    scq = aexp[0][g4][t];
-    if (QJL) {
-      const uint4 l2 = *reinterpret_cast<const uint4*>(&alimb[1][t * 128 + 16 * g4]);
-      const uint4 h2 = *reinterpret_cast<const uint4*>(&alimb[1][t * 128 + 64 + 16 * g4]);
-      Asq = v8i{(int)l2.x, (int)l2.y, (int)l2.z, (int)l2.w, (int)h2.x, (int)h2.y, (int)h2.z, (int)h2.w};
-      scsq = aexp[1][g4][t];
-    } else {
-      Asq = Aq;
-    }
-  }
-  float ak[NTK], av[NTV];
-#pragma unroll
-  for (int T = 0; T < NTK; ++T) ak[T] = a.tb.ak[T];
+  // running max (log2 units) of head g4 (this lane's logits row) and of head
+  // t / 4 (this lane's result column); both follow the same step maxima
+  float av[NTV];
 #pragma unroll
   for (int T = 0; T < NTV; ++T) av[T] = a.tb.av[T];
-
-  const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
-  const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
-  // running max (log2 units) of head g4 (this lane's logits row) and of head
-  // t / 4 (this lane's result column); both follow the same block maxima
   float m_a = -INFINITY, m_b = -INFINITY;
   float lsum = 0.0f;   // this lane's share of the denominator of head g4
   v4f accV[2][NTV];
@@ -342,143 +320,316 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // the fourth limb column of each head stays zero (three limbs are written)
-  for (int k = tid; k < 4 * 128; k += kThreads) plimb[(4 * (k >> 7) + 3) * 128 + (k & 127)] = 0;
-
-  // ----------------------------------------------------------- main loop
-  for (int blk = blk0; blk < blk1; ++blk) {
-    const int n_t = min(kBlock, len - blk * kBlock);
-    BlockRegs<KB, VB> nx2;
-    if (blk + 2 < blk1)
-      load_block<KB, QJL, VB>(nx2, a.kc + (slot0 + blk + 2) * a.k_block_bytes,
-                              a.vc + (slot0 + blk + 2) * a.v_block_bytes, w, t, g4);
-
-    // logits of k-slots 32w + 2t + c for head g4: every MFMA of the block is
-    // issued before any result is read
-    v4f dT[2][NTK];
-    v4f dQ[2];
+  if (n_iter > 0) {   // uniform over the workgroup
+    // query and sketch loads go out first (their results return first), then
+    // the first kR blocks of each group
+    const int jq = tid & 31, ic = tid >> 5;   // sketch rows 4jq..4jq+3, coordinates 8ic..8ic+7
+    float4 st4[8];
+    if (QJL) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t wd[KB];
-#pragma unroll
-      for (int p = 0; p < KB; ++p) wd[p] = c ? cur.kp[p].y : cur.kp[p].x;
-#pragma unroll
-      for (int T = 0; T < NTK; ++T)
-        dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
-      if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4(c ? cur.ks.y : cur.ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
+      for (int u = 0; u < 8; ++u) st4[u] = *reinterpret_cast<const float4*>(a.tb.st + (8 * ic + u) * kM + 4 * jq);
     }
-    float lg2[2];
+    // (unconditional loads: a branch here would make the compiler wait for
+    // every block load before the set-up arithmetic)
+    const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + h * G + min(w & 3, G - 1)) * kD;
+    const float qa = qp[lane], qb = qp[lane + 64];
+    const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
+    float ak[NTK];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float code = 0.0f;
+    for (int T = 0; T < NTK; ++T) ak[T] = a.tb.ak[T];
+    // every load whose result is needed before the main loop is issued above
+    // this point: the counter of outstanding loads drains in order, so a
+    // later one would wait for all block loads
+    __builtin_amdgcn_sched_barrier(0);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0 * a.k_block_bytes, a.k_block_bytes, blk1);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0 * a.v_block_bytes, a.v_block_bytes, blk1);
+    const int kbb = static_cast<int>(a.k_block_bytes), vbb = static_cast<int>(a.v_block_bytes);
+    BlockRegs<KB, VB> ring[kR];
 #pragma unroll
-      for (int T = 0; T < NTK; ++T) code = fmaf(ak[T], (dT[c][T][0] + dT[c][T][1]) + (dT[c][T][2] + dT[c][T][3]), code);
-      const float qj = QJL ? (dQ[c][0] + dQ[c][1]) + (dQ[c][2] + dQ[c][3]) : 0.0f;
-      const int tok = pos_of_slot(32 * w + 2 * t + c);
-      const float nk = h2f(c ? (cur.kn >> 16) : cur.kn);
-      const float rk = QJL ? h2f(c ? (cur.kr >> 16) : cur.kr) : 0.0f;
-      const float l2 = alpha2 * nk * code + beta2 * rk * qj;
-      const bool valid = (tok < n_t) && (g4 < G);
-      if (a.logits != nullptr && valid)
-        a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g4) * a.max_ctx + blk * kBlock + tok] = l2 * kLn2;
-      lg2[c] = valid ? l2 : -INFINITY;
+    for (int r = 0; r < kR; ++r) {
+      const int bi = blk0 + gr + 2 * r;   // past blk1: reads as zero
+      load_block<KB, QJL, VB>(ring[r], rk, rv, bi * kbb, bi * vbb, wl, t, g4);
     }
 
-    // block max per head (4 waves); the running max only moves when a block
-    // exceeds it by 2^8, so rescaling is rare and p stays below 256
-    const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
-    if (t == 0) wred[w][g4] = mloc;
+    // ------------------------------------------------------------- set-up
+    // waves 0..3 rotate the query of head w in registers: q_raw = H D_K q
+    if (w < 4) {
+      float q_lo = (w < G) ? qa * da : 0.0f;
+      float q_hi = (w < G) ? qb * db : 0.0f;
+      wave_fwht128(q_lo, q_hi, lane);
+      qr[w * kD + lane] = q_lo;
+      qr[w * kD + lane + 64] = q_hi;
+      float qm = fmaxf(fabsf(q_lo), fabsf(q_hi));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) qm = fmaxf(qm, __shfl_xor(qm, off, 64));
+      if (lane == 0) hmax[0][w] = qm;
+    }
     __syncthreads();
-    const int hb = t >> 2;
-    const float bm_a = fmaxf(fmaxf(wred[0][g4], wred[1][g4]), fmaxf(wred[2][g4], wred[3][g4]));
-    const float bm_b = fmaxf(fmaxf(wred[0][hb], wred[1][hb]), fmaxf(wred[2][hb], wred[3][hb]));
-    const float mn_a = (bm_a > m_a + 8.0f) ? bm_a : m_a;
-    const float mn_b = (bm_b > m_b + 8.0f) ? bm_b : m_b;
-    const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_a - mn_a);
-    const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_b - mn_b);
-    m_a = mn_a;
-    m_b = mn_b;
-
-    // probabilities and fp8 limbs of p * value radius (3 limbs, ~12 bits)
-    const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - m_a);
-    const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - m_a);
-    lsum = lsum * fh + (p0 + p1);
-    float r0 = (p0 > 0.0f) ? p0 * h2f(cur.vn) : 0.0f;
-    float r1 = (p1 > 0.0f) ? p1 * h2f(cur.vn >> 16) : 0.0f;
-    const float pm = row_max16(fmaxf(r0, r1));
-    const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 7 : 0;
-    uint32_t ebytes = 127u << 24;
+    if (QJL) {
+      // sq = S q_raw / sqrt d: partial sums over 8 coordinates per thread, then over the 16 partials
+      float acc[4][4];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int sj = s0 - 4 * j;
-      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(r0, -sj),
-                                                     __builtin_amdgcn_ldexpf(r1, -sj), 0, false);
-      if (j < 2) {
-        r0 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), sj);
-        r1 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), sj);
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[g][jj] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float qv = qr[g * kD + 8 * ic + u];
+          acc[g][0] = fmaf(st4[u].x, qv, acc[g][0]);
+          acc[g][1] = fmaf(st4[u].y, qv, acc[g][1]);
+          acc[g][2] = fmaf(st4[u].z, qv, acc[g][2]);
+          acc[g][3] = fmaf(st4[u].w, qv, acc[g][3]);
+        }
       }
-      *reinterpret_cast<uint16_t*>(&plimb[(4 * g4 + j) * 128 + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
-      ebytes |= static_cast<uint32_t>(min(max(sj + 127, 1), 254)) << (8 * j);
-    }
-    if (t == 0) *reinterpret_cast<uint32_t*>(&pexp[w][4 * g4]) = ebytes;
-    __syncthreads();
-
-    // weighted sum of value terms for coordinates 32w + 16r + (row), columns (head, limb)
-    if (__any(fv != 1.0f)) {   // rescale only when some head's max moved
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(&sred[ic][g * kM + 4 * jq]) = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+      __syncthreads();
+      // thread tid owns output tid: head tid / 128, so waves 2g and 2g+1 cover head g
+      float sum = 0.0f;
 #pragma unroll
-        for (int T = 0; T < NTV; ++T) accV[r][T] *= fv;
+      for (int c = 0; c < 16; ++c) sum += sred[c][tid];
+      sum *= inv_sqrt_d;
+      sqs[tid] = sum;
+      float m1 = fabsf(sum);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+      if (lane == 0) hmax[1][w] = m1;
+      __syncthreads();
     }
-    v8i Pv;
     {
-      const uint4 lo = *reinterpret_cast<const uint4*>(&plimb[t * 128 + 16 * g4]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(&plimb[t * 128 + 64 + 16 * g4]);
-      Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      // fp8 limbs of q_raw (waves 0..3, set 0) and sq (waves 4..7, set 1), one
+      // E8M0 exponent per (set, head); wave (set, g) writes k-slots 2l, 2l+1 of
+      // head g, k-slot k holding coordinate pos_of_slot(k)
+      const int set = w >> 2;
+      const int g = w & 3;
+      if (set == 0 || QJL) {
+        const int k0 = 2 * lane;
+        const float* src = set == 0 ? qr + g * kD : sqs + g * kM;
+        float u0 = src[pos_of_slot(k0)];
+        float u1 = src[pos_of_slot(k0 + 1)];
+        const float m = set == 0 ? hmax[0][g] : fmaxf(hmax[1][2 * g], hmax[1][2 * g + 1]);
+        const int s0 = (m >= 1e-30f) ? exponent_of(m) - 7 : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sj = s0 - 4 * j;
+          const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(u0, -sj),
+                                                         __builtin_amdgcn_ldexpf(u1, -sj), 0, false);
+          u0 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), sj);
+          u1 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), sj);
+          *reinterpret_cast<uint16_t*>(&alimb[set][(4 * g + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
+          if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(sj + 127, 1), 254));
+        }
+      }
     }
-    const int scp = pexp[g4][t];
+    // the fourth limb column of each head stays zero (three limbs are written)
+    for (int k = tid; k < 2 * 4 * 128; k += kThreads) plimb[k >> 9][(4 * ((k >> 7) & 3) + 3) * 128 + (k & 127)] = 0;
+    __syncthreads();
+    v8i Aq, Asq;
+    int scq, scsq = 127;
+    {
+      const uint4 lo = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 16 * g4]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 64 + 16 * g4]);
+      Aq = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      scq = aexp[0][g4][t];
+      if (QJL) {
+        const uint4 l2 = *reinterpret_cast<const uint4*>(&alimb[1][t * 128 + 16 * g4]);
+        const uint4 h2 = *reinterpret_cast<const uint4*>(&alimb[1][t * 128 + 64 + 16 * g4]);
+        Asq = v8i{(int)l2.x, (int)l2.y, (int)l2.z, (int)l2.w, (int)h2.x, (int)h2.y, (int)h2.z, (int)h2.w};
+        scsq = aexp[1][g4][t];
+      } else {
+        Asq = Aq;
+      }
+    }
+    const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
+    const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
+    uint8_t* my_plimb = plimb[gr];
+
+    // --------------------------------------------------------- main loop
+    // step i: group gr takes block blk0 + gr + 2i from ring slot i % kR; in
+    // the main loop it refills that slot with block blk0 + gr + 2(i + kR).
+    // The loop runs whole rounds of the ring with no side exits and the last
+    // partial round follows as nested conditionals: exits in the middle of a
+    // round would give the compiler paths on which a slot was loaded more
+    // recently, and it would then wait for loads issued in the same step.
+    auto step = [&](BlockRegs<KB, VB>& cur, int i) __attribute__((always_inline)) {
+      const int blk = blk0 + gr + 2 * i;
+      const int n_t = (blk < blk1) ? min(kBlock, len - blk * kBlock) : 0;
+
+      // logits of k-slots 32wl + 2t + c for head g4: every MFMA of the block
+      // is issued before any result is read
+      v4f dT[2][NTK];
+      v4f dQ[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint32_t wd[KB];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) wd[p] = c ? cur.kp[p].y : cur.kp[p].x;
+#pragma unroll
+        for (int T = 0; T < NTK; ++T)
+          dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
+        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4(c ? cur.ks.y : cur.ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
+      }
+      float lg2[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float code = 0.0f;
+#pragma unroll
+        for (int T = 0; T < NTK; ++T)
+          code = fmaf(ak[T], (dT[c][T][0] + dT[c][T][1]) + (dT[c][T][2] + dT[c][T][3]), code);
+        const float qj = QJL ? (dQ[c][0] + dQ[c][1]) + (dQ[c][2] + dQ[c][3]) : 0.0f;
+        const int tok = pos_of_slot(32 * wl + 2 * t + c);
+        const float nk = h2f(c ? (cur.kn >> 16) : cur.kn);
+        const float rho = QJL ? h2f(c ? (cur.kr >> 16) : cur.kr) : 0.0f;
+        const float l2 = alpha2 * nk * code + beta2 * rho * qj;
+        const bool valid = (tok < n_t) && (g4 < G);
+        if (a.logits != nullptr && valid)
+          a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g4) * a.max_ctx + blk * kBlock + tok] = l2 * kLn2;
+        lg2[c] = valid ? l2 : -INFINITY;
+      }
+
+      // step max per head (8 waves, both blocks); the running max only
+      // moves when a step exceeds it by 2^8, so rescaling is rare and p
+      // stays below 256
+      const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
+      if (t == 0) wred[w][g4] = mloc;
+      __syncthreads();
+      const int hb = t >> 2;
+      float bm_a = wred[0][g4], bm_b = wred[0][hb];
+#pragma unroll
+      for (int u = 1; u < kWaves; ++u) {
+        bm_a = fmaxf(bm_a, wred[u][g4]);
+        bm_b = fmaxf(bm_b, wred[u][hb]);
+      }
+      const float mn_a = (bm_a > m_a + 8.0f) ? bm_a : m_a;
+      const float mn_b = (bm_b > m_b + 8.0f) ? bm_b : m_b;
+      const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_a - mn_a);
+      const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_b - mn_b);
+      m_a = mn_a;
+      m_b = mn_b;
+
+      // probabilities and fp8 limbs of p * value radius (3 limbs, ~12 bits)
+      const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - m_a);
+      const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - m_a);
+      lsum = lsum * fh + (p0 + p1);
+      float r0 = (p0 > 0.0f) ? p0 * h2f(cur.vn) : 0.0f;
+      float r1 = (p1 > 0.0f) ? p1 * h2f(cur.vn >> 16) : 0.0f;
+      const float pm = row_max16(fmaxf(r0, r1));
+      const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 7 : 0;
+      uint32_t ebytes = 127u << 24;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int sj = s0 - 4 * j;
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(r0, -sj),
+                                                       __builtin_amdgcn_ldexpf(r1, -sj), 0, false);
+        if (j < 2) {
+          r0 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), sj);
+          r1 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), sj);
+        }
+        *reinterpret_cast<uint16_t*>(&my_plimb[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) =
+            static_cast<uint16_t>(pk & 0xffff);
+        ebytes |= static_cast<uint32_t>(min(max(sj + 127, 1), 254)) << (8 * j);
+      }
+      if (t == 0) *reinterpret_cast<uint32_t*>(&pexp[gr][wl][4 * g4]) = ebytes;
+      __syncthreads();
+      // (no third barrier: the next writes of wred and of this group's
+      // limbs come after the next step's first barrier, which every wave
+      // reaches only after its reads below)
+
+      // weighted sum of value terms for coordinates 32wl + 16r + (row), columns (head, limb)
+      if (__any(fv != 1.0f)) {   // rescale only when some head's max moved
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
+      }
+      v8i Pv;
+      {
+        const uint4 lo = *reinterpret_cast<const uint4*>(&my_plimb[t * 128 + 16 * g4]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&my_plimb[t * 128 + 64 + 16 * g4]);
+        Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      const int scp = pexp[gr][g4][t];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+        for (int T = 0; T < NTV; ++T)
+          accV[rr][T] = mfma_fp4_fp8(expand_fp4(term_word<VB>(cur.vw[rr], T)), Pv, accV[rr][T], scp);
+      }
+    };
+    int i0 = 0;
+    for (; i0 + kR <= n_iter; i0 += kR) {
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        step(ring[r], i0 + r);
+        // refill after the last read of this slot (the scheduling barrier
+        // keeps the loads from being hoisted above it, which would force
+        // copies that wait for the new data)
+        __builtin_amdgcn_sched_barrier(0);
+        const int bn = blk0 + gr + 2 * (i0 + r + kR);   // past blk1: reads as zero
+        load_block<KB, QJL, VB>(ring[r], rk, rv, bn * kbb, bn * vbb, wl, t, g4);
+      }
+    }
+    const int rem = n_iter - i0;   // 0 .. kR - 1, uniform
+    if (rem > 0) {
+      step(ring[0], i0);
+      if (rem > 1) {
+        step(ring[1], i0 + 1);
+        if constexpr (kR > 3) {
+          if (rem > 2) step(ring[2], i0 + 2);
+        }
+      }
+    }
+  }
+
+  // ------------------------------------------------------------- partials
+  // denominator per (wave, head); running max per head; the two groups'
+  // weighted sums per coordinate
+  {
+    const float ls = row_sum16(lsum);
+    if (t == 0) wred[w][g4] = ls;
+    if (w == 0 && t == 0) mrun[g4] = m_a;
+    const int hc = t >> 2;   // head of this lane's result column
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
+      float v[4];
 #pragma unroll
-      for (int T = 0; T < NTV; ++T) accV[r][T] = mfma_fp4_fp8(expand_fp4(term_word<VB>(cur.vw[r], T)), Pv, accV[r][T], scp);
+      for (int i = 0; i < 4; ++i) {
+        float s = 0.0f;
+#pragma unroll
+        for (int T = 0; T < NTV; ++T) s = fmaf(av[T], accV[r][T][i], s);
+        s += __shfl_xor(s, 1, 64);   // sum the 4 limb columns of head hc
+        s += __shfl_xor(s, 2, 64);
+        v[i] = s;
+      }
+      if (hc < G && (t & 3) == 0)
+        *reinterpret_cast<float4*>(&obuf[gr][hc][32 * wl + 16 * r + 4 * g4]) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    __syncthreads();
-    cur = nx1;
-    nx1 = nx2;
   }
-
-  // ----------------------------------------------------------- partials
-  // denominator per head: lanes of row g4 in every wave
-  const float ls = row_sum16(lsum);
-  if (t == 0) wred[w][g4] = ls;
   __syncthreads();
-  const int hc = t >> 2;   // head of this lane's result column
-  const int64_t pstride = kPartialStride;
+  if (w < G) {
+    // wave w: head w, o = D_V H (sum of both groups) / d
+    float lo = obuf[0][w][lane] + obuf[1][w][lane];
+    float hi = obuf[0][w][lane + 64] + obuf[1][w][lane + 64];
+    wave_fwht128(lo, hi, lane);
+    const float inv_d = 1.0f / static_cast<float>(kD);
+    lo *= a.tb.dv[lane] * inv_d;
+    hi *= a.tb.dv[lane + 64] * inv_d;
+    float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + w) * a.n_splits + split) * kPartialStride;
+    store_coherent(pp + lane, lo);
+    store_coherent(pp + 64 + lane, hi);
+    if (lane == 0) {
+      float l = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = 0.0f;
-#pragma unroll
-      for (int T = 0; T < NTV; ++T) s = fmaf(av[T], accV[r][T][i], s);
-      s += __shfl_xor(s, 1, 64);    // sum the 4 limb columns of head hc
-      s += __shfl_xor(s, 2, 64);
-      v[i] = s;
+      for (int u = 0; u < kWaves; ++u) l += wred[u][w];
+      store_coherent(pp + kD, mrun[w] * kLn2);
+      store_coherent(pp + kD + 1, l);
     }
-    if (hc < G && (t & 3) == 0) {
-      float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + hc) * a.n_splits + split) * pstride;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) store_coherent(pp + 32 * w + 16 * r + 4 * g4 + i, v[i]);
-    }
-  }
-  if (w == 0 && g4 == 0 && (t & 3) == 0 && hc < G) {   // one lane per head: running max and denominator
-    float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + hc) * a.n_splits + split) * pstride;
-    store_coherent(pp + kD, m_b * kLn2);
-    store_coherent(pp + kD + 1, (wred[0][hc] + wred[1][hc]) + (wred[2][hc] + wred[3][hc]));
   }
   if (!arrive_last(a.counters + b * a.n_kv + h, a.n_splits, &s_last)) return;
-  combine_splits(a, b, h, qr, kThreads);
+  merge_splits(a, b, h, __builtin_amdgcn_readfirstlane(w), lane);
 }
 
 template <int KB, bool QJL, int VB>
@@ -500,15 +651,23 @@ hipError_t launch_v(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+bool decode_mfma_applies(int k_codec, int v_codec, int group) {
+  return v_codec == POLAR && group <= 4 && (k_codec == POLAR || k_codec == POLAR_QJL);
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  if (a.v_codec != POLAR || a.group > 4) return hipErrorNotSupported;
+  if (!decode_mfma_applies(a.k_codec, a.v_codec, a.group)) return hipErrorNotSupported;
+  // block byte offsets (up to n_blocks + 2 kRing blocks) are 32-bit buffer offsets
+  const int64_t span = (static_cast<int64_t>(a.n_blocks) + 2 * kRing + 2) * std::max(a.k_block_bytes, a.v_block_bytes);
+  if (span >= (int64_t{1} << 31) || static_cast<int64_t>(a.n_splits) * kPartialStride * 4 >= (int64_t{1} << 31))
+    return hipErrorNotSupported;
   if (a.k_codec == POLAR_QJL) {
     switch (a.k_bits) {
       case 2: return launch_v<2, true>(a, stream);
       case 3: return launch_v<3, true>(a, stream);
       case 4: return launch_v<4, true>(a, stream);
     }
-  } else if (a.k_codec == POLAR) {
+  } else {
     switch (a.k_bits) {
       case 2: return launch_v<2, false>(a, stream);
       case 3: return launch_v<3, false>(a, stream);

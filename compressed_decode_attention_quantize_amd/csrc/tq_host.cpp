@@ -305,12 +305,18 @@ tq::Tables tables(const tq_config* c, const void* params) {
   return t;
 }
 
+int64_t target_workgroups(const tq_config* c) {
+  return tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads) ? tq::kMfmaWorkgroups
+                                                                                        : tq::kValuWorkgroups;
+}
+
 int decode_chunk_blocks(const tq_config* c, int32_t max_seq_len) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return c->decode_chunk / kBlock;
-  // aim for about 512 workgroups over the whole grid (2 per compute unit)
+  // aim for the kernel's workgroup count over the whole grid
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-  const int64_t want_splits = std::max<int64_t>(1, (512 + pairs - 1) / pairs);
+  const int64_t target = target_workgroups(c);
+  const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
   return static_cast<int>(std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits));
 }
 
@@ -326,7 +332,8 @@ int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return (blocks + c->decode_chunk / kBlock - 1) / (c->decode_chunk / kBlock);
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-  const int64_t want_splits = std::max<int64_t>(1, (512 + pairs - 1) / pairs);
+  const int64_t target = target_workgroups(c);
+  const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
   return static_cast<int>(std::min<int64_t>(blocks, want_splits));
 }
 

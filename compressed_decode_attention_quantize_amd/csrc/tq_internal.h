@@ -113,7 +113,13 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Matrix-core decode for POLAR / POLAR_QJL keys with POLAR values and G <= 4;
 // returns hipErrorNotSupported for other configurations.
+bool decode_mfma_applies(int k_codec, int v_codec, int group);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// Workgroups the automatic split count aims for: the matrix-core kernel runs
+// one 512-thread workgroup per compute unit (256 on the target chip), the
+// VALU kernel about two 256-thread workgroups per compute unit.
+constexpr int kMfmaWorkgroups = 256;
+constexpr int kValuWorkgroups = 512;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 
 }  // namespace tq
