@@ -59,7 +59,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;   // two groups of four
-constexpr int kRing = 4;    // blocks in flight per group (3 for 4-bit keys with 4-bit values: registers)
+constexpr int kRing = 4;    // most ring slots (block pairs) in shared memory
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -143,54 +143,71 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, 127, 0, sb);
 }
 
-template <int KB, int VB>
-struct BlockRegs {
-  uint2 kp[KB];       // key code words, slots 32w + 2t and +1, coordinate group g4
-  uint2 ks;           // sign words
-  uint32_t kn, kr, vn;  // two fp16 key radii, residual norms, value radii
-  uint32_t vw[2][VB];   // value words for coordinates 32w + 16r + t, positions 32 g4 ..
+// Byte layout of one cache block (128 positions) and of the shared-memory
+// ring that stages two blocks per step.
+template <int KB, bool QJL, int VB>
+struct Fmt {
+  static constexpr int kNorms = 2048 * KB + (QJL ? 2048 : 0);         // fp16 radii after planes (and signs)
+  static constexpr int kBytes = kNorms + 256 + (QJL ? 256 : 0);       // K block
+  static constexpr int vBytes = 2048 * VB + 256;                       // V block: planes, fp16 radii
+  static constexpr int kChunks = (2 * kBytes + 1023) / 1024;           // 1 KB copy units per step (two blocks)
+  static constexpr int vChunks = (2 * vBytes + 1023) / 1024;
+  static constexpr int perWave = (kChunks + vChunks + kWaves - 1) / kWaves;   // copies per wave per step
+  static constexpr int slotBytes = (kChunks + vChunks) * 1024;
+  static constexpr int kOtherLds = 31 * 1024;   // everything else the kernel keeps in shared memory
+  static constexpr int slotsFit = (160 * 1024 - kOtherLds) / slotBytes;
+  static constexpr int nSlots = slotsFit < kRing ? slotsFit : kRing;
+  static_assert(nSlots >= 2, "ring needs two slots");
 };
 
-// Buffer resource over one (sequence, KV head)'s blocks [0, n_valid): loads at
+// Buffer resource over one (sequence, KV head)'s blocks [0, n_valid): reads at
 // offsets past the end return zero without touching memory (raw buffer,
-// stride 0; the range check covers the per-lane offset), so blocks past a
-// split's chunk need no branch around their loads.
+// stride 0; the range check covers the per-lane offset).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t block_bytes, int n_valid) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0),
                                            static_cast<int>(block_bytes * n_valid), 0x00020000);
 }
-__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ uint2 ld64(__amdgpu_buffer_rsrc_t r, int off) {
-  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-  const v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  return make_uint2(x[0], x[1]);
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Copies the two blocks b0, b0 + 1 (K region then V region) into a ring slot
+// straight from memory into shared memory, 1 KB per instruction (lane l moves
+// bytes 16l..16l+15 of its unit).  Every wave issues the same number of copies;
+// units past the data read zero into a junk buffer, so the count of
+// outstanding copies per wave is the same at every step.
+template <int KB, bool QJL, int VB>
+__device__ __forceinline__ void copy_pair(uint8_t* slot, uint8_t* junk, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, int b0, int w, int lane) {
+  using F = Fmt<KB, QJL, VB>;
+#pragma unroll
+  for (int j = 0; j < F::perWave; ++j) {
+    const int q = w + kWaves * j;   // unit, uniform over the wave
+    const bool isk = q < F::kChunks;
+    const bool isv = !isk && q < F::kChunks + F::vChunks;
+    const int off = isk ? b0 * F::kBytes + 1024 * q + 16 * lane
+                        : (isv ? b0 * F::vBytes + 1024 * (q - F::kChunks) + 16 * lane : 0x7fff0000 + 16 * lane);
+    uint8_t* dst = (isk || isv) ? slot + 1024 * q : junk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, (lds_void_t*)(dst), 16, off, 0, 0, 0);
+  }
 }
 
-// Loads the operands of one block at byte offsets kofs / vofs of the K / V
-// resources; w is the wave within its group.
-template <int KB, bool QJL, int VB>
-__device__ __forceinline__ void load_block(BlockRegs<KB, VB>& R, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                           int kofs, int vofs, int w, int t, int g4) {
-  const int so = 4 * (g4 * kBlock + 32 * w + 2 * t);
-#pragma unroll
-  for (int p = 0; p < KB; ++p) R.kp[p] = ld64(rk, kofs + p * 16 * kBlock + so);
-  int after = kofs + 16 * KB * kBlock;
-  if (QJL) {
-    R.ks = ld64(rk, after + so);
-    after += 16 * kBlock;
-    R.kr = ld32(rk, after + 2 * kBlock + 2 * (32 * w + 2 * t));
-  } else {
-    R.ks = make_uint2(0u, 0u);
-    R.kr = 0u;
-  }
-  R.kn = ld32(rk, after + 2 * (32 * w + 2 * t));
-  R.vn = ld32(rv, vofs + 16 * VB * kD + 2 * (32 * w + 2 * t));
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int p = 0; p < VB; ++p) R.vw[r][p] = ld32(rv, vofs + 4 * (p * 4 * kD + g4 * kD + 32 * w + 16 * r + t));
+// Workgroup barrier for shared-memory data only: waits for this wave's
+// shared-memory operations, not for its copies in flight (a fenced barrier
+// would drain those), and keeps the compiler from moving memory accesses
+// across it.  Copies into the ring are covered by explicit waits.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Waits until at most n copies (or other vector memory operations) issued by
+// this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Max / sum over the 32 lanes of each half-wave (rows via DPP, then the
@@ -272,9 +289,17 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int h, 
 
 template <int KB, bool QJL, int VB>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
+  using F = Fmt<KB, QJL, VB>;
   constexpr int NTK = NTerms<KB>::n;
   constexpr int NTV = NTerms<VB>::n;
-  constexpr int kR = (KB + VB >= 8) ? kRing - 1 : kRing;
+  constexpr int NS = F::nSlots;
+  // ring of block pairs: one array per slot, so that the compiler can tell
+  // the slots' copies apart when it places its waits
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[F::slotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[F::slotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[NS > 2 ? F::slotBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot3[NS > 3 ? F::slotBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t junk[1024];
   __shared__ float qr[4 * kD];              // q_raw = H D_K q per head (zero rows past G)
   __shared__ float sqs[4 * kM];             // S q_raw / sqrt d
   __shared__ __attribute__((aligned(16))) uint8_t alimb[2][16 * 128];  // fp8 limbs [set][row = 4g + j][k]
@@ -284,14 +309,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ float wred[kWaves][4];
   __shared__ float hmax[2][kWaves];         // per-wave max |value| for the limb exponents
   __shared__ float mrun[4];                 // running max per head at the end (log2 units)
-  __shared__ __attribute__((aligned(16))) float sred[16][4 * kM];   // partial sketch sums
-  __shared__ __attribute__((aligned(16))) float obuf[2][4][kD];     // per group: weighted sums
+  __shared__ __attribute__((aligned(16))) float sred[8][4 * kM];   // partial sketch sums; later the group sums
   __shared__ int s_last;
+  uint8_t* const slots[4] = {slot0, slot1, slot2, slot3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int gr = w >> 2;   // group: blocks blk0 + gr, blk0 + gr + 2, ...
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: buffer resources stay scalar
+  const int gr = w >> 2;   // group: the first or second block of each step
   const int wl = w & 3;    // wave within the group
   const int t = lane & 15;
   const int g4 = lane >> 4;
@@ -304,14 +329,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int blk0 = split * a.chunk_blocks;
   const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
   const int n_iter = max(0, (blk1 - blk0 + 1) / 2);   // steps of two blocks
-  const int64_t slot0 = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
+  const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const float inv_sqrt_d = 0.08838834764831845f;
 
-  // running max (log2 units) of head g4 (this lane's logits row) and of head
-  // t / 4 (this lane's result column); both follow the same step maxima
   float av[NTV];
 #pragma unroll
   for (int T = 0; T < NTV; ++T) av[T] = a.tb.av[T];
+  // running max (log2 units) of head g4 (this lane's logits row) and of head
+  // t / 4 (this lane's result column); both follow the same step maxima
   float m_a = -INFINITY, m_b = -INFINITY;
   float lsum = 0.0f;   // this lane's share of the denominator of head g4
   v4f accV[2][NTV];
@@ -321,35 +346,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (n_iter > 0) {   // uniform over the workgroup
-    // query and sketch loads go out first (their results return first), then
-    // the first kR blocks of each group
-    const int jq = tid & 31, ic = tid >> 5;   // sketch rows 4jq..4jq+3, coordinates 8ic..8ic+7
-    float4 st4[8];
+    // loads the set-up needs are issued first (outstanding loads retire in
+    // order), then the copies of the first NS - 1 block pairs
+    const int jq = tid & 63;   // sketch rows 2jq, 2jq + 1; coordinates 16w .. 16w + 15
+    float2 st2[16];
     if (QJL) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) st4[u] = *reinterpret_cast<const float4*>(a.tb.st + (8 * ic + u) * kM + 4 * jq);
+      for (int u = 0; u < 16; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.st + (16 * w + u) * kM + 2 * jq);
     }
-    // (unconditional loads: a branch here would make the compiler wait for
-    // every block load before the set-up arithmetic)
     const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + h * G + min(w & 3, G - 1)) * kD;
     const float qa = qp[lane], qb = qp[lane + 64];
     const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
     float ak[NTK];
 #pragma unroll
     for (int T = 0; T < NTK; ++T) ak[T] = a.tb.ak[T];
-    // every load whose result is needed before the main loop is issued above
-    // this point: the counter of outstanding loads drains in order, so a
-    // later one would wait for all block loads
     __builtin_amdgcn_sched_barrier(0);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0 * a.k_block_bytes, a.k_block_bytes, blk1);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0 * a.v_block_bytes, a.v_block_bytes, blk1);
-    const int kbb = static_cast<int>(a.k_block_bytes), vbb = static_cast<int>(a.v_block_bytes);
-    BlockRegs<KB, VB> ring[kR];
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, blk1);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
 #pragma unroll
-    for (int r = 0; r < kR; ++r) {
-      const int bi = blk0 + gr + 2 * r;   // past blk1: reads as zero
-      load_block<KB, QJL, VB>(ring[r], rk, rv, bi * kbb, bi * vbb, wl, t, g4);
-    }
+    for (int r = 0; r < NS - 1; ++r) copy_pair<KB, QJL, VB>(slots[r], junk, rk, rv, blk0 + 2 * r, w, lane);
 
     // ------------------------------------------------------------- set-up
     // waves 0..3 rotate the query of head w in registers: q_raw = H D_K q
@@ -364,40 +379,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       for (int off = 32; off >= 1; off >>= 1) qm = fmaxf(qm, __shfl_xor(qm, off, 64));
       if (lane == 0) hmax[0][w] = qm;
     }
-    __syncthreads();
+    lds_barrier();
     if (QJL) {
-      // sq = S q_raw / sqrt d: partial sums over 8 coordinates per thread, then over the 16 partials
-      float acc[4][4];
+      // sq = S q_raw / sqrt d: partial sums over 16 coordinates per thread, then over the 8 partials
+      float acc[4][2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[g][jj] = 0.0f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float qv = qr[g * kD + 8 * ic + u];
-          acc[g][0] = fmaf(st4[u].x, qv, acc[g][0]);
-          acc[g][1] = fmaf(st4[u].y, qv, acc[g][1]);
-          acc[g][2] = fmaf(st4[u].z, qv, acc[g][2]);
-          acc[g][3] = fmaf(st4[u].w, qv, acc[g][3]);
+          const float qv = qr[g * kD + 16 * w + u];
+          acc[g][0] = fmaf(st2[u].x, qv, acc[g][0]);
+          acc[g][1] = fmaf(st2[u].y, qv, acc[g][1]);
         }
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(&sred[ic][g * kM + 4 * jq]) = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
-      __syncthreads();
+      for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g * kM + 2 * jq]) = make_float2(acc[g][0], acc[g][1]);
+      lds_barrier();
       // thread tid owns output tid: head tid / 128, so waves 2g and 2g+1 cover head g
       float sum = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) sum += sred[c][tid];
+      for (int c = 0; c < 8; ++c) sum += sred[c][tid];
       sum *= inv_sqrt_d;
       sqs[tid] = sum;
       float m1 = fabsf(sum);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
       if (lane == 0) hmax[1][w] = m1;
-      __syncthreads();
+      lds_barrier();
     }
     {
       // fp8 limbs of q_raw (waves 0..3, set 0) and sq (waves 4..7, set 1), one
@@ -426,7 +436,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     }
     // the fourth limb column of each head stays zero (three limbs are written)
     for (int k = tid; k < 2 * 4 * 128; k += kThreads) plimb[k >> 9][(4 * ((k >> 7) & 3) + 3) * 128 + (k & 127)] = 0;
-    __syncthreads();
+    // the first pair has landed (this wave's copies; the barrier covers the others')
+    wait_vm<(NS - 2) * F::perWave>();
+    lds_barrier();
     v8i Aq, Asq;
     int scq, scsq = 127;
     {
@@ -446,31 +458,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
     const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
     uint8_t* my_plimb = plimb[gr];
+    const int so = 4 * (g4 * kBlock + 32 * wl + 2 * t);   // this lane's key words in a block
+    const int sn = 2 * (32 * wl + 2 * t);                 // its two fp16 per-position fields
 
     // --------------------------------------------------------- main loop
-    // step i: group gr takes block blk0 + gr + 2i from ring slot i % kR; in
-    // the main loop it refills that slot with block blk0 + gr + 2(i + kR).
-    // The loop runs whole rounds of the ring with no side exits and the last
-    // partial round follows as nested conditionals: exits in the middle of a
-    // round would give the compiler paths on which a slot was loaded more
-    // recently, and it would then wait for loads issued in the same step.
-    auto step = [&](BlockRegs<KB, VB>& cur, int i) __attribute__((always_inline)) {
-      const int blk = blk0 + gr + 2 * i;
+    // Step i processes blocks blk0 + 2i (group 0) and blk0 + 2i + 1 (group 1)
+    // from ring slot i % NS.  After its first barrier (every wave has then
+    // finished step i - 1) it refills slot (i - 1) % NS with the pair of step
+    // i + NS - 1; before its second barrier each wave waits for its copies of
+    // the pair of step i + 1.
+    auto step = [&](uint8_t* cur, uint8_t* refill, int i) __attribute__((always_inline)) {
+      const int blk = blk0 + 2 * i + gr;
       const int n_t = (blk < blk1) ? min(kBlock, len - blk * kBlock) : 0;
+      const uint8_t* kb = cur + gr * F::kBytes;
+      const uint8_t* vb = cur + F::kChunks * 1024 + gr * F::vBytes;
 
       // logits of k-slots 32wl + 2t + c for head g4: every MFMA of the block
       // is issued before any result is read
+      uint2 kp[KB];
+#pragma unroll
+      for (int p = 0; p < KB; ++p) kp[p] = *reinterpret_cast<const uint2*>(kb + p * 2048 + so);
+      const uint2 ks = QJL ? *reinterpret_cast<const uint2*>(kb + 2048 * KB + so) : make_uint2(0u, 0u);
+      const uint32_t kn = *reinterpret_cast<const uint32_t*>(kb + F::kNorms + sn);
+      const uint32_t kr = QJL ? *reinterpret_cast<const uint32_t*>(kb + F::kNorms + 256 + sn) : 0u;
       v4f dT[2][NTK];
       v4f dQ[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         uint32_t wd[KB];
 #pragma unroll
-        for (int p = 0; p < KB; ++p) wd[p] = c ? cur.kp[p].y : cur.kp[p].x;
+        for (int p = 0; p < KB; ++p) wd[p] = c ? kp[p].y : kp[p].x;
 #pragma unroll
         for (int T = 0; T < NTK; ++T)
           dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
-        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4(c ? cur.ks.y : cur.ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
+        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4(c ? ks.y : ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
       }
       float lg2[2];
 #pragma unroll
@@ -481,21 +502,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           code = fmaf(ak[T], (dT[c][T][0] + dT[c][T][1]) + (dT[c][T][2] + dT[c][T][3]), code);
         const float qj = QJL ? (dQ[c][0] + dQ[c][1]) + (dQ[c][2] + dQ[c][3]) : 0.0f;
         const int tok = pos_of_slot(32 * wl + 2 * t + c);
-        const float nk = h2f(c ? (cur.kn >> 16) : cur.kn);
-        const float rho = QJL ? h2f(c ? (cur.kr >> 16) : cur.kr) : 0.0f;
-        const float l2 = alpha2 * nk * code + beta2 * rho * qj;
+        const float nk = h2f(c ? (kn >> 16) : kn);
+        const float rho = QJL ? h2f(c ? (kr >> 16) : kr) : 0.0f;
+        // explicit roundings: every unrolled copy of the step computes the same bits
+        const float l2 = fmaf(__fmul_rn(alpha2, nk), code, QJL ? __fmul_rn(__fmul_rn(beta2, rho), qj) : 0.0f);
         const bool valid = (tok < n_t) && (g4 < G);
         if (a.logits != nullptr && valid)
-          a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g4) * a.max_ctx + blk * kBlock + tok] = l2 * kLn2;
+          a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
         lg2[c] = valid ? l2 : -INFINITY;
       }
 
-      // step max per head (8 waves, both blocks); the running max only
-      // moves when a step exceeds it by 2^8, so rescaling is rare and p
-      // stays below 256
+      // step max per head (8 waves, both blocks); the running max only moves
+      // when a step exceeds it by 2^8, so rescaling is rare and p stays below 256
       const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
       if (t == 0) wred[w][g4] = mloc;
-      __syncthreads();
+      lds_barrier();
+      copy_pair<KB, QJL, VB>(refill, junk, rk, rv, blk0 + 2 * (i + NS - 1), w, lane);
       const int hb = t >> 2;
       float bm_a = wred[0][g4], bm_b = wred[0][hb];
 #pragma unroll
@@ -511,11 +533,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       m_b = mn_b;
 
       // probabilities and fp8 limbs of p * value radius (3 limbs, ~12 bits)
+      const uint32_t vn = *reinterpret_cast<const uint32_t*>(vb + 2048 * VB + sn);
       const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - m_a);
       const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - m_a);
       lsum = lsum * fh + (p0 + p1);
-      float r0 = (p0 > 0.0f) ? p0 * h2f(cur.vn) : 0.0f;
-      float r1 = (p1 > 0.0f) ? p1 * h2f(cur.vn >> 16) : 0.0f;
+      float r0 = (p0 > 0.0f) ? p0 * h2f(vn) : 0.0f;
+      float r1 = (p1 > 0.0f) ? p1 * h2f(vn >> 16) : 0.0f;
       const float pm = row_max16(fmaxf(r0, r1));
       const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 7 : 0;
       uint32_t ebytes = 127u << 24;
@@ -533,10 +556,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         ebytes |= static_cast<uint32_t>(min(max(sj + 127, 1), 254)) << (8 * j);
       }
       if (t == 0) *reinterpret_cast<uint32_t*>(&pexp[gr][wl][4 * g4]) = ebytes;
-      __syncthreads();
-      // (no third barrier: the next writes of wred and of this group's
-      // limbs come after the next step's first barrier, which every wave
-      // reaches only after its reads below)
+      wait_vm<(NS - 2) * F::perWave>();   // this wave's copies of the next pair have landed
+      lds_barrier();
+      // (no third barrier: the next writes of wred and of this group's limbs
+      // come after the next step's first barrier, which every wave reaches
+      // only after its reads below)
 
       // weighted sum of value terms for coordinates 32wl + 16r + (row), columns (head, limb)
       if (__any(fv != 1.0f)) {   // rescale only when some head's max moved
@@ -554,31 +578,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       const int scp = pexp[gr][g4][t];
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
+        uint32_t vw[VB];
 #pragma unroll
-        for (int T = 0; T < NTV; ++T)
-          accV[rr][T] = mfma_fp4_fp8(expand_fp4(term_word<VB>(cur.vw[rr], T)), Pv, accV[rr][T], scp);
+        for (int p = 0; p < VB; ++p)
+          vw[p] = *reinterpret_cast<const uint32_t*>(vb + 4 * (p * 4 * kD + g4 * kD + 32 * wl + 16 * rr + t));
+#pragma unroll
+        for (int T = 0; T < NTV; ++T) accV[rr][T] = mfma_fp4_fp8(expand_fp4(term_word<VB>(vw, T)), Pv, accV[rr][T], scp);
       }
     };
+    // whole rounds of the ring, then the last partial round; slot indices are
+    // compile-time constants in every step
     int i0 = 0;
-    for (; i0 + kR <= n_iter; i0 += kR) {
+    for (; i0 + NS <= n_iter; i0 += NS) {
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        step(ring[r], i0 + r);
-        // refill after the last read of this slot (the scheduling barrier
-        // keeps the loads from being hoisted above it, which would force
-        // copies that wait for the new data)
-        __builtin_amdgcn_sched_barrier(0);
-        const int bn = blk0 + gr + 2 * (i0 + r + kR);   // past blk1: reads as zero
-        load_block<KB, QJL, VB>(ring[r], rk, rv, bn * kbb, bn * vbb, wl, t, g4);
-      }
+      for (int r = 0; r < NS; ++r) step(slots[r], slots[(r + NS - 1) % NS], i0 + r);
     }
-    const int rem = n_iter - i0;   // 0 .. kR - 1, uniform
+    const int rem = n_iter - i0;   // 0 .. NS - 1, uniform
     if (rem > 0) {
-      step(ring[0], i0);
+      step(slots[0], slots[NS - 1], i0);
       if (rem > 1) {
-        step(ring[1], i0 + 1);
-        if constexpr (kR > 3) {
-          if (rem > 2) step(ring[2], i0 + 2);
+        step(slots[1], slots[0], i0 + 1);
+        if constexpr (NS > 3) {
+          if (rem > 2) step(slots[2], slots[1], i0 + 2);
         }
       }
     }
@@ -586,7 +607,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
   // ------------------------------------------------------------- partials
   // denominator per (wave, head); running max per head; the two groups'
-  // weighted sums per coordinate
+  // weighted sums per coordinate (in the sketch buffer, free by now)
+  float (*obuf)[4][kD] = reinterpret_cast<float (*)[4][kD]>(&sred[0][0]);
   {
     const float ls = row_sum16(lsum);
     if (t == 0) wred[w][g4] = ls;
@@ -629,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     }
   }
   if (!arrive_last(a.counters + b * a.n_kv + h, a.n_splits, &s_last)) return;
-  merge_splits(a, b, h, __builtin_amdgcn_readfirstlane(w), lane);
+  merge_splits(a, b, h, w, lane);
 }
 
 template <int KB, bool QJL, int VB>
@@ -658,7 +680,7 @@ bool decode_mfma_applies(int k_codec, int v_codec, int group) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (!decode_mfma_applies(a.k_codec, a.v_codec, a.group)) return hipErrorNotSupported;
   // block byte offsets (up to n_blocks + 2 kRing blocks) are 32-bit buffer offsets
-  const int64_t span = (static_cast<int64_t>(a.n_blocks) + 2 * kRing + 2) * std::max(a.k_block_bytes, a.v_block_bytes);
+  const int64_t span = (static_cast<int64_t>(a.n_blocks) + 2 * kRing + 4) * std::max(a.k_block_bytes, a.v_block_bytes);
   if (span >= (int64_t{1} << 31) || static_cast<int64_t>(a.n_splits) * kPartialStride * 4 >= (int64_t{1} << 31))
     return hipErrorNotSupported;
   if (a.k_codec == POLAR_QJL) {
