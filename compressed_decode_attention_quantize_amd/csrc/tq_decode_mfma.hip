@@ -11,15 +11,22 @@
 //    over the odd subsets T (b = 2: 2 terms; 3: 4; 4: 8).  Each term is a
 //    +/-1 vector whose bits are a code plane or the XOR of three planes, and
 //    <q, C[c]> = sum_T a_T <q, s_T>.  The QJL term <Sq, sign> has the same form.
-//  * A +/-1 bit vector becomes an fp4 (e2m1) matrix operand in two integer
-//    operations per 8 elements; the query side (q_raw = H D_K q and
-//    sq = S q_raw / sqrt d) is split into four fp8 (e4m3) limbs with one
-//    E8M0 scale per 32 elements (about 16 significant bits), so
-//    v_mfma_scale_f32_16x16x128_f8f6f4 computes 4 heads x 4 limbs x 16
-//    positions x 128 coordinates per instruction with fp32 accumulation.
+//  * A bit vector becomes an fp4 (e2m1) matrix operand in one integer
+//    operation per 8 elements by leaving each bit where it lies and filling
+//    the other fields of its nibble (see expand_fp4_affine): the elements are
+//    affine in the signs, and the offset, one constant per head, is removed
+//    after the product.  Value words use the two-operation +/-1 form.
+//  * The query side (q_raw = H D_K q and sq = S q_raw / sqrt d) is written as
+//    four base-32 fixed-point digits, integers in [-16, 16] that e4m3 holds
+//    exactly, with one E8M0 scale per digit (about 19 significant bits).  The
+//    products are then small integers, and the 128-term sums of
+//    v_mfma_scale_f32_16x16x128_f8f6f4 are exact; with floating-point limbs
+//    the instruction's accumulation loses low bits of the small products.
+//    One instruction covers 4 heads x 4 digits x 16 positions x 128
+//    coordinates.
 //  * The weighted sum is the same contraction over positions: value planes
-//    (32 positions per word) are the fp4 operand, p * radius is split into
-//    fp8 limbs per 32 positions (three limbs, about 12 significant bits).
+//    (32 positions per word) are the fp4 operand, p * radius is written as
+//    three base-32 digits per 32 positions (about 14 significant bits).
 //
 // Operand layouts of the 16x16x128 instruction (lane l, element e): rows or
 // columns are l % 16; an fp4 operand holds k = 32 (l / 16) + e; an fp8
@@ -32,17 +39,17 @@
 // each lane's operands whole 8-byte loads.
 //
 // Mapping: grid (split, KV head, sequence); a workgroup is eight waves in two
-// groups of four that take alternate 128-position blocks of the split's chunk
-// in lockstep.  Within a group, wave w computes the logits of the block's
-// positions in k-slots [32w, 32w+32) (2 MFMA column groups), the eight waves
-// share each step's maximum (shared memory), each group writes its fp8 limbs
-// of p * radius, and wave w then computes its group's weighted sum for
-// coordinates [32w, 32w+32) over the group's block.  Each group keeps four
-// blocks of loads in flight in registers; the query set-up (rotation, sketch,
-// limbs) is done once per workgroup while the first loads are outstanding.
-// The two groups' sums are added in shared memory and rotated back
-// (D_V H / d) before they leave the workgroup, so the workgroup that merges
-// the splits only forms a weighted average.
+// groups of four, one per compute unit.  Each step takes two 128-position
+// blocks, one per group, from a ring of shared-memory slots that direct
+// memory-to-shared-memory copies fill several steps ahead.  Within a group,
+// wave w computes the logits of its block's positions in k-slots [32w, 32w+32)
+// (2 MFMA column groups), the eight waves share each step's maximum, each
+// group writes the digits of p * radius, and wave w then computes its group's
+// weighted sum for coordinates [32w, 32w+32).  The query set-up (rotation,
+// sketch, digits) is done once per workgroup while the first copies are in
+// flight.  The two groups' sums are added in shared memory and rotated back
+// (D_V H / d) before they leave the workgroup, so the workgroup that merges the
+// splits only forms a weighted average.
 
 #include <hip/hip_fp16.h>
 
@@ -56,6 +63,9 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+// read-only data at wave-uniform addresses: loads through the scalar cache
+typedef __attribute__((address_space(4))) const v4f cv4f;
+typedef __attribute__((address_space(4))) const float cfloat;
 
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;   // two groups of four
@@ -94,6 +104,23 @@ __device__ __forceinline__ v8i expand_fp4(uint32_t w) {
   return r;
 }
 
+// 32 bits -> 32 fp4 elements with each bit used where it lies: element
+// 8d + n is nibble n of dword d and takes bit 4n + d of w into nibble field d,
+// the other fields fixed: d = 0 (mantissa) {4, 6}, d = 1 (low exponent bit)
+// {2, 4}, d = 2 (high exponent bit) {0, 2}, d = 3 (sign) {+1, -1}.  With
+// s = +1 for a set bit the element is 5 + s, 3 + s, 1 + s, -s: one AND(-OR) per
+// dword.  The matrix operand on the other side carries -1 on the d = 3
+// elements, and the offsets 5, 3, 1 are removed with one constant per head.
+__device__ __forceinline__ v8i expand_fp4_affine(uint32_t w) {
+  v8i r;
+  r[0] = static_cast<int>((w & 0x11111111u) | 0x66666666u);
+  r[1] = static_cast<int>((w & 0x22222222u) | 0x44444444u);
+  r[2] = static_cast<int>(w & 0x44444444u);
+  r[3] = static_cast<int>((w & 0x88888888u) | 0x22222222u);
+  r[4] = r[5] = r[6] = r[7] = 0;
+  return r;
+}
+
 // Max / sum over the 16 lanes of a row (DPP: xor 1, xor 2, half-row mirror,
 // row mirror); every lane of the row ends with the result.
 __device__ __forceinline__ float row_max16(float x) {
@@ -111,23 +138,58 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// Value of lane (l ^ H) for lane l, by the cheapest cross-lane route: DPP
+// within 16-lane rows (xor 1, 2 as quad permutations; xor 4 = xor 3 then
+// xor 7; xor 8 = xor 7 then xor 15 via the half-row and row mirrors), the
+// 32-lane swizzle for xor 16, a permute for xor 32.
+template <int H>
+__device__ __forceinline__ float lane_xor(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (H == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  if constexpr (H == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  if constexpr (H == 4) {
+    const int u = __builtin_amdgcn_update_dpp(0, v, 0x1B, 0xF, 0xF, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, false));
+  }
+  if constexpr (H == 8) {
+    const int u = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x140, 0xF, 0xF, false));
+  }
+  if constexpr (H == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x401F));
+  if constexpr (H == 32) return __shfl_xor(x, 32, 64);
+  return x;
+}
+
+template <int H>
+__device__ __forceinline__ void butterfly(float& lo, float& hi, int lane) {
+  const float plo = lane_xor<H>(lo), phi = lane_xor<H>(hi);
+  const bool up = (lane & H) != 0;
+  lo = up ? plo - lo : lo + plo;
+  hi = up ? phi - hi : hi + phi;
+}
+
 // Raw Sylvester FWHT of 128 values held as (lo = coord lane, hi = coord lane+64).
 __device__ __forceinline__ void wave_fwht128(float& lo, float& hi, int lane) {
-#pragma unroll
-  for (int hh = 1; hh < 64; hh <<= 1) {
-    const float plo = __shfl_xor(lo, hh, 64);
-    const float phi = __shfl_xor(hi, hh, 64);
-    if (lane & hh) {
-      lo = plo - lo;
-      hi = phi - hi;
-    } else {
-      lo = lo + plo;
-      hi = hi + phi;
-    }
-  }
+  butterfly<1>(lo, hi, lane);
+  butterfly<2>(lo, hi, lane);
+  butterfly<4>(lo, hi, lane);
+  butterfly<8>(lo, hi, lane);
+  butterfly<16>(lo, hi, lane);
+  butterfly<32>(lo, hi, lane);
   const float x = lo, y = hi;
   lo = x + y;
   hi = x - y;
+}
+
+__device__ __forceinline__ float wave_max64(float x) {
+  x = row_max16(x);
+  x = fmaxf(x, lane_xor<16>(x));
+  return fmaxf(x, lane_xor<32>(x));
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+  x = row_sum16(x);
+  x += lane_xor<16>(x);
+  return x + lane_xor<32>(x);
 }
 
 __device__ __forceinline__ int exponent_of(float x) {   // floor(log2 x), x > 0 normal
@@ -309,6 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ float wred[kWaves][4];
   __shared__ float hmax[2][kWaves];         // per-wave max |value| for the limb exponents
   __shared__ float mrun[4];                 // running max per head at the end (log2 units)
+  __shared__ float cconst[2][4];            // offsets of the affine key operand per (set, head)
   __shared__ __attribute__((aligned(16))) float sred[8][4 * kM];   // partial sketch sums; later the group sums
   __shared__ int s_last;
   uint8_t* const slots[4] = {slot0, slot1, slot2, slot3};
@@ -347,94 +410,113 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
   if (n_iter > 0) {   // uniform over the workgroup
     // loads the set-up needs are issued first (outstanding loads retire in
-    // order), then the copies of the first NS - 1 block pairs
+    // order): the rotation's inputs, this wave's slice of the raw queries,
+    // the sketch table; then the copies of the first NS - 1 block pairs
+    const float* qb0 = a.q + (static_cast<int64_t>(b) * a.n_q + h * G) * kD;
+    const float* qp = qb0 + min(w & 3, G - 1) * kD;
+    const float qa = qp[lane], qb = qp[lane + 64];
+    const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
+    // lane l: raw query coordinate 16w + l % 16 of head l / 16 (zero past G)
+    const float qsl = qb0[min(lane >> 4, G - 1) * kD + 16 * w + (lane & 15)];
     const int jq = tid & 63;   // sketch rows 2jq, 2jq + 1; coordinates 16w .. 16w + 15
     float2 st2[16];
     if (QJL) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.st + (16 * w + u) * kM + 2 * jq);
+      for (int u = 0; u < 16; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.shd + (16 * w + u) * kM + 2 * jq);
     }
-    const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + h * G + min(w & 3, G - 1)) * kD;
-    const float qa = qp[lane], qb = qp[lane + 64];
-    const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
     float ak[NTK];
+    float aksum = 0.0f;
+    {
+      const cfloat* akp = (const cfloat*)(a.tb.ak);
 #pragma unroll
-    for (int T = 0; T < NTK; ++T) ak[T] = a.tb.ak[T];
+      for (int T = 0; T < NTK; ++T) ak[T] = akp[T];
+    }
     __builtin_amdgcn_sched_barrier(0);
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, blk1);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
-#pragma unroll
-    for (int r = 0; r < NS - 1; ++r) copy_pair<KB, QJL, VB>(slots[r], junk, rk, rv, blk0 + 2 * r, w, lane);
+    // the first NS - 1 pairs (at most three) are issued one per set-up phase
+    // (pair 0 here), so that the copies proceed while the waves compute
+    copy_pair<KB, QJL, VB>(slots[0], junk, rk, rv, blk0, w, lane);
 
     // ------------------------------------------------------------- set-up
-    // waves 0..3 rotate the query of head w in registers: q_raw = H D_K q
+    // waves 0..3 rotate the query of head w in registers (q_raw = H D_K q);
+    // meanwhile every wave forms its share of the sketch S q_raw / sqrt d as
+    // (S H D_K / sqrt d) q, which needs no rotated query
     if (w < 4) {
       float q_lo = (w < G) ? qa * da : 0.0f;
       float q_hi = (w < G) ? qb * db : 0.0f;
       wave_fwht128(q_lo, q_hi, lane);
       qr[w * kD + lane] = q_lo;
       qr[w * kD + lane + 64] = q_hi;
-      float qm = fmaxf(fabsf(q_lo), fabsf(q_hi));
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) qm = fmaxf(qm, __shfl_xor(qm, off, 64));
+      const float qm = wave_max64(fmaxf(fabsf(q_lo), fabsf(q_hi)));
       if (lane == 0) hmax[0][w] = qm;
     }
-    lds_barrier();
     if (QJL) {
-      // sq = S q_raw / sqrt d: partial sums over 16 coordinates per thread, then over the 8 partials
       float acc[4][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
+      const float qsv = ((lane >> 4) < G) ? qsl : 0.0f;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float qv = qr[g * kD + 16 * w + u];
-          acc[g][0] = fmaf(st2[u].x, qv, acc[g][0]);
-          acc[g][1] = fmaf(st2[u].y, qv, acc[g][1]);
+          const int x = __builtin_amdgcn_readlane(__float_as_int(qsv), 16 * g + u);
+          acc[g][0] = fmaf(st2[u].x, __int_as_float(x), acc[g][0]);
+          acc[g][1] = fmaf(st2[u].y, __int_as_float(x), acc[g][1]);
         }
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g * kM + 2 * jq]) = make_float2(acc[g][0], acc[g][1]);
-      lds_barrier();
+    }
+    lds_barrier();
+    if constexpr (NS > 2) copy_pair<KB, QJL, VB>(slots[1], junk, rk, rv, blk0 + 2, w, lane);
+    if (QJL) {
       // thread tid owns output tid: head tid / 128, so waves 2g and 2g+1 cover head g
       float sum = 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) sum += sred[c][tid];
-      sum *= inv_sqrt_d;
       sqs[tid] = sum;
-      float m1 = fabsf(sum);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, off, 64));
+      const float m1 = wave_max64(fabsf(sum));
       if (lane == 0) hmax[1][w] = m1;
       lds_barrier();
     }
     {
-      // fp8 limbs of q_raw (waves 0..3, set 0) and sq (waves 4..7, set 1), one
-      // E8M0 exponent per (set, head); wave (set, g) writes k-slots 2l, 2l+1 of
-      // head g, k-slot k holding coordinate pos_of_slot(k)
+      // base-32 digits of q' (waves 0..3, set 0: q_raw; waves 4..7, set 1:
+      // sq), leading exponent per (set, head); wave (set, g) writes k-slots 2l,
+      // 2l+1 of head g, k-slot k holding coordinate pos_of_slot(k).  q' is the
+      // value with its sign flipped on the k-slots that meet the sign field of
+      // the key operand, (k mod 32) / 8 == 3; the set's constant is the sum of
+      // 5, 3, 1, 0 times the digit-exact q' over the k-slots of field 0..3.
       const int set = w >> 2;
       const int g = w & 3;
       if (set == 0 || QJL) {
         const int k0 = 2 * lane;
+        const int fld = (k0 & 31) >> 3;
         const float* src = set == 0 ? qr + g * kD : sqs + g * kM;
-        float u0 = src[pos_of_slot(k0)];
-        float u1 = src[pos_of_slot(k0 + 1)];
+        const float u0 = (fld == 3) ? -src[pos_of_slot(k0)] : src[pos_of_slot(k0)];
+        const float u1 = (fld == 3) ? -src[pos_of_slot(k0 + 1)] : src[pos_of_slot(k0 + 1)];
         const float m = set == 0 ? hmax[0][g] : fmaxf(hmax[1][2 * g], hmax[1][2 * g + 1]);
-        const int s0 = (m >= 1e-30f) ? exponent_of(m) - 7 : 0;
+        const int s0 = (m >= 1e-30f) ? exponent_of(m) - 3 : 0;   // |u| 2^-s0 < 16
+        float r0 = __builtin_amdgcn_ldexpf(u0, -s0), r1 = __builtin_amdgcn_ldexpf(u1, -s0);
+        float t0 = 0.0f, t1 = 0.0f;   // digit-exact values, in units of 2^s0
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int sj = s0 - 4 * j;
-          const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(u0, -sj),
-                                                         __builtin_amdgcn_ldexpf(u1, -sj), 0, false);
-          u0 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), sj);
-          u1 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), sj);
+          const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
+          const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+          t0 = fmaf(d0, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t0);
+          t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
+          r0 = (r0 - d0) * 32.0f;
+          r1 = (r1 - d1) * 32.0f;
           *reinterpret_cast<uint16_t*>(&alimb[set][(4 * g + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
-          if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(sj + 127, 1), 254));
+          if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
         }
+        const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
+        const float c = __builtin_amdgcn_ldexpf(wave_sum64(wf * (t0 + t1)), s0);
+        if (lane == 0) cconst[set][g] = c;
       }
     }
-    // the fourth limb column of each head stays zero (three limbs are written)
+    if constexpr (NS > 3) copy_pair<KB, QJL, VB>(slots[2], junk, rk, rv, blk0 + 4, w, lane);
+    // the fourth digit column of each head stays zero (three digits are written)
     for (int k = tid; k < 2 * 4 * 128; k += kThreads) plimb[k >> 9][(4 * ((k >> 7) & 3) + 3) * 128 + (k & 127)] = 0;
     // the first pair has landed (this wave's copies; the barrier covers the others')
     wait_vm<(NS - 2) * F::perWave>();
@@ -455,6 +537,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         Asq = Aq;
       }
     }
+#pragma unroll
+    for (int T = 0; T < NTK; ++T) aksum += ak[T];
+    // offsets of the affine key operand for this lane's head g4: every term
+    // carries the same per-head constant, the code sum carries it times sum a_T
+    const float cq = cconst[0][g4] * aksum;
+    const float csq = QJL ? cconst[1][g4] : 0.0f;
     const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
     const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
     uint8_t* my_plimb = plimb[gr];
@@ -490,17 +578,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         for (int p = 0; p < KB; ++p) wd[p] = c ? kp[p].y : kp[p].x;
 #pragma unroll
         for (int T = 0; T < NTK; ++T)
-          dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
-        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4(c ? ks.y : ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
+          dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4_affine(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
+        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? ks.y : ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
       }
       float lg2[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        float code = 0.0f;
+        float code = -cq;
 #pragma unroll
         for (int T = 0; T < NTK; ++T)
           code = fmaf(ak[T], (dT[c][T][0] + dT[c][T][1]) + (dT[c][T][2] + dT[c][T][3]), code);
-        const float qj = QJL ? (dQ[c][0] + dQ[c][1]) + (dQ[c][2] + dQ[c][3]) : 0.0f;
+        const float qj = QJL ? ((dQ[c][0] + dQ[c][1]) + (dQ[c][2] + dQ[c][3])) - csq : 0.0f;
         const int tok = pos_of_slot(32 * wl + 2 * t + c);
         const float nk = h2f(c ? (kn >> 16) : kn);
         const float rho = QJL ? h2f(c ? (kr >> 16) : kr) : 0.0f;
@@ -532,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       m_a = mn_a;
       m_b = mn_b;
 
-      // probabilities and fp8 limbs of p * value radius (3 limbs, ~12 bits)
+      // probabilities and base-32 digits of p * value radius (3 digits, ~14 bits)
       const uint32_t vn = *reinterpret_cast<const uint32_t*>(vb + 2048 * VB + sn);
       const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - m_a);
       const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - m_a);
@@ -540,20 +628,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       float r0 = (p0 > 0.0f) ? p0 * h2f(vn) : 0.0f;
       float r1 = (p1 > 0.0f) ? p1 * h2f(vn >> 16) : 0.0f;
       const float pm = row_max16(fmaxf(r0, r1));
-      const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 7 : 0;
+      const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
+      r0 = __builtin_amdgcn_ldexpf(r0, -s0);
+      r1 = __builtin_amdgcn_ldexpf(r1, -s0);
       uint32_t ebytes = 127u << 24;
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
-        const int sj = s0 - 4 * j;
-        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(r0, -sj),
-                                                       __builtin_amdgcn_ldexpf(r1, -sj), 0, false);
+        const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
         if (j < 2) {
-          r0 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), sj);
-          r1 -= __builtin_amdgcn_ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), sj);
+          r0 = (r0 - d0) * 32.0f;
+          r1 = (r1 - d1) * 32.0f;
         }
         *reinterpret_cast<uint16_t*>(&my_plimb[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) =
             static_cast<uint16_t>(pk & 0xffff);
-        ebytes |= static_cast<uint32_t>(min(max(sj + 127, 1), 254)) << (8 * j);
+        ebytes |= static_cast<uint32_t>(min(max(s0 - 5 * j + 127, 1), 254)) << (8 * j);
       }
       if (t == 0) *reinterpret_cast<uint32_t*>(&pexp[gr][wl][4 * g4]) = ebytes;
       wait_vm<(NS - 2) * F::perWave>();   // this wave's copies of the next pair have landed

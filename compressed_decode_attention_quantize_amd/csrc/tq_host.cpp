@@ -273,6 +273,24 @@ void build_params(const tq_config* c, uint8_t* img) {
     fill_sketch(Stream(c->seed, c->layer, 2), m, d, S);
     for (int j = 0; j < m; ++j)
       for (int i = 0; i < d; ++i) ST[static_cast<size_t>(i) * m + j] = S[static_cast<size_t>(j) * d + i];
+    // S q_raw / sqrt d = (S H D_K / sqrt d) q: row j of S H is the raw FWHT of
+    // row j of S (H is symmetric); fp64 throughout, one rounding to fp32
+    const float* DK = reinterpret_cast<const float*>(img + L.dk);
+    float* SHD = reinterpret_cast<float*>(img + L.shd);
+    std::vector<double> row(d);
+    const double inv_sqrt_d = 1.0 / std::sqrt(static_cast<double>(d));
+    for (int j = 0; j < m; ++j) {
+      for (int i = 0; i < d; ++i) row[i] = S[static_cast<size_t>(j) * d + i];
+      for (int h = 1; h < d; h <<= 1)
+        for (int i = 0; i < d; i += 2 * h)
+          for (int k = i; k < i + h; ++k) {
+            const double x = row[k], y = row[k + h];
+            row[k] = x + y;
+            row[k + h] = x - y;
+          }
+      for (int i = 0; i < d; ++i)
+        SHD[static_cast<size_t>(i) * m + j] = static_cast<float>(row[i] * DK[i] * inv_sqrt_d);
+    }
   }
   if (c->k_codec == TQ_CODEC_POLAR || c->k_codec == TQ_CODEC_POLAR_QJL) {
     const Codebook cb = make_codebook(d, c->k_bits);
@@ -302,6 +320,7 @@ tq::Tables tables(const tq_config* c, const void* params) {
   t.vb = reinterpret_cast<const float*>(p + L.vb);
   t.ak = reinterpret_cast<const float*>(p + L.ak);
   t.av = reinterpret_cast<const float*>(p + L.av);
+  t.shd = reinterpret_cast<const float*>(p + L.shd);
   return t;
 }
 

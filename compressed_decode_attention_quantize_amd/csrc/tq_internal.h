@@ -30,6 +30,7 @@ struct ParamsLayout {
   uint64_t ck, kb;   // float[16] K centroids, float[16] K boundaries (2^b-1 used)
   uint64_t cv, vb;   // same for V
   uint64_t ak, av;   // float[8] odd multilinear coefficients of the K / V codebooks
+  uint64_t shd;      // float[d][m]: (S H D_K / sqrt d)^T, the sketch of a query before rotation
   uint64_t total;
 };
 
@@ -46,6 +47,7 @@ inline ParamsLayout params_layout(int d, int m) {
   L.vb = o; o += 64;
   L.ak = o; o += 32;
   L.av = o; o += 32;
+  L.shd = o; o += 4ull * m * d;
   L.total = (o + 255) & ~255ull;
   return L;
 }
@@ -65,6 +67,7 @@ struct Tables {
   const float* vb;
   const float* ak;
   const float* av;
+  const float* shd;  // [d][m]
 };
 
 struct QuantArgs {

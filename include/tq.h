@@ -113,7 +113,9 @@ tq_status tq_params_bytes(const tq_config* cfg, uint64_t* bytes);
  * Contents: signs D_K, D_V (+/-1, fp32[d]) drawn from counter-form SplitMix64
  * keyed by (seed, layer); the Gaussian sketch S (fp32[m][d], Box-Muller) and
  * its transpose; Lloyd-Max codebooks for the law of a rotated unit vector's
- * coordinate (fp16-exact centroids, fp32 midpoint boundaries).  This is the
+ * coordinate (fp16-exact centroids, fp32 midpoint boundaries); and, for
+ * QJL keys, (S H D_K / sqrt d)^T (fp32[d][m], from fp64 products), which maps
+ * a query before rotation straight to its sketch.  This is the
  * "distribution known in advance" of the PolarQuant paragraph and the fixed
  * transform of "Principe de quantification sans calibration".  Pure host. */
 tq_status tq_params_host(const tq_config* cfg, void* host_params, uint64_t bytes);

@@ -3,6 +3,7 @@ declared symbol; size queries and host-built parameters agree with the
 oracle's independent implementation; argument checks return the documented
 status before any device call (no GPU needed)."""
 import ctypes
+import math
 import os
 import re
 
@@ -81,6 +82,15 @@ def test_params_match_oracle_tables(tq, orc, kw, seed, layer):
         L = 1 << kw["v_bits"]
         assert np.array_equal(cv[:L], orc.f16_to_f32(P.cv16))
         assert np.array_equal(vb[:L - 1], P.vbounds)
+    if m:
+        # sketch of a query before its rotation: (S H D_K / sqrt d)^T, H the
+        # Sylvester matrix built here from its definition H[i][j] = (-1)^popcount(i & j)
+        idx = np.arange(d)
+        H = np.where(np.bitwise_count(idx[:, None] & idx[None, :]) % 2 == 1, -1.0, 1.0)
+        want = (P.S.astype(np.float64) @ H * P.DK.astype(np.float64)[None, :] / math.sqrt(d)).T
+        off += 4 * 16 + 2 * 8
+        SHD = f[off:off + m * d].reshape(d, m)
+        assert np.allclose(SHD, want, rtol=2e-7, atol=1e-6)
 
 
 def _cfg(tq, **kw):
