@@ -112,12 +112,23 @@ def compare_records(spec, P, G, R, lens, x_k=None, label=""):
     return st
 
 
+MIN_RMS_POSITIONS = 16
+
+
 def check_logits(gpu_lg, ref_lg, n, label="", skip=None):
     """gpu_lg, ref_lg: [n_pairs][>=n]; skip: optional bool mask [n_pairs][n]
-    of positions excluded (records that differ by a counted sign exception)."""
+    of positions excluded (records that differ by a counted sign exception).
+
+    Bar: |d| <= LOGIT_REL * max(|ref|, rms of that head's logits).  A row of
+    fewer than MIN_RMS_POSITIONS positions takes the rms over every row of
+    the call instead: over one position the row rms is |ref| itself, and the
+    bar would turn back into the pure relative error that is undefined near 0."""
     g = np.asarray(gpu_lg, np.float64)[:, :n]
     r = np.asarray(ref_lg, np.float64)[:, :n]
-    rms = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
+    if n >= MIN_RMS_POSITIONS:
+        rms = np.sqrt(np.mean(r * r, axis=1, keepdims=True))
+    else:
+        rms = np.full((r.shape[0], 1), np.sqrt(np.mean(r * r)) if r.size else 0.0)
     tol = LOGIT_REL * np.maximum(np.abs(r), rms)
     bad = np.abs(g - r) > tol
     if skip is not None:
