@@ -13,8 +13,10 @@ quantize-append half of the metric is measured in its own timed region: the
 32768-position prefill of each of the 32 layers, reported as tokens/s.
 
 Also printed: the roofline of the decode kernel (algorithmic bytes per launch
-over its mean launch duration, from HIP events on the launch stream), and the
-oracle's CPU throughput on a bounded sample (single-threaded).
+over its mean launch duration, from HIP events on the launch stream around the
+timed region), the HBM traffic per launch measured with rocprofv3 counters
+(from profiles/, when taken on the current kernel sources), and the oracle's
+CPU throughput on a bounded sample (single-threaded).
 """
 from __future__ import annotations
 
@@ -28,6 +30,72 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+DECODE_KERNEL = "decode_mfma_kernel"   # name fragment of the timed decode kernel
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama8b_ctx32k_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc", f)
+                  for f in ("tq_decode_mfma.hip", "tq_device.h", "tq_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload, layers):
+    """HBM bytes per decode launch measured with rocprofv3 counters (FETCH_SIZE
+    + WRITE_SIZE, scaled by what they read for a copy of known size), if the
+    committed measurement was taken on this workload and the kernel sources
+    have not changed since; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.strip().split("=", 1) for l in fh if "=" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash") != kernel_source_hash() or kv.get("workload") != workload:
+        return None
+    return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+
+
+def summarize_counters(fetch_csv, write_csv, copy_mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernel and of
+    the calibration copy, from two rocprofv3 --pmc runs; prints key=value
+    lines (bytes per decode launch after dividing by the copy's read/write
+    factor)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    out = {}
+    for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        dec = [v for n, vs in vals.items() if DECODE_KERNEL in n for v in vs]
+        # the calibration copy: the dispatches whose counter is nearest the copy size
+        want = copy_mib * 1024.0
+        cands = [v for n, vs in vals.items() if DECODE_KERNEL not in n for v in vs if v > 0.5 * want]
+        if not dec or not cands:
+            raise SystemExit(f"{path}: no {DECODE_KERNEL} or copy dispatches with {counter}")
+        dec.sort()
+        med = dec[len(dec) // 2]
+        copy = sorted(cands, key=lambda v: abs(v - want))[0]
+        factor = copy / want
+        out[f"{tag}_kib_per_launch_raw"] = med
+        out[f"{tag}_copy_kib"] = copy
+        out[f"{tag}_copy_factor"] = round(factor, 4)
+        out[f"{tag}_bytes_per_launch"] = round(med * 1024.0 / factor)
+        out[f"{tag}_dispatches"] = len(dec)
+    return out
 
 
 def algorithmic_decode_bytes(w, cfg, tq, lens):
@@ -86,7 +154,19 @@ def main():
     ap.add_argument("--workload", default="llama8b_b1_ctx32k")
     ap.add_argument("--layers", type=int, default=0, help="layer caches to cycle (0 = workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device to device three times (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--calibration-mib", type=int, default=256)
     args = ap.parse_args()
+    if args.summarize_counters:
+        res = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.calibration_mib)
+        res["source_hash"] = kernel_source_hash()
+        res["workload"] = args.workload
+        for k_, v_ in res.items():
+            print(f"{k_}={v_}")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -150,14 +230,9 @@ def main():
     wall = time.perf_counter() - t0
     step_ms = s0.elapsed_time(s1) / args.steps
 
-    # per-launch durations of the decode kernel (events on its stream)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
-          for _ in range(args.steps)]
-    for st in range(args.steps):
-        step(ev[st])
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for row in ev for (a, b) in row]
-    launch_ms = sum(durs) / len(durs)
+    # average duration of one decode launch: the timed region (HIP events on
+    # the launch stream) holds only back-to-back decode launches
+    launch_ms = step_ms / n_layers
 
     value = n_layers * bytes_per_launch / (step_ms / 1e3) / 1e9
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
@@ -183,14 +258,21 @@ def main():
         "append_ms_per_layer": round(append_s * 1e3, 4),
         "decode_us_per_layer": round(step_ms * 1e3 / n_layers, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "bytes_per_launch": bytes_per_launch,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": committed_traffic(w.name, n_layers),
+                     "kernel": DECODE_KERNEL, "bytes_per_launch": bytes_per_launch,
                      "launch_us": round(launch_ms * 1e3, 3)},
         "wall_s_timed": round(wall, 4),
         "device": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, data_seed)
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(result))
 
 
