@@ -62,6 +62,7 @@ namespace tq {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 // read-only data at wave-uniform addresses: loads through the scalar cache
 typedef __attribute__((address_space(4))) const v4f cv4f;
@@ -75,7 +76,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int B>
 struct NTerms {
-  static constexpr int n = (B == 2) ? 2 : (B == 3 ? 4 : 8);
+  static constexpr int n = (B == 2) ? 2 : (B == 3 ? 4 : (B == 4 ? 8 : 1));
 };
 
 // Bits of term T: code planes for T < B, then XORs of three planes.
@@ -209,8 +210,9 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4
 // ring that stages two blocks per step.
 template <int KB, bool QJL, int VB>
 struct Fmt {
-  static constexpr int kNorms = 2048 * KB + (QJL ? 2048 : 0);         // fp16 radii after planes (and signs)
-  static constexpr int kBytes = kNorms + 256 + (QJL ? 256 : 0);       // K block
+  static constexpr bool q8 = KB == 8;   // q8 keys: int8[128][128], then fp16 scales [128][4]
+  static constexpr int kNorms = q8 ? 0 : 2048 * KB + (QJL ? 2048 : 0);   // fp16 radii after planes (and signs)
+  static constexpr int kBytes = q8 ? 128 * 128 + 128 * 8 : kNorms + 256 + (QJL ? 256 : 0);   // K block
   static constexpr int vBytes = 2048 * VB + 256;                       // V block: planes, fp16 radii
   static constexpr int kChunks = (2 * kBytes + 1023) / 1024;           // 1 KB copy units per step (two blocks)
   static constexpr int vChunks = (2 * vBytes + 1023) / 1024;
@@ -237,6 +239,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // bytes 16l..16l+15 of its unit).  Every wave issues the same number of copies;
 // units past the data read zero into a junk buffer, so the count of
 // outstanding copies per wave is the same at every step.
+// q8 key rows (128 B per position) are stored in shared memory with their
+// 16-byte granules permuted: granule j of position tok sits at granule
+// j ^ q8_swizzle(tok) of its row.  The sixteen positions one matrix operand
+// reads together then fall on distinct banks (plain rows share every bank).
+__device__ __forceinline__ int q8_swizzle(int tok) { return ((tok >> 3) & 3) | ((tok & 2) << 1); }
+
 template <int KB, bool QJL, int VB>
 __device__ __forceinline__ void copy_pair(uint8_t* slot, uint8_t* junk, __amdgpu_buffer_rsrc_t rk,
                                           __amdgpu_buffer_rsrc_t rv, int b0, int w, int lane) {
@@ -246,7 +254,13 @@ __device__ __forceinline__ void copy_pair(uint8_t* slot, uint8_t* junk, __amdgpu
     const int q = w + kWaves * j;   // unit, uniform over the wave
     const bool isk = q < F::kChunks;
     const bool isv = !isk && q < F::kChunks + F::vChunks;
-    const int off = isk ? b0 * F::kBytes + 1024 * q + 16 * lane
+    int kgr = 64 * q + lane;   // granule of the pair's K region this lane fills
+    if constexpr (F::q8) {
+      const int half = (kgr >= F::kBytes / 16) ? 1 : 0;
+      const int g = kgr - half * (F::kBytes / 16);
+      if (g < kBlock * kD / 16) kgr = half * (F::kBytes / 16) + (g & ~7) + ((g & 7) ^ q8_swizzle(g >> 3));
+    }
+    const int off = isk ? b0 * F::kBytes + 16 * kgr
                         : (isv ? b0 * F::vBytes + 1024 * (q - F::kChunks) + 16 * lane : 0x7fff0000 + 16 * lane);
     uint8_t* dst = (isk || isv) ? slot + 1024 * q : junk;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, (lds_void_t*)(dst), 16, off, 0, 0, 0);
@@ -289,19 +303,19 @@ __device__ __forceinline__ float half_sum32(float x) {
 // sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.  Wave g merges head g; splits
 // are taken 32 at a time with every load of a round in flight together; lane
 // (half, i4) accumulates float4 i4 of the round's splits of parity half.
-__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int h, int w, int lane) {
+__device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int hq0, int G, uint32_t* counter, int w,
+                                             int lane) {
   // every split has arrived (counter); the partials were written through to
   // the device-coherent level and are read back with device-scope coherent
   // loads (sc1), so no cache invalidation is needed
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   typedef uint32_t v2u __attribute__((ext_vector_type(2)));
   constexpr int kCoherent = 16;   // sc1
-  const int G = a.group;
   if (w < G) {
     const int pstride = kPartialStride;
     const int i4 = lane & 31;
     const int half = lane >> 5;
-    const float* pp = a.partials + (static_cast<int64_t>(b) * a.n_q + h * G + w) * a.n_splits * kPartialStride;
+    const float* pp = a.partials + (static_cast<int64_t>(b) * a.n_q + hq0 + w) * a.n_splits * kPartialStride;
     const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(pp), static_cast<short>(0), a.n_splits * pstride * 4, 0x00020000);
     float M = -INFINITY, L = 0.0f;
@@ -342,16 +356,17 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int h, 
     A.w += __shfl_xor(A.w, 32, 64);
     if (half == 0) {
       const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-      *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.n_q + h * G + w) * kD + 4 * i4) =
+      *reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.n_q + hq0 + w) * kD + 4 * i4) =
           make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
     }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(a.counters + b * a.n_kv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int KB, bool QJL, int VB>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
   using F = Fmt<KB, QJL, VB>;
+  constexpr bool KQ8 = F::q8;
   constexpr int NTK = NTerms<KB>::n;
   constexpr int NTV = NTerms<VB>::n;
   constexpr int NS = F::nSlots;
@@ -372,6 +387,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ float hmax[2][kWaves];         // per-wave max |value| for the limb exponents
   __shared__ float mrun[4];                 // running max per head at the end (log2 units)
   __shared__ float cconst[2][4];            // offsets of the affine key operand per (set, head)
+  __shared__ __attribute__((aligned(8))) int8_t qdig[4][3][kD];   // q8 keys: base-128 digits of q per head
+  __shared__ int qexp8[4];                  // q8 keys: leading exponent per head
   __shared__ __attribute__((aligned(16))) float sred[8][4 * kM];   // partial sketch sums; later the group sums
   __shared__ int s_last;
   uint8_t* const slots[4] = {slot0, slot1, slot2, slot3};
@@ -384,9 +401,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int t = lane & 15;
   const int g4 = lane >> 4;
   const int split = blockIdx.x;
-  const int h = blockIdx.y;
+  const int nhg = (a.group + 3) >> 2;      // groups of up to four query heads per KV head
+  const int h = blockIdx.y / nhg;          // KV head
+  const int hg = blockIdx.y - h * nhg;     // head group of this workgroup
   const int b = blockIdx.z;
-  const int G = a.group;
+  const int G = min(4, a.group - 4 * hg);  // query heads served here
+  const int hq0 = h * a.group + 4 * hg;    // the first of them
+  uint32_t* const counter = a.counters + static_cast<int64_t>(b) * a.n_kv * nhg + blockIdx.y;
   const int len = min(a.seq_lens[b], a.max_ctx);
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
@@ -412,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // loads the set-up needs are issued first (outstanding loads retire in
     // order): the rotation's inputs, this wave's slice of the raw queries,
     // the sketch table; then the copies of the first NS - 1 block pairs
-    const float* qb0 = a.q + (static_cast<int64_t>(b) * a.n_q + h * G) * kD;
+    const float* qb0 = a.q + (static_cast<int64_t>(b) * a.n_q + hq0) * kD;
     const float* qp = qb0 + min(w & 3, G - 1) * kD;
     const float qa = qp[lane], qb = qp[lane + 64];
     const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
@@ -442,7 +463,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // waves 0..3 rotate the query of head w in registers (q_raw = H D_K q);
     // meanwhile every wave forms its share of the sketch S q_raw / sqrt d as
     // (S H D_K / sqrt d) q, which needs no rotated query
-    if (w < 4) {
+    if constexpr (KQ8) {
+      // q8 keys meet the query unrotated: three base-128 digits of q per head,
+      // integers in [-64, 64], for the int8 matrix instruction
+      if (w < 4) {
+        const float x0 = (w < G) ? qa : 0.0f, x1 = (w < G) ? qb : 0.0f;
+        const float m = wave_max64(fmaxf(fabsf(x0), fabsf(x1)));
+        const int e = (m >= 1e-30f) ? exponent_of(m) - 5 : 0;   // |q| 2^-e < 64
+        float r0 = __builtin_amdgcn_ldexpf(x0, -e), r1 = __builtin_amdgcn_ldexpf(x1, -e);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const float d0 = rintf(r0), d1 = rintf(r1);
+          qdig[w][j][lane] = static_cast<int8_t>(d0);
+          qdig[w][j][lane + 64] = static_cast<int8_t>(d1);
+          r0 = (r0 - d0) * 128.0f;
+          r1 = (r1 - d1) * 128.0f;
+        }
+        if (lane == 0) qexp8[w] = e;
+      }
+    } else if (w < 4) {
       float q_lo = (w < G) ? qa * da : 0.0f;
       float q_hi = (w < G) ? qb * db : 0.0f;
       wave_fwht128(q_lo, q_hi, lane);
@@ -489,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       // 5, 3, 1, 0 times the digit-exact q' over the k-slots of field 0..3.
       const int set = w >> 2;
       const int g = w & 3;
-      if (set == 0 || QJL) {
+      if (!KQ8 && (set == 0 || QJL)) {
         const int k0 = 2 * lane;
         const int fld = (k0 & 31) >> 3;
         const float* src = set == 0 ? qr + g * kD : sqs + g * kM;
@@ -522,8 +561,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     wait_vm<(NS - 2) * F::perWave>();
     lds_barrier();
     v8i Aq, Asq;
-    int scq, scsq = 127;
-    {
+    int scq = 127, scsq = 127;
+    long A8[4] = {0, 0, 0, 0};   // q8 keys: row t = (head t / 4, digit t % 4) over coordinates 32cb + 8g4 ..
+    float qsc8 = 0.0f;           // q8 keys: 2^e log2(e) / sqrt d for this lane's head g4
+    if constexpr (KQ8) {
+      const int hh = t >> 2, dd = t & 3;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) A8[cb] = (dd < 3) ? *reinterpret_cast<const long*>(&qdig[hh][dd][32 * cb + 8 * g4]) : 0;
+      qsc8 = __builtin_amdgcn_ldexpf(kLog2e * inv_sqrt_d, qexp8[g4]);
+    } else {
       const uint4 lo = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 16 * g4]);
       const uint4 hi = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 64 + 16 * g4]);
       Aq = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -541,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     for (int T = 0; T < NTK; ++T) aksum += ak[T];
     // offsets of the affine key operand for this lane's head g4: every term
     // carries the same per-head constant, the code sum carries it times sum a_T
-    const float cq = cconst[0][g4] * aksum;
+    const float cq = KQ8 ? 0.0f : cconst[0][g4] * aksum;
     const float csq = QJL ? cconst[1][g4] : 0.0f;
     const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
     const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
@@ -563,6 +609,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
       // logits of k-slots 32wl + 2t + c for head g4: every MFMA of the block
       // is issued before any result is read
+      float lg2[2];
+      if constexpr (KQ8) {
+        // q8: per 32-coordinate block cb, exact int32 sums of q digits times
+        // k8, combined as D0 + D1 2^-7 + D2 2^-14 and scaled by the block's s16
+        v4i dI[2][4];
+        uint2 sc[2];
+        int tok2[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          tok2[c] = pos_of_slot(32 * wl + 2 * t + c);
+          const uint8_t* row = kb + tok2[c] * kD;
+          sc[c] = *reinterpret_cast<const uint2*>(kb + kBlock * kD + tok2[c] * 8);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const int gran = (2 * cb + (g4 >> 1)) ^ q8_swizzle(tok2[c]);
+            dI[c][cb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                A8[cb], *reinterpret_cast<const long*>(row + 16 * gran + 8 * (g4 & 1)), v4i{0, 0, 0, 0}, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          float code = 0.0f;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            float v = fmaf(static_cast<float>(dI[c][cb][1]), 0.0078125f, static_cast<float>(dI[c][cb][0]));
+            v = fmaf(static_cast<float>(dI[c][cb][2]), 6.103515625e-05f, v);
+            const uint32_t sw = (cb < 2) ? sc[c].x : sc[c].y;
+            code = fmaf(h2f((cb & 1) ? (sw >> 16) : sw), v, code);
+          }
+          const int tok = tok2[c];
+          const float l2 = __fmul_rn(qsc8, code);
+          const bool valid = (tok < n_t) && (g4 < G);
+          if (a.logits != nullptr && valid)
+            a.logits[(static_cast<int64_t>(b) * a.n_q + hq0 + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
+          lg2[c] = valid ? l2 : -INFINITY;
+        }
+      } else {
       uint2 kp[KB];
 #pragma unroll
       for (int p = 0; p < KB; ++p) kp[p] = *reinterpret_cast<const uint2*>(kb + p * 2048 + so);
@@ -581,7 +664,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4_affine(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
         if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? ks.y : ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
       }
-      float lg2[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         float code = -cq;
@@ -596,8 +678,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         const float l2 = fmaf(__fmul_rn(alpha2, nk), code, QJL ? __fmul_rn(__fmul_rn(beta2, rho), qj) : 0.0f);
         const bool valid = (tok < n_t) && (g4 < G);
         if (a.logits != nullptr && valid)
-          a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
+          a.logits[(static_cast<int64_t>(b) * a.n_q + hq0 + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
         lg2[c] = valid ? l2 : -INFINITY;
+      }
       }
 
       // step max per head (8 waves, both blocks); the running max only moves
@@ -728,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const float inv_d = 1.0f / static_cast<float>(kD);
     lo *= a.tb.dv[lane] * inv_d;
     hi *= a.tb.dv[lane + 64] * inv_d;
-    float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + w) * a.n_splits + split) * kPartialStride;
+    float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + hq0 + w) * a.n_splits + split) * kPartialStride;
     store_coherent(pp + lane, lo);
     store_coherent(pp + 64 + lane, hi);
     if (lane == 0) {
@@ -739,13 +822,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       store_coherent(pp + kD + 1, l);
     }
   }
-  if (!arrive_last(a.counters + b * a.n_kv + h, a.n_splits, &s_last)) return;
-  merge_splits(a, b, h, w, lane);
+  if (!arrive_last(counter, a.n_splits, &s_last)) return;
+  merge_splits(a, b, hq0, G, counter, w, lane);
 }
 
 template <int KB, bool QJL, int VB>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_splits, a.n_kv, a.batch);
+  dim3 grid(a.n_splits, a.n_kv * ((a.group + 3) / 4), a.batch);
   hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -763,7 +846,7 @@ hipError_t launch_v(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool decode_mfma_applies(int k_codec, int v_codec, int group) {
-  return v_codec == POLAR && group <= 4 && (k_codec == POLAR || k_codec == POLAR_QJL);
+  return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL || k_codec == Q8_BLOCK32);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
@@ -772,6 +855,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int64_t span = (static_cast<int64_t>(a.n_blocks) + 2 * kRing + 4) * std::max(a.k_block_bytes, a.v_block_bytes);
   if (span >= (int64_t{1} << 31) || static_cast<int64_t>(a.n_splits) * kPartialStride * 4 >= (int64_t{1} << 31))
     return hipErrorNotSupported;
+  if (a.k_codec == Q8_BLOCK32) return launch_v<8, false>(a, stream);
   if (a.k_codec == POLAR_QJL) {
     switch (a.k_bits) {
       case 2: return launch_v<2, true>(a, stream);

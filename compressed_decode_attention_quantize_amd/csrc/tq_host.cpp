@@ -324,16 +324,24 @@ tq::Tables tables(const tq_config* c, const void* params) {
   return t;
 }
 
-int64_t target_workgroups(const tq_config* c) {
-  return tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads) ? tq::kMfmaWorkgroups
-                                                                                        : tq::kValuWorkgroups;
+bool mfma_path(const tq_config* c) {
+  return tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
+}
+
+int64_t target_workgroups(const tq_config* c) { return mfma_path(c) ? tq::kMfmaWorkgroups : tq::kValuWorkgroups; }
+
+// Independent (sequence, KV head, head group) units the splits multiply: the
+// matrix-core kernel serves up to four query heads per workgroup.
+int64_t split_units(const tq_config* c) {
+  const int64_t groups = mfma_path(c) ? (c->n_q_heads / c->n_kv_heads + 3) / 4 : 1;
+  return static_cast<int64_t>(c->batch) * c->n_kv_heads * groups;
 }
 
 int decode_chunk_blocks(const tq_config* c, int32_t max_seq_len) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return c->decode_chunk / kBlock;
   // aim for the kernel's workgroup count over the whole grid
-  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int64_t pairs = split_units(c);
   const int64_t target = target_workgroups(c);
   const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
   return static_cast<int>(std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits));
@@ -350,7 +358,7 @@ int decode_splits(const tq_config* c, int32_t max_seq_len) {
 int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return (blocks + c->decode_chunk / kBlock - 1) / (c->decode_chunk / kBlock);
-  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int64_t pairs = split_units(c);
   const int64_t target = target_workgroups(c);
   const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
   return static_cast<int>(std::min<int64_t>(blocks, want_splits));
@@ -457,7 +465,7 @@ tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, u
   if (bytes == nullptr || max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
   const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
   const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
-  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * 4;
+  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * (tq::kMaxGroup / 4) * 4;
   *bytes = ((partial + 255) & ~255ull) + ((counters + 255) & ~255ull);
   return TQ_OK;
 }
