@@ -400,14 +400,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int wl = w & 3;    // wave within the group
   const int t = lane & 15;
   const int g4 = lane >> 4;
-  const int split = blockIdx.x;
+  // Workgroup -> (split, KV head, sequence, head group).  Workgroups are
+  // dispatched to the 8 XCDs round-robin by linear id, so the head groups of
+  // one (split, KV head, sequence) unit get ids 8 apart: they run at the same
+  // time on one XCD and read the unit's blocks through the same L2.
   const int nhg = (a.group + 3) >> 2;      // groups of up to four query heads per KV head
-  const int h = blockIdx.y / nhg;          // KV head
-  const int hg = blockIdx.y - h * nhg;     // head group of this workgroup
-  const int b = blockIdx.z;
+  const int n_units = a.n_splits * a.n_kv * a.batch;
+  const int id = blockIdx.x;
+  const int kx = id >> 3;
+  const int unit = (kx / nhg) * 8 + (id & 7);
+  if (unit >= n_units) return;             // padding of the grid to whole rounds of 8
+  const int hg = kx - (kx / nhg) * nhg;    // head group of this workgroup
+  const int split = unit % a.n_splits;
+  const int h = (unit / a.n_splits) % a.n_kv;   // KV head
+  const int b = unit / (a.n_splits * a.n_kv);
   const int G = min(4, a.group - 4 * hg);  // query heads served here
   const int hq0 = h * a.group + 4 * hg;    // the first of them
-  uint32_t* const counter = a.counters + static_cast<int64_t>(b) * a.n_kv * nhg + blockIdx.y;
+  uint32_t* const counter = a.counters + (static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg;
   const int len = min(a.seq_lens[b], a.max_ctx);
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
@@ -828,7 +837,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 
 template <int KB, bool QJL, int VB>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_splits, a.n_kv * ((a.group + 3) / 4), a.batch);
+  const int n_units = a.n_splits * a.n_kv * a.batch;
+  dim3 grid(((n_units + 7) / 8) * 8 * ((a.group + 3) / 4));
   hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
