@@ -122,77 +122,6 @@ __device__ __forceinline__ v8i expand_fp4_affine(uint32_t w) {
   return r;
 }
 
-// Max / sum over the 16 lanes of a row (DPP: xor 1, xor 2, half-row mirror,
-// row mirror); every lane of the row ends with the result.
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
-  return x;
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-  return x;
-}
-
-// Value of lane (l ^ H) for lane l, by the cheapest cross-lane route: DPP
-// within 16-lane rows (xor 1, 2 as quad permutations; xor 4 = xor 3 then
-// xor 7; xor 8 = xor 7 then xor 15 via the half-row and row mirrors), the
-// 32-lane swizzle for xor 16, a permute for xor 32.
-template <int H>
-__device__ __forceinline__ float lane_xor(float x) {
-  const int v = __float_as_int(x);
-  if constexpr (H == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
-  if constexpr (H == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
-  if constexpr (H == 4) {
-    const int u = __builtin_amdgcn_update_dpp(0, v, 0x1B, 0xF, 0xF, false);
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x141, 0xF, 0xF, false));
-  }
-  if constexpr (H == 8) {
-    const int u = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, u, 0x140, 0xF, 0xF, false));
-  }
-  if constexpr (H == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x401F));
-  if constexpr (H == 32) return __shfl_xor(x, 32, 64);
-  return x;
-}
-
-template <int H>
-__device__ __forceinline__ void butterfly(float& lo, float& hi, int lane) {
-  const float plo = lane_xor<H>(lo), phi = lane_xor<H>(hi);
-  const bool up = (lane & H) != 0;
-  lo = up ? plo - lo : lo + plo;
-  hi = up ? phi - hi : hi + phi;
-}
-
-// Raw Sylvester FWHT of 128 values held as (lo = coord lane, hi = coord lane+64).
-__device__ __forceinline__ void wave_fwht128(float& lo, float& hi, int lane) {
-  butterfly<1>(lo, hi, lane);
-  butterfly<2>(lo, hi, lane);
-  butterfly<4>(lo, hi, lane);
-  butterfly<8>(lo, hi, lane);
-  butterfly<16>(lo, hi, lane);
-  butterfly<32>(lo, hi, lane);
-  const float x = lo, y = hi;
-  lo = x + y;
-  hi = x - y;
-}
-
-__device__ __forceinline__ float wave_max64(float x) {
-  x = row_max16(x);
-  x = fmaxf(x, lane_xor<16>(x));
-  return fmaxf(x, lane_xor<32>(x));
-}
-__device__ __forceinline__ float wave_sum64(float x) {
-  x = row_sum16(x);
-  x += lane_xor<16>(x);
-  return x + lane_xor<32>(x);
-}
-
 __device__ __forceinline__ int exponent_of(float x) {   // floor(log2 x), x > 0 normal
   return static_cast<int>((__float_as_uint(x) >> 23) & 0xffu) - 127;
 }

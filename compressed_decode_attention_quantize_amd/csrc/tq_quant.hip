@@ -11,7 +11,8 @@
 // the append and walks its positions in order.  Lane l holds coordinates l
 // and l + 64 of the current vector:
 //   * FWHT stages h = 1..32 pair lane l with lane l ^ h (cross-lane
-//     butterflies); stage h = 64 pairs the two registers of a lane.  The
+//     butterflies through DPP / swizzle / permute); stage h = 64 pairs the
+//     two registers of a lane.  The
 //     stage order and the pairing are those of the format, and add/sub are
 //     exact IEEE operations, so the rotated values are bit-identical to any
 //     other engine that follows the format.
@@ -30,12 +31,13 @@
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
-constexpr int kWavesPerWg = 4;
+constexpr int kWavesPerWg = 16;   // one copy of S^T in LDS serves 16 wavefronts
 
 __device__ __forceinline__ float load_in(const void* p, int64_t idx, int dtype) {
   if (dtype == IN_F32) return reinterpret_cast<const float*>(p)[idx];
@@ -50,32 +52,17 @@ __device__ __forceinline__ uint16_t norm_to_f16(float n) {
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
-// Raw Sylvester FWHT of 128 values held as (lo = coord lane, hi = coord lane+64).
-__device__ __forceinline__ void wave_fwht128(float& lo, float& hi, int lane) {
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float plo = __shfl_xor(lo, h, 64);
-    const float phi = __shfl_xor(hi, h, 64);
-    if (lane & h) {
-      lo = plo - lo;   // upper element of the pair: a - b
-      hi = phi - hi;
-    } else {
-      lo = lo + plo;   // lower element: a + b
-      hi = hi + phi;
-    }
-  }
-  const float a = lo, b = hi;
-  lo = a + b;
-  hi = a - b;
-}
-
 // fp64 pairwise tree of squares: level 64 in-lane, then xor butterflies.
 __device__ __forceinline__ double wave_tree_sumsq(float lo, float hi) {
   const double a = static_cast<double>(lo) * static_cast<double>(lo);
   const double b = static_cast<double>(hi) * static_cast<double>(hi);
   double s = a + b;
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) s = s + __shfl_xor(s, w, 64);
+  s = s + lane_xor<32>(s);
+  s = s + lane_xor<16>(s);
+  s = s + lane_xor<8>(s);
+  s = s + lane_xor<4>(s);
+  s = s + lane_xor<2>(s);
+  s = s + lane_xor<1>(s);
   return s;
 }
 
@@ -115,7 +102,7 @@ __device__ __forceinline__ PolarOut polar_codes(float x_lo, float x_hi, const fl
   return o;
 }
 
-__global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerWg) void quant_kernel(QuantArgs a) {
   extern __shared__ float st_lds[];   // [128][128] S^T when the key codec has QJL
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -164,11 +151,11 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
       row[lane + 64] = xk_hi;
     } else if (a.k_codec == Q8_BLOCK32) {
       float m_lo = fabsf(xk_lo), m_hi = fabsf(xk_hi);
-#pragma unroll
-      for (int w = 16; w >= 1; w >>= 1) {   // stays inside each 32-lane block
-        m_lo = fmaxf(m_lo, __shfl_xor(m_lo, w, 64));
-        m_hi = fmaxf(m_hi, __shfl_xor(m_hi, w, 64));
-      }
+      // max inside each 32-lane block
+      m_lo = fmaxf(m_lo, lane_xor<16>(m_lo));
+      m_hi = fmaxf(m_hi, lane_xor<16>(m_hi));
+      m_lo = row_max16(m_lo);
+      m_hi = row_max16(m_hi);
       const uint16_t s_lo = norm_to_f16(m_lo / 127.0f);
       const uint16_t s_hi = norm_to_f16(m_hi / 127.0f);
       const float sf_lo = f16_to_f32(s_lo), sf_hi = f16_to_f32(s_hi);
