@@ -7,238 +7,522 @@
 // codebook for that law; for keys, add the signs of a Gaussian sketch of the
 // residual and the residual's norm (the 1-bit QJL corrector).
 //
-// Mapping: one wavefront owns one (sequence, KV head, 32-position group) of
-// the append and walks its positions in order.  Lane l holds coordinates l
-// and l + 64 of the current vector:
-//   * FWHT stages h = 1..32 pair lane l with lane l ^ h (cross-lane
-//     butterflies through DPP / swizzle / permute); stage h = 64 pairs the
-//     two registers of a lane.  The
-//     stage order and the pairing are those of the format, and add/sub are
-//     exact IEEE operations, so the rotated values are bit-identical to any
-//     other engine that follows the format.
-//   * sums of squares are fp64 pairwise trees (register pair, then xor
-//     butterflies 32..1), the tree the format fixes.
-//   * the b code bit-planes and the sign plane are wave ballots; key planes
-//     are token-major words (at the position's slot inside its block), value
-//     planes accumulate one bit per position in
-//     coordinate-major words that the wavefront owns for the whole group
-//     (read-modify-write keeps bits of positions it does not write).
-//   * the sketch S r (m = 128 rows) reads S^T from LDS, one row pair per lane,
-//     broadcasting r_i with readlane.
+// Mapping: a wavefront owns one (sequence, KV head, 32-position group) of the
+// append and takes it as two tiles of 16 positions.  Inside a tile, lane l
+// serves position l & 15 with 32 of its 128 coordinates in registers; the
+// four lanes l & 15 + 16 g (g = 0..3) of a position hold the rest.  Which
+// coordinate bit sits on a register-index bit and which on lane bit 4 or 5
+// changes as the work proceeds: a permlane swap of a register pair across
+// lane bit 4 or 5 exchanges the roles of that lane bit and that register bit.
+// With it,
+//   * every FWHT stage and every level of the fp64 pairwise norm tree is an
+//     in-lane add/sub: stages and levels keep the format's order (stages
+//     h = 1..64, tree levels 64..1) and pairing, so the rotated values and
+//     the norms are bit-identical to any engine that follows the format;
+//   * the residual of a tile, r[16 positions][128], is already the A operand
+//     of the fp32 matrix instruction, so the sketch S r of 16 positions is
+//     256 MFMA 16x16x4 against S^T staged once per workgroup in LDS;
+//   * code bits come from a binary search over the sorted boundaries; key
+//     bit-planes (token-major words) are packed in-lane, value bit-planes
+//     (coordinate-major words, one bit per position) are wave ballots.
 // This file is compiled with -ffp-contract=off: the residual uses an explicit
 // fmaf and nothing else may be fused.
 
-#include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 
-#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
-constexpr int kWavesPerWg = 16;   // one copy of S^T in LDS serves 16 wavefronts
+constexpr int kWavesPerWg = 8;
+constexpr int kSRow = kD + 4;   // padded LDS row of S (floats): conflict-free 16-byte reads
 
-__device__ __forceinline__ float load_in(const void* p, int64_t idx, int dtype) {
-  if (dtype == IN_F32) return reinterpret_cast<const float*>(p)[idx];
-  const uint16_t h = reinterpret_cast<const uint16_t*>(p)[idx];
-  if (dtype == IN_BF16) return __uint_as_float(static_cast<uint32_t>(h) << 16);
-  return __half2float(__ushort_as_half(h));
-}
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint16_t norm_to_f16(float n) {
   return __half_as_ushort(__float2half_rn(fminf(n, 65504.0f)));
 }
-
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
-// fp64 pairwise tree of squares: level 64 in-lane, then xor butterflies.
-__device__ __forceinline__ double wave_tree_sumsq(float lo, float hi) {
-  const double a = static_cast<double>(lo) * static_cast<double>(lo);
-  const double b = static_cast<double>(hi) * static_cast<double>(hi);
-  double s = a + b;
-  s = s + lane_xor<32>(s);
-  s = s + lane_xor<16>(s);
-  s = s + lane_xor<8>(s);
-  s = s + lane_xor<4>(s);
-  s = s + lane_xor<2>(s);
-  s = s + lane_xor<1>(s);
-  return s;
+// ---------------------------------------------------------------- exchanges
+// xswap<LB>(a, b): afterwards, in every lane, a holds the value whose lane
+// bit LB is 0 and b the value whose lane bit LB is 1, both of register a in
+// lanes with bit LB clear and of register b in the others.  The lane bit
+// then indexes the former register pair and the register slot the former
+// lane bit.
+template <int LB>
+__device__ __forceinline__ void xswap_u(uint32_t& a, uint32_t& b) {
+  if constexpr (LB == 5) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  }
+}
+template <int LB>
+__device__ __forceinline__ void xswap(float& a, float& b) {
+  uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  xswap_u<LB>(ua, ub);
+  a = __uint_as_float(ua);
+  b = __uint_as_float(ub);
+}
+template <int LB>
+__device__ __forceinline__ void xswap(double& a, double& b) {
+  const uint64_t ua = static_cast<uint64_t>(__double_as_longlong(a));
+  const uint64_t ub = static_cast<uint64_t>(__double_as_longlong(b));
+  uint32_t alo = static_cast<uint32_t>(ua), ahi = static_cast<uint32_t>(ua >> 32);
+  uint32_t blo = static_cast<uint32_t>(ub), bhi = static_cast<uint32_t>(ub >> 32);
+  xswap_u<LB>(alo, blo);
+  xswap_u<LB>(ahi, bhi);
+  a = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(ahi) << 32) | alo));
+  b = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(bhi) << 32) | blo));
+}
+// v + (v of lane ^ (1 << LB)), identical in both lanes.
+template <int LB>
+__device__ __forceinline__ double pair_sum(double v) {
+  double a = v, b = v;
+  xswap<LB>(a, b);
+  return a + b;
+}
+template <int LB>
+__device__ __forceinline__ uint32_t partner(uint32_t v) {
+  uint32_t a = v, b = v;
+  xswap_u<LB>(a, b);
+  return ((threadIdx.x >> LB) & 1) ? a : b;
 }
 
-__device__ __forceinline__ uint32_t pick_word(uint64_t mlo, uint64_t mhi, int j) {
-  const uint64_t m = (j < 2) ? mlo : mhi;
-  return (j & 1) ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
+// ------------------------------------------------------------- norm tree
+// fp64 pairwise tree of squares over the 128 coordinates of each position,
+// level 64 (pairs c, c + 64) first, then 32, ..., 1.  v holds coordinate bit
+// 6 on register bit 4 and bits 0..3 on register bits 0..3; lane bit C5 holds
+// coordinate bit 5 and the other of lane bits 4/5 coordinate bit 4.  Every
+// lane of the position returns the sum.
+template <int C5>
+__device__ __forceinline__ double tree_sumsq(const float (&v)[32]) {
+  constexpr int C4 = 9 - C5;
+  double t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {   // level 64: a^2 and b^2 are exact, one rounding
+    const double a = static_cast<double>(v[i]), b = static_cast<double>(v[i + 16]);
+    t[i] = fma(a, a, b * b);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {    // level 32 (coordinate bit 5 on lane bit C5)
+    xswap<C5>(t[i], t[i + 8]);
+    t[i] = t[i] + t[i + 8];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {    // level 16 (bit 4 on lane bit C4)
+    xswap<C4>(t[i], t[i + 4]);
+    t[i] = t[i] + t[i + 4];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {    // level 8 (bit 3, moved to lane bit C5)
+    xswap<C5>(t[i], t[i + 2]);
+    t[i] = t[i] + t[i + 2];
+  }
+  xswap<C4>(t[0], t[1]);           // level 4 (bit 2, moved to lane bit C4)
+  t[0] = t[0] + t[1];
+  t[0] = pair_sum<C5>(t[0]);       // level 2 (bit 1 on lane bit C5)
+  return pair_sum<C4>(t[0]);       // level 1 (bit 0 on lane bit C4)
 }
 
-struct PolarOut {
-  int c_lo, c_hi;
-  float y_lo, y_hi;
-  uint16_t n16;
+// ------------------------------------------------------------------ FWHT
+__device__ __forceinline__ void bfly(float& a, float& b) {
+  const float x = a, y = b;
+  a = x + y;
+  b = x - y;
+}
+// Raw Sylvester FWHT, stages h = 1, 2, ..., 64 in that order.  On entry v
+// holds coordinate bits 0..3 on register bits 0..3, bit 6 on register bit 4,
+// bit 5 on lane bit 4 and bit 4 on lane bit 5.  On exit bits 0..3 and 6 are
+// where they were, bit 4 is on lane bit 4 and bit 5 on lane bit 5.
+__device__ __forceinline__ void fwht_tile(float (&v)[32]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if ((i & h) == 0) bfly(v[i], v[i + h]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {   // h = 16: bit 4 to register bit 4, bit 6 to lane bit 5
+    xswap<5>(v[i], v[i + 16]);
+    bfly(v[i], v[i + 16]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {   // h = 32: bit 5 to register bit 4, bit 4 to lane bit 4
+    xswap<4>(v[i], v[i + 16]);
+    bfly(v[i], v[i + 16]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {   // h = 64: bit 6 to register bit 4, bit 5 to lane bit 5
+    xswap<5>(v[i], v[i + 16]);
+    bfly(v[i], v[i + 16]);
+  }
+}
+
+// -------------------------------------------------------------- codebook
+// Bits of the code of y: the number of thresholds below y (thresholds sorted
+// ascending), found by a binary search; bit[k] is bit k of the code.
+template <int B>
+__device__ __forceinline__ void code_bits(float y, const float (&thr)[15], bool (&bit)[4]) {
+#pragma unroll
+  for (int k = B - 1; k >= 0; --k) {
+    constexpr int kMax = 1 << (B - 1);
+    float cand[kMax];
+    const int n = 1 << (B - 1 - k);
+#pragma unroll
+    for (int m = 0; m < kMax; ++m)
+      if (m < n) cand[m] = thr[m * (2 << k) + (1 << k) - 1];
+#pragma unroll
+    for (int j = k + 1; j < B; ++j) {   // select by the known bits, lowest first
+      const int half = 1 << (B - 1 - j);
+#pragma unroll
+      for (int m = 0; m < kMax / 2; ++m)
+        if (m < half) cand[m] = bit[j] ? cand[2 * m + 1] : cand[2 * m];
+    }
+    bit[k] = y > cand[0];
+  }
+}
+template <int B>
+__device__ __forceinline__ float centroid(const float (&cv)[16], const bool (&bit)[4]) {
+  float cand[1 << B];
+#pragma unroll
+  for (int m = 0; m < (1 << B); ++m) cand[m] = cv[m];
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int half = 1 << (B - 1 - j);
+#pragma unroll
+    for (int m = 0; m < (1 << (B - 1)); ++m)
+      if (m < half) cand[m] = bit[j] ? cand[2 * m + 1] : cand[2 * m];
+  }
+  return cand[0];
+}
+
+// ----------------------------------------------------------------- loads
+// The 32 input values at element offset idx (coordinates 32 g .. 32 g + 31).
+__device__ __forceinline__ void load_row(const void* p, int64_t idx, int dtype, float (&v)[32]) {
+  if (dtype == IN_F32) {
+    const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + idx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 f = s[i];
+      v[4 * i] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  } else {
+    const uint4* s = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + idx);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = s[i];
+      w[4 * i] = u.x;
+      w[4 * i + 1] = u.y;
+      w[4 * i + 2] = u.z;
+      w[4 * i + 3] = u.w;
+    }
+    if (dtype == IN_BF16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[2 * i] = f16_to_f32(static_cast<uint16_t>(w[i]));
+        v[2 * i + 1] = f16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+      }
+    }
+  }
+}
+
+// D x for the 32 coordinates 32 g + i of this lane (D = +/-1, exact).
+__device__ __forceinline__ void apply_signs(float (&v)[32], const float* D, int g) {
+  const float4* d4 = reinterpret_cast<const float4*>(D + 32 * g);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 d = d4[i];
+    v[4 * i] *= d.x;
+    v[4 * i + 1] *= d.y;
+    v[4 * i + 2] *= d.z;
+    v[4 * i + 3] *= d.w;
+  }
+}
+
+// Rotation and radius of a tile: v (loaded, natural layout) becomes y = H D x
+// in the FWHT's exit layout; returns the fp32 radius (rounded once from the
+// fp64 tree) of this lane's position.
+__device__ __forceinline__ float rotate(float (&v)[32], const float* D, int g) {
+  apply_signs(v, D, g);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) xswap<5>(v[i], v[i + 16]);   // bit 6 to register bit 4, bit 4 to lane bit 5
+  const double ss = tree_sumsq<4>(v);
+  fwht_tile(v);
+  return static_cast<float>(sqrt(ss));
+}
+
+struct Unit {
+  int b, h, t0, t1, grp;
+  uint8_t* kblk;
+  uint8_t* vblk;
 };
 
-// Rotation, radius and angle codes of one vector; also writes its code planes
-// (token-major) when `kplanes` is non-null.
-__device__ __forceinline__ PolarOut polar_codes(float x_lo, float x_hi, const float* D,
-                                                const float* bounds, int bits, int lane) {
-  PolarOut o;
-  float y_lo = D[lane] * x_lo;
-  float y_hi = D[lane + 64] * x_hi;
-  wave_fwht128(y_lo, y_hi, lane);
-  const double ss = wave_tree_sumsq(x_lo, x_hi);
-  const float n = static_cast<float>(sqrt(ss));
-  o.n16 = norm_to_f16(n);
-  int c_lo = 0, c_hi = 0;
-  const int levels = 1 << bits;
-  for (int j = 0; j + 1 < levels; ++j) {
-    const float thr = bounds[j] * n;
-    c_lo += (y_lo > thr) ? 1 : 0;
-    c_hi += (y_hi > thr) ? 1 : 0;
+// --------------------------------------------------------------- kernel
+template <int KB, int VB, bool QJL>
+__device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds, int lane) {
+  constexpr bool kPolar = KB > 0;
+  const int p = lane & 15;
+  const int g = lane >> 4;
+  const int k_codec = a.k_codec;
+  const int plane_words = (kD / 32) * kBlock;
+  float kthr_b[15], vthr_b[15], kc[16];
+#pragma unroll
+  for (int j = 0; j < 15; ++j) {
+    kthr_b[j] = (kPolar && j < (1 << KB) - 1) ? a.tb.kb[j] : 0.0f;
+    vthr_b[j] = (VB > 0 && j < (1 << VB) - 1) ? a.tb.vb[j] : 0.0f;
   }
-  o.c_lo = c_lo;
-  o.c_hi = c_hi;
-  o.y_lo = y_lo;
-  o.y_hi = y_hi;
-  return o;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) kc[j] = (kPolar && j < (1 << KB)) ? a.tb.ck[j] : 0.0f;
+
+  // value bit-plane words owned by this lane: coordinates p + 16 g and p + 16 g + 64
+  uint32_t vw_lo[2][4] = {}, vw_hi[2][4] = {};
+  const int base = u.grp * 32;
+
+#pragma unroll 1
+  for (int tile = 0; tile < 2; ++tile) {
+    const int tb = base + 16 * tile;
+    if (tb + 16 <= u.t0 || tb >= u.t1) continue;   // uniform
+    const int pos = tb + p;
+    const bool valid = pos >= u.t0 && pos < u.t1;
+    const int pos_c = min(max(pos, u.t0), u.t1 - 1);
+    const int t = pos_c % kBlock;
+    const int start = a.seq_lens[u.b];
+    const int64_t in_idx = ((static_cast<int64_t>(u.b) * a.n_new + (pos_c - start)) * a.n_kv + u.h) * kD + 32 * g;
+
+    // ---------------------------------------------------------- keys
+    float v[32];
+    load_row(a.k_new, in_idx, a.in_dtype, v);
+    if (!kPolar && k_codec == RAW_F32) {
+      if (valid) {
+        float4* row = reinterpret_cast<float4*>(reinterpret_cast<float*>(u.kblk) + t * kD + 32 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) row[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      }
+    } else if (!kPolar && k_codec == Q8_BLOCK32) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+      const uint16_t s16 = norm_to_f16(m / 127.0f);
+      const float sf = f16_to_f32(s16);
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int k = 0;
+          if (sf > 0.0f) k = static_cast<int>(fminf(fmaxf(rintf(v[4 * i + e] / sf), -127.0f), 127.0f));
+          word |= (static_cast<uint32_t>(k) & 0xFFu) << (8 * e);
+        }
+        w[i] = word;
+      }
+      if (valid) {
+        uint4* row = reinterpret_cast<uint4*>(u.kblk + t * kD + 32 * g);
+        row[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        row[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        reinterpret_cast<uint16_t*>(u.kblk + kBlock * kD)[t * (kD / 32) + g] = s16;
+      }
+    } else if constexpr (kPolar) {
+      const float n = rotate(v, a.tb.dk, g);
+      const uint16_t n16 = norm_to_f16(n);
+      const float nf = f16_to_f32(n16);
+      float thr[15];
+#pragma unroll
+      for (int j = 0; j < 15; ++j) thr[j] = kthr_b[j] * n;
+      uint32_t hw[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int s = 31; s >= 0; --s) {
+        bool bit[4] = {false, false, false, false};
+        code_bits<KB>(v[s], thr, bit);
+#pragma unroll
+        for (int q = 0; q < KB; ++q) hw[q] = hw[q] + hw[q] + (bit[q] ? 1u : 0u);
+        if constexpr (QJL) v[s] = fmaf(-nf, centroid<KB>(kc, bit), v[s]);   // residual
+        if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);   // bounds the live code masks
+      }
+      // plane words: the lane's bits s < 16 are bits 16 (g & 1) + s of word
+      // g >> 1, bits s >= 16 those of word (g >> 1) + 2; the lane of the other
+      // g & 1 holds the other halves
+      const bool odd = g & 1;
+      const int word = (g >> 1) + (odd ? 2 : 0);
+      const int slot = slot_of(t);
+      uint32_t* planes = reinterpret_cast<uint32_t*>(u.kblk);
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        const uint32_t o = partner<4>(hw[q]);
+        const uint32_t wv = odd ? ((o >> 16) | (hw[q] & 0xFFFF0000u)) : ((hw[q] & 0xFFFFu) | (o << 16));
+        if (valid) planes[q * plane_words + word * kBlock + slot] = wv;
+      }
+      uint8_t* after = u.kblk + 4 * KB * plane_words;
+      if constexpr (QJL) {
+        const double sr = tree_sumsq<5>(v);
+        const float rho = static_cast<float>(sqrt(sr / static_cast<double>(kD)));
+        // sketch Z = S R: rows = sketch rows, columns = the tile's positions.
+        // neg[w] collects, in this lane, the signs of its position's rows
+        // 32 w + 16 (mt & 1) + 4 g + i at bit 16 (mt & 1) + i.
+        uint32_t neg[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const float4* srow = reinterpret_cast<const float4*>(s_lds + (16 * mt + p) * kSRow + 16 * g);
+          float4 aq[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            aq[i] = srow[i];
+            aq[4 + i] = srow[16 + i];   // coordinates 64 + 16 g + ...
+          }
+          v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < 32; ++s) {
+            const float4 q4 = aq[s >> 2];
+            const float av = (s & 3) == 0 ? q4.x : (s & 3) == 1 ? q4.y : (s & 3) == 2 ? q4.z : q4.w;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, v[s], acc, 0, 0, 0);
+          }
+          // acc[i]: sketch row 16 mt + 4 g + i of position p; a zero sum is +0
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            neg[mt >> 1] |= (__float_as_uint(acc[i]) >> 31) << (16 * (mt & 1) + i);
+        }
+        // sign bit [z >= 0] at 16 (mt & 1) + 4 g + i; then OR over the four
+        // lanes of the position, leaving word g in lane g
+        uint32_t sw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sw[w] = (~neg[w] & 0x000F000Fu) << (4 * g);
+        xswap_u<4>(sw[0], sw[1]);
+        xswap_u<4>(sw[2], sw[3]);
+        uint32_t sa = sw[0] | sw[1], sb = sw[2] | sw[3];   // words g & 1 and (g & 1) + 2
+        xswap_u<5>(sa, sb);
+        if (valid) {
+          uint32_t* sgn = reinterpret_cast<uint32_t*>(after);
+          sgn[g * kBlock + slot] = sa | sb;
+        }
+        after += 4 * (kM / 32) * kBlock;
+        if (valid && g == 0) reinterpret_cast<uint16_t*>(after + 2 * kBlock)[slot] = norm_to_f16(rho);
+      }
+      if (valid && g == 0) reinterpret_cast<uint16_t*>(after)[slot] = n16;
+    }
+
+    // -------------------------------------------------------- values
+    load_row(a.v_new, in_idx, a.in_dtype, v);
+    if constexpr (VB == 0) {
+      if (valid) {
+        float4* row = reinterpret_cast<float4*>(reinterpret_cast<float*>(u.vblk) + t * kD + 32 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) row[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      }
+    } else {
+      const float n = rotate(v, a.tb.dv, g);
+      const uint16_t n16 = norm_to_f16(n);
+      float thr[15];
+#pragma unroll
+      for (int j = 0; j < 15; ++j) thr[j] = vthr_b[j] * n;
+      const int shift = 16 * g;
+      int pz = p;
+      asm volatile("" : "+v"(pz));   // keeps the per-register lane tests below inside the tile
+#pragma unroll
+      for (int s = 0; s < 32; ++s) {
+        bool bit[4] = {false, false, false, false};
+        code_bits<VB>(v[s], thr, bit);
+        if (!valid) bit[0] = bit[1] = bit[2] = bit[3] = false;
+        const bool mine = pz == (s & 15);
+#pragma unroll
+        for (int q = 0; q < VB; ++q) {
+          // ballot bit l: position l & 15, coordinate (s & 15) + 16 (l >> 4) + 64 (s >> 4)
+          const uint32_t c = static_cast<uint32_t>(__ballot(bit[q]) >> shift);
+          if (tile == 0) {
+            vw_lo[s >> 4][q] = mine ? c : vw_lo[s >> 4][q];
+          } else {
+            vw_hi[s >> 4][q] = mine ? c : vw_hi[s >> 4][q];
+          }
+        }
+        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (valid && g == 0) reinterpret_cast<uint16_t*>(u.vblk + 4 * VB * 4 * kD)[slot_of(t)] = n16;
+    }
+  }
+
+  if constexpr (VB > 0) {
+    // coordinate-major words of this 32-position group; bits of positions
+    // outside [t0, t1) keep what the cache holds
+    const int lo = u.t0 - base, hi = u.t1 - base;   // 0 <= lo < hi <= 32
+    const uint32_t keep = ~(((hi == 32) ? 0xFFFFFFFFu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u));
+    uint32_t* planes = reinterpret_cast<uint32_t*>(u.vblk);
+    const int j = (base % kBlock) / 32;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int coord = p + 16 * g + 64 * half;
+#pragma unroll
+      for (int q = 0; q < VB; ++q) {
+        uint32_t* w = planes + q * 4 * kD + j * kD + coord;
+        const uint32_t nw = (vw_lo[half][q] & 0xFFFFu) | (vw_hi[half][q] << 16);
+        *w = keep ? ((*w & keep) | nw) : nw;
+      }
+    }
+  }
 }
 
+template <int KB, int VB, bool QJL>
 __global__ __launch_bounds__(64 * kWavesPerWg) void quant_kernel(QuantArgs a) {
-  extern __shared__ float st_lds[];   // [128][128] S^T when the key codec has QJL
+  __shared__ float s_lds[QJL ? kM * kSRow : 1];   // S, row j = sketch row, padded rows
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  if (a.k_codec == POLAR_QJL) {
-    const float4* src = reinterpret_cast<const float4*>(a.tb.st);
-    float4* dst = reinterpret_cast<float4*>(st_lds);
-    for (int i = threadIdx.x; i < kD * kM / 4; i += blockDim.x) dst[i] = src[i];
+  if constexpr (QJL) {
+    const float4* src = reinterpret_cast<const float4*>(a.tb.s);
+    for (int i = threadIdx.x; i < kM * kD / 4; i += blockDim.x) {
+      const int row = i / (kD / 4), c4 = i % (kD / 4);
+      *reinterpret_cast<float4*>(s_lds + row * kSRow + 4 * c4) = src[i];
+    }
     __syncthreads();
   }
 
   const int item = blockIdx.x * kWavesPerWg + wave;
   const int total = a.batch * a.n_kv * a.groups_per_seq;
   if (item >= total) return;
-  const int g = item % a.groups_per_seq;
+  Unit u;
+  const int gi = item % a.groups_per_seq;
   const int rest = item / a.groups_per_seq;
-  const int h = rest % a.n_kv;
-  const int b = rest / a.n_kv;
-  const int start = a.seq_lens[b];
+  u.h = rest % a.n_kv;
+  u.b = rest / a.n_kv;
+  const int start = a.seq_lens[u.b];
   const int end = start + a.n_new;
-  const int grp = start / 32 + g;
-  int t0 = max(start, grp * 32);
-  int t1 = min(end, grp * 32 + 32);
-  t1 = min(t1, a.max_ctx);
-  if (t0 >= t1) return;
-  const int blk = t0 / kBlock;
-  const int64_t slot = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks + blk;
-  uint8_t* kblk = a.kc + slot * a.k_block_bytes;
-  uint8_t* vblk = a.vc + slot * a.v_block_bytes;
+  u.grp = start / 32 + gi;
+  u.t0 = max(start, u.grp * 32);
+  u.t1 = min(min(end, u.grp * 32 + 32), a.max_ctx);
+  if (u.t0 >= u.t1) return;
+  const int blk = u.t0 / kBlock;
+  const int64_t slot = (static_cast<int64_t>(u.b) * a.n_kv + u.h) * a.n_blocks + blk;
+  u.kblk = a.kc + slot * a.k_block_bytes;
+  u.vblk = a.vc + slot * a.v_block_bytes;
+  quant_unit<KB, VB, QJL>(a, u, s_lds, lane);
+}
 
-  // value bit words for this group: plane p, coordinates lane and lane+64
-  uint32_t vw_lo[4] = {0, 0, 0, 0};
-  uint32_t vw_hi[4] = {0, 0, 0, 0};
-  uint32_t vmask = 0;
-
-  for (int pos = t0; pos < t1; ++pos) {
-    const int t = pos % kBlock;
-    const int64_t in_idx = ((static_cast<int64_t>(b) * a.n_new + (pos - start)) * a.n_kv + h) * kD;
-
-    // ------------------------------------------------------------ keys
-    const float xk_lo = load_in(a.k_new, in_idx + lane, a.in_dtype);
-    const float xk_hi = load_in(a.k_new, in_idx + lane + 64, a.in_dtype);
-    if (a.k_codec == RAW_F32) {
-      float* row = reinterpret_cast<float*>(kblk) + t * kD;
-      row[lane] = xk_lo;
-      row[lane + 64] = xk_hi;
-    } else if (a.k_codec == Q8_BLOCK32) {
-      float m_lo = fabsf(xk_lo), m_hi = fabsf(xk_hi);
-      // max inside each 32-lane block
-      m_lo = fmaxf(m_lo, lane_xor<16>(m_lo));
-      m_hi = fmaxf(m_hi, lane_xor<16>(m_hi));
-      m_lo = row_max16(m_lo);
-      m_hi = row_max16(m_hi);
-      const uint16_t s_lo = norm_to_f16(m_lo / 127.0f);
-      const uint16_t s_hi = norm_to_f16(m_hi / 127.0f);
-      const float sf_lo = f16_to_f32(s_lo), sf_hi = f16_to_f32(s_hi);
-      int k_lo = 0, k_hi = 0;
-      if (sf_lo > 0.0f) k_lo = static_cast<int>(fminf(fmaxf(rintf(xk_lo / sf_lo), -127.0f), 127.0f));
-      if (sf_hi > 0.0f) k_hi = static_cast<int>(fminf(fmaxf(rintf(xk_hi / sf_hi), -127.0f), 127.0f));
-      int8_t* row = reinterpret_cast<int8_t*>(kblk) + t * kD;
-      row[lane] = static_cast<int8_t>(k_lo);
-      row[lane + 64] = static_cast<int8_t>(k_hi);
-      uint16_t* sc = reinterpret_cast<uint16_t*>(kblk + kBlock * kD) + t * (kD / 32);
-      if ((lane & 31) == 0) {
-        sc[lane >> 5] = s_lo;          // blocks 0, 1
-        sc[2 + (lane >> 5)] = s_hi;    // blocks 2, 3
-      }
-    } else {
-      const PolarOut o = polar_codes(xk_lo, xk_hi, a.tb.dk, a.tb.kb, a.k_bits, lane);
-      uint32_t* planes = reinterpret_cast<uint32_t*>(kblk);
-      const int plane_words = (kD / 32) * kBlock;
-      for (int p = 0; p < a.k_bits; ++p) {
-        const uint64_t mlo = __ballot((o.c_lo >> p) & 1);
-        const uint64_t mhi = __ballot((o.c_hi >> p) & 1);
-        if (lane < 4) planes[p * plane_words + lane * kBlock + slot_of(t)] = pick_word(mlo, mhi, lane);
-      }
-      uint8_t* after = kblk + 4 * a.k_bits * plane_words;
-      if (a.k_codec == POLAR_QJL) {
-        const float nf = f16_to_f32(o.n16);
-        const float r_lo = fmaf(-nf, a.tb.ck[o.c_lo], o.y_lo);
-        const float r_hi = fmaf(-nf, a.tb.ck[o.c_hi], o.y_hi);
-        const double sr = wave_tree_sumsq(r_lo, r_hi);
-        const float rho = static_cast<float>(sqrt(sr / static_cast<double>(kD)));
-        float z_lo = 0.0f, z_hi = 0.0f;
-        for (int i = 0; i < 64; ++i) {
-          const float rl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_lo), i));
-          const float rh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_hi), i));
-          z_lo = fmaf(st_lds[i * kM + lane], rl, z_lo);
-          z_lo = fmaf(st_lds[(i + 64) * kM + lane], rh, z_lo);
-          z_hi = fmaf(st_lds[i * kM + lane + 64], rl, z_hi);
-          z_hi = fmaf(st_lds[(i + 64) * kM + lane + 64], rh, z_hi);
-        }
-        const uint64_t slo = __ballot(z_lo >= 0.0f);
-        const uint64_t shi = __ballot(z_hi >= 0.0f);
-        uint32_t* sgn = reinterpret_cast<uint32_t*>(after);
-        if (lane < 4) sgn[lane * kBlock + slot_of(t)] = pick_word(slo, shi, lane);
-        after += 4 * (kM / 32) * kBlock;
-        if (lane == 0) reinterpret_cast<uint16_t*>(after + 2 * kBlock)[slot_of(t)] = norm_to_f16(rho);
-      }
-      if (lane == 0) reinterpret_cast<uint16_t*>(after)[slot_of(t)] = o.n16;
-    }
-
-    // ---------------------------------------------------------- values
-    const float xv_lo = load_in(a.v_new, in_idx + lane, a.in_dtype);
-    const float xv_hi = load_in(a.v_new, in_idx + lane + 64, a.in_dtype);
-    if (a.v_codec == RAW_F32) {
-      float* row = reinterpret_cast<float*>(vblk) + t * kD;
-      row[lane] = xv_lo;
-      row[lane + 64] = xv_hi;
-    } else {
-      const PolarOut o = polar_codes(xv_lo, xv_hi, a.tb.dv, a.tb.vb, a.v_bits, lane);
-      const uint32_t bit = 1u << (t & 31);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        if (p < a.v_bits) {
-          if ((o.c_lo >> p) & 1) vw_lo[p] |= bit;
-          if ((o.c_hi >> p) & 1) vw_hi[p] |= bit;
-        }
-      }
-      vmask |= bit;
-      if (lane == 0) reinterpret_cast<uint16_t*>(vblk + 4 * a.v_bits * 4 * kD)[slot_of(t)] = o.n16;
-    }
+template <int KB, bool QJL>
+hipError_t launch_k(const QuantArgs& a, int grid, hipStream_t stream) {
+  const dim3 blk(64 * kWavesPerWg);
+  switch (a.v_codec == POLAR ? a.v_bits : 0) {
+    case 0: hipLaunchKernelGGL((quant_kernel<KB, 0, QJL>), dim3(grid), blk, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((quant_kernel<KB, 2, QJL>), dim3(grid), blk, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((quant_kernel<KB, 3, QJL>), dim3(grid), blk, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((quant_kernel<KB, 4, QJL>), dim3(grid), blk, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
   }
-
-  if (a.v_codec == POLAR) {
-    uint32_t* planes = reinterpret_cast<uint32_t*>(vblk);
-    const int j = (t0 % kBlock) / 32;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p < a.v_bits) {
-        uint32_t* w = planes + p * 4 * kD + j * kD;
-        w[lane] = (w[lane] & ~vmask) | vw_lo[p];
-        w[lane + 64] = (w[lane + 64] & ~vmask) | vw_hi[p];
-      }
-    }
-  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -247,9 +531,23 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   const int total = a.batch * a.n_kv * a.groups_per_seq;
   if (total <= 0 || a.n_new <= 0) return hipSuccess;
   const int grid = (total + kWavesPerWg - 1) / kWavesPerWg;
-  const size_t lds = (a.k_codec == POLAR_QJL) ? sizeof(float) * kD * kM : 0;
-  hipLaunchKernelGGL(quant_kernel, dim3(grid), dim3(64 * kWavesPerWg), lds, stream, a);
-  return hipGetLastError();
+  if (a.k_codec == POLAR_QJL) {
+    switch (a.k_bits) {
+      case 2: return launch_k<2, true>(a, grid, stream);
+      case 3: return launch_k<3, true>(a, grid, stream);
+      case 4: return launch_k<4, true>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (a.k_codec == POLAR) {
+    switch (a.k_bits) {
+      case 2: return launch_k<2, false>(a, grid, stream);
+      case 3: return launch_k<3, false>(a, grid, stream);
+      case 4: return launch_k<4, false>(a, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return launch_k<0, false>(a, grid, stream);
 }
 
 }  // namespace tq

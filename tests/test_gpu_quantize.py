@@ -171,3 +171,43 @@ def test_dequantize_matches_oracle(wname, qjl):
                   else R.vraw[i].astype(np.float64))
             for got, ref in ((ko[t, h], kr), (vo[t, h], vr)):
                 assert np.max(np.abs(got - ref)) <= 1e-5 * max(np.linalg.norm(ref), 1e-30)
+
+
+APPEND_CODECS = {   # name -> (k_codec, k_bits, v_codec, v_bits)
+    "qjl2_v2": (tq.POLAR_QJL, 2, tq.POLAR, 2),
+    "qjl4_raw": (tq.POLAR_QJL, 4, tq.RAW_F32, 32),
+    "polar2_v4": (tq.POLAR, 2, tq.POLAR, 4),
+    "polar3_v3": (tq.POLAR, 3, tq.POLAR, 3),
+    "polar4_raw": (tq.POLAR, 4, tq.RAW_F32, 32),
+    "q8_v3": (tq.Q8_BLOCK32, 8, tq.POLAR, 3),
+    "q8_raw": (tq.Q8_BLOCK32, 8, tq.RAW_F32, 32),
+    "raw_polar2": (tq.RAW_F32, 32, tq.POLAR, 2),
+    "raw_raw": (tq.RAW_F32, 32, tq.RAW_F32, 32),
+}
+
+
+@pytest.mark.parametrize("codec", list(APPEND_CODECS))
+def test_append_every_codec(codec):
+    """Every key/value codec pair the kernels take, appended in ragged pieces
+    (a lone position, a partial 16-position tile, a whole block) into two
+    sequences, against the oracle's records."""
+    kc_, kb_, vc_, vb_ = APPEND_CODECS[codec]
+    cfg = tq.make_config(n_q_heads=8, n_kv_heads=2, batch=2, max_ctx=300, k_codec=kc_, k_bits=kb_,
+                         v_codec=vc_, v_bits=vb_, seed=42, layer=5)
+    print(f"[append codec] {codec}", flush=True)
+    L = tq.KVLayer(cfg, DEV)
+    g = torch.Generator().manual_seed(list(APPEND_CODECS).index(codec) + 77)
+    k = torch.randn((2, 300, 2, 128), generator=g)
+    v = torch.randn((2, 300, 2, 128), generator=g)
+    k[:, :, :, 5] *= 9.0
+    pos = 0
+    for n in (1, 9, 22, 128, 140):
+        L.append(k[:, pos:pos + n].to(DEV).contiguous(), v[:, pos:pos + n].to(DEV).contiguous())
+        pos += n
+    torch.cuda.synchronize()
+    spec = spec_of(cfg)
+    P = oracle.Params(spec, 42, 5)
+    kn, vn = widen_np(k), widen_np(v)
+    R = oracle_quantize(spec, P, kn, vn, [300, 300])
+    G = gpu_records(spec, L.k_cache, L.v_cache, [300, 300])
+    print(compare_records(spec, P, G, R, [300, 300], kn, codec))
