@@ -22,14 +22,17 @@
 //   * the residual of a tile, r[16 positions][128], is already the A operand
 //     of the fp32 matrix instruction, so the sketch S r of 16 positions is
 //     256 MFMA 16x16x4 against S^T staged once per workgroup in LDS;
-//   * code bits come from a binary search over the sorted boundaries; key
-//     bit-planes (token-major words) are packed in-lane, value bit-planes
-//     (coordinate-major words, one bit per position) are wave ballots.
+//   * code bits come from a binary search over the sorted boundaries and
+//     are shifted into in-lane words (an add with the compare mask as carry);
+//     key bit-planes (token-major words) take them as they are, value
+//     bit-planes (coordinate-major words, one bit per position) after a
+//     16 x 16 bit transpose across the 16 lanes of a row.
 // This file is compiled with -ffp-contract=off: the residual uses an explicit
 // fmaf and nothing else may be fused.
 
 #include <hip/hip_fp16.h>
 
+#include "tq_device.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -93,6 +96,31 @@ __device__ __forceinline__ uint32_t partner(uint32_t v) {
   uint32_t a = v, b = v;
   xswap_u<LB>(a, b);
   return ((threadIdx.x >> LB) & 1) ? a : b;
+}
+
+// 2 w + (bit of this lane in mask m): shifts one code bit into a packed word.
+__device__ __forceinline__ uint32_t shift_in(uint32_t w, uint64_t m) {
+  uint32_t r;
+  uint64_t carry_out;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(carry_out) : "v"(w), "s"(m));
+  return r;
+}
+
+// One step of a 16 x 16 bit transpose inside each 16-lane row: lane p holds
+// row p of two matrices (bits 0..15 and 16..31); the off-diagonal K x K
+// blocks of every 2K x 2K block trade places with lane p ^ K.
+template <int K>
+__device__ __forceinline__ uint32_t transpose_step(uint32_t w, int p) {
+  constexpr uint32_t M = K == 8 ? 0xFF00FF00u : K == 4 ? 0xF0F0F0F0u : K == 2 ? 0xCCCCCCCCu : 0xAAAAAAAAu;
+  const uint32_t o = static_cast<uint32_t>(lane_xor_i<K>(static_cast<int>(w)));
+  return (p & K) ? ((w & M) | ((o >> K) & ~M)) : ((w & ~M) | ((o << K) & M));
+}
+// Afterwards lane p holds, at bit c (+ 16), bit p (+ 16) of lane c's word.
+__device__ __forceinline__ uint32_t transpose16(uint32_t w, int p) {
+  w = transpose_step<8>(w, p);
+  w = transpose_step<4>(w, p);
+  w = transpose_step<2>(w, p);
+  return transpose_step<1>(w, p);
 }
 
 // ------------------------------------------------------------- norm tree
@@ -292,7 +320,7 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
   for (int j = 0; j < 16; ++j) kc[j] = (kPolar && j < (1 << KB)) ? a.tb.ck[j] : 0.0f;
 
   // value bit-plane words owned by this lane: coordinates p + 16 g and p + 16 g + 64
-  uint32_t vw_lo[2][4] = {}, vw_hi[2][4] = {};
+  uint32_t vw_lo[4] = {}, vw_hi[4] = {};   // per plane: tile 0 / tile 1 transposed words
   const int base = u.grp * 32;
 
 #pragma unroll 1
@@ -352,9 +380,11 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
         bool bit[4] = {false, false, false, false};
         code_bits<KB>(v[s], thr, bit);
 #pragma unroll
-        for (int q = 0; q < KB; ++q) hw[q] = hw[q] + hw[q] + (bit[q] ? 1u : 0u);
-        if constexpr (QJL) v[s] = fmaf(-nf, centroid<KB>(kc, bit), v[s]);   // residual
-        if ((s & 3) == 0) __builtin_amdgcn_sched_barrier(0);   // bounds the live code masks
+        for (int q = 0; q < KB; ++q) hw[q] = shift_in(hw[q], __ballot(bit[q]));
+        if constexpr (QJL) {
+          v[s] = fmaf(-nf, centroid<KB>(kc, bit), v[s]);   // residual
+          asm volatile("" : "+v"(v[s]));   // here, while the code masks are live
+        }
       }
       // plane words: the lane's bits s < 16 are bits 16 (g & 1) + s of word
       // g >> 1, bits s >= 16 those of word (g >> 1) + 2; the lane of the other
@@ -431,26 +461,24 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
       float thr[15];
 #pragma unroll
       for (int j = 0; j < 15; ++j) thr[j] = vthr_b[j] * n;
-      const int shift = 16 * g;
-      int pz = p;
-      asm volatile("" : "+v"(pz));   // keeps the per-register lane tests below inside the tile
+      // bit s of wv[q]: plane q of coordinate (s & 15) + 16 g + 64 (s >> 4)
+      uint32_t wv[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < 32; ++s) {
+      for (int s = 31; s >= 0; --s) {
         bool bit[4] = {false, false, false, false};
         code_bits<VB>(v[s], thr, bit);
-        if (!valid) bit[0] = bit[1] = bit[2] = bit[3] = false;
-        const bool mine = pz == (s & 15);
 #pragma unroll
-        for (int q = 0; q < VB; ++q) {
-          // ballot bit l: position l & 15, coordinate (s & 15) + 16 (l >> 4) + 64 (s >> 4)
-          const uint32_t c = static_cast<uint32_t>(__ballot(bit[q]) >> shift);
-          if (tile == 0) {
-            vw_lo[s >> 4][q] = mine ? c : vw_lo[s >> 4][q];
-          } else {
-            vw_hi[s >> 4][q] = mine ? c : vw_hi[s >> 4][q];
-          }
+        for (int q = 0; q < VB; ++q) wv[q] = shift_in(wv[q], __ballot(bit[q]));
+      }
+      // transposed: bit p (+ 16) = position p of coordinate p' + 16 g (+ 64), p' = this lane's p
+#pragma unroll
+      for (int q = 0; q < VB; ++q) {
+        const uint32_t tw = transpose16(wv[q], p);
+        if (tile == 0) {
+          vw_lo[q] = tw;
+        } else {
+          vw_hi[q] = tw;
         }
-        if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
       if (valid && g == 0) reinterpret_cast<uint16_t*>(u.vblk + 4 * VB * 4 * kD)[slot_of(t)] = n16;
     }
@@ -469,8 +497,9 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
 #pragma unroll
       for (int q = 0; q < VB; ++q) {
         uint32_t* w = planes + q * 4 * kD + j * kD + coord;
-        const uint32_t nw = (vw_lo[half][q] & 0xFFFFu) | (vw_hi[half][q] << 16);
-        *w = keep ? ((*w & keep) | nw) : nw;
+        const uint32_t nw = half ? ((vw_lo[q] >> 16) | (vw_hi[q] & 0xFFFF0000u))
+                                 : ((vw_lo[q] & 0xFFFFu) | (vw_hi[q] << 16));
+        *w = keep ? ((*w & keep) | (nw & ~keep)) : nw;
       }
     }
   }
