@@ -506,7 +506,7 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
 }
 
 template <int KB, int VB, bool QJL>
-__global__ __launch_bounds__(64 * kWavesPerWg) void quant_kernel(QuantArgs a) {
+__global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(4))) void quant_kernel(QuantArgs a) {
   __shared__ float s_lds[QJL ? kM * kSRow : 1];   // S, row j = sketch row, padded rows
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
