@@ -112,12 +112,20 @@ __device__ __forceinline__ v8i expand_fp4(uint32_t w) {
 // s = +1 for a set bit the element is 5 + s, 3 + s, 1 + s, -s: one AND(-OR) per
 // dword.  The matrix operand on the other side carries -1 on the d = 3
 // elements, and the offsets 5, 3, 1 are removed with one constant per head.
+// (w & m) | c as one v_and_or_b32; the mask rides in a scalar register and
+// the fill in a vector register (a three-operand instruction here takes no
+// literal), both set once outside the loops.
+__device__ __forceinline__ int and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return static_cast<int>(r);
+}
 __device__ __forceinline__ v8i expand_fp4_affine(uint32_t w) {
   v8i r;
-  r[0] = static_cast<int>((w & 0x11111111u) | 0x66666666u);
-  r[1] = static_cast<int>((w & 0x22222222u) | 0x44444444u);
+  r[0] = and_or(w, 0x11111111u, 0x66666666u);
+  r[1] = and_or(w, 0x22222222u, 0x44444444u);
   r[2] = static_cast<int>(w & 0x44444444u);
-  r[3] = static_cast<int>((w & 0x88888888u) | 0x22222222u);
+  r[3] = and_or(w, 0x88888888u, 0x22222222u);
   r[4] = r[5] = r[6] = r[7] = 0;
   return r;
 }
@@ -312,6 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ uint8_t aexp[2][4][16];        // E8M0 scale [set][k / 32][row]
   __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * 128];  // per group: limbs of p * radius [col][k]
   __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];       // per group: [k / 32][col]
+  __shared__ float rwb[2][kWaves][4];       // per step parity: each wave's reference per head
   __shared__ float wred[kWaves][4];
   __shared__ float hmax[2][kWaves];         // per-wave max |value| for the limb exponents
   __shared__ float mrun[4];                 // running max per head at the end (log2 units)
@@ -321,6 +330,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ __attribute__((aligned(16))) float sred[8][4 * kM];   // partial sketch sums; later the group sums
   __shared__ int s_last;
   uint8_t* const slots[4] = {slot0, slot1, slot2, slot3};
+  // digit buffers of odd steps: the query's digit buffers, free once the
+  // operands are in registers
+  uint8_t* const plimb0 = &plimb[0][0];
+  uint8_t* const plimb1 = &alimb[0][0];
+  uint8_t* const pexp0 = &pexp[0][0][0];
+  uint8_t* const pexp1 = &aexp[0][0][0];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -493,8 +508,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       }
     }
     if constexpr (NS > 3) copy_pair<KB, QJL, VB>(slots[2], junk, rk, rv, blk0 + 4, w, lane);
-    // the fourth digit column of each head stays zero (three digits are written)
-    for (int k = tid; k < 2 * 4 * 128; k += kThreads) plimb[k >> 9][(4 * ((k >> 7) & 3) + 3) * 128 + (k & 127)] = 0;
     // the first pair has landed (this wave's copies; the barrier covers the others')
     wait_vm<(NS - 2) * F::perWave>();
     lds_barrier();
@@ -529,17 +542,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const float csq = QJL ? cconst[1][g4] : 0.0f;
     const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
     const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
-    uint8_t* my_plimb = plimb[gr];
     const int so = 4 * (g4 * kBlock + 32 * wl + 2 * t);   // this lane's key words in a block
     const int sn = 2 * (32 * wl + 2 * t);                 // its two fp16 per-position fields
 
     // --------------------------------------------------------- main loop
     // Step i processes blocks blk0 + 2i (group 0) and blk0 + 2i + 1 (group 1)
-    // from ring slot i % NS.  After its first barrier (every wave has then
-    // finished step i - 1) it refills slot (i - 1) % NS with the pair of step
-    // i + NS - 1; before its second barrier each wave waits for its copies of
-    // the pair of step i + 1.
-    auto step = [&](uint8_t* cur, uint8_t* refill, int i) __attribute__((always_inline)) {
+    // from ring slot i % NS, with one barrier, between the probability digits
+    // and the weighted sum.  After it (every wave has then finished step
+    // i - 1) the step refills slot (i - 1) % NS with the pair of step
+    // i + NS - 1; before it each wave waits for its copies of the pair of step
+    // i + 1 (issued in step i - 1), which the next step reads right after this
+    // one's weighted sum.  With two slots the pair of step i + 1 is only
+    // issued in step i, and a second barrier ends the step.
+    // Part A of step i: logits of the group's key block, this wave's
+    // reference, the probability digits.  Carried to part B: the reference and
+    // the sum of this lane's two probabilities.
+    auto partA = [&](const uint8_t* cur, int i, float& rw_out, float& ps_out) __attribute__((always_inline)) {
       const int blk = blk0 + 2 * i + gr;
       const int n_t = (blk < blk1) ? min(kBlock, len - blk * kBlock) : 0;
       const uint8_t* kb = cur + gr * F::kBytes;
@@ -621,31 +639,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       }
       }
 
-      // step max per head (8 waves, both blocks); the running max only moves
-      // when a step exceeds it by 2^8, so rescaling is rare and p stays below 256
+      // This wave's reference per head (row g4): the integer ceiling of its
+      // step maximum, log2 units.  p <= 1 is formed against it without waiting
+      // for the other waves; after the barrier every wave brings the eight
+      // references to the common running one through exact powers of two (the
+      // E8M0 scales of the probability digits and the denominators).  The
+      // running reference only moves when a step exceeds it by 2^8.
+      const int par = i & 1;   // the digit buffers alternate: one barrier per step
+      uint8_t* const pl = (par ? plimb1 : plimb0) + gr * (16 * 128);
+      uint8_t* const pe = (par ? pexp1 : pexp0) + gr * 64;
       const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
-      if (t == 0) wred[w][g4] = mloc;
-      lds_barrier();
-      copy_pair<KB, QJL, VB>(refill, junk, rk, rv, blk0 + 2 * (i + NS - 1), w, lane);
-      const int hb = t >> 2;
-      float bm_a = wred[0][g4], bm_b = wred[0][hb];
-#pragma unroll
-      for (int u = 1; u < kWaves; ++u) {
-        bm_a = fmaxf(bm_a, wred[u][g4]);
-        bm_b = fmaxf(bm_b, wred[u][hb]);
-      }
-      const float mn_a = (bm_a > m_a + 8.0f) ? bm_a : m_a;
-      const float mn_b = (bm_b > m_b + 8.0f) ? bm_b : m_b;
-      const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_a - mn_a);
-      const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_b - mn_b);
-      m_a = mn_a;
-      m_b = mn_b;
+      const float rw = (mloc == -INFINITY) ? -INFINITY : ceilf(mloc);
+      if (t == 0) rwb[par][w][g4] = rw;
 
       // probabilities and base-32 digits of p * value radius (3 digits, ~14 bits)
       const uint32_t vn = *reinterpret_cast<const uint32_t*>(vb + 2048 * VB + sn);
-      const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - m_a);
-      const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - m_a);
-      lsum = lsum * fh + (p0 + p1);
+      const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - rw);
+      const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - rw);
       float r0 = (p0 > 0.0f) ? p0 * h2f(vn) : 0.0f;
       float r1 = (p1 > 0.0f) ? p1 * h2f(vn >> 16) : 0.0f;
       const float pm = row_max16(fmaxf(r0, r1));
@@ -654,26 +664,50 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       r1 = __builtin_amdgcn_ldexpf(r1, -s0);
       uint32_t ebytes = 127u << 24;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
-        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
-        if (j < 2) {
-          r0 = (r0 - d0) * 32.0f;
-          r1 = (r1 - d1) * 32.0f;
+      for (int j = 0; j < 4; ++j) {
+        int pk = 0;   // the fourth digit row stays zero
+        if (j < 3) {
+          const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+          if (j < 2) {
+            r0 = (r0 - d0) * 32.0f;
+            r1 = (r1 - d1) * 32.0f;
+          }
+          ebytes |= static_cast<uint32_t>(min(max(s0 - 5 * j + 127, 1), 254)) << (8 * j);
         }
-        *reinterpret_cast<uint16_t*>(&my_plimb[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) =
-            static_cast<uint16_t>(pk & 0xffff);
-        ebytes |= static_cast<uint32_t>(min(max(s0 - 5 * j + 127, 1), 254)) << (8 * j);
+        *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
       }
-      if (t == 0) *reinterpret_cast<uint32_t*>(&pexp[gr][wl][4 * g4]) = ebytes;
-      wait_vm<(NS - 2) * F::perWave>();   // this wave's copies of the next pair have landed
-      lds_barrier();
-      // (no third barrier: the next writes of wred and of this group's limbs
-      // come after the next step's first barrier, which every wave reaches
-      // only after its reads below)
+      if (t == 0) *reinterpret_cast<uint32_t*>(&pe[16 * wl + 4 * g4]) = ebytes;
+      rw_out = rw;
+      ps_out = p0 + p1;
+    };
+
+    // Part B of step i (after the barrier that follows every wave's part A):
+    // the common running references, then the weighted sum of the group's
+    // value block.
+    auto partB = [&](const uint8_t* cur, int i, float rw, float ps) __attribute__((always_inline)) {
+      const uint8_t* vb = cur + F::kChunks * 1024 + gr * F::vBytes;
+      const int par = i & 1;
+      const uint8_t* const pl = (par ? plimb1 : plimb0) + gr * (16 * 128);
+      const uint8_t* const pe = (par ? pexp1 : pexp0) + gr * 64;
+      // running references of head g4 (denominator) and head t / 4 (result column)
+      const int hb = t >> 2;
+      float ra = rwb[par][0][g4], rb = rwb[par][0][hb];
+#pragma unroll
+      for (int u = 1; u < kWaves; ++u) {
+        ra = fmaxf(ra, rwb[par][u][g4]);
+        rb = fmaxf(rb, rwb[par][u][hb]);
+      }
+      const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
+      const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
+      const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_a - mn_a));
+      const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_b - mn_b));
+      lsum = lsum * fh + ((rw == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(ps, static_cast<int>(rw - mn_a)));
+      m_a = mn_a;
+      m_b = mn_b;
 
       // weighted sum of value terms for coordinates 32wl + 16r + (row), columns (head, limb)
-      if (__any(fv != 1.0f)) {   // rescale only when some head's max moved
+      if (__any(fv != 1.0f)) {   // rescale only when some head's reference moved
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
@@ -681,11 +715,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       }
       v8i Pv;
       {
-        const uint4 lo = *reinterpret_cast<const uint4*>(&my_plimb[t * 128 + 16 * g4]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&my_plimb[t * 128 + 64 + 16 * g4]);
+        const uint4 lo = *reinterpret_cast<const uint4*>(&pl[t * 128 + 16 * g4]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&pl[t * 128 + 64 + 16 * g4]);
         Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-      const int scp = pexp[gr][g4][t];
+      // k-block g4 holds the positions of wave g4 of this group: its digits
+      // carry 2^(its reference - the running one)
+      const float rk = rwb[par][4 * gr + g4][hb];
+      const int adj = (rk == -INFINITY) ? 0 : static_cast<int>(rk - m_b);
+      const int scp = min(max(static_cast<int>(pe[16 * g4 + t]) + adj, 1), 254);
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         uint32_t vw[VB];
@@ -694,6 +732,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
           vw[p] = *reinterpret_cast<const uint32_t*>(vb + 4 * (p * 4 * kD + g4 * kD + 32 * wl + 16 * rr + t));
 #pragma unroll
         for (int T = 0; T < NTV; ++T) accV[rr][T] = mfma_fp4_fp8(expand_fp4(term_word<VB>(vw, T)), Pv, accV[rr][T], scp);
+      }
+    };
+
+    // The barrier between part A of step i and part B: with three or more
+    // slots the pair of step i + 1 was issued a step ago, and this wave's
+    // copies of it must have landed (everyone's, after the barrier).  Every
+    // wave is then past part B of step i - 1: refill that slot with the pair of
+    // step i + NS - 1.
+    auto sync = [&](uint8_t* refill, int i) __attribute__((always_inline)) {
+      if constexpr (NS >= 3) wait_vm<(NS - 3) * F::perWave>();
+      lds_barrier();
+      copy_pair<KB, QJL, VB>(refill, junk, rk, rv, blk0 + 2 * (i + NS - 1), w, lane);
+    };
+    // step i: A(i), barrier and refill, B(i); with two slots a second barrier
+    // after waiting for the pair of step i + 1
+    auto step = [&](uint8_t* cur, uint8_t* refill, int i) __attribute__((always_inline)) {
+      float rw, ps;
+      partA(cur, i, rw, ps);
+      sync(refill, i);
+      partB(cur, i, rw, ps);
+      if constexpr (NS == 2) {
+        wait_vm<0>();
+        lds_barrier();
       }
     };
     // whole rounds of the ring, then the last partial round; slot indices are
