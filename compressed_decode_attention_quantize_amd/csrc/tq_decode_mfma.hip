@@ -171,11 +171,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Copies the two blocks b0, b0 + 1 (K region then V region) into a ring slot
-// straight from memory into shared memory, 1 KB per instruction (lane l moves
-// bytes 16l..16l+15 of its unit).  Every wave issues the same number of copies;
-// units past the data read zero into a junk buffer, so the count of
-// outstanding copies per wave is the same at every step.
 // q8 key rows (128 B per position) are stored in shared memory with their
 // 16-byte granules permuted: granule j of position tok sits at granule
 // j ^ q8_swizzle(tok) of its row.  The sixteen positions one matrix operand
@@ -183,26 +178,43 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ int q8_swizzle(int tok) { return ((tok >> 3) & 3) | ((tok & 2) << 1); }
 
 template <int KB, bool QJL, int VB>
-__device__ __forceinline__ void copy_pair(uint8_t* slot, uint8_t* junk, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, int b0, int w, int lane) {
+struct PairCopier {
   using F = Fmt<KB, QJL, VB>;
+  int lo[F::perWave];   // per-lane byte offset of each copy, less the block term
+  // lane offsets and units of this wave's copies (q = w + 8 j)
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-  for (int j = 0; j < F::perWave; ++j) {
-    const int q = w + kWaves * j;   // unit, uniform over the wave
-    const bool isk = q < F::kChunks;
-    const bool isv = !isk && q < F::kChunks + F::vChunks;
-    int kgr = 64 * q + lane;   // granule of the pair's K region this lane fills
-    if constexpr (F::q8) {
-      const int half = (kgr >= F::kBytes / 16) ? 1 : 0;
-      const int g = kgr - half * (F::kBytes / 16);
-      if (g < kBlock * kD / 16) kgr = half * (F::kBytes / 16) + (g & ~7) + ((g & 7) ^ q8_swizzle(g >> 3));
+    for (int j = 0; j < F::perWave; ++j) {
+      const int q = w + kWaves * j;
+      const bool isk = q < F::kChunks;
+      const bool isv = !isk && q < F::kChunks + F::vChunks;
+      int kgr = 64 * q + lane;   // granule of the pair's K region this lane fills
+      if constexpr (F::q8) {
+        const int half = (kgr >= F::kBytes / 16) ? 1 : 0;
+        const int g = kgr - half * (F::kBytes / 16);
+        if (g < kBlock * kD / 16) kgr = half * (F::kBytes / 16) + (g & ~7) + ((g & 7) ^ q8_swizzle(g >> 3));
+      }
+      lo[j] = isk ? 16 * kgr : (isv ? 1024 * (q - F::kChunks) + 16 * lane : 0x7fff0000 + 16 * lane);
     }
-    const int off = isk ? b0 * F::kBytes + 16 * kgr
-                        : (isv ? b0 * F::vBytes + 1024 * (q - F::kChunks) + 16 * lane : 0x7fff0000 + 16 * lane);
-    uint8_t* dst = (isk || isv) ? slot + 1024 * q : junk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, (lds_void_t*)(dst), 16, off, 0, 0, 0);
   }
-}
+  // Copies the two blocks b0, b0 + 1 (K region then V region) into a ring
+  // slot straight from memory into shared memory, 1 KB per instruction (lane
+  // l moves bytes 16l..16l+15 of its unit).  Every wave issues the same number
+  // of copies; units past the data read zero into a junk buffer, so the count
+  // of outstanding copies per wave is the same at every step.
+  __device__ __forceinline__ void copy(uint8_t* slot, uint8_t* junk, __amdgpu_buffer_rsrc_t rk,
+                                       __amdgpu_buffer_rsrc_t rv, int b0, int w) const {
+#pragma unroll
+    for (int j = 0; j < F::perWave; ++j) {
+      const int q = w + kWaves * j;   // unit, uniform over the wave
+      const bool isk = q < F::kChunks;
+      const bool isv = !isk && q < F::kChunks + F::vChunks;
+      const int stride = isk ? F::kBytes : (isv ? F::vBytes : 0);   // uniform
+      uint8_t* dst = (isk || isv) ? slot + 1024 * q : junk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, (lds_void_t*)(dst), 16, lo[j] + b0 * stride, 0, 0, 0);
+    }
+  }
+};
 
 // Workgroup barrier for shared-memory data only: waits for this wave's
 // shared-memory operations, not for its copies in flight (a fenced barrier
@@ -410,7 +422,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
     // the first NS - 1 pairs (at most three) are issued one per set-up phase
     // (pair 0 here), so that the copies proceed while the waves compute
-    copy_pair<KB, QJL, VB>(slots[0], junk, rk, rv, blk0, w, lane);
+    PairCopier<KB, QJL, VB> cp;
+    cp.init(w, lane);
+    cp.copy(slots[0], junk, rk, rv, blk0, w);
 
     // ------------------------------------------------------------- set-up
     // waves 0..3 rotate the query of head w in registers (q_raw = H D_K q);
@@ -461,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g * kM + 2 * jq]) = make_float2(acc[g][0], acc[g][1]);
     }
     lds_barrier();
-    if constexpr (NS > 2) copy_pair<KB, QJL, VB>(slots[1], junk, rk, rv, blk0 + 2, w, lane);
+    if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + 2, w);
     if (QJL) {
       // thread tid owns output tid: head tid / 128, so waves 2g and 2g+1 cover head g
       float sum = 0.0f;
@@ -507,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
         if (lane == 0) cconst[set][g] = c;
       }
     }
-    if constexpr (NS > 3) copy_pair<KB, QJL, VB>(slots[2], junk, rk, rv, blk0 + 4, w, lane);
+    if constexpr (NS > 3) cp.copy(slots[2], junk, rk, rv, blk0 + 4, w);
     // the first pair has landed (this wave's copies; the barrier covers the others')
     wait_vm<(NS - 2) * F::perWave>();
     lds_barrier();
@@ -743,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     auto sync = [&](uint8_t* refill, int i) __attribute__((always_inline)) {
       if constexpr (NS >= 3) wait_vm<(NS - 3) * F::perWave>();
       lds_barrier();
-      copy_pair<KB, QJL, VB>(refill, junk, rk, rv, blk0 + 2 * (i + NS - 1), w, lane);
+      cp.copy(refill, junk, rk, rv, blk0 + 2 * (i + NS - 1), w);
     };
     // step i: A(i), barrier and refill, B(i); with two slots a second barrier
     // after waiting for the pair of step i + 1
