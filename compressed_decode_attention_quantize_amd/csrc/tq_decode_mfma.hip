@@ -327,14 +327,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ __attribute__((aligned(1024))) uint8_t slot3[NS > 3 ? F::slotBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t junk[1024];
   __shared__ float qr[4 * kD];              // q_raw = H D_K q per head (zero rows past G)
-  __shared__ float sqs[4 * kM];             // S q_raw / sqrt d
   __shared__ __attribute__((aligned(16))) uint8_t alimb[2][16 * 128];  // fp8 limbs [set][row = 4g + j][k]
   __shared__ uint8_t aexp[2][4][16];        // E8M0 scale [set][k / 32][row]
   __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * 128];  // per group: limbs of p * radius [col][k]
   __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];       // per group: [k / 32][col]
   __shared__ float rwb[2][kWaves][4];       // per step parity: each wave's reference per head
   __shared__ float wred[kWaves][4];
-  __shared__ float hmax[2][kWaves];         // per-wave max |value| for the limb exponents
   __shared__ float mrun[4];                 // running max per head at the end (log2 units)
   __shared__ float cconst[2][4];            // offsets of the affine key operand per (set, head)
   __shared__ __attribute__((aligned(8))) int8_t qdig[4][3][kD];   // q8 keys: base-128 digits of q per head
@@ -373,6 +371,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int G = min(4, a.group - 4 * hg);  // query heads served here
   const int hq0 = h * a.group + 4 * hg;    // the first of them
   uint32_t* const counter = a.counters + (static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg;
+  // loads the set-up needs are issued first, before the sequence length they
+  // do not depend on: this wave's query rows, the rotation signs, its slice
+  // of the sketch table, the codebook coefficients
+  const float* qb0 = a.q + (static_cast<int64_t>(b) * a.n_q + hq0) * kD;
+  const float* qp = qb0 + min(w & 3, G - 1) * kD;
+  const float qa = qp[lane], qb = qp[lane + 64];
+  const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
+  // lane l: raw query coordinate 16w + l % 16 of head l / 16 (zero past G)
+  const float qsl = qb0[min(lane >> 4, G - 1) * kD + 16 * w + (lane & 15)];
+  const int jq = threadIdx.x & 63;   // sketch rows 2jq, 2jq + 1; coordinates 16w .. 16w + 15
+  float2 st2[16];
+  if (QJL) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.shd + (16 * w + u) * kM + 2 * jq);
+  }
+  float ak[NTK];
+  {
+    const cfloat* akp = (const cfloat*)(a.tb.ak);
+#pragma unroll
+    for (int T = 0; T < NTK; ++T) ak[T] = akp[T];
+  }
   const int len = min(a.seq_lens[b], a.max_ctx);
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
@@ -395,28 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (n_iter > 0) {   // uniform over the workgroup
-    // loads the set-up needs are issued first (outstanding loads retire in
-    // order): the rotation's inputs, this wave's slice of the raw queries,
-    // the sketch table; then the copies of the first NS - 1 block pairs
-    const float* qb0 = a.q + (static_cast<int64_t>(b) * a.n_q + hq0) * kD;
-    const float* qp = qb0 + min(w & 3, G - 1) * kD;
-    const float qa = qp[lane], qb = qp[lane + 64];
-    const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
-    // lane l: raw query coordinate 16w + l % 16 of head l / 16 (zero past G)
-    const float qsl = qb0[min(lane >> 4, G - 1) * kD + 16 * w + (lane & 15)];
-    const int jq = tid & 63;   // sketch rows 2jq, 2jq + 1; coordinates 16w .. 16w + 15
-    float2 st2[16];
-    if (QJL) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.shd + (16 * w + u) * kM + 2 * jq);
-    }
-    float ak[NTK];
     float aksum = 0.0f;
-    {
-      const cfloat* akp = (const cfloat*)(a.tb.ak);
-#pragma unroll
-      for (int T = 0; T < NTK; ++T) ak[T] = akp[T];
-    }
     __builtin_amdgcn_sched_barrier(0);
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, blk1);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
@@ -427,9 +425,46 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     cp.copy(slots[0], junk, rk, rv, blk0, w);
 
     // ------------------------------------------------------------- set-up
-    // waves 0..3 rotate the query of head w in registers (q_raw = H D_K q);
-    // meanwhile every wave forms its share of the sketch S q_raw / sqrt d as
-    // (S H D_K / sqrt d) q, which needs no rotated query
+    // Waves 0..3 rotate the query of head w in registers (q_raw = H D_K q)
+    // and write its digits; meanwhile every wave forms its share of the
+    // sketch S q_raw / sqrt d as (S H D_K / sqrt d) q, which needs no rotated
+    // query, and after one barrier waves 4..7 add the shares and write the
+    // sketch's digits.
+    //
+    // Digits: base-32 fixed point of q' with one leading exponent per 32
+    // k-slots (the E8M0 scales are per row and per 32 k-slots), k-slot k
+    // holding coordinate (or sketch row) pos_of_slot(k); q' is the value with
+    // its sign flipped on the k-slots that meet the sign field of the key
+    // operand, (k mod 32) / 8 == 3.  The set's constant is the sum of 5, 3, 1,
+    // 0 times the digit-exact q' over the k-slots of field 0..3.  Lane l of
+    // the writing wave takes k-slots 2l, 2l + 1, so the 32 k-slots of an
+    // exponent are the 16 lanes of a row.
+    auto write_digits = [&](int set, int g, float u0, float u1) __attribute__((always_inline)) {
+      const int k0 = 2 * lane;
+      const int fld = (k0 & 31) >> 3;
+      if (fld == 3) {
+        u0 = -u0;
+        u1 = -u1;
+      }
+      const float m = row_max16(fmaxf(fabsf(u0), fabsf(u1)));
+      const int s0 = (m >= 1e-30f) ? exponent_of(m) - 3 : 0;   // |u| 2^-s0 < 16
+      float r0 = __builtin_amdgcn_ldexpf(u0, -s0), r1 = __builtin_amdgcn_ldexpf(u1, -s0);
+      float t0 = 0.0f, t1 = 0.0f;   // digit-exact values, in units of 2^s0
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+        t0 = fmaf(d0, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t0);
+        t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
+        r0 = (r0 - d0) * 32.0f;
+        r1 = (r1 - d1) * 32.0f;
+        *reinterpret_cast<uint16_t*>(&alimb[set][(4 * g + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
+        if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
+      }
+      const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
+      const float c = wave_sum64(__builtin_amdgcn_ldexpf(wf * (t0 + t1), s0));
+      if (lane == 0) cconst[set][g] = c;
+    };
     if constexpr (KQ8) {
       // q8 keys meet the query unrotated: three base-128 digits of q per head,
       // integers in [-64, 64], for the int8 matrix instruction
@@ -454,8 +489,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       wave_fwht128(q_lo, q_hi, lane);
       qr[w * kD + lane] = q_lo;
       qr[w * kD + lane + 64] = q_hi;
-      const float qm = wave_max64(fmaxf(fabsf(q_lo), fabsf(q_hi)));
-      if (lane == 0) hmax[0][w] = qm;
+      // the same wave reads back its own rotated query in k-slot order
+      write_digits(0, w, qr[w * kD + pos_of_slot(2 * lane)], qr[w * kD + pos_of_slot(2 * lane + 1)]);
     }
     if (QJL) {
       float acc[4][2];
@@ -473,53 +508,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g * kM + 2 * jq]) = make_float2(acc[g][0], acc[g][1]);
-    }
-    lds_barrier();
-    if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + 2, w);
-    if (QJL) {
-      // thread tid owns output tid: head tid / 128, so waves 2g and 2g+1 cover head g
-      float sum = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) sum += sred[c][tid];
-      sqs[tid] = sum;
-      const float m1 = wave_max64(fabsf(sum));
-      if (lane == 0) hmax[1][w] = m1;
       lds_barrier();
-    }
-    {
-      // base-32 digits of q' (waves 0..3, set 0: q_raw; waves 4..7, set 1:
-      // sq), leading exponent per (set, head); wave (set, g) writes k-slots 2l,
-      // 2l+1 of head g, k-slot k holding coordinate pos_of_slot(k).  q' is the
-      // value with its sign flipped on the k-slots that meet the sign field of
-      // the key operand, (k mod 32) / 8 == 3; the set's constant is the sum of
-      // 5, 3, 1, 0 times the digit-exact q' over the k-slots of field 0..3.
-      const int set = w >> 2;
-      const int g = w & 3;
-      if (!KQ8 && (set == 0 || QJL)) {
-        const int k0 = 2 * lane;
-        const int fld = (k0 & 31) >> 3;
-        const float* src = set == 0 ? qr + g * kD : sqs + g * kM;
-        const float u0 = (fld == 3) ? -src[pos_of_slot(k0)] : src[pos_of_slot(k0)];
-        const float u1 = (fld == 3) ? -src[pos_of_slot(k0 + 1)] : src[pos_of_slot(k0 + 1)];
-        const float m = set == 0 ? hmax[0][g] : fmaxf(hmax[1][2 * g], hmax[1][2 * g + 1]);
-        const int s0 = (m >= 1e-30f) ? exponent_of(m) - 3 : 0;   // |u| 2^-s0 < 16
-        float r0 = __builtin_amdgcn_ldexpf(u0, -s0), r1 = __builtin_amdgcn_ldexpf(u1, -s0);
-        float t0 = 0.0f, t1 = 0.0f;   // digit-exact values, in units of 2^s0
+      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + 2, w);
+      if (w >= 4) {
+        // sketch rows pos_of_slot(2 lane), pos_of_slot(2 lane + 1) of head w - 4
+        const int g = w - 4;
+        const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
+        float u0 = 0.0f, u1 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
-          const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
-          t0 = fmaf(d0, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t0);
-          t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
-          r0 = (r0 - d0) * 32.0f;
-          r1 = (r1 - d1) * 32.0f;
-          *reinterpret_cast<uint16_t*>(&alimb[set][(4 * g + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
-          if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
+        for (int c = 0; c < 8; ++c) {
+          u0 += sred[c][g * kM + r0];
+          u1 += sred[c][g * kM + r1];
         }
-        const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
-        const float c = __builtin_amdgcn_ldexpf(wave_sum64(wf * (t0 + t1)), s0);
-        if (lane == 0) cconst[set][g] = c;
+        write_digits(1, g, u0, u1);
       }
+    } else {
+      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + 2, w);
     }
     if constexpr (NS > 3) cp.copy(slots[2], junk, rk, rv, blk0 + 4, w);
     // the first pair has landed (this wave's copies; the barrier covers the others')
