@@ -68,9 +68,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const v4f cv4f;
 typedef __attribute__((address_space(4))) const float cfloat;
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;   // two groups of four
-constexpr int kRing = 4;    // most ring slots (block pairs) in shared memory
+constexpr int kRing = 4;    // most ring slots in shared memory
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -145,18 +143,23 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4
 
 // Byte layout of one cache block (128 positions) and of the shared-memory
 // ring that stages two blocks per step.
-template <int KB, bool QJL, int VB>
+// NG block groups (four wavefronts each) per workgroup: with one group two
+// workgroups share a compute unit and each may take half of its shared memory.
+template <int KB, bool QJL, int VB, int NG>
 struct Fmt {
+  static constexpr int waves = 4 * NG;
+  static constexpr int threads = 64 * waves;
+  static constexpr int ldsBudget = (NG == 2 ? 160 : 80) * 1024;
   static constexpr bool q8 = KB == 8;   // q8 keys: int8[128][128], then fp16 scales [128][4]
   static constexpr int kNorms = q8 ? 0 : 2048 * KB + (QJL ? 2048 : 0);   // fp16 radii after planes (and signs)
   static constexpr int kBytes = q8 ? 128 * 128 + 128 * 8 : kNorms + 256 + (QJL ? 256 : 0);   // K block
   static constexpr int vBytes = 2048 * VB + 256;                       // V block: planes, fp16 radii
-  static constexpr int kChunks = (2 * kBytes + 1023) / 1024;           // 1 KB copy units per step (two blocks)
-  static constexpr int vChunks = (2 * vBytes + 1023) / 1024;
-  static constexpr int perWave = (kChunks + vChunks + kWaves - 1) / kWaves;   // copies per wave per step
+  static constexpr int kChunks = (NG * kBytes + 1023) / 1024;          // 1 KB copy units per step (NG blocks)
+  static constexpr int vChunks = (NG * vBytes + 1023) / 1024;
+  static constexpr int perWave = (kChunks + vChunks + waves - 1) / waves;   // copies per wave per step
   static constexpr int slotBytes = (kChunks + vChunks) * 1024;
-  static constexpr int kOtherLds = 31 * 1024;   // everything else the kernel keeps in shared memory
-  static constexpr int slotsFit = (160 * 1024 - kOtherLds) / slotBytes;
+  static constexpr int kOtherLds = (NG == 2 ? 31 : 20) * 1024;   // everything else the kernel keeps in shared memory
+  static constexpr int slotsFit = (ldsBudget - kOtherLds) / slotBytes;
   static constexpr int nSlots = slotsFit < kRing ? slotsFit : kRing;
   static_assert(nSlots >= 2, "ring needs two slots");
 };
@@ -177,15 +180,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // reads together then fall on distinct banks (plain rows share every bank).
 __device__ __forceinline__ int q8_swizzle(int tok) { return ((tok >> 3) & 3) | ((tok & 2) << 1); }
 
-template <int KB, bool QJL, int VB>
+template <int KB, bool QJL, int VB, int NG>
 struct PairCopier {
-  using F = Fmt<KB, QJL, VB>;
+  using F = Fmt<KB, QJL, VB, NG>;
   int lo[F::perWave];   // per-lane byte offset of each copy, less the block term
   // lane offsets and units of this wave's copies (q = w + 8 j)
   __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
     for (int j = 0; j < F::perWave; ++j) {
-      const int q = w + kWaves * j;
+      const int q = w + F::waves * j;
       const bool isk = q < F::kChunks;
       const bool isv = !isk && q < F::kChunks + F::vChunks;
       int kgr = 64 * q + lane;   // granule of the pair's K region this lane fills
@@ -206,7 +209,7 @@ struct PairCopier {
                                        __amdgpu_buffer_rsrc_t rv, int b0, int w) const {
 #pragma unroll
     for (int j = 0; j < F::perWave; ++j) {
-      const int q = w + kWaves * j;   // unit, uniform over the wave
+      const int q = w + F::waves * j;   // unit, uniform over the wave
       const bool isk = q < F::kChunks;
       const bool isv = !isk && q < F::kChunks + F::vChunks;
       const int stride = isk ? F::kBytes : (isv ? F::vBytes : 0);   // uniform
@@ -312,9 +315,10 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int hq0
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int KB, bool QJL, int VB>
-__global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) {
-  using F = Fmt<KB, QJL, VB>;
+template <int KB, bool QJL, int VB, int NG>
+__global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) {
+  using F = Fmt<KB, QJL, VB, NG>;
+  constexpr int kWaves = F::waves;
   constexpr bool KQ8 = F::q8;
   constexpr int NTK = NTerms<KB>::n;
   constexpr int NTV = NTerms<VB>::n;
@@ -329,15 +333,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __shared__ float qr[4 * kD];              // q_raw = H D_K q per head (zero rows past G)
   __shared__ __attribute__((aligned(16))) uint8_t alimb[2][16 * 128];  // fp8 limbs [set][row = 4g + j][k]
   __shared__ uint8_t aexp[2][4][16];        // E8M0 scale [set][k / 32][row]
-  __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * 128];  // per group: limbs of p * radius [col][k]
-  __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];       // per group: [k / 32][col]
+  __shared__ __attribute__((aligned(16))) uint8_t plimb[NG][16 * 128];  // per group: limbs of p * radius [col][k]
+  __shared__ __attribute__((aligned(4))) uint8_t pexp[NG][4][16];       // per group: [k / 32][col]
   __shared__ float rwb[2][kWaves][4];       // per step parity: each wave's reference per head
   __shared__ float wred[kWaves][4];
   __shared__ float mrun[4];                 // running max per head at the end (log2 units)
   __shared__ float cconst[2][4];            // offsets of the affine key operand per (set, head)
   __shared__ __attribute__((aligned(8))) int8_t qdig[4][3][kD];   // q8 keys: base-128 digits of q per head
   __shared__ int qexp8[4];                  // q8 keys: leading exponent per head
-  __shared__ __attribute__((aligned(16))) float sred[8][4 * kM];   // partial sketch sums; later the group sums
+  __shared__ __attribute__((aligned(16))) float sred[kWaves][4 * kM];   // partial sketch sums; later the group sums
   __shared__ int s_last;
   uint8_t* const slots[4] = {slot0, slot1, slot2, slot3};
   // digit buffers of odd steps: the query's digit buffers, free once the
@@ -378,13 +382,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const float* qp = qb0 + min(w & 3, G - 1) * kD;
   const float qa = qp[lane], qb = qp[lane + 64];
   const float da = a.tb.dk[lane], db = a.tb.dk[lane + 64];
-  // lane l: raw query coordinate 16w + l % 16 of head l / 16 (zero past G)
-  const float qsl = qb0[min(lane >> 4, G - 1) * kD + 16 * w + (lane & 15)];
-  const int jq = threadIdx.x & 63;   // sketch rows 2jq, 2jq + 1; coordinates 16w .. 16w + 15
-  float2 st2[16];
+  // the sketch's inputs: this wave takes coordinates [kCpw w, kCpw (w + 1));
+  // lane l holds raw query coordinate kCpw w + 16 c + l % 16 of head l / 16
+  // (zero past G) and sketch rows 2 (l % 64), 2 (l % 64) + 1 of the table
+  constexpr int kCpw = kD / kWaves;
+  float qsl[kCpw / 16];
+#pragma unroll
+  for (int c = 0; c < kCpw / 16; ++c) qsl[c] = qb0[min(lane >> 4, G - 1) * kD + kCpw * w + 16 * c + (lane & 15)];
+  const int jq = threadIdx.x & 63;
+  float2 st2[kCpw];
   if (QJL) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.shd + (16 * w + u) * kM + 2 * jq);
+    for (int u = 0; u < kCpw; ++u) st2[u] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * w + u) * kM + 2 * jq);
   }
   float ak[NTK];
   {
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
   const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
-  const int n_iter = max(0, (blk1 - blk0 + 1) / 2);   // steps of two blocks
+  const int n_iter = max(0, (blk1 - blk0 + NG - 1) / NG);   // steps of NG blocks
   const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const float inv_sqrt_d = 0.08838834764831845f;
 
@@ -420,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
     // the first NS - 1 pairs (at most three) are issued one per set-up phase
     // (pair 0 here), so that the copies proceed while the waves compute
-    PairCopier<KB, QJL, VB> cp;
+    PairCopier<KB, QJL, VB, NG> cp;
     cp.init(w, lane);
     cp.copy(slots[0], junk, rk, rv, blk0, w);
 
@@ -496,12 +505,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
       float acc[4][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
-      const float qsv = ((lane >> 4) < G) ? qsl : 0.0f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < kCpw; ++u) {
+        const float qsv = ((lane >> 4) < G) ? qsl[u >> 4] : 0.0f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int x = __builtin_amdgcn_readlane(__float_as_int(qsv), 16 * g + u);
+          const int x = __builtin_amdgcn_readlane(__float_as_int(qsv), 16 * g + (u & 15));
           acc[g][0] = fmaf(st2[u].x, __int_as_float(x), acc[g][0]);
           acc[g][1] = fmaf(st2[u].y, __int_as_float(x), acc[g][1]);
         }
@@ -509,23 +518,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
       for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g * kM + 2 * jq]) = make_float2(acc[g][0], acc[g][1]);
       lds_barrier();
-      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + 2, w);
-      if (w >= 4) {
-        // sketch rows pos_of_slot(2 lane), pos_of_slot(2 lane + 1) of head w - 4
-        const int g = w - 4;
+      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + NG, w);
+      if (w >= kWaves - 4) {
+        // sketch rows pos_of_slot(2 lane), pos_of_slot(2 lane + 1) of head g
+        const int g = w - (kWaves - 4);
         const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
         float u0 = 0.0f, u1 = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < kWaves; ++c) {
           u0 += sred[c][g * kM + r0];
           u1 += sred[c][g * kM + r1];
         }
         write_digits(1, g, u0, u1);
       }
     } else {
-      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + 2, w);
+      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + NG, w);
     }
-    if constexpr (NS > 3) cp.copy(slots[2], junk, rk, rv, blk0 + 4, w);
+    if constexpr (NS > 3) cp.copy(slots[2], junk, rk, rv, blk0 + 2 * NG, w);
     // the first pair has landed (this wave's copies; the barrier covers the others')
     wait_vm<(NS - 2) * F::perWave>();
     lds_barrier();
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     // reference, the probability digits.  Carried to part B: the reference and
     // the sum of this lane's two probabilities.
     auto partA = [&](const uint8_t* cur, int i, float& rw_out, float& ps_out) __attribute__((always_inline)) {
-      const int blk = blk0 + 2 * i + gr;
+      const int blk = blk0 + NG * i + gr;
       const int n_t = (blk < blk1) ? min(kBlock, len - blk * kBlock) : 0;
       const uint8_t* kb = cur + gr * F::kBytes;
       const uint8_t* vb = cur + F::kChunks * 1024 + gr * F::vBytes;
@@ -761,7 +770,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
     auto sync = [&](uint8_t* refill, int i) __attribute__((always_inline)) {
       if constexpr (NS >= 3) wait_vm<(NS - 3) * F::perWave>();
       lds_barrier();
-      cp.copy(refill, junk, rk, rv, blk0 + 2 * (i + NS - 1), w);
+      cp.copy(refill, junk, rk, rv, blk0 + NG * (i + NS - 1), w);
     };
     // step i: A(i), barrier and refill, B(i); with two slots a second barrier
     // after waiting for the pair of step i + 1
@@ -822,8 +831,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a) 
   __syncthreads();
   if (w < G) {
     // wave w: head w, o = D_V H (sum of both groups) / d
-    float lo = obuf[0][w][lane] + obuf[1][w][lane];
-    float hi = obuf[0][w][lane + 64] + obuf[1][w][lane + 64];
+    float lo = obuf[0][w][lane], hi = obuf[0][w][lane + 64];
+    if constexpr (NG == 2) {
+      lo += obuf[1][w][lane];
+      hi += obuf[1][w][lane + 64];
+    }
     wave_fwht128(lo, hi, lane);
     const float inv_d = 1.0f / static_cast<float>(kD);
     lo *= a.tb.dv[lane] * inv_d;
@@ -847,7 +859,8 @@ template <int KB, bool QJL, int VB>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * ((a.group + 3) / 4));
-  hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB>), grid, dim3(kThreads), 0, stream, a);
+  constexpr int NG = (KB == 8) ? 1 : 2;   // as decode_mfma_groups
+  hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -862,6 +875,10 @@ hipError_t launch_v(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// q8 keys (large slots, three head groups per KV head at G = 12) run best as
+// two workgroups of one group per compute unit; the others as one of two.
+int decode_mfma_groups(int k_codec) { return k_codec == Q8_BLOCK32 ? 1 : 2; }
 
 bool decode_mfma_applies(int k_codec, int v_codec, int group) {
   return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL || k_codec == Q8_BLOCK32);

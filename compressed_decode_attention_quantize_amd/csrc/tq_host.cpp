@@ -328,7 +328,9 @@ bool mfma_path(const tq_config* c) {
   return tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
 }
 
-int64_t target_workgroups(const tq_config* c) { return mfma_path(c) ? tq::kMfmaWorkgroups : tq::kValuWorkgroups; }
+int64_t target_workgroups(const tq_config* c) {
+  return mfma_path(c) ? tq::kMfmaUnitWorkgroups / tq::decode_mfma_groups(c->k_codec) : tq::kValuWorkgroups;
+}
 
 // Independent (sequence, KV head, head group) units the splits multiply: the
 // matrix-core kernel serves up to four query heads per workgroup.

@@ -118,10 +118,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // returns hipErrorNotSupported for other configurations.
 bool decode_mfma_applies(int k_codec, int v_codec, int group);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-// Workgroups the automatic split count aims for: the matrix-core kernel runs
-// one 512-thread workgroup per compute unit (256 on the target chip), the
-// VALU kernel about two 256-thread workgroups per compute unit.
-constexpr int kMfmaWorkgroups = 256;
+// Block groups (of four wavefronts) per workgroup of the matrix-core decode
+// kernel for a key codec: with one group two independent workgroups share a
+// compute unit, with two groups one workgroup of eight wavefronts fills it.
+int decode_mfma_groups(int k_codec);
+// Workgroups the automatic split count aims for: the matrix-core kernel fills
+// the 256 compute units of the target chip (512 / groups workgroups), the
+// VALU kernel runs about two 256-thread workgroups per compute unit.
+constexpr int kMfmaUnitWorkgroups = 512;
 constexpr int kValuWorkgroups = 512;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 
