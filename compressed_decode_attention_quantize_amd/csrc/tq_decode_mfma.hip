@@ -1,5 +1,6 @@
 // tq_decode_mfma.hip -- decode attention on the gfx950 matrix cores, for
-// POLAR / POLAR_QJL keys and POLAR values with up to 4 query heads per KV head.
+// POLAR, POLAR_QJL or q8 keys and POLAR values, with up to 16 query heads per
+// KV head served in head groups of four.
 //
 // Same result as the VALU kernel (logits with the QJL-corrected estimator,
 // softmax, rotated-frame weighted sum of values; wis-web.com reader,
@@ -38,18 +39,19 @@
 // the per-position key fields and value radii at slot_of(position), which makes
 // each lane's operands whole 8-byte loads.
 //
-// Mapping: grid (split, KV head, sequence); a workgroup is eight waves in two
-// groups of four, one per compute unit.  Each step takes two 128-position
-// blocks, one per group, from a ring of shared-memory slots that direct
-// memory-to-shared-memory copies fill several steps ahead.  Within a group,
-// wave w computes the logits of its block's positions in k-slots [32w, 32w+32)
-// (2 MFMA column groups), the eight waves share each step's maximum, each
-// group writes the digits of p * radius, and wave w then computes its group's
-// weighted sum for coordinates [32w, 32w+32).  The query set-up (rotation,
-// sketch, digits) is done once per workgroup while the first copies are in
-// flight.  The two groups' sums are added in shared memory and rotated back
-// (D_V H / d) before they leave the workgroup, so the workgroup that merges the
-// splits only forms a weighted average.
+// Mapping: grid (split, KV head, sequence, head group); a workgroup is NG
+// groups of four waves (NG = 2: one workgroup per compute unit; NG = 1: two).
+// Each step takes NG 128-position blocks, one per group, from a ring of
+// shared-memory slots that direct memory-to-shared-memory copies fill several
+// steps ahead.  Within a group, wave w computes the logits of its block's
+// positions in k-slots [32w, 32w+32) (2 MFMA column groups) and the digits of
+// p * radius for them; after the step's one barrier the waves agree on the
+// running reference and wave w computes its group's weighted sum for
+// coordinates [32w, 32w+32).  The query set-up (rotation, sketch, digits) is
+// done once per workgroup while the first copies are in flight.  The groups'
+// sums are added in shared memory and rotated back (D_V H / d) before they
+// leave the workgroup, so the workgroup that merges the splits only forms a
+// weighted average.
 
 #include <hip/hip_fp16.h>
 
@@ -142,7 +144,7 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i& a, const v8i& b, const v4
 }
 
 // Byte layout of one cache block (128 positions) and of the shared-memory
-// ring that stages two blocks per step.
+// ring that stages NG blocks per step.
 // NG block groups (four wavefronts each) per workgroup: with one group two
 // workgroups share a compute unit and each may take half of its shared memory.
 template <int KB, bool QJL, int VB, int NG>
@@ -191,7 +193,7 @@ struct PairCopier {
       const int q = w + F::waves * j;
       const bool isk = q < F::kChunks;
       const bool isv = !isk && q < F::kChunks + F::vChunks;
-      int kgr = 64 * q + lane;   // granule of the pair's K region this lane fills
+      int kgr = 64 * q + lane;   // granule of the step's K region this lane fills
       if constexpr (F::q8) {
         const int half = (kgr >= F::kBytes / 16) ? 1 : 0;
         const int g = kgr - half * (F::kBytes / 16);
@@ -200,7 +202,7 @@ struct PairCopier {
       lo[j] = isk ? 16 * kgr : (isv ? 1024 * (q - F::kChunks) + 16 * lane : 0x7fff0000 + 16 * lane);
     }
   }
-  // Copies the two blocks b0, b0 + 1 (K region then V region) into a ring
+  // Copies the NG blocks from b0 (K region then V region) into a ring
   // slot straight from memory into shared memory, 1 KB per instruction (lane
   // l moves bytes 16l..16l+15 of its unit).  Every wave issues the same number
   // of copies; units past the data read zero into a junk buffer, so the count
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
   constexpr int NTK = NTerms<KB>::n;
   constexpr int NTV = NTerms<VB>::n;
   constexpr int NS = F::nSlots;
-  // ring of block pairs: one array per slot, so that the compiler can tell
+  // ring of step blocks: one array per slot, so that the compiler can tell
   // the slots' copies apart when it places its waits
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[F::slotBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[F::slotBytes];
@@ -427,8 +429,8 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
     __builtin_amdgcn_sched_barrier(0);
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, blk1);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
-    // the first NS - 1 pairs (at most three) are issued one per set-up phase
-    // (pair 0 here), so that the copies proceed while the waves compute
+    // the blocks of the first NS - 1 steps (at most three) are issued one per set-up phase
+    // (step 0's here), so that the copies proceed while the waves compute
     PairCopier<KB, QJL, VB, NG> cp;
     cp.init(w, lane);
     cp.copy(slots[0], junk, rk, rv, blk0, w);
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
       if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + NG, w);
     }
     if constexpr (NS > 3) cp.copy(slots[2], junk, rk, rv, blk0 + 2 * NG, w);
-    // the first pair has landed (this wave's copies; the barrier covers the others')
+    // the first step's blocks have landed (this wave's copies; the barrier covers the others')
     wait_vm<(NS - 2) * F::perWave>();
     lds_barrier();
     v8i Aq, Asq;
@@ -576,10 +578,10 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
     // Step i processes blocks blk0 + 2i (group 0) and blk0 + 2i + 1 (group 1)
     // from ring slot i % NS, with one barrier, between the probability digits
     // and the weighted sum.  After it (every wave has then finished step
-    // i - 1) the step refills slot (i - 1) % NS with the pair of step
-    // i + NS - 1; before it each wave waits for its copies of the pair of step
+    // i - 1) the step refills slot (i - 1) % NS with the blocks of step
+    // i + NS - 1; before it each wave waits for its copies of the blocks of step
     // i + 1 (issued in step i - 1), which the next step reads right after this
-    // one's weighted sum.  With two slots the pair of step i + 1 is only
+    // one's weighted sum.  With two slots the blocks of step i + 1 is only
     // issued in step i, and a second barrier ends the step.
     // Part A of step i: logits of the group's key block, this wave's
     // reference, the probability digits.  Carried to part B: the reference and
@@ -763,17 +765,17 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
     };
 
     // The barrier between part A of step i and part B: with three or more
-    // slots the pair of step i + 1 was issued a step ago, and this wave's
-    // copies of it must have landed (everyone's, after the barrier).  Every
-    // wave is then past part B of step i - 1: refill that slot with the pair of
-    // step i + NS - 1.
+    // slots the blocks of step i + 1 were issued a step ago, and this wave's
+    // copies of them must have landed (everyone's, after the barrier).  Every
+    // wave is then past part B of step i - 1: refill that slot with the
+    // blocks of step i + NS - 1.
     auto sync = [&](uint8_t* refill, int i) __attribute__((always_inline)) {
       if constexpr (NS >= 3) wait_vm<(NS - 3) * F::perWave>();
       lds_barrier();
       cp.copy(refill, junk, rk, rv, blk0 + NG * (i + NS - 1), w);
     };
     // step i: A(i), barrier and refill, B(i); with two slots a second barrier
-    // after waiting for the pair of step i + 1
+    // after waiting for the blocks of step i + 1
     auto step = [&](uint8_t* cur, uint8_t* refill, int i) __attribute__((always_inline)) {
       float rw, ps;
       partA(cur, i, rw, ps);
