@@ -424,16 +424,20 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (n_iter > 0) {   // uniform over the workgroup
+  {
+    // The query set-up and the ring's first copies do not wait for the
+    // sequence length: the first copies range over the whole cache of this
+    // (sequence, KV head) (blocks past the sequence are read but never
+    // weighted), the loop's copies only over [0, blk1).
     float aksum = 0.0f;
     __builtin_amdgcn_sched_barrier(0);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, blk1);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
+    const __amdgpu_buffer_rsrc_t rk0 = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, a.n_blocks);
+    const __amdgpu_buffer_rsrc_t rv0 = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, a.n_blocks);
     // the blocks of the first NS - 1 steps (at most three) are issued one per set-up phase
     // (step 0's here), so that the copies proceed while the waves compute
     PairCopier<KB, QJL, VB, NG> cp;
     cp.init(w, lane);
-    cp.copy(slots[0], junk, rk, rv, blk0, w);
+    cp.copy(slots[0], junk, rk0, rv0, blk0, w);
 
     // ------------------------------------------------------------- set-up
     // Waves 0..3 rotate the query of head w in registers (q_raw = H D_K q)
@@ -500,8 +504,9 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
       wave_fwht128(q_lo, q_hi, lane);
       qr[w * kD + lane] = q_lo;
       qr[w * kD + lane + 64] = q_hi;
-      // the same wave reads back its own rotated query in k-slot order
-      write_digits(0, w, qr[w * kD + pos_of_slot(2 * lane)], qr[w * kD + pos_of_slot(2 * lane + 1)]);
+      // the same wave reads back its own rotated query in k-slot order (with a
+      // sketch, after the barrier, beside the waves that write its digits)
+      if constexpr (!QJL) write_digits(0, w, qr[w * kD + pos_of_slot(2 * lane)], qr[w * kD + pos_of_slot(2 * lane + 1)]);
     }
     if (QJL) {
       float acc[4][2];
@@ -520,7 +525,8 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
       for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g * kM + 2 * jq]) = make_float2(acc[g][0], acc[g][1]);
       lds_barrier();
-      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + NG, w);
+      if constexpr (NS > 2) cp.copy(slots[1], junk, rk0, rv0, blk0 + NG, w);
+      if (w < 4) write_digits(0, w, qr[w * kD + pos_of_slot(2 * lane)], qr[w * kD + pos_of_slot(2 * lane + 1)]);
       if (w >= kWaves - 4) {
         // sketch rows pos_of_slot(2 lane), pos_of_slot(2 lane + 1) of head g
         const int g = w - (kWaves - 4);
@@ -534,9 +540,9 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
         write_digits(1, g, u0, u1);
       }
     } else {
-      if constexpr (NS > 2) cp.copy(slots[1], junk, rk, rv, blk0 + NG, w);
+      if constexpr (NS > 2) cp.copy(slots[1], junk, rk0, rv0, blk0 + NG, w);
     }
-    if constexpr (NS > 3) cp.copy(slots[2], junk, rk, rv, blk0 + 2 * NG, w);
+    if constexpr (NS > 3) cp.copy(slots[2], junk, rk0, rv0, blk0 + 2 * NG, w);
     // the first step's blocks have landed (this wave's copies; the barrier covers the others')
     wait_vm<(NS - 2) * F::perWave>();
     lds_barrier();
@@ -573,6 +579,9 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
     const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
     const int so = 4 * (g4 * kBlock + 32 * wl + 2 * t);   // this lane's key words in a block
     const int sn = 2 * (32 * wl + 2 * t);                 // its two fp16 per-position fields
+    // the loop's copies: blocks past the split's sequence read zero
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.kc + slot0_idx * a.k_block_bytes, a.k_block_bytes, blk1);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.vc + slot0_idx * a.v_block_bytes, a.v_block_bytes, blk1);
 
     // --------------------------------------------------------- main loop
     // Step i processes blocks blk0 + 2i (group 0) and blk0 + 2i + 1 (group 1)
@@ -788,6 +797,7 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
     };
     // whole rounds of the ring, then the last partial round; slot indices are
     // compile-time constants in every step
+    if (n_iter > 0) {   // uniform over the workgroup
     int i0 = 0;
     for (; i0 + NS <= n_iter; i0 += NS) {
 #pragma unroll
@@ -803,6 +813,7 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
         }
       }
     }
+    }   // n_iter > 0
   }
 
   // ------------------------------------------------------------- partials
