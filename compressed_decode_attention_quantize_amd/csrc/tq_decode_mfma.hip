@@ -403,7 +403,10 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
 #pragma unroll
     for (int T = 0; T < NTK; ++T) ak[T] = akp[T];
   }
-  const int len = min(a.seq_lens[b], a.max_ctx);
+  // a scalar load: a vector load here would make the first wait for it also
+  // wait for every query and table load issued before it
+  typedef __attribute__((address_space(4))) const int cint;
+  const int len = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
   const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
