@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit (no GPU)")
     ap.add_argument("--calibration-mib", type=int, default=256)
+    ap.add_argument("--policy", default="", metavar="K/V/PROTECT",
+                    help="per-layer cache types, e.g. turbo3/turbo2/2: keys turbo3, values turbo2, the first "
+                         "and last 2 layers in q8_0 (a mixed-codec stack instead of the workload's codecs)")
     args = ap.parse_args()
     if args.summarize_counters:
         res = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.calibration_mib)
@@ -192,7 +195,15 @@ def main():
     # ------------------------------------------------ inputs and layer caches
     k, v = synth.make_kv(w, w.ctx, seed=data_seed, device=dev)
     q = synth.make_q(w, seed=data_seed + 1000, device=dev)
-    layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l), dev, zero=False) for l in range(n_layers)]
+    policy = None
+    if args.policy:
+        from compressed_decode_attention_quantize_amd import presets
+        kt, vt, prot = (args.policy.split("/") + ["0"])[:3]
+        policy = presets.layer_policy(n_layers, kt, vt, int(prot))
+        layers = [tq.KVLayer(presets.config(tq.config_for(w, seed=42, layer=l), policy[l], l), dev, zero=False)
+                  for l in range(n_layers)]
+    else:
+        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l), dev, zero=False) for l in range(n_layers)]
     torch.cuda.synchronize()
 
     # ------------------------------------------ append: prefill of every layer
@@ -212,6 +223,9 @@ def main():
     lens = [w.ctx] * w.batch
     cfg0 = layers[0].cfg
     bytes_per_launch, krec, vrec = algorithmic_decode_bytes(w, cfg0, tq, lens)
+    if policy is not None:   # mean over the stack's layers
+        per_layer = [algorithmic_decode_bytes(w, L.cfg, tq, lens)[0] for L in layers]
+        bytes_per_launch = sum(per_layer) // n_layers
     outs = [torch.empty_like(q) for _ in layers]
 
     def step(events=None):
@@ -270,7 +284,19 @@ def main():
         "wall_s_timed": round(wall, 4),
         "device": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline:
+    if policy is not None:
+        packed = sum(sum(tq.cache_bytes(L.cfg)) for L in layers)
+        fp16 = n_layers * w.batch * ((w.ctx + 127) // 128) * 128 * w.n_kv * 2 * w.d * 2
+        result["metric"] = "decode attention HBM GB/s over a mixed-codec layer stack"
+        result["config"]["policy"] = {"spec": args.policy, "layers": [f"{c.k_type}/{c.v_type}" for c in policy]}
+        result["config"]["k_codec"] = result["config"]["v_codec"] = "per layer"
+        result["config"].pop("record_bytes")
+        result["cache_bytes_total"] = packed
+        result["compression_vs_fp16"] = round(fp16 / packed, 3)
+        result["roofline"]["traffic"] = None
+        result.pop("append_tokens_per_s")
+        result.pop("append_ms_per_layer")
+    if not args.no_cpu_baseline and policy is None:
         result["cpu_baseline"] = cpu_baseline(w, data_seed)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)

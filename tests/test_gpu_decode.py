@@ -19,6 +19,8 @@ CODECS = {   # name -> (k_codec, k_bits, v_codec, v_bits)
     "qjl3_v2": (tq.POLAR_QJL, 3, tq.POLAR, 2),
     "qjl4_v4": (tq.POLAR_QJL, 4, tq.POLAR, 4),
     "q8_v2": (tq.Q8_BLOCK32, 8, tq.POLAR, 2),
+    "q8_v4": (tq.Q8_BLOCK32, 8, tq.POLAR, 4),
+    "qjl2_v3": (tq.POLAR_QJL, 2, tq.POLAR, 3),
     "polar2_v2": (tq.POLAR, 2, tq.POLAR, 2),
     "polar4_raw": (tq.POLAR, 4, tq.RAW_F32, 32),
     "raw_polar3": (tq.RAW_F32, 32, tq.POLAR, 3),
