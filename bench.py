@@ -167,6 +167,12 @@ def main():
     ap.add_argument("--policy", default="", metavar="K/V/PROTECT",
                     help="per-layer cache types, e.g. turbo3/turbo2/2: keys turbo3, values turbo2, the first "
                          "and last 2 layers in q8_0 (a mixed-codec stack instead of the workload's codecs)")
+    ap.add_argument("--sparse-v", type=int, default=0, metavar="T",
+                    help="decode skips the value work of blocks whose weights are all below 2^(1-T) of the "
+                         "running maximum (0 = dense)")
+    ap.add_argument("--focus-every", type=int, default=0, metavar="E",
+                    help="peaked attention: one planted key per E positions that the query heads score "
+                         "about 16 nats above the rest (0 = the workload's plain keys)")
     args = ap.parse_args()
     if args.summarize_counters:
         res = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.calibration_mib)
@@ -195,15 +201,19 @@ def main():
     # ------------------------------------------------ inputs and layer caches
     k, v = synth.make_kv(w, w.ctx, seed=data_seed, device=dev)
     q = synth.make_q(w, seed=data_seed + 1000, device=dev)
+    if args.focus_every:
+        k, _ = synth.plant_focus_keys(w, k, q, seed=data_seed + 2000, every=args.focus_every)
     policy = None
     if args.policy:
         from compressed_decode_attention_quantize_amd import presets
         kt, vt, prot = (args.policy.split("/") + ["0"])[:3]
         policy = presets.layer_policy(n_layers, kt, vt, int(prot))
-        layers = [tq.KVLayer(presets.config(tq.config_for(w, seed=42, layer=l), policy[l], l), dev, zero=False)
+        layers = [tq.KVLayer(presets.config(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v),
+                                            policy[l], l), dev, zero=False)
                   for l in range(n_layers)]
     else:
-        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l), dev, zero=False) for l in range(n_layers)]
+        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v), dev, zero=False)
+                  for l in range(n_layers)]
     torch.cuda.synchronize()
 
     # ------------------------------------------ append: prefill of every layer
@@ -296,7 +306,11 @@ def main():
         result["roofline"]["traffic"] = None
         result.pop("append_tokens_per_s")
         result.pop("append_ms_per_layer")
-    if not args.no_cpu_baseline and policy is None:
+    if args.sparse_v or args.focus_every:
+        result["config"]["sparse_v"] = args.sparse_v
+        result["config"]["focus_every"] = args.focus_every
+        result["data"] = "synthetic, planted focus keys" if args.focus_every else "synthetic"
+    if not args.no_cpu_baseline and policy is None and not (args.sparse_v or args.focus_every):
         result["cpu_baseline"] = cpu_baseline(w, data_seed)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)

@@ -420,6 +420,11 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
   // running max (log2 units) of head g4 (this lane's logits row) and of head
   // t / 4 (this lane's result column); both follow the same step maxima
   float m_a = -INFINITY, m_b = -INFINITY;
+  // Sparse-V: the largest step reference of head t / 4 so far (not lazy), and
+  // the skip distance in log2 units
+  float m_top = -INFINITY;
+  const bool sparse_v = a.sparse_v > 0;
+  const float tau_v = static_cast<float>(a.sparse_v);
   float lsum = 0.0f;   // this lane's share of the denominator of head g4
   v4f accV[2][NTV];
 #pragma unroll
@@ -753,6 +758,17 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
           for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
+      }
+      // Sparse-V: a group block whose four wave references lie more than
+      // tau_v below the running maximum for every head it serves holds only
+      // weights below 2^-tau_v of the largest one (both sides are integer
+      // ceilings); its value work is skipped, its weights stay in lsum
+      if (sparse_v) {
+        m_top = fmaxf(m_top, rb);
+        float rblk = rwb[par][4 * gr][hb];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) rblk = fmaxf(rblk, rwb[par][4 * gr + u][hb]);
+        if (__all((rblk == -INFINITY) || (rblk < m_top - tau_v))) return;
       }
       v8i Pv;
       {

@@ -39,7 +39,7 @@ bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
 tq_status check_cfg(const tq_config* c) {
   if (c == nullptr) return TQ_EINVAL;
-  if (c->abi_version != TQ_ABI_VERSION || c->reserved != 0) return TQ_EINVAL;
+  if (c->abi_version != TQ_ABI_VERSION || c->sparse_v < 0 || c->sparse_v > 60) return TQ_EINVAL;
   if (!is_pow2(c->head_dim) || c->head_dim < 16 || c->head_dim > 256) return TQ_EINVAL;
   if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads != 0) return TQ_EINVAL;
   if (c->batch < 1 || c->max_ctx < 1) return TQ_EINVAL;
@@ -513,6 +513,7 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
   a.k_bits = cfg->k_bits;
   a.v_codec = cfg->v_codec;
   a.v_bits = cfg->v_bits;
+  a.sparse_v = cfg->sparse_v;
   a.k_block_bytes = kBlock * k_record_bytes(cfg);
   a.v_block_bytes = kBlock * v_record_bytes(cfg);
   hipError_t e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));

@@ -97,6 +97,7 @@ struct DecodeArgs {
   int32_t batch, n_q, n_kv, group, max_ctx, n_blocks;
   int32_t chunk_blocks, n_splits;
   int32_t k_codec, k_bits, v_codec, v_bits;
+  int32_t sparse_v;   // 0, or skip value work of blocks below 2^-sparse_v of the running maximum
   int64_t k_block_bytes, v_block_bytes;
 };
 

@@ -77,7 +77,7 @@ def config(base: tq.Config, codecs: LayerCodecs, layer: int) -> tq.Config:
     rotation and sketch are per layer)."""
     return tq.make_config(base.head_dim, base.n_q_heads, base.n_kv_heads, base.batch, base.max_ctx,
                           codecs.k_codec, codecs.k_bits, base.qjl_m or 128, codecs.v_codec, codecs.v_bits,
-                          base.decode_chunk, base.seed, layer)
+                          base.decode_chunk, base.seed, layer, base.sparse_v)
 
 
 def record_bits(codecs: LayerCodecs, d: int = 128, m: int = 128):

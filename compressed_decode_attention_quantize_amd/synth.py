@@ -135,6 +135,31 @@ def make_q(w: Workload, seed: int, device="cpu", batch: int | None = None):
     return q.to(_tdtype(w)).to(torch.float32)
 
 
+def plant_focus_keys(w: Workload, k: torch.Tensor, q: torch.Tensor, seed: int, every: int = 1024,
+                     logit: float = 16.0, n_tokens: int | None = None) -> torch.Tensor:
+    """Peaked attention for the decode query q: in every window of `every`
+    positions one seeded position per (sequence, KV head) gets the key
+    logit * sqrt(d) * qbar / |qbar|^2, qbar the mean query of the head's
+    group, so that the group's heads score it near `logit` (natural units)
+    while the other keys keep their N(0, 1)-scale scores.  Returns a copy of
+    k (same dtype, [batch][n][n_kv][d]) and the planted positions
+    [batch][n_kv][n_windows]."""
+    B, n, n_kv, d = k.shape
+    n = n if n_tokens is None else n_tokens
+    g = _gen(k.device, seed)
+    qbar = q.to(torch.float32).view(B, n_kv, w.group, d).mean(2)                  # B, n_kv, d
+    key = (logit * d ** 0.5) * qbar / (qbar * qbar).sum(-1, keepdim=True)
+    n_win = (n + every - 1) // every
+    off = torch.randint(0, every, (B, n_kv, n_win), generator=g, device=k.device)
+    pos = torch.arange(n_win, device=k.device).view(1, 1, -1) * every + off
+    pos = torch.minimum(pos, torch.full_like(pos, n - 1))
+    out = k.clone()
+    bi = torch.arange(B, device=k.device).view(B, 1, 1).expand_as(pos)
+    hi = torch.arange(n_kv, device=k.device).view(1, n_kv, 1).expand_as(pos)
+    out[bi, pos, hi] = key.view(B, n_kv, 1, d).expand(B, n_kv, n_win, d).to(k.dtype)
+    return out, pos
+
+
 def widen(x: torch.Tensor) -> torch.Tensor:
     """Exact widening of f32 / bf16 / f16 inputs to fp32."""
     return x.to(torch.float32)

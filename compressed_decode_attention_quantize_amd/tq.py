@@ -40,7 +40,7 @@ class Config(ctypes.Structure):
                 ("k_codec", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("qjl_m", ctypes.c_int32),
                 ("v_codec", ctypes.c_int32), ("v_bits", ctypes.c_int32),
                 ("decode_chunk", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("layer", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("layer", ctypes.c_int32), ("sparse_v", ctypes.c_int32)]
 
 
 _lib = None
@@ -101,7 +101,7 @@ def _stream(stream=None):
 
 def make_config(head_dim=128, n_q_heads=8, n_kv_heads=2, batch=1, max_ctx=1024, k_codec=POLAR_QJL,
                 k_bits=3, qjl_m=128, v_codec=POLAR, v_bits=3, decode_chunk=0, seed=42,
-                layer=0) -> Config:
+                layer=0, sparse_v=0) -> Config:
     if k_codec != POLAR_QJL:
         qjl_m = 0
     if k_codec == RAW_F32:
@@ -111,14 +111,14 @@ def make_config(head_dim=128, n_q_heads=8, n_kv_heads=2, batch=1, max_ctx=1024, 
     if v_codec == RAW_F32:
         v_bits = 32
     return Config(ABI_VERSION, head_dim, n_q_heads, n_kv_heads, batch, max_ctx, k_codec, k_bits,
-                  qjl_m, v_codec, v_bits, decode_chunk, seed, layer, 0)
+                  qjl_m, v_codec, v_bits, decode_chunk, seed, layer, sparse_v)
 
 
 def config_for(w: "synth.Workload", seed=42, layer=0, max_ctx=None, batch=None,
-               decode_chunk=0) -> Config:
+               decode_chunk=0, sparse_v=0) -> Config:
     return make_config(w.d, w.n_q, w.n_kv, w.batch if batch is None else batch,
                        w.ctx if max_ctx is None else max_ctx, CODEC_IDS[w.k_codec], w.k_bits, w.m,
-                       CODEC_IDS[w.v_codec], w.v_bits, decode_chunk, seed, layer)
+                       CODEC_IDS[w.v_codec], w.v_bits, decode_chunk, seed, layer, sparse_v)
 
 
 # --------------------------------------------------------------- ABI calls

@@ -83,7 +83,19 @@ typedef struct tq_config {
   int32_t decode_chunk;   /* positions per split-K workgroup, a multiple of 128; 0 = automatic */
   uint64_t seed;          /* rotation signs and sketch are drawn from (seed, layer) */
   int32_t layer;
-  int32_t reserved;       /* must be 0 */
+  int32_t sparse_v;       /* decode: 0 = dense; t in 1..60 = Sparse-V (the
+                           * wis-web.com reader article on the llama.cpp fork,
+                           * its third finding): a 128-position block skips
+                           * its value work when, for every query head it
+                           * serves, the ceiling of its largest log2-logit is
+                           * more than t below the ceiling of the running
+                           * maximum of its split; every weight it leaves out
+                           * is then below 2^-t of the largest weight.  Its
+                           * weights still count in the softmax denominator.
+                           * Which blocks are skipped depends on the split
+                           * schedule.  Honoured by the matrix-core path
+                           * (POLAR, POLAR_QJL or Q8 keys with POLAR values,
+                           * G <= 16); other codecs decode densely. */
 } tq_config;
 
 /* Text for a status code (static storage). */

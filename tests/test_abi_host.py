@@ -102,7 +102,7 @@ def _cfg(tq, **kw):
     ("n_q_heads", 7, 1), ("n_kv_heads", 0, 1), ("batch", 0, 1), ("max_ctx", 0, 1),
     ("k_bits", 9, 1), ("k_bits", 5, 2), ("qjl_m", 96, 1), ("qjl_m", 64, 2), ("v_codec", 2, 2),
     ("v_codec", 3, 2), ("v_codec", 9, 1), ("k_codec", 7, 1), ("decode_chunk", 100, 1),
-    ("reserved", 1, 1), ("v_bits", 5, 2),
+    ("sparse_v", -1, 1), ("sparse_v", 61, 1), ("v_bits", 5, 2),
 ])
 def test_config_validation(tq, field, value, status):
     cfg = _cfg(tq)
