@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tq_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
-RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32 = 0, 1, 2, 3
+RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32, POLAR_TREE = 0, 1, 2, 3, 4
 BLOCK = 128
 
 _u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
@@ -56,6 +56,12 @@ class _KRec(ctypes.Structure):
 
 class _VRec(ctypes.Structure):
     _fields_ = [("codes", _vp), ("n16", _vp), ("raw", _vp)]
+
+
+class TreeTab(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("b", ctypes.c_int), ("levels", ctypes.c_int),
+                ("bits", ctypes.c_int * 13), ("cent", (ctypes.c_double * 256) * 13),
+                ("bnd", (ctypes.c_double * 255) * 13)]
 
 
 _lib = None
@@ -115,6 +121,21 @@ def lib() -> ctypes.CDLL:
     L.or_decode_pairs.argtypes = [ctypes.POINTER(Spec), _f32p, _f32p, _u16p, _u16p, _vp,
                                   ctypes.POINTER(_KRec), ctypes.POINTER(_VRec), _i32p, _f32p,
                                   ctypes.c_int, _i32p, _f64p, _vp]
+    for fn in ("or_angle_mass", "or_angle_moment1"):
+        getattr(L, fn).restype = ctypes.c_double
+        getattr(L, fn).argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+    L.or_angle_codebook.restype = ctypes.c_int
+    L.or_angle_codebook.argtypes = [ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.POINTER(ctypes.c_double)]
+    L.or_tree_angles.restype = ctypes.c_double
+    L.or_tree_angles.argtypes = [_f64p, ctypes.c_int, _f64p]
+    L.or_tree_from_angles.argtypes = [_f64p, ctypes.c_double, ctypes.c_int, _f64p]
+    L.or_tree_tables.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(TreeTab)]
+    L.or_quantize_tree.argtypes = [_f32p, ctypes.c_int, _f32p, ctypes.POINTER(TreeTab), _u8p,
+                                   ctypes.POINTER(ctypes.c_uint16), _vp]
+    L.or_dequant_tree.argtypes = [ctypes.c_int, _f32p, ctypes.POINTER(TreeTab), _u8p, ctypes.c_uint16, _f64p]
+    L.or_tree_table.restype = ctypes.POINTER(TreeTab)
+    L.or_tree_table.argtypes = [ctypes.c_int]
+    L.or_tree_prepare()   # tables of the whole-cache helpers, before any threaded use
     _lib = L
     return L
 
@@ -263,6 +284,76 @@ def dequant_q8(k8, s16) -> np.ndarray:
     return out
 
 
+# ------------------------------------------------- recursive polar ----
+
+def angle_codebook(level: int, bits: int):
+    """(centroids, boundaries, mse, Lloyd rounds) of the level's angle law."""
+    n = 1 << bits
+    c = np.zeros(n, np.float64)
+    bnd = np.zeros(max(n - 1, 1), np.float64)
+    mse = ctypes.c_double()
+    it = lib().or_angle_codebook(level, bits, c, bnd, ctypes.byref(mse))
+    if it < 0:
+        raise ValueError("bad angle codebook arguments")
+    return c, bnd[:n - 1], mse.value, it
+
+
+def angle_mass(level, a, c):
+    return lib().or_angle_mass(level, a, c)
+
+
+def angle_moment1(level, a, c):
+    return lib().or_angle_moment1(level, a, c)
+
+
+def tree_angles(y):
+    """(angles in heap slots [d] (slot 0 unused), radius) of a vector."""
+    y = np.ascontiguousarray(y, np.float64)
+    ang = np.zeros(y.size, np.float64)
+    r = lib().or_tree_angles(y, y.size, ang)
+    return ang, r
+
+
+def tree_from_angles(ang, r):
+    ang = np.ascontiguousarray(ang, np.float64)
+    y = np.zeros(ang.size, np.float64)
+    lib().or_tree_from_angles(ang, float(r), ang.size, y)
+    return y
+
+
+def tree_tables(b: int, d: int = 128) -> TreeTab:
+    T = TreeTab()
+    lib().or_tree_tables(d, b, ctypes.byref(T))
+    return T
+
+
+def tree_table_arrays(T: TreeTab):
+    """Per level l = 1..levels: (bits, centroids, boundaries) as numpy arrays."""
+    out = {}
+    for l in range(1, T.levels + 1):
+        n = 1 << T.bits[l]
+        out[l] = (T.bits[l], np.array(T.cent[l][:n]), np.array(T.bnd[l][:n - 1]))
+    return out
+
+
+def quantize_tree(x, D, T: TreeTab):
+    x = np.ascontiguousarray(x, np.float32)
+    codes = np.zeros(x.size, np.uint8)
+    n16 = ctypes.c_uint16()
+    amargin = np.zeros(x.size, np.float64)
+    lib().or_quantize_tree(x, x.size, np.ascontiguousarray(D, np.float32), ctypes.byref(T), codes,
+                           ctypes.byref(n16), _ptr(amargin))
+    return dict(codes=codes, n16=n16.value, amargin=amargin)
+
+
+def dequant_tree(D, T: TreeTab, codes, n16) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    out = np.zeros(codes.size, np.float64)
+    lib().or_dequant_tree(codes.size, np.ascontiguousarray(D, np.float32), ctypes.byref(T), codes,
+                          int(n16), out)
+    return out
+
+
 # ------------------------------------------------------ whole caches ----
 
 def make_spec(d=128, n_q=8, n_kv=2, batch=1, max_ctx=1024, k_codec=POLAR_QJL, k_bits=3,
@@ -308,15 +399,15 @@ class Records:
         self.spec = s
         self.n = n
         kc, vc = s.k_codec, s.v_codec
-        self.kcodes = np.zeros((n, d) if kc in (POLAR, POLAR_QJL) else 1, np.uint8)
-        self.kn16 = np.zeros(n if kc in (POLAR, POLAR_QJL) else 1, np.uint16)
+        self.kcodes = np.zeros((n, d) if kc in (POLAR, POLAR_QJL, POLAR_TREE) else 1, np.uint8)
+        self.kn16 = np.zeros(n if kc in (POLAR, POLAR_QJL, POLAR_TREE) else 1, np.uint16)
         self.signs = np.zeros((n, s.m) if kc == POLAR_QJL else 1, np.uint8)
         self.rho16 = np.zeros(n if kc == POLAR_QJL else 1, np.uint16)
         self.k8 = np.zeros((n, d) if kc == Q8_BLOCK32 else 1, np.int8)
         self.s16 = np.zeros((n, d // 32) if kc == Q8_BLOCK32 else 1, np.uint16)
         self.kraw = np.zeros((n, d) if kc == RAW_F32 else 1, np.float32)
-        self.vcodes = np.zeros((n, d) if vc == POLAR else 1, np.uint8)
-        self.vn16 = np.zeros(n if vc == POLAR else 1, np.uint16)
+        self.vcodes = np.zeros((n, d) if vc in (POLAR, POLAR_TREE) else 1, np.uint8)
+        self.vn16 = np.zeros(n if vc in (POLAR, POLAR_TREE) else 1, np.uint16)
         self.vraw = np.zeros((n, d) if vc == RAW_F32 else 1, np.float32)
 
     def _k(self):

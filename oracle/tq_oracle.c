@@ -429,6 +429,244 @@ void or_dequant_q8(int d, const int8_t* k8, const uint16_t* s16, double* out) {
 }
 
 /* ===================================================================== */
+/* Recursive polar codec (POLAR_TREE)                                    */
+/* ===================================================================== */
+/*
+ * [P1]'s Cartesian-to-polar paragraph read literally: the rotated vector y
+ * (d = 2^L coordinates) is rewritten as one radius and d - 1 angles by
+ * pairing recursively.  Level 1 pairs the coordinates (y_2i, y_2i+1): angle
+ * atan2(y_2i+1, y_2i) in [0, 2 pi).  Level l >= 2 pairs the radii of two
+ * sibling nodes of level l - 1: angle atan2(r_right, r_left) in [0, pi/2].
+ * The last radius is |y|.  For a spherically symmetric y the angles are
+ * independent, level 1 uniform on the circle and level l distributed with
+ * density prop. to sin(2 theta)^(2^(l-1) - 1) on [0, pi/2] (the squared
+ * radii of the two halves are chi-square with 2^(l-1) degrees each) -- the
+ * "distribution known in advance" of the paragraph.
+ *
+ * Angles live in heap slots: the node at slot s (1 <= s < d) has children
+ * 2s and 2s + 1, slots d .. 2d - 1 being the coordinates y_0 .. y_d-1.  So
+ * slot d/2 + i is level-1 pair i, slot 2^(L-l) + k is node k of level l, slot
+ * 1 is the root, slot 0 is unused.
+ *
+ * Reading of the bit budget (the pages give none): with b bits per
+ * coordinate, level 1 angles take b + 1 bits and every other angle b - 1
+ * bits, (d/2)(b + 1) + (d/2 - 1)(b - 1) = d b - 1 bits, plus the fp16 radius:
+ * the same record size as the per-coordinate codec with b bits.  Level 1 uses
+ * the uniform quantiser of the circle (cells [2 pi j / 2^(b+1), 2 pi (j+1) /
+ * 2^(b+1)], centroid at the middle); higher levels a Lloyd-Max codebook for
+ * their density.  Decisions: code = #{ boundaries below the angle } (ties go
+ * to the lower cell), angles from fp64 atan2 of fp64 coordinates and radii.
+ */
+
+static int or_tree_levels(int d) {
+  int L = 0;
+  while ((1 << L) < d) L++;
+  return L;
+}
+
+/* level of heap slot s (1 <= s < d) */
+static int or_slot_level(int d, int s) {
+  int L = or_tree_levels(d), k = 0;
+  while ((2 << k) <= s) k++;   /* k = floor(log2 s) */
+  return L - k;
+}
+
+static double or_angle_weight(int level, double th) {
+  double v = sin(2.0 * th);
+  if (v <= 0.0) return 0.0;
+  return pow(v, (double)((1 << (level - 1)) - 1));
+}
+
+static double or_angle_simpson(int level, double a, double c, int moment) {
+  if (c <= a) return 0.0;
+  double h = (c - a) / OR_SIMPSON_N;
+  double acc = 0.0;
+  for (int k = 0; k <= OR_SIMPSON_N; k++) {
+    double t = a + h * k;
+    double f = or_angle_weight(level, t);
+    if (moment == 1) f *= t;
+    if (moment == 2) f *= t * t;
+    double wk = (k == 0 || k == OR_SIMPSON_N) ? 1.0 : ((k & 1) ? 4.0 : 2.0);
+    acc += wk * f;
+  }
+  return acc * h / 3.0;
+}
+
+double or_angle_mass(int level, double a, double c) { return or_angle_simpson(level, a, c, 0); }
+double or_angle_moment1(int level, double a, double c) { return or_angle_simpson(level, a, c, 1); }
+
+/* Codebook of the level-`level` angle with `bits` bits: cent[2^bits] in
+ * increasing order, bounds[2^bits - 1] (midpoints), *mse = E[(theta -
+ * Q(theta))^2] under the level's law.  Level 1: uniform quantiser of [0, 2 pi).
+ * Level >= 2: Lloyd-Max, symmetric about pi/4 (the density is), iterated on
+ * [0, pi/4] until no centroid moves by more than 1e-13.  Returns the number
+ * of Lloyd rounds (0 for level 1), or -1 on bad arguments. */
+int or_angle_codebook(int level, int bits, double* cent, double* bounds, double* mse) {
+  if (level < 1 || level > 12 || bits < 1 || bits > 8) return -1;
+  int n = 1 << bits;
+  if (level == 1) {
+    double w = 2.0 * M_PI / n;
+    for (int j = 0; j < n; j++) cent[j] = (j + 0.5) * w;
+    for (int j = 0; j + 1 < n; j++) bounds[j] = (j + 1) * w;
+    if (mse) *mse = w * w / 12.0;
+    return 0;
+  }
+  int K = n / 2;
+  double q = M_PI / 4.0;
+  double* c = (double*)malloc(sizeof(double) * K);
+  double* e = (double*)malloc(sizeof(double) * (K + 1));
+  for (int k = 0; k < K; k++) c[k] = q * (k + 0.5) / K;
+  int it;
+  for (it = 1; it <= 100000; it++) {
+    e[0] = 0.0;
+    for (int k = 1; k < K; k++) e[k] = 0.5 * (c[k - 1] + c[k]);
+    e[K] = q;
+    double moved = 0.0;
+    for (int k = 0; k < K; k++) {
+      double nc = or_angle_simpson(level, e[k], e[k + 1], 1) / or_angle_simpson(level, e[k], e[k + 1], 0);
+      if (fabs(nc - c[k]) > moved) moved = fabs(nc - c[k]);
+      c[k] = nc;
+    }
+    if (moved <= 1e-13) break;
+  }
+  for (int k = 0; k < K; k++) {
+    cent[k] = c[k];
+    cent[n - 1 - k] = 2.0 * q - c[k];
+  }
+  for (int j = 0; j + 1 < n; j++) bounds[j] = 0.5 * (cent[j] + cent[j + 1]);
+  bounds[K - 1] = q;
+  if (mse) {
+    double num = 0.0, den = or_angle_simpson(level, 0.0, q, 0);
+    e[0] = 0.0;
+    for (int k = 1; k < K; k++) e[k] = 0.5 * (c[k - 1] + c[k]);
+    e[K] = q;
+    for (int k = 0; k < K; k++) {
+      double m0 = or_angle_simpson(level, e[k], e[k + 1], 0);
+      double m1 = or_angle_simpson(level, e[k], e[k + 1], 1);
+      double m2 = or_angle_simpson(level, e[k], e[k + 1], 2);
+      num += m2 - 2.0 * c[k] * m1 + c[k] * c[k] * m0;
+    }
+    *mse = num / den;
+  }
+  free(c);
+  free(e);
+  return it;
+}
+
+/* Angles of y (fp64) in heap slots ang[1..d-1]; returns |y|.  Signed zeros
+ * are read as +0. */
+double or_tree_angles(const double* y, int d, double* ang) {
+  double* r2 = (double*)malloc(sizeof(double) * 2 * d);
+  for (int i = 0; i < d; i++) r2[d + i] = y[i] * y[i];
+  for (int s = d - 1; s >= 1; s--) r2[s] = r2[2 * s] + r2[2 * s + 1];
+  ang[0] = 0.0;
+  for (int s = 1; s < d; s++) {
+    if (s >= d / 2) {
+      double a = y[2 * s - d] + 0.0, b = y[2 * s + 1 - d] + 0.0;
+      double th = atan2(b, a);
+      if (th < 0.0) th += 2.0 * M_PI;
+      ang[s] = th;
+    } else {
+      ang[s] = atan2(sqrt(r2[2 * s + 1]), sqrt(r2[2 * s]));
+    }
+  }
+  double r = sqrt(r2[1]);
+  free(r2);
+  return r;
+}
+
+/* Inverse of or_tree_angles: y from the radius r and the angles. */
+void or_tree_from_angles(const double* ang, double r, int d, double* y) {
+  double* rad = (double*)malloc(sizeof(double) * 2 * d);
+  rad[1] = r;
+  for (int s = 1; s < d; s++) {
+    rad[2 * s] = rad[s] * cos(ang[s]);
+    rad[2 * s + 1] = rad[s] * sin(ang[s]);
+  }
+  for (int i = 0; i < d; i++) y[i] = rad[d + i];
+  free(rad);
+}
+
+void or_tree_tables(int d, int b, or_tree_tab* T) {
+  int L = or_tree_levels(d);
+  T->d = d;
+  T->b = b;
+  T->levels = L;
+  for (int l = 1; l <= L; l++) {
+    T->bits[l] = (l == 1) ? b + 1 : b - 1;
+    or_angle_codebook(l, T->bits[l], T->cent[l], T->bnd[l], NULL);
+  }
+}
+
+/* One vector: y = H (D . x) in fp32 as for POLAR, n16 as for POLAR, then the
+ * angles of y (fp64) and per slot the code #{ j : B_j < angle }.  amargin
+ * (optional, [d]) gets the distance of each angle to the nearest decision
+ * boundary, the wrap-around at 0 = 2 pi included for level 1. */
+void or_quantize_tree(const float* x, int d, const float* D, const or_tree_tab* T,
+                      uint8_t* codes, uint16_t* n16, double* amargin) {
+  float* y = (float*)malloc(sizeof(float) * d);
+  double* yd = (double*)malloc(sizeof(double) * d);
+  double* ang = (double*)malloc(sizeof(double) * d);
+  for (int i = 0; i < d; i++) y[i] = D[i] * x[i];
+  or_fwht_f32(y, d);
+  double s = or_tree_sumsq_f32(x, d);
+  *n16 = or_norm_to_f16((float)sqrt(s));
+  for (int i = 0; i < d; i++) yd[i] = (double)y[i];
+  or_tree_angles(yd, d, ang);
+  codes[0] = 0;
+  if (amargin) amargin[0] = 1e300;
+  for (int sl = 1; sl < d; sl++) {
+    int l = or_slot_level(d, sl);
+    int nb = 1 << T->bits[l];
+    int c = 0;
+    double mg = 1e300;
+    for (int j = 0; j + 1 < nb; j++) {
+      if (ang[sl] > T->bnd[l][j]) c++;
+      double dd = fabs(ang[sl] - T->bnd[l][j]);
+      if (dd < mg) mg = dd;
+    }
+    if (l == 1) {
+      if (ang[sl] < mg) mg = ang[sl];
+      if (2.0 * M_PI - ang[sl] < mg) mg = 2.0 * M_PI - ang[sl];
+    }
+    codes[sl] = (uint8_t)c;
+    if (amargin) amargin[sl] = mg;
+  }
+  free(ang);
+  free(yd);
+  free(y);
+}
+
+/* x_hat = D . H (sqrt(d) n16 u) / d, u the unit vector whose angles are the
+ * code centroids (H H = d I). */
+void or_dequant_tree(int d, const float* D, const or_tree_tab* T, const uint8_t* codes,
+                     uint16_t n16, double* out) {
+  double* ang = (double*)malloc(sizeof(double) * d);
+  ang[0] = 0.0;
+  for (int sl = 1; sl < d; sl++) ang[sl] = T->cent[or_slot_level(d, sl)][codes[sl]];
+  or_tree_from_angles(ang, sqrt((double)d) * (double)or_f16_to_f32(n16), d, out);
+  or_fwht_f64(out, d);
+  for (int i = 0; i < d; i++) out[i] = (double)D[i] * out[i] / (double)d;
+  free(ang);
+}
+
+/* Tables for the whole-cache helpers, one per b = 2..4 at d = 128, built by
+ * or_tree_prepare before any other call uses them. */
+static or_tree_tab or_tree_cache[5];
+static int or_tree_ready = 0;
+
+void or_tree_prepare(void) {
+  if (or_tree_ready) return;
+  for (int b = 2; b <= 4; b++) or_tree_tables(128, b, &or_tree_cache[b]);
+  or_tree_ready = 1;
+}
+
+const or_tree_tab* or_tree_table(int b) {
+  if (!or_tree_ready || b < 2 || b > 4) return NULL;
+  return &or_tree_cache[b];
+}
+
+/* ===================================================================== */
 /* Layout                                                                */
 /* ===================================================================== */
 /*
@@ -452,6 +690,18 @@ void or_dequant_q8(int d, const int8_t* k8, const uint16_t* s16, double* out) {
  *   plane p:          u32 word[4][d]; bit e of word[j][i] = bit p of the code
  *                     of coordinate i of token 32 j + e (natural order)
  *   n16[128] fp16 at slot pi(t)
+ * K block, POLAR_TREE with b bits (angle slots a = 0..d-1, slot 0 unused):
+ *   plane p < b - 1:  u32 word[d/32][128]; bit e of word[j][pi(t)] = bit p of
+ *                     the code of angle slot 32 j + e of token t
+ *   2 level-1 planes: u32 word[d/64][128]; bit e of word[j][pi(t)] = bit
+ *                     b - 1 + x (plane x) of the code of slot d/2 + 32 j + e
+ *   n16[128] fp16 at slot pi(t)
+ * V block, POLAR_TREE with b bits:
+ *   plane p < b - 1:  u32 word[4][d]; bit e of word[j][a] = bit p of the code
+ *                     of angle slot a of token 32 j + e
+ *   2 level-1 planes: u32 word[4][d/2]; bit e of word[j][a - d/2] = bit
+ *                     b - 1 + x of the code of slot a of token 32 j + e
+ *   n16[128] fp16 at slot pi(t)
  */
 
 static int or_nblocks(const or_spec* s) { return (s->max_ctx + OR_BLOCK - 1) / OR_BLOCK; }
@@ -459,7 +709,8 @@ static int or_nblocks(const or_spec* s) { return (s->max_ctx + OR_BLOCK - 1) / O
 int64_t or_k_record_bytes(const or_spec* s) {
   switch (s->k_codec) {
     case OR_RAW_F32: return 4 * (int64_t)s->d;
-    case OR_POLAR: return (int64_t)s->k_bits * s->d / 8 + 2;
+    case OR_POLAR:
+    case OR_POLAR_TREE: return (int64_t)s->k_bits * s->d / 8 + 2;
     case OR_POLAR_QJL: return (int64_t)s->k_bits * s->d / 8 + s->m / 8 + 4;
     case OR_Q8_BLOCK32: return (int64_t)s->d + 2 * (s->d / 32);
   }
@@ -468,7 +719,8 @@ int64_t or_k_record_bytes(const or_spec* s) {
 int64_t or_v_record_bytes(const or_spec* s) {
   switch (s->v_codec) {
     case OR_RAW_F32: return 4 * (int64_t)s->d;
-    case OR_POLAR: return (int64_t)s->v_bits * s->d / 8 + 2;
+    case OR_POLAR:
+    case OR_POLAR_TREE: return (int64_t)s->v_bits * s->d / 8 + 2;
   }
   return -1;
 }
@@ -521,6 +773,23 @@ void or_pack_k(const or_spec* s, int b, int pos, int h, const or_krec* r, int64_
   int nb = s->k_bits;
   int sl = or_slot(t);
   int64_t plane_words = (int64_t)(d / 32) * OR_BLOCK;
+  if (s->k_codec == OR_POLAR_TREE) {
+    for (int p = 0; p < nb - 1; p++) {
+      for (int a = 0; a < d; a++) {
+        int bit = (r->codes[rec * d + a] >> p) & 1;
+        or_setbit(blk, p * plane_words + (int64_t)(a / 32) * OR_BLOCK + sl, a % 32, bit);
+      }
+    }
+    uint8_t* l1 = blk + 4 * (nb - 1) * plane_words;
+    for (int x = 0; x < 2; x++) {
+      for (int a = d / 2; a < d; a++) {
+        int bit = (r->codes[rec * d + a] >> (nb - 1 + x)) & 1;
+        or_setbit(l1, x * (plane_words / 2) + (int64_t)((a - d / 2) / 32) * OR_BLOCK + sl, a % 32, bit);
+      }
+    }
+    memcpy(l1 + 4 * plane_words + 2 * sl, &r->n16[rec], 2);
+    return;
+  }
   for (int p = 0; p < nb; p++) {
     for (int i = 0; i < d; i++) {
       int bit = (r->codes[rec * d + i] >> p) & 1;
@@ -555,6 +824,24 @@ void or_unpack_k(const or_spec* s, int b, int pos, int h, const uint8_t* kc, or_
   int nb = s->k_bits;
   int sl = or_slot(t);
   int64_t plane_words = (int64_t)(d / 32) * OR_BLOCK;
+  if (s->k_codec == OR_POLAR_TREE) {
+    const uint8_t* l1 = blk + 4 * (nb - 1) * plane_words;
+    for (int a = 0; a < d; a++) {
+      int c = 0;
+      for (int p = 0; p < nb - 1; p++) {
+        c |= or_getbit(blk, p * plane_words + (int64_t)(a / 32) * OR_BLOCK + sl, a % 32) << p;
+      }
+      if (a >= d / 2) {
+        for (int x = 0; x < 2; x++) {
+          c |= or_getbit(l1, x * (plane_words / 2) + (int64_t)((a - d / 2) / 32) * OR_BLOCK + sl, a % 32)
+               << (nb - 1 + x);
+        }
+      }
+      r->codes[rec * d + a] = (uint8_t)c;
+    }
+    memcpy(&r->n16[rec], l1 + 4 * plane_words + 2 * sl, 2);
+    return;
+  }
   for (int i = 0; i < d; i++) {
     int c = 0;
     for (int p = 0; p < nb; p++) {
@@ -583,6 +870,23 @@ void or_pack_v(const or_spec* s, int b, int pos, int h, const or_vrec* r, int64_
   }
   int nb = s->v_bits;
   int64_t plane_words = 4 * (int64_t)d;
+  if (s->v_codec == OR_POLAR_TREE) {
+    for (int p = 0; p < nb - 1; p++) {
+      for (int a = 0; a < d; a++) {
+        int bit = (r->codes[rec * d + a] >> p) & 1;
+        or_setbit(blk, p * plane_words + (int64_t)(t / 32) * d + a, t % 32, bit);
+      }
+    }
+    uint8_t* l1 = blk + 4 * (nb - 1) * plane_words;
+    for (int x = 0; x < 2; x++) {
+      for (int a = d / 2; a < d; a++) {
+        int bit = (r->codes[rec * d + a] >> (nb - 1 + x)) & 1;
+        or_setbit(l1, x * (plane_words / 2) + (int64_t)(t / 32) * (d / 2) + (a - d / 2), t % 32, bit);
+      }
+    }
+    memcpy(l1 + 4 * plane_words + 2 * or_slot(t), &r->n16[rec], 2);
+    return;
+  }
   for (int p = 0; p < nb; p++) {
     for (int i = 0; i < d; i++) {
       int bit = (r->codes[rec * d + i] >> p) & 1;
@@ -602,6 +906,24 @@ void or_unpack_v(const or_spec* s, int b, int pos, int h, const uint8_t* vc, or_
   }
   int nb = s->v_bits;
   int64_t plane_words = 4 * (int64_t)d;
+  if (s->v_codec == OR_POLAR_TREE) {
+    const uint8_t* l1 = blk + 4 * (nb - 1) * plane_words;
+    for (int a = 0; a < d; a++) {
+      int c = 0;
+      for (int p = 0; p < nb - 1; p++) {
+        c |= or_getbit(blk, p * plane_words + (int64_t)(t / 32) * d + a, t % 32) << p;
+      }
+      if (a >= d / 2) {
+        for (int x = 0; x < 2; x++) {
+          c |= or_getbit(l1, x * (plane_words / 2) + (int64_t)(t / 32) * (d / 2) + (a - d / 2), t % 32)
+               << (nb - 1 + x);
+        }
+      }
+      r->codes[rec * d + a] = (uint8_t)c;
+    }
+    memcpy(&r->n16[rec], l1 + 4 * plane_words + 2 * or_slot(t), 2);
+    return;
+  }
   for (int i = 0; i < d; i++) {
     int c = 0;
     for (int p = 0; p < nb; p++) {
@@ -639,6 +961,9 @@ void or_quantize_k_many(const or_spec* s, const float* DK, const uint16_t* c16,
                           out->codes + rec * d, &out->n16[rec], out->signs + rec * s->m,
                           &out->rho16[rec], NULL, NULL, NULL);
         break;
+      case OR_POLAR_TREE:
+        or_quantize_tree(xv, d, DK, or_tree_table(s->k_bits), out->codes + rec * d, &out->n16[rec], NULL);
+        break;
     }
   }
 }
@@ -652,6 +977,8 @@ void or_quantize_v_many(const or_spec* s, const float* DV, const uint16_t* c16,
     int64_t rec = out_off + k;
     if (s->v_codec == OR_RAW_F32) {
       memcpy(out->raw + rec * d, xv, 4 * (size_t)d);
+    } else if (s->v_codec == OR_POLAR_TREE) {
+      or_quantize_tree(xv, d, DV, or_tree_table(s->v_bits), out->codes + rec * d, &out->n16[rec], NULL);
     } else {
       or_quantize_polar(xv, d, s->v_bits, DV, c16, bounds, 0, NULL,
                         out->codes + rec * d, &out->n16[rec], NULL, NULL, NULL, NULL, NULL);
@@ -673,6 +1000,9 @@ static void or_dequant_k(const or_spec* s, const float* DK, const uint16_t* ck16
     case OR_Q8_BLOCK32:
       or_dequant_q8(d, kr->k8 + rec * d, kr->s16 + rec * (d / 32), out);
       break;
+    case OR_POLAR_TREE:
+      or_dequant_tree(d, DK, or_tree_table(s->k_bits), kr->codes + rec * d, kr->n16[rec], out);
+      break;
     default:
       or_dequant_polar(d, DK, ck16, kr->codes + rec * d, kr->n16[rec], out);
       break;
@@ -684,6 +1014,8 @@ static void or_dequant_v(const or_spec* s, const float* DV, const uint16_t* cv16
   int d = s->d;
   if (s->v_codec == OR_RAW_F32) {
     for (int i = 0; i < d; i++) out[i] = (double)vr->raw[rec * d + i];
+  } else if (s->v_codec == OR_POLAR_TREE) {
+    or_dequant_tree(d, DV, or_tree_table(s->v_bits), vr->codes + rec * d, vr->n16[rec], out);
   } else {
     or_dequant_polar(d, DV, cv16, vr->codes + rec * d, vr->n16[rec], out);
   }

@@ -37,7 +37,7 @@ extern "C" {
 #endif
 
 /* ---- codec identifiers (same numbering as the public ABI, restated) ---- */
-enum { OR_RAW_F32 = 0, OR_POLAR = 1, OR_POLAR_QJL = 2, OR_Q8_BLOCK32 = 3 };
+enum { OR_RAW_F32 = 0, OR_POLAR = 1, OR_POLAR_QJL = 2, OR_Q8_BLOCK32 = 3, OR_POLAR_TREE = 4 };
 enum { OR_BLOCK = 128 };   /* tokens per cache block */
 
 /* ---- fp16 ---- */
@@ -95,6 +95,31 @@ void or_dequant_polar_qjl(int d, int m, const float* D, const uint16_t* c16, con
                           const uint8_t* codes, uint16_t n16, const uint8_t* signs,
                           uint16_t rho16, double* out);
 void or_dequant_q8(int d, const int8_t* k8, const uint16_t* s16, double* out);
+
+/* ---- recursive polar codec (POLAR_TREE): one radius and d - 1 angles in
+ *      heap slots 1..d-1 (slot d/2 + i = level-1 pair i, slot 2^(L-l) + k =
+ *      node k of level l); see the .c file for the reading ---- */
+typedef struct {
+  int d, b, levels;
+  int bits[13];            /* per level 1..levels */
+  double cent[13][256];    /* centroids per level, increasing */
+  double bnd[13][255];     /* decision boundaries per level */
+} or_tree_tab;
+/* angle law of level l >= 2: density prop. to sin(2 theta)^(2^(l-1)-1) on [0, pi/2] */
+double or_angle_mass(int level, double a, double c);
+double or_angle_moment1(int level, double a, double c);
+int or_angle_codebook(int level, int bits, double* cent, double* bounds, double* mse);
+double or_tree_angles(const double* y, int d, double* ang);
+void or_tree_from_angles(const double* ang, double r, int d, double* y);
+void or_tree_tables(int d, int b, or_tree_tab* T);
+void or_quantize_tree(const float* x, int d, const float* D, const or_tree_tab* T,
+                      uint8_t* codes, uint16_t* n16, double* amargin);
+void or_dequant_tree(int d, const float* D, const or_tree_tab* T, const uint8_t* codes,
+                     uint16_t n16, double* out);
+/* tables for b = 2..4 at d = 128 used by the whole-cache helpers; prepare
+ * once before any other call (not thread-safe), then read-only */
+void or_tree_prepare(void);
+const or_tree_tab* or_tree_table(int b);
 
 /* ---- whole-cache helpers ---------------------------------------------
  * A "layer spec" describes one layer's cache: the codecs and sizes.  All
