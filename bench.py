@@ -173,6 +173,9 @@ def main():
     ap.add_argument("--focus-every", type=int, default=0, metavar="E",
                     help="peaked attention: one planted key per E positions that the query heads score "
                          "about 16 nats above the rest (0 = the workload's plain keys)")
+    ap.add_argument("--tree-bits", default="", metavar="KB/VB",
+                    help="store keys and values with the recursive polar codec at KB and VB bits instead of the "
+                         "workload's codecs (e.g. 3/2)")
     args = ap.parse_args()
     if args.summarize_counters:
         res = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.calibration_mib)
@@ -210,6 +213,11 @@ def main():
         policy = presets.layer_policy(n_layers, kt, vt, int(prot))
         layers = [tq.KVLayer(presets.config(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v),
                                             policy[l], l), dev, zero=False)
+                  for l in range(n_layers)]
+    elif args.tree_bits:
+        tkb, tvb = (int(x) for x in args.tree_bits.split("/"))
+        layers = [tq.KVLayer(tq.make_config(w.d, w.n_q, w.n_kv, w.batch, w.ctx, tq.POLAR_TREE, tkb, 0,
+                                            tq.POLAR_TREE, tvb, 0, 42, l, args.sparse_v), dev, zero=False)
                   for l in range(n_layers)]
     else:
         layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v), dev, zero=False)
@@ -306,11 +314,17 @@ def main():
         result["roofline"]["traffic"] = None
         result.pop("append_tokens_per_s")
         result.pop("append_ms_per_layer")
+    if args.tree_bits:
+        result["metric"] = "decode attention HBM GB/s on packed KV, recursive polar codec; quantize-append tokens/s"
+        result["config"]["k_codec"] = f"polar_tree b{tkb}"
+        result["config"]["v_codec"] = f"polar_tree b{tvb}"
+        result["roofline"]["traffic"] = None
+        result["roofline"]["kernel"] = "decode_kernel"
     if args.sparse_v or args.focus_every:
         result["config"]["sparse_v"] = args.sparse_v
         result["config"]["focus_every"] = args.focus_every
         result["data"] = "synthetic, planted focus keys" if args.focus_every else "synthetic"
-    if not args.no_cpu_baseline and policy is None and not (args.sparse_v or args.focus_every):
+    if not args.no_cpu_baseline and policy is None and not (args.sparse_v or args.focus_every or args.tree_bits):
         result["cpu_baseline"] = cpu_baseline(w, data_seed)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)

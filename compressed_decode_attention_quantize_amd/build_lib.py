@@ -26,6 +26,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 UNITS = [
     ("tq_host.cpp", []),
     ("tq_quant.hip", ["-ffp-contract=off"]),
+    ("tq_quant_tree.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
     ("tq_dequant.hip", []),

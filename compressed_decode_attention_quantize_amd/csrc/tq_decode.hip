@@ -11,6 +11,14 @@
 // rotated frame: acc = sum_t p_t n16V_t C_V[c_t], out = D_V H acc / d (one
 // inverse transform per head instead of one per position).  q8 keys use the
 // unrotated query and per-block scales; RAW tensors are used as stored.
+// Recursive polar tensors (the radius + angle step read as a pairwise tree)
+// stand for y_hat = sqrt(d) n16 u, u the unit vector of the code angles: a
+// key's logit is n16 <q_raw, u> / d with <q_raw, u> = sum over the 64
+// level-1 pairs of (q_2i cos + q_2i+1 sin of the pair's angle) times the
+// product of its ancestors' cos (left child) or sin (right child), walked
+// top-down so that every node's angle is looked up once; a value coordinate
+// u_i is the product over the 7 levels of the cos or sin of its ancestors'
+// angles.
 //
 // Mapping: grid (split, KV head, sequence); a 256-thread workgroup serves
 // all G query heads of its KV head over one chunk of 128-position blocks,
@@ -34,6 +42,75 @@ namespace tq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kHeadsPerThread = kMaxGroup / 2;
+
+// Recursive polar: (cos, sin) of the centroid angles, level 1 at [0][code],
+// level l >= 2 at [l][code].
+struct TreeLds {
+  float2 l1[32];
+  float2 up[8][8];
+};
+
+// code of an angle slot of one key from its word J (slot / 32, a constant
+// at every call) and bit e: w[p][J] for the b - 1 shared planes, x[k][J - 2]
+// for the two extra level-1 planes
+template <int J>
+__device__ __forceinline__ int tree_key_code(const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int nb1, int e) {
+  int c = 0;
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    if (p < nb1) c |= ((w[p][J] >> e) & 1u) << p;
+  if constexpr (J >= 2) {
+    c |= ((x[0][J - 2] >> e) & 1u) << nb1;
+    c |= ((x[1][J - 2] >> e) & 1u) << (nb1 + 1);
+  }
+  return c;
+}
+
+// dot[h] += <q_raw, u> over the subtree of level-6 node N6 (coordinates
+// 64 N6 .. 64 N6 + 63), its weight w6 being the root's cos or sin
+template <int N6>
+__device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int nb1,
+                                              const TreeLds& tab, const float* qv, int hpar, int G,
+                                              float (&dot)[kHeadsPerThread]) {
+  const float2 c6 = tab.up[6][tree_key_code<0>(w, x, nb1, 2 + N6)];
+#pragma unroll 1
+  for (int n5 = 2 * N6; n5 < 2 * N6 + 2; ++n5) {
+    const float w5 = w6 * ((n5 & 1) ? c6.y : c6.x);
+    const float2 c5 = tab.up[5][tree_key_code<0>(w, x, nb1, 4 + n5)];
+#pragma unroll 1
+    for (int n4 = 2 * n5; n4 < 2 * n5 + 2; ++n4) {
+      const float w4 = w5 * ((n4 & 1) ? c5.y : c5.x);
+      const float2 c4 = tab.up[4][tree_key_code<0>(w, x, nb1, 8 + n4)];
+#pragma unroll 1
+      for (int n3 = 2 * n4; n3 < 2 * n4 + 2; ++n3) {
+        const float w3 = w4 * ((n3 & 1) ? c4.y : c4.x);
+        const float2 c3 = tab.up[3][tree_key_code<0>(w, x, nb1, 16 + n3)];
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const int n2 = 2 * n3 + b2;
+          const float w2 = w3 * (b2 ? c3.y : c3.x);
+          const float2 c2 = tab.up[2][tree_key_code<1>(w, x, nb1, n2)];   // slot 32 + n2
+#pragma unroll
+          for (int b1 = 0; b1 < 2; ++b1) {
+            const int i = 2 * n2 + b1;   // level-1 pair, slot 64 + i (word 2 + N6)
+            const float w1 = w2 * (b1 ? c2.y : c2.x);
+            const float2 cs = tab.l1[tree_key_code<2 + N6>(w, x, nb1, i & 31)];
+            const float a0 = w1 * cs.x, a1 = w1 * cs.y;
+#pragma unroll
+            for (int u = 0; u < kHeadsPerThread; ++u) {
+              const int g = hpar + 2 * u;
+              if (g < G) {
+                const float2 q2 = *reinterpret_cast<const float2*>(qv + g * kD + 2 * i);
+                dot[u] = fmaf(q2.x, a0, fmaf(q2.y, a1, dot[u]));
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 
@@ -53,6 +130,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ float sq[kMaxGroup * kM];   // S q_raw / sqrt(d) per head
   __shared__ float pt[kMaxGroup * kBlock];  // logits, then p * value radius
   __shared__ float kcb[16], vcb[16];
+  __shared__ TreeLds ktree, vtree;
   __shared__ float m_run[kMaxGroup], l_run[kMaxGroup], scale[kMaxGroup];
   __shared__ int s_last;
 
@@ -70,8 +148,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   for (int k = tid; k < G * kD; k += kThreads) {
     const int g = k / kD, i = k % kD;
     float v = a.q[(static_cast<int64_t>(b) * a.n_q + h * G + g) * kD + i];
-    if (a.k_codec == POLAR || a.k_codec == POLAR_QJL) v *= a.tb.dk[i];
+    if (a.k_codec == POLAR || a.k_codec == POLAR_QJL || a.k_codec == POLAR_TREE) v *= a.tb.dk[i];
     qv[k] = v;
+  }
+  if (tid < 32) {
+    if (a.k_codec == POLAR_TREE) ktree.l1[tid] = a.tb.tk->cs1[tid];
+    if (a.v_codec == POLAR_TREE) vtree.l1[tid] = a.tb.tv->cs1[tid];
+  } else if (tid < 96) {
+    const int l = (tid - 32) >> 3, c = (tid - 32) & 7;
+    if (a.k_codec == POLAR_TREE) ktree.up[l][c] = a.tb.tk->cs[l][c];
+    if (a.v_codec == POLAR_TREE) vtree.up[l][c] = a.tb.tv->cs[l][c];
   }
   if (tid < 16) {
     kcb[tid] = a.tb.ck[tid];
@@ -81,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     m_run[tid] = -INFINITY;
     l_run[tid] = 0.0f;
   }
-  if (a.k_codec == POLAR || a.k_codec == POLAR_QJL) block_fwht128(qv, G, kThreads);   // q_raw = H D_K q
+  if (a.k_codec == POLAR || a.k_codec == POLAR_QJL || a.k_codec == POLAR_TREE)
+    block_fwht128(qv, G, kThreads);   // q_raw = H D_K q
   __syncthreads();
   if (a.k_codec == POLAR_QJL) {
     for (int k = tid; k < G * kM; k += kThreads) {
@@ -170,6 +257,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(after)[slot_of(t)]);
 #pragma unroll
           for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = alpha * n16 * cdot[u] + beta * rho * sdot[u];
+        } else if (a.k_codec == POLAR_TREE) {
+          const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
+          const int sl = slot_of(t);
+          const int nb1 = kbits - 1;
+          uint32_t w[3][4] = {}, x[2][2];
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            if (p < nb1)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) w[p][j] = planes[(p * 4 + j) * kBlock + sl];
+          const uint32_t* l1 = planes + nb1 * 4 * kBlock;
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) x[k][j] = l1[(k * 2 + j) * kBlock + sl];
+          const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
+          float dot[kHeadsPerThread] = {};
+          const float2 c7 = ktree.up[7][tree_key_code<0>(w, x, nb1, 1)];
+          tree_half_dot<0>(c7.x, w, x, nb1, ktree, qv, hpar, G, dot);
+          tree_half_dot<1>(c7.y, w, x, nb1, ktree, qv, hpar, G, dot);
+#pragma unroll
+          for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = n16 * dot[u] * (1.0f / static_cast<float>(kD));
         } else if (a.k_codec == Q8_BLOCK32) {
           const int8_t* row = reinterpret_cast<const int8_t*>(kb) + t * kD;
           const uint16_t* sc = reinterpret_cast<const uint16_t*>(kb + kBlock * kD) + t * (kD / 32);
@@ -230,10 +339,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const float p1 = (lane + 64 < n_t) ? __expf(l1 - mn) : 0.0f;
       const float sum = wave_sum(p0 + p1);
       float vr0 = 1.0f, vr1 = 1.0f;
-      if (a.v_codec == POLAR) {
+      if (a.v_codec == POLAR || a.v_codec == POLAR_TREE) {
+        // the radius field sits after 4 b d bytes of code words in both layouts;
+        // the recursive codec's y_hat is sqrt(d) n16 u
         const uint16_t* vn = reinterpret_cast<const uint16_t*>(vb + 4 * vbits * 4 * kD);
-        vr0 = (lane < n_t) ? f16_to_f32(vn[slot_of(lane)]) : 0.0f;
-        vr1 = (lane + 64 < n_t) ? f16_to_f32(vn[slot_of(lane + 64)]) : 0.0f;
+        const float sc = (a.v_codec == POLAR_TREE) ? 11.313708498984761f : 1.0f;
+        vr0 = (lane < n_t) ? sc * f16_to_f32(vn[slot_of(lane)]) : 0.0f;
+        vr1 = (lane + 64 < n_t) ? sc * f16_to_f32(vn[slot_of(lane + 64)]) : 0.0f;
       }
       pt[g * kBlock + lane] = p0 * vr0;
       pt[g * kBlock + lane + 64] = p1 * vr1;
@@ -270,6 +382,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           for (int u = 0; u < kMaxGroup / 2; ++u) {
             const int g = hpar + 2 * u;
             if (g < G) acc[u] = fmaf(pt[g * kBlock + t], cv, acc[u]);
+          }
+        }
+      }
+    } else if (a.v_codec == POLAR_TREE) {
+      // coordinate ci: its level-1 pair is slot 64 + ci / 2, its level-l
+      // ancestor slot 2^(7 - l) + ci / 2^l; the factor is the sin of an
+      // ancestor's angle when ci lies in its right half, else the cos
+      const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
+      const int nb1 = vbits - 1;
+      const uint32_t* l1 = planes + nb1 * 4 * kD;
+      for (int j = 0; j * 32 < n_t; ++j) {
+        uint32_t w[3][7] = {}, x[2];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          if (p < nb1) {
+            w[p][0] = planes[(p * 4 + j) * kD + 64 + (ci >> 1)];
+#pragma unroll
+            for (int l = 2; l <= 7; ++l) w[p][l - 1] = planes[(p * 4 + j) * kD + (1 << (7 - l)) + (ci >> l)];
+          }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) x[k] = l1[(k * 4 + j) * (kD / 2) + (ci >> 1)];
+        const int e_end = min(32, n_t - j * 32);
+        for (int e = 0; e < e_end; ++e) {
+          int c = 0;
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            if (p < nb1) c |= ((w[p][0] >> e) & 1u) << p;
+          c |= ((x[0] >> e) & 1u) << nb1;
+          c |= ((x[1] >> e) & 1u) << (nb1 + 1);
+          const float2 cs1 = vtree.l1[c];
+          float uval = (ci & 1) ? cs1.y : cs1.x;
+#pragma unroll
+          for (int l = 2; l <= 7; ++l) {
+            int cl = 0;
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              if (p < nb1) cl |= ((w[p][l - 1] >> e) & 1u) << p;
+            const float2 cs = vtree.up[l][cl];
+            uval *= ((ci >> (l - 1)) & 1) ? cs.y : cs.x;
+          }
+          const int t = j * 32 + e;
+#pragma unroll
+          for (int u = 0; u < kMaxGroup / 2; ++u) {
+            const int g = hpar + 2 * u;
+            if (g < G) acc[u] = fmaf(pt[g * kBlock + t], uval, acc[u]);
           }
         }
       }

@@ -6,6 +6,10 @@
 // QJL correction rho sqrt(pi/2)/m R^T S^T sign (R = H D / sqrt d), whose
 // inner product with a query is the estimator's correction term (the
 // article's QJL paragraph).  q8 keys are s16 * k8; RAW is a copy.
+// Recursive polar records (the radius + angle step read as a pairwise tree)
+// give y_hat = sqrt(d) n16 u, coordinate i of u being the product over the 7
+// levels of the cos or sin of its ancestors' centroid angles (sin when i lies
+// in the right half of the ancestor), then the same inverse rotation.
 //
 // Mapping: one wavefront per (position, KV head); lane l produces
 // coordinates l and l + 64; the transform is the same cross-lane FWHT as on
@@ -40,6 +44,19 @@ __device__ __forceinline__ void wave_fwht128(float& lo, float& hi, int lane) {
   hi = a - b;
 }
 
+// u_i from the codes of its ancestors: code(s) returns the code of angle slot s
+template <typename CodeOf>
+__device__ __forceinline__ float tree_coord(int i, const TreeTab* T, CodeOf code) {
+  const float2 c1 = T->cs1[code(64 + (i >> 1))];
+  float u = (i & 1) ? c1.y : c1.x;
+#pragma unroll
+  for (int l = 2; l <= 7; ++l) {
+    const float2 cs = T->cs[l][code((1 << (7 - l)) + (i >> l))];
+    u *= ((i >> (l - 1)) & 1) ? cs.y : cs.x;
+  }
+  return u;
+}
+
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * kWavesPerWg + (threadIdx.x >> 6);
@@ -65,6 +82,23 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       const uint16_t* sc = reinterpret_cast<const uint16_t*>(kb + kBlock * kD) + t * (kD / 32);
       lo = f16_to_f32(sc[lane >> 5]) * static_cast<float>(row[lane]);
       hi = f16_to_f32(sc[2 + (lane >> 5)]) * static_cast<float>(row[lane + 64]);
+    } else if (a.k_codec == POLAR_TREE) {
+      const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
+      const int nb1 = a.k_bits - 1;
+      const uint32_t* l1 = planes + nb1 * 4 * kBlock;
+      auto code = [&](int s) {
+        int c = 0;
+        for (int p = 0; p < nb1; ++p) c |= ((planes[(p * 4 + (s >> 5)) * kBlock + sl] >> (s & 31)) & 1u) << p;
+        if (s >= 64)
+          for (int x = 0; x < 2; ++x) c |= ((l1[(x * 2 + (s >> 5) - 2) * kBlock + sl] >> (s & 31)) & 1u) << (nb1 + x);
+        return c;
+      };
+      const float r = 11.313708498984761f * f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
+      lo = r * tree_coord(lane, a.tb.tk, code);
+      hi = r * tree_coord(lane + 64, a.tb.tk, code);
+      wave_fwht128(lo, hi, lane);
+      lo = a.tb.dk[lane] * lo * inv_d;
+      hi = a.tb.dk[lane + 64] * hi * inv_d;
     } else {
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
       const int plane_words = (kD / 32) * kBlock;
@@ -112,6 +146,24 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       const float* row = reinterpret_cast<const float*>(vb) + t * kD;
       lo = row[lane];
       hi = row[lane + 64];
+    } else if (a.v_codec == POLAR_TREE) {
+      const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
+      const int nb1 = a.v_bits - 1;
+      const uint32_t* l1 = planes + nb1 * 4 * kD;
+      const int j = t >> 5, e = t & 31;
+      auto code = [&](int s) {
+        int c = 0;
+        for (int p = 0; p < nb1; ++p) c |= ((planes[(p * 4 + j) * kD + s] >> e) & 1u) << p;
+        if (s >= 64)
+          for (int x = 0; x < 2; ++x) c |= ((l1[(x * 4 + j) * (kD / 2) + s - 64] >> e) & 1u) << (nb1 + x);
+        return c;
+      };
+      const float r = 11.313708498984761f * f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 2 * 4 * (kD / 2))[sl]);
+      lo = r * tree_coord(lane, a.tb.tv, code);
+      hi = r * tree_coord(lane + 64, a.tb.tv, code);
+      wave_fwht128(lo, hi, lane);
+      lo = a.tb.dv[lane] * lo * inv_d;
+      hi = a.tb.dv[lane + 64] * hi * inv_d;
     } else {
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
       int c_lo = 0, c_hi = 0;

@@ -130,10 +130,11 @@ __device__ inline bool arrive_last(uint32_t* counter, int n_splits, int* s_flag)
 }
 
 // Split-K merge done by the last workgroup of a (sequence, KV head): partials
-// hold, per query head and split, acc[128] (rotated frame for POLAR values),
-// the running max m (natural-log units) and the softmax denominator l.  Writes
-// out = D_V H (sum_s acc_s e^{m_s - M}) / (d sum_s l_s e^{m_s - M}) for POLAR
-// values, the same without the inverse rotation for RAW values.  obuf is a
+// hold, per query head and split, acc[128] (rotated frame for POLAR and
+// recursive polar values), the running max m (natural-log units) and the
+// softmax denominator l.  Writes out = D_V H (sum_s acc_s e^{m_s - M}) /
+// (d sum_s l_s e^{m_s - M}) for rotated values, the same without the inverse
+// rotation for RAW values.  obuf is a
 // shared buffer of G*128 floats.  One wavefront per query head; splits are
 // taken 32 at a time with every load of a chunk in flight together; lane
 // (half, i4) accumulates float4 i4 of the chunk's splits of parity half.
@@ -198,12 +199,13 @@ __device__ inline void combine_splits(const DecodeArgs& a, int b, int h, float* 
       obuf[g * kD + 4 * i4 + 3] = A.w * inv;
     }
   }
-  if (a.v_codec == POLAR) block_fwht128(obuf, G, nthreads);   // H acc; D_V and 1/d below
+  const bool rotated = (a.v_codec == POLAR || a.v_codec == POLAR_TREE);
+  if (rotated) block_fwht128(obuf, G, nthreads);   // H acc; D_V and 1/d below
   __syncthreads();
   for (int k = threadIdx.x; k < G * kD; k += nthreads) {
     const int g = k / kD, i = k % kD;
     float v = obuf[k];
-    if (a.v_codec == POLAR) v = v * a.tb.dv[i] * (1.0f / static_cast<float>(kD));
+    if (rotated) v = v * a.tb.dv[i] * (1.0f / static_cast<float>(kD));
     a.out[(static_cast<int64_t>(b) * a.n_q + h * G + g) * kD + i] = v;
   }
   if (threadIdx.x == 0) __hip_atomic_store(a.counters + b * a.n_kv + h, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -11,7 +11,12 @@
 //   * the codebook is the Lloyd-Max quantiser of the coordinate law of a
 //     uniformly random unit vector scaled by sqrt(d), density proportional to
 //     (1 - t^2/d)^((d-3)/2); centroids are stored as fp16-exact values and
-//     the decision boundaries as the fp32 midpoints of adjacent centroids.
+//     the decision boundaries as the fp32 midpoints of adjacent centroids;
+//   * the recursive polar codec (the article's radius + angle step taken
+//     literally, pairwise and level by level) quantises level-1 angles
+//     uniformly on the circle and the angles of level l >= 2, whose law is
+//     proportional to sin(2 theta)^(2^(l-1) - 1) on [0, pi/2], with their
+//     Lloyd-Max codebooks.
 // Integrals use composite 16-point Gauss-Legendre quadrature.
 
 #include <hip/hip_runtime.h>
@@ -60,6 +65,9 @@ tq_status check_cfg(const tq_config* c) {
     case TQ_CODEC_Q8_BLOCK32:
       if (c->k_bits != 8 || c->qjl_m != 0) return TQ_EINVAL;
       break;
+    case TQ_CODEC_POLAR_TREE:
+      if (c->k_bits < 2 || c->k_bits > 8 || c->qjl_m != 0) return TQ_EINVAL;
+      break;
     default:
       return TQ_EINVAL;
   }
@@ -69,6 +77,9 @@ tq_status check_cfg(const tq_config* c) {
       break;
     case TQ_CODEC_POLAR:
       if (c->v_bits < 1 || c->v_bits > 8) return TQ_EINVAL;
+      break;
+    case TQ_CODEC_POLAR_TREE:
+      if (c->v_bits < 2 || c->v_bits > 8) return TQ_EINVAL;
       break;
     case TQ_CODEC_POLAR_QJL:
     case TQ_CODEC_Q8_BLOCK32:
@@ -84,6 +95,8 @@ tq_status check_cfg(const tq_config* c) {
     return TQ_EUNSUPPORTED;
   if (c->k_codec == TQ_CODEC_POLAR_QJL && c->qjl_m != kM) return TQ_EUNSUPPORTED;
   if (c->v_codec == TQ_CODEC_POLAR && (c->v_bits < 2 || c->v_bits > 4)) return TQ_EUNSUPPORTED;
+  if (c->k_codec == TQ_CODEC_POLAR_TREE && c->k_bits > 4) return TQ_EUNSUPPORTED;
+  if (c->v_codec == TQ_CODEC_POLAR_TREE && c->v_bits > 4) return TQ_EUNSUPPORTED;
   return TQ_OK;
 }
 
@@ -95,7 +108,8 @@ int64_t k_record_bytes(const tq_config* c) {
   const int64_t d = c->head_dim;
   switch (c->k_codec) {
     case TQ_CODEC_RAW_F32: return 4 * d;
-    case TQ_CODEC_POLAR: return c->k_bits * d / 8 + 2;
+    case TQ_CODEC_POLAR:
+    case TQ_CODEC_POLAR_TREE: return c->k_bits * d / 8 + 2;
     case TQ_CODEC_POLAR_QJL: return c->k_bits * d / 8 + c->qjl_m / 8 + 4;
     default: return d + 2 * (d / 32);
   }
@@ -258,6 +272,95 @@ Codebook make_codebook(int d, int bits) {
   return cb;
 }
 
+// ------------------------------------------- recursive polar codebooks
+
+// int_a^c t^moment sin(2t)^(2^(level-1) - 1) dt, 32 panels of 16-point Gauss-Legendre
+double angle_integral(int level, double a, double c, int moment) {
+  static const GaussLegendre16 gl;
+  const int panels = 32;
+  const double hw = (c - a) / panels;
+  const int ex = (1 << (level - 1)) - 1;
+  double total = 0.0;
+  for (int p = 0; p < panels; ++p) {
+    const double mid = a + (p + 0.5) * hw;
+    double s = 0.0;
+    for (int k = 0; k < 16; ++k) {
+      const double t = mid + 0.5 * hw * gl.x[k];
+      double f = 1.0;
+      const double sv = std::sin(2.0 * t);
+      for (int e = 0; e < ex; ++e) f *= sv;
+      if (moment == 1) f *= t;
+      s += gl.w[k] * f;
+    }
+    total += 0.5 * hw * s;
+  }
+  return total;
+}
+
+// Lloyd-Max centroids (increasing) and boundaries of the level-l angle law
+// on [0, pi/2] with 2^bits codes; the law is symmetric about pi/4, so the
+// lower half is iterated and mirrored.
+void angle_lloyd(int level, int bits, double* cent, double* bnd) {
+  const int n = 1 << bits, half = n / 2;
+  const double q = 0.25 * M_PI;
+  std::vector<double> c(half), e(half + 1);
+  for (int k = 0; k < half; ++k) c[k] = q * (k + 0.5) / half;
+  for (int round = 0; round < 100000; ++round) {
+    e[0] = 0.0;
+    for (int k = 1; k < half; ++k) e[k] = 0.5 * (c[k - 1] + c[k]);
+    e[half] = q;
+    double moved = 0.0;
+    for (int k = 0; k < half; ++k) {
+      const double nc = angle_integral(level, e[k], e[k + 1], 1) / angle_integral(level, e[k], e[k + 1], 0);
+      moved = std::max(moved, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (moved <= 1e-13) break;
+  }
+  for (int k = 0; k < half; ++k) {
+    cent[k] = c[k];
+    cent[n - 1 - k] = 2.0 * q - c[k];
+  }
+  for (int j = 0; j + 1 < n; ++j) bnd[j] = (j == half - 1) ? q : 0.5 * (cent[j] + cent[j + 1]);
+}
+
+tq::TreeTab make_tree_tab(int bits) {
+  static std::mutex mu;
+  static std::map<int, tq::TreeTab> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(bits);
+  if (it != cache.end()) return it->second;
+  tq::TreeTab t{};
+  // level 1: 2^(bits+1) cells of the circle; a quadrant holds 2^(bits-1)
+  const int n1 = 1 << (bits + 1), per_q = n1 / 4;
+  for (int c = 0; c < n1; ++c) {
+    const double th = (c + 0.5) * 2.0 * M_PI / n1;
+    t.cs1[c] = make_float2(static_cast<float>(std::cos(th)), static_cast<float>(std::sin(th)));
+  }
+  // a boundary at pi/4 gets cos^2 = sin^2 = 1/2 exactly, so that an angle on
+  // it (equal radii) goes to the lower cell like any other tie
+  for (int j = 0; j + 1 < per_q; ++j) {
+    const double beta = (j + 1) * 0.5 * M_PI / per_q;
+    const bool mid = 2 * (j + 1) == per_q;
+    t.c2_1[j] = mid ? 0.5 : std::cos(beta) * std::cos(beta);
+    t.s2_1[j] = mid ? 0.5 : std::sin(beta) * std::sin(beta);
+  }
+  // levels 2..7: 2^(bits-1) codes each
+  const int nl = 1 << (bits - 1);
+  for (int l = 2; l <= 7; ++l) {
+    double cent[8], bnd[7];
+    angle_lloyd(l, bits - 1, cent, bnd);
+    for (int c = 0; c < nl; ++c) t.cs[l][c] = make_float2(static_cast<float>(std::cos(cent[c])), static_cast<float>(std::sin(cent[c])));
+    for (int j = 0; j + 1 < nl; ++j) {
+      const bool mid = 2 * (j + 1) == nl;   // the symmetric codebook's middle boundary is pi/4
+      t.c2[l][j] = mid ? 0.5 : std::cos(bnd[j]) * std::cos(bnd[j]);
+      t.s2[l][j] = mid ? 0.5 : std::sin(bnd[j]) * std::sin(bnd[j]);
+    }
+  }
+  cache[bits] = t;
+  return t;
+}
+
 // ------------------------------------------------------- params image
 
 void build_params(const tq_config* c, uint8_t* img) {
@@ -304,6 +407,14 @@ void build_params(const tq_config* c, uint8_t* img) {
     std::memcpy(img + L.vb, cb.bounds, 64);
     std::memcpy(img + L.av, cb.coeffs, 32);
   }
+  if (c->k_codec == TQ_CODEC_POLAR_TREE) {
+    const tq::TreeTab t = make_tree_tab(c->k_bits);
+    std::memcpy(img + L.tk, &t, sizeof t);
+  }
+  if (c->v_codec == TQ_CODEC_POLAR_TREE) {
+    const tq::TreeTab t = make_tree_tab(c->v_bits);
+    std::memcpy(img + L.tv, &t, sizeof t);
+  }
 }
 
 tq::Tables tables(const tq_config* c, const void* params) {
@@ -321,6 +432,8 @@ tq::Tables tables(const tq_config* c, const void* params) {
   t.ak = reinterpret_cast<const float*>(p + L.ak);
   t.av = reinterpret_cast<const float*>(p + L.av);
   t.shd = reinterpret_cast<const float*>(p + L.shd);
+  t.tk = reinterpret_cast<const tq::TreeTab*>(p + L.tk);
+  t.tv = reinterpret_cast<const tq::TreeTab*>(p + L.tv);
   return t;
 }
 
@@ -458,7 +571,10 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params, void* k_c
   a.v_bits = cfg->v_bits;
   a.k_block_bytes = kBlock * k_record_bytes(cfg);
   a.v_block_bytes = kBlock * v_record_bytes(cfg);
-  return tq::launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EDEVICE;
+  hipError_t e = tq::launch_quantize(a, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && (cfg->k_codec == TQ_CODEC_POLAR_TREE || cfg->v_codec == TQ_CODEC_POLAR_TREE))
+    e = tq::launch_quantize_tree(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
 
 tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, uint64_t* bytes) {

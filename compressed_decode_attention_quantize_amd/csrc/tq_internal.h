@@ -22,6 +22,17 @@ __host__ __device__ inline int slot_of(int t) { return 32 * (t >> 5) + 8 * (t & 
 // Inverse: the position stored in slot s.
 __host__ __device__ inline int pos_of_slot(int s) { return 32 * (s >> 5) + 4 * (s & 7) + ((s & 31) >> 3); }
 
+// Recursive polar codec ("radius + angle" tree) tables of one tensor with b
+// bits: level-1 angles take b + 1 bits (uniform on the circle), the angles of
+// levels 2..7 take b - 1 bits (Lloyd-Max for their law).  Decisions compare
+// squared radii against cos^2 / sin^2 of the boundary angles in fp64.
+struct TreeTab {
+  float2 cs1[32];              // level 1: (cos, sin) of the centroid angle of each code
+  float2 cs[8][8];             // level l = 2..7 at [l]: (cos, sin) of each code's centroid angle
+  double c2_1[8], s2_1[8];     // level 1: cos^2, sin^2 of the boundaries inside a quadrant
+  double c2[8][8], s2[8][8];   // level l = 2..7 at [l]: cos^2, sin^2 of its boundaries
+};
+
 // Byte offsets inside the parameter image (all fp32 arrays).
 struct ParamsLayout {
   uint64_t dk, dv;   // float[d] rotation signs (+/-1) for K and V
@@ -31,6 +42,7 @@ struct ParamsLayout {
   uint64_t cv, vb;   // same for V
   uint64_t ak, av;   // float[8] odd multilinear coefficients of the K / V codebooks
   uint64_t shd;      // float[d][m]: (S H D_K / sqrt d)^T, the sketch of a query before rotation
+  uint64_t tk, tv;   // TreeTab of K and of V (recursive polar codec)
   uint64_t total;
 };
 
@@ -48,12 +60,15 @@ inline ParamsLayout params_layout(int d, int m) {
   L.ak = o; o += 32;
   L.av = o; o += 32;
   L.shd = o; o += 4ull * m * d;
+  o = (o + 255) & ~255ull;
+  L.tk = o; o += (sizeof(TreeTab) + 255) & ~static_cast<uint64_t>(255);
+  L.tv = o; o += (sizeof(TreeTab) + 255) & ~static_cast<uint64_t>(255);
   L.total = (o + 255) & ~255ull;
   return L;
 }
 
 // Codec ids (mirror tq.h; kernels are compiled without it).
-enum { RAW_F32 = 0, POLAR = 1, POLAR_QJL = 2, Q8_BLOCK32 = 3 };
+enum { RAW_F32 = 0, POLAR = 1, POLAR_QJL = 2, Q8_BLOCK32 = 3, POLAR_TREE = 4 };
 enum { IN_F32 = 0, IN_BF16 = 1, IN_F16 = 2 };
 
 struct Tables {
@@ -68,6 +83,8 @@ struct Tables {
   const float* ak;
   const float* av;
   const float* shd;  // [d][m]
+  const TreeTab* tk;
+  const TreeTab* tv;
 };
 
 struct QuantArgs {
@@ -129,5 +146,8 @@ int decode_mfma_groups(int k_codec);
 constexpr int kMfmaUnitWorkgroups = 512;
 constexpr int kValuWorkgroups = 512;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+// Append for tensors stored with the recursive polar codec (the other kernel
+// skips them).
+hipError_t launch_quantize_tree(const QuantArgs& a, hipStream_t stream);
 
 }  // namespace tq

@@ -450,7 +450,7 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
     // -------------------------------------------------------- values
     load_row(a.v_new, in_idx, a.in_dtype, v);
     if constexpr (VB == 0) {
-      if (valid) {
+      if (valid && a.v_codec == RAW_F32) {   // recursive polar values have their own kernel
         float4* row = reinterpret_cast<float4*>(reinterpret_cast<float*>(u.vblk) + t * kD + 32 * g);
 #pragma unroll
         for (int i = 0; i < 8; ++i) row[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -560,6 +560,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
   const int total = a.batch * a.n_kv * a.groups_per_seq;
   if (total <= 0 || a.n_new <= 0) return hipSuccess;
   const int grid = (total + kWavesPerWg - 1) / kWavesPerWg;
+  // recursive polar tensors have their own kernel: with K stored that way the
+  // K part below matches no branch and writes nothing
+  if (a.k_codec == POLAR_TREE && a.v_codec == POLAR_TREE) return hipSuccess;
   if (a.k_codec == POLAR_QJL) {
     switch (a.k_bits) {
       case 2: return launch_k<2, true>(a, grid, stream);

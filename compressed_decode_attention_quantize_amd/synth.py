@@ -18,7 +18,7 @@ import dataclasses
 import torch
 
 # codec names shared by both sides; each side maps them to its own ids
-RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32 = "raw_f32", "polar", "polar_qjl", "q8_block32"
+RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32, POLAR_TREE = "raw_f32", "polar", "polar_qjl", "q8_block32", "polar_tree"
 
 
 @dataclasses.dataclass(frozen=True)

@@ -18,12 +18,12 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 ABI_VERSION = 1
 BLOCK_TOKENS = 128
 OK, EINVAL, EUNSUPPORTED, ECAPACITY, EWORKSPACE, EDEVICE = range(6)
-RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32 = range(4)
+RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32, POLAR_TREE = range(5)
 F32, BF16, F16 = range(3)
 DEQ_QJL = 1
 
 CODEC_IDS = {synth.RAW_F32: RAW_F32, synth.POLAR: POLAR, synth.POLAR_QJL: POLAR_QJL,
-             synth.Q8_BLOCK32: Q8_BLOCK32}
+             synth.Q8_BLOCK32: Q8_BLOCK32, synth.POLAR_TREE: POLAR_TREE}
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 

@@ -59,8 +59,12 @@ typedef enum {
   TQ_CODEC_RAW_F32 = 0,     /* bypass: fp32 copy (exact attention) */
   TQ_CODEC_POLAR = 1,       /* rotation + fp16 radius + b-bit angle codes */
   TQ_CODEC_POLAR_QJL = 2,   /* POLAR + 1-bit QJL sketch of the residual (K only) */
-  TQ_CODEC_Q8_BLOCK32 = 3   /* 8-bit symmetric per-32 block, fp16 scale, unrotated
+  TQ_CODEC_Q8_BLOCK32 = 3,  /* 8-bit symmetric per-32 block, fp16 scale, unrotated
                                (the article's "K in q8_0"; K only) */
+  TQ_CODEC_POLAR_TREE = 4   /* the PolarQuant paragraph's Cartesian-to-polar step
+                               taken literally: rotation + fp16 radius + 127
+                               angles of a pairwise tree (K or V, b = 2..4 bits
+                               per coordinate on average, no QJL) */
 } tq_codec;
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
@@ -78,8 +82,8 @@ typedef struct tq_config {
   int32_t k_codec;        /* tq_codec */
   int32_t k_bits;         /* POLAR*: 2..4; Q8: 8; RAW: 32 */
   int32_t qjl_m;          /* POLAR_QJL: sketch rows (128); otherwise 0 */
-  int32_t v_codec;        /* TQ_CODEC_RAW_F32 or TQ_CODEC_POLAR */
-  int32_t v_bits;         /* POLAR: 2..4; RAW: 32 */
+  int32_t v_codec;        /* TQ_CODEC_RAW_F32, TQ_CODEC_POLAR or TQ_CODEC_POLAR_TREE */
+  int32_t v_bits;         /* POLAR*: 2..4; RAW: 32 */
   int32_t decode_chunk;   /* positions per split-K workgroup, a multiple of 128; 0 = automatic */
   uint64_t seed;          /* rotation signs and sketch are drawn from (seed, layer) */
   int32_t layer;
@@ -112,6 +116,15 @@ const char* tq_status_string(tq_status s);
  *   V POLAR (b bits): b planes u32[4][d] (bit e of word [j][i] = bit p of the
  *     code of coordinate i of position 32j+e), then fp16 radius[128] at s(t);
  *   RAW: fp32[128][d].
+ *   POLAR_TREE (b bits): 127 angle codes per position in heap slots a = 1..d-1
+ *     (slot d/2 + i = level-1 pair i, slot 2^(L-l) + k = node k of level l,
+ *     L = log2 d; slot 0 unused); level-1 codes have b + 1 bits, the others
+ *     b - 1.  K: b - 1 planes u32[d/32][128] (bit e of word [j][s(t)] = bit p
+ *     of slot 32j+e's code), then 2 planes u32[d/64][128] for bits b - 1 and
+ *     b of slots d/2 + 32j + e, then fp16 radius[128] at s(t).  V: b - 1 planes
+ *     u32[4][d] (bit e of word [j][a] = bit p of slot a's code of position
+ *     32j+e), then 2 planes u32[4][d/2] (word [j][a - d/2]), then fp16
+ *     radius[128] at s(t).  Same record size as POLAR with b bits.
  * Here t is the position inside its block and s(t) = 32(t/32) + 8(t%4) +
  * (t%32)/4, a fixed permutation inside each group of 32 positions.
  * Per position and head: K 3b+QJL 68 B, 4b+QJL 84 B, q8 136 B; V b bits
@@ -148,7 +161,11 @@ tq_status tq_init_params(const tq_config* cfg, void* params, uint64_t bytes, voi
  * n = |x| -> fp16, angle codes = nearest codebook centroid of y/n (bit
  * planes); keys with QJL add r = y - n16 C[code], its norm |r|/sqrt(d) ->
  * fp16 and the m sign bits of S r.  Q8 keys and RAW tensors are stored as
- * described at tq_cache_bytes.  Positions of a 32-position group that this
+ * described at tq_cache_bytes.  POLAR_TREE: the same y and radius, then the
+ * pairwise tree of y (level 1: angle of (y_2i, y_2i+1) on the circle, b + 1
+ * bits, uniform cells; level l >= 2: atan2 of the two child radii in
+ * [0, pi/2], b - 1 bits, Lloyd-Max for the law sin(2t)^(2^(l-1) - 1)); a code
+ * counts the boundaries below its angle.  Positions of a 32-position group that this
  * call does not write keep their bits.  n_new == 0 is a no-op that does not
  * examine the buffer pointers. */
 tq_status tq_quantize_append(const tq_config* cfg, const void* params, void* k_cache,

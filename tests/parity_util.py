@@ -7,6 +7,8 @@ Bars:
   QJL sign bits: bit-exact except entries whose oracle sketch value lies
     within 1e-5 of zero in units of the rotated residual norm, and at most
     1e-4 of all sign bits;
+  recursive polar angle codes: the same rule, for angles within 1e-5 rad of
+    a decision boundary (the wrap-around at 0 = 2 pi included);
   logits: |gpu - oracle| <= 1e-3 * max(|oracle|, rms of that head's logits);
   outputs: |gpu - oracle| <= 2e-3.
 """
@@ -70,10 +72,30 @@ def oracle_quantize_threaded(spec, P, k, v, n):
     return R
 
 
-def compare_records(spec, P, G, R, lens, x_k=None, label=""):
+def _tree_mismatches(spec, D, bits, Gc, Rc, sel, x, label):
+    """Angle codes of the recursive polar codec: equal except within the
+    band of a decision boundary (checked on the oracle's own margins)."""
+    diff = (Gc != Rc) & sel[:, None]
+    n_bad = int(diff.sum())
+    assert n_bad <= SIGN_FRACTION * int(sel.sum()) * spec.d + 1, f"{label}: {n_bad} angle codes differ"
+    if n_bad:
+        assert x is not None, f"{label}: angle codes differ and no inputs to check the band"
+        T = oracle.tree_tables(bits, spec.d)
+        for rec in np.unique(np.nonzero(diff)[0]):
+            h = rec % spec.n_kv
+            pos = (rec // spec.n_kv) % spec.max_ctx
+            b = rec // (spec.n_kv * spec.max_ctx)
+            r = oracle.quantize_tree(x[b, pos, h], D, T)
+            bad = np.nonzero(diff[rec])[0]
+            assert np.all(r["amargin"][bad] < SIGN_BAND), f"{label}: angle code outside the band"
+    return n_bad
+
+
+def compare_records(spec, P, G, R, lens, x_k=None, label="", x_v=None):
     """Compare GPU-unpacked records G with oracle records R over positions
-    [0, lens[b]).  x_k (numpy [batch][n][n_kv][d]) lets sign mismatches be
-    checked against the oracle's sketch margin.  Returns a stats dict."""
+    [0, lens[b]).  x_k, x_v (numpy [batch][n][n_kv][d]) let sign and angle
+    code mismatches be checked against the oracle's margins.  Returns a
+    stats dict."""
     sel = np.zeros(R.n, bool)
     for b in range(spec.batch):
         for pos in range(int(lens[b])):
@@ -99,6 +121,10 @@ def compare_records(spec, P, G, R, lens, x_k=None, label=""):
                 r = oracle.quantize_polar(x_k[b, pos, h], P.DK, P.ck16, P.kbounds, spec.k_bits, spec.m, P.S)
                 bad = np.nonzero(diff[rec])[0]
                 assert np.all(np.abs(r["z"][bad]) < SIGN_BAND * r["rrot"]), f"{label}: sign outside band"
+    if kc == oracle.POLAR_TREE:
+        assert np.array_equal(G.kn16[sel], R.kn16[sel]), f"{label}: key radii differ"
+        st["k_angle_mismatch"] = _tree_mismatches(spec, P.DK, spec.k_bits, G.kcodes, R.kcodes, sel, x_k,
+                                                  label + " keys")
     if kc == oracle.Q8_BLOCK32:
         assert np.array_equal(G.k8[sel], R.k8[sel]), f"{label}: q8 codes differ"
         assert np.array_equal(G.s16[sel], R.s16[sel]), f"{label}: q8 scales differ"
@@ -107,6 +133,10 @@ def compare_records(spec, P, G, R, lens, x_k=None, label=""):
     if vc == oracle.POLAR:
         assert np.array_equal(G.vcodes[sel], R.vcodes[sel]), f"{label}: value codes differ"
         assert np.array_equal(G.vn16[sel], R.vn16[sel]), f"{label}: value radii differ"
+    elif vc == oracle.POLAR_TREE:
+        assert np.array_equal(G.vn16[sel], R.vn16[sel]), f"{label}: value radii differ"
+        st["v_angle_mismatch"] = _tree_mismatches(spec, P.DV, spec.v_bits, G.vcodes, R.vcodes, sel, x_v,
+                                                  label + " values")
     else:
         assert np.array_equal(G.vraw[sel], R.vraw[sel])
     return st

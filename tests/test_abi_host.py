@@ -175,3 +175,51 @@ def test_dequantize_argument_checks(tq):
 def test_status_strings(tq):
     assert tq.status_string(tq.ECAPACITY) == "append exceeds cache capacity"
     assert tq.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 4), (3, 3), (4, 2)])
+def test_tree_tables_match_oracle_codebooks(tq, orc, kb, vb):
+    """Recursive polar tables of the parameter image (cos / sin of every
+    centroid angle, cos^2 / sin^2 of every boundary) against the oracle's
+    per-level codebooks, built with another quadrature."""
+    cfg = tq.make_config(k_codec=tq.POLAR_TREE, k_bits=kb, v_codec=tq.POLAR_TREE, v_bits=vb)
+    img = tq.params_host(cfg)
+    d = 128
+    off = 4 * d * 2 + 64 * 4 + 32 * 2          # signs, no sketch, the per-coordinate codebooks
+    tk = (off + 255) & ~255
+    for base, b in ((tk, kb), (tk + 2048, vb)):
+        raw = img[base: base + 1920]
+        cs1 = raw[0:256].view(np.float32).reshape(32, 2)
+        cs = raw[256:768].view(np.float32).reshape(8, 8, 2)
+        c2_1, s2_1 = raw[768:832].view(np.float64), raw[832:896].view(np.float64)
+        c2, s2 = raw[896:1408].view(np.float64).reshape(8, 8), raw[1408:1920].view(np.float64).reshape(8, 8)
+        c, _, _, _ = orc.angle_codebook(1, b + 1)
+        n1 = 1 << (b + 1)
+        assert np.allclose(cs1[:n1, 0], np.cos(c), atol=1e-7) and np.allclose(cs1[:n1, 1], np.sin(c), atol=1e-7)
+        per_q = n1 // 4
+        beta = (np.arange(1, per_q)) * (math.pi / 2) / per_q
+        assert np.allclose(c2_1[:per_q - 1], np.cos(beta) ** 2, atol=1e-15)
+        assert np.allclose(s2_1[:per_q - 1], np.sin(beta) ** 2, atol=1e-15)
+        for l in range(2, 8):
+            c, bnd, _, _ = orc.angle_codebook(l, b - 1)
+            nl = 1 << (b - 1)
+            assert np.allclose(cs[l, :nl, 0], np.cos(c), atol=2e-7), l
+            assert np.allclose(cs[l, :nl, 1], np.sin(c), atol=2e-7), l
+            assert np.allclose(c2[l, :nl - 1], np.cos(bnd) ** 2, atol=1e-11), l
+            assert np.allclose(s2[l, :nl - 1], np.sin(bnd) ** 2, atol=1e-11), l
+    n = ctypes.c_uint64()
+    assert tq.lib().tq_params_bytes(ctypes.byref(cfg), ctypes.byref(n)) == tq.OK and n.value == tk + 4096
+
+
+def test_tree_config_validation(tq):
+    k, v = ctypes.c_uint64(), ctypes.c_uint64()
+    for kw, status in [(dict(k_codec=tq.POLAR_TREE, k_bits=1), tq.EINVAL),
+                       (dict(k_codec=tq.POLAR_TREE, k_bits=5), tq.EUNSUPPORTED),
+                       (dict(v_codec=tq.POLAR_TREE, v_bits=1), tq.EINVAL),
+                       (dict(v_codec=tq.POLAR_TREE, v_bits=6), tq.EUNSUPPORTED),
+                       (dict(k_codec=tq.POLAR_TREE, k_bits=3), tq.OK)]:
+        cfg = tq.make_config(**kw)
+        assert tq.lib().tq_cache_bytes(ctypes.byref(cfg), ctypes.byref(k), ctypes.byref(v)) == status, kw
+    cfg = tq.make_config(k_codec=tq.POLAR_TREE, k_bits=3)
+    cfg.qjl_m = 128
+    assert tq.lib().tq_cache_bytes(ctypes.byref(cfg), ctypes.byref(k), ctypes.byref(v)) == tq.EINVAL
