@@ -151,6 +151,49 @@ def cpu_baseline(w, seed):
     }
 
 
+def serve_steps(args, w, layers, q, dev, tq, synth, seed, bytes_per_launch):
+    """Serving steps over the layer stack: step s appends one position per
+    sequence at length ctx + s to every layer and decodes q over ctx + s + 1
+    positions.  Lengths are prepared per step beforehand, so the timed region
+    holds only the library's launches."""
+    import torch
+    n_steps = args.steps
+    total = args.warmup + n_steps
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 3000)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    kn = torch.randn((total, w.batch, 1, w.n_kv, w.d), generator=g, device=dev).to(dt)
+    vn = torch.randn((total, w.batch, 1, w.n_kv, w.d), generator=g, device=dev).to(dt)
+    lens = [torch.full((w.batch,), w.ctx + s, dtype=torch.int32, device=dev) for s in range(total + 1)]
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        for L in layers:
+            if args.serve == "fused":
+                tq.append_decode(L.cfg, L.params, L.k_cache, L.v_cache, lens[s], w.ctx + s, kn[s], vn[s], q, out,
+                                 L.workspace)
+            else:
+                tq.quantize_append(L.cfg, L.params, L.k_cache, L.v_cache, lens[s], w.ctx + s, kn[s], vn[s])
+                tq.decode_attention(L.cfg, L.params, L.k_cache, L.v_cache, lens[s + 1], w.ctx + s + 1, q, out,
+                                    L.workspace)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(args.warmup, total):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_steps
+    return {"serve": {"mode": args.serve, "steps": n_steps, "ms_per_step_all_layers": round(ms, 4),
+                      "us_per_layer_step": round(ms * 1e3 / len(layers), 3),
+                      "tokens_per_s": round(w.batch / (ms / 1e3), 1),
+                      "decode_bytes_per_layer_step": bytes_per_launch}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +219,9 @@ def main():
     ap.add_argument("--tree-bits", default="", metavar="KB/VB",
                     help="store keys and values with the recursive polar codec at KB and VB bits instead of the "
                          "workload's codecs (e.g. 3/2)")
+    ap.add_argument("--serve", choices=["fused", "separate"], default="",
+                    help="time serving steps instead of bare decodes: each step appends one position per sequence "
+                         "to every layer and decodes over it, in one launch (fused) or two (separate)")
     args = ap.parse_args()
     if args.summarize_counters:
         res = summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.calibration_mib)
@@ -220,7 +266,9 @@ def main():
                                             tq.POLAR_TREE, tvb, 0, 42, l, args.sparse_v), dev, zero=False)
                   for l in range(n_layers)]
     else:
-        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v), dev, zero=False)
+        room = (args.warmup + args.steps) if args.serve else 0   # serving steps append past the prefill
+        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v, max_ctx=w.ctx + room), dev,
+                             zero=False)
                   for l in range(n_layers)]
     torch.cuda.synchronize()
 
@@ -324,7 +372,10 @@ def main():
         result["config"]["sparse_v"] = args.sparse_v
         result["config"]["focus_every"] = args.focus_every
         result["data"] = "synthetic, planted focus keys" if args.focus_every else "synthetic"
-    if not args.no_cpu_baseline and policy is None and not (args.sparse_v or args.focus_every or args.tree_bits):
+    if args.serve:
+        result.update(serve_steps(args, w, layers, q, dev, tq, synth, data_seed, bytes_per_launch))
+    if not args.no_cpu_baseline and policy is None and not (args.sparse_v or args.focus_every or args.tree_bits
+                                                            or args.serve):
         result["cpu_baseline"] = cpu_baseline(w, data_seed)
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const int G = a.group;
-  const int len = min(a.seq_lens[b], a.max_ctx);   // never read past the capacity
+  const int len = min(a.seq_lens[b] + a.len_add, a.max_ctx);   // never read past the capacity
   const float inv_sqrt_d = 0.08838834764831845f;   // 1/sqrt(128)
 
   // ---------------------------------------------------------- prologue

@@ -59,6 +59,9 @@
 
 #include "tq_device.h"
 #include "tq_internal.h"
+#include "tq_quant_unit.h"
+// the quantiser above is exact-rounding code; the decode below may contract
+#pragma clang fp contract(fast)
 
 namespace tq {
 namespace {
@@ -317,8 +320,53 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int hq0
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int KB, bool QJL, int VB, int NG>
-__global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) {
+// Serving step (a launch with a new position per sequence): the workgroups
+// whose split holds position len_in of (sequence b, KV head h) first store
+// that position's record, quantised by wavefront 0 exactly as the append
+// kernel quantises it (same per-group routine, S read from the parameter
+// image), and start their copies of the cache only afterwards.  With several
+// head groups per KV head each of them writes the same bytes.
+template <int KB, bool QJL, int VB>
+__device__ __forceinline__ void fused_append(const DecodeArgs& a, int b, int h, int len_in, int w, int lane) {
+  if (w == 0) {
+    QuantArgs qa{};
+    qa.tb = a.tb;
+    qa.kc = const_cast<uint8_t*>(a.kc);
+    qa.vc = const_cast<uint8_t*>(a.vc);
+    qa.seq_lens = a.seq_lens;
+    qa.k_new = a.k_new;
+    qa.v_new = a.v_new;
+    qa.in_dtype = a.in_dtype;
+    qa.batch = a.batch;
+    qa.n_kv = a.n_kv;
+    qa.max_ctx = a.max_ctx;
+    qa.n_blocks = a.n_blocks;
+    qa.n_new = 1;
+    qa.groups_per_seq = 2;
+    qa.k_codec = a.k_codec;
+    qa.k_bits = a.k_bits;
+    qa.v_codec = a.v_codec;
+    qa.v_bits = a.v_bits;
+    qa.k_block_bytes = a.k_block_bytes;
+    qa.v_block_bytes = a.v_block_bytes;
+    qunit::Unit u;
+    u.b = b;
+    u.h = h;
+    u.t0 = len_in;
+    u.t1 = len_in + 1;
+    u.grp = len_in >> 5;
+    const int64_t cslot = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks + len_in / kBlock;
+    u.kblk = qa.kc + cslot * a.k_block_bytes;
+    u.vblk = qa.vc + cslot * a.v_block_bytes;
+    qunit::quant_unit<(KB == 8 ? 0 : KB), VB, QJL, kD>(qa, u, a.tb.s, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the record's stores have completed
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale vector-cache lines of the block
+}
+
+template <int KB, bool QJL, int VB, int NG, bool FUSED>
+__device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   using F = Fmt<KB, QJL, VB, NG>;
   constexpr int kWaves = F::waves;
   constexpr bool KQ8 = F::q8;
@@ -406,7 +454,12 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
   // a scalar load: a vector load here would make the first wait for it also
   // wait for every query and table load issued before it
   typedef __attribute__((address_space(4))) const int cint;
-  const int len = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
+  const int len_in = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
+  if constexpr (FUSED) {
+    if (len_in < a.max_ctx && (len_in / kBlock) / a.chunk_blocks == split)
+      fused_append<KB, QJL, VB>(a, b, h, len_in, w, lane);
+  }
+  const int len = FUSED ? min(len_in + 1, a.max_ctx) : len_in;
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split * a.chunk_blocks;
   const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
@@ -887,12 +940,26 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) 
   merge_splits(a, b, hq0, G, counter, w, lane);
 }
 
+template <int KB, bool QJL, int VB, int NG>
+__global__ __launch_bounds__(256 * NG, 2) void decode_mfma_kernel(DecodeArgs a) {
+  decode_mfma_body<KB, QJL, VB, NG, false>(a);
+}
+
+// the serving step: the same decode, after the new position is stored
+template <int KB, bool QJL, int VB, int NG>
+__global__ __launch_bounds__(256 * NG, 2) void decode_append_kernel(DecodeArgs a) {
+  decode_mfma_body<KB, QJL, VB, NG, true>(a);
+}
+
 template <int KB, bool QJL, int VB>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * ((a.group + 3) / 4));
   constexpr int NG = (KB == 8) ? 1 : 2;   // as decode_mfma_groups
-  hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
+  if (a.k_new != nullptr)
+    hipLaunchKernelGGL((decode_append_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -479,6 +479,110 @@ int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
   return static_cast<int>(std::min<int64_t>(blocks, want_splits));
 }
 
+// ------------------------------------------------------ entry helpers
+
+// partials [batch][n_q][splits][kPartialStride] fp32, then the completion
+// counters [batch][n_kv][kMaxGroup / 4] u32, each 256-byte aligned
+uint64_t workspace_need(const tq_config* cfg, int32_t max_seq_len) {
+  const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
+  const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
+  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * (tq::kMaxGroup / 4) * 4;
+  return ((partial + 255) & ~255ull) + ((counters + 255) & ~255ull);
+}
+
+tq_status check_append(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, int32_t max_seq_len, const void* k_new, const void* v_new,
+                       int32_t in_dtype, int32_t n_new) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (n_new < 0 || max_seq_len < 0) return TQ_EINVAL;
+  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_EINVAL;
+  if (static_cast<int64_t>(max_seq_len) + n_new > cfg->max_ctx) return TQ_ECAPACITY;
+  if (n_new == 0) return TQ_OK;
+  if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr ||
+      k_new == nullptr || v_new == nullptr)
+    return TQ_EINVAL;
+  if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
+      !aligned(k_new, in_dtype == TQ_F32 ? 4 : 2) || !aligned(v_new, in_dtype == TQ_F32 ? 4 : 2))
+    return TQ_EINVAL;
+  return TQ_OK;
+}
+
+hipError_t launch_append(const tq_config* cfg, const void* params, void* k_cache, void* v_cache,
+                         const int32_t* seq_lens, const void* k_new, const void* v_new, int32_t in_dtype,
+                         int32_t n_new, hipStream_t stream) {
+  tq::QuantArgs a{};
+  a.tb = tables(cfg, params);
+  a.kc = static_cast<uint8_t*>(k_cache);
+  a.vc = static_cast<uint8_t*>(v_cache);
+  a.seq_lens = seq_lens;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.in_dtype = in_dtype;
+  a.batch = cfg->batch;
+  a.n_kv = cfg->n_kv_heads;
+  a.max_ctx = cfg->max_ctx;
+  a.n_blocks = n_blocks(cfg);
+  a.n_new = n_new;
+  a.groups_per_seq = (n_new + 31) / 32 + 1;
+  a.k_codec = cfg->k_codec;
+  a.k_bits = cfg->k_bits;
+  a.v_codec = cfg->v_codec;
+  a.v_bits = cfg->v_bits;
+  a.k_block_bytes = kBlock * k_record_bytes(cfg);
+  a.v_block_bytes = kBlock * v_record_bytes(cfg);
+  hipError_t e = tq::launch_quantize(a, stream);
+  if (e == hipSuccess && (cfg->k_codec == TQ_CODEC_POLAR_TREE || cfg->v_codec == TQ_CODEC_POLAR_TREE))
+    e = tq::launch_quantize_tree(a, stream);
+  return e;
+}
+
+// Checks and kernel arguments of a decode over lengths up to max_seq_len.
+tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int32_t max_seq_len, const float* q, float* out, float* logits,
+                         void* workspace, uint64_t workspace_bytes, tq::DecodeArgs* out_args) {
+  const tq_status st = check_cfg(cfg);
+  if (st != TQ_OK) return st;
+  if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr || q == nullptr ||
+      out == nullptr || workspace == nullptr)
+    return TQ_EINVAL;
+  if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
+      !aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256) || (logits && !aligned(logits, 4)))
+    return TQ_EINVAL;
+  if (max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
+  const int splits = decode_splits(cfg, max_seq_len);
+  const uint64_t partial =
+      static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * decode_splits_bound(cfg, max_seq_len) * tq::kPartialStride * 4;
+  if (workspace_bytes < workspace_need(cfg, max_seq_len)) return TQ_EWORKSPACE;
+  tq::DecodeArgs& a = *out_args;
+  a = tq::DecodeArgs{};
+  a.tb = tables(cfg, params);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.vc = static_cast<const uint8_t*>(v_cache);
+  a.seq_lens = seq_lens;
+  a.q = q;
+  a.out = out;
+  a.logits = logits;
+  a.partials = static_cast<float*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + ((partial + 255) & ~255ull));
+  a.batch = cfg->batch;
+  a.n_q = cfg->n_q_heads;
+  a.n_kv = cfg->n_kv_heads;
+  a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.max_ctx = cfg->max_ctx;
+  a.n_blocks = n_blocks(cfg);
+  a.chunk_blocks = decode_chunk_blocks(cfg, max_seq_len);
+  a.n_splits = splits;
+  a.k_codec = cfg->k_codec;
+  a.k_bits = cfg->k_bits;
+  a.v_codec = cfg->v_codec;
+  a.v_bits = cfg->v_bits;
+  a.sparse_v = cfg->sparse_v;
+  a.k_block_bytes = kBlock * k_record_bytes(cfg);
+  a.v_block_bytes = kBlock * v_record_bytes(cfg);
+  return TQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -539,41 +643,11 @@ tq_status tq_init_params(const tq_config* cfg, void* params, uint64_t bytes, voi
 tq_status tq_quantize_append(const tq_config* cfg, const void* params, void* k_cache, void* v_cache,
                              const int32_t* seq_lens, int32_t max_seq_len, const void* k_new,
                              const void* v_new, int32_t in_dtype, int32_t n_new, void* stream) {
-  const tq_status st = check_cfg(cfg);
-  if (st != TQ_OK) return st;
-  if (n_new < 0 || max_seq_len < 0) return TQ_EINVAL;
-  if (in_dtype != TQ_F32 && in_dtype != TQ_BF16 && in_dtype != TQ_F16) return TQ_EINVAL;
-  if (static_cast<int64_t>(max_seq_len) + n_new > cfg->max_ctx) return TQ_ECAPACITY;
-  if (n_new == 0) return TQ_OK;   // nothing to write; buffers are not examined
-  if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr ||
-      k_new == nullptr || v_new == nullptr)
-    return TQ_EINVAL;
-  if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
-      !aligned(k_new, in_dtype == TQ_F32 ? 4 : 2) || !aligned(v_new, in_dtype == TQ_F32 ? 4 : 2))
-    return TQ_EINVAL;
-  tq::QuantArgs a{};
-  a.tb = tables(cfg, params);
-  a.kc = static_cast<uint8_t*>(k_cache);
-  a.vc = static_cast<uint8_t*>(v_cache);
-  a.seq_lens = seq_lens;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.in_dtype = in_dtype;
-  a.batch = cfg->batch;
-  a.n_kv = cfg->n_kv_heads;
-  a.max_ctx = cfg->max_ctx;
-  a.n_blocks = n_blocks(cfg);
-  a.n_new = n_new;
-  a.groups_per_seq = (n_new + 31) / 32 + 1;
-  a.k_codec = cfg->k_codec;
-  a.k_bits = cfg->k_bits;
-  a.v_codec = cfg->v_codec;
-  a.v_bits = cfg->v_bits;
-  a.k_block_bytes = kBlock * k_record_bytes(cfg);
-  a.v_block_bytes = kBlock * v_record_bytes(cfg);
-  hipError_t e = tq::launch_quantize(a, static_cast<hipStream_t>(stream));
-  if (e == hipSuccess && (cfg->k_codec == TQ_CODEC_POLAR_TREE || cfg->v_codec == TQ_CODEC_POLAR_TREE))
-    e = tq::launch_quantize_tree(a, static_cast<hipStream_t>(stream));
+  const tq_status st = check_append(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, k_new, v_new, in_dtype,
+                                    n_new);
+  if (st != TQ_OK || n_new == 0) return st;   // n_new == 0: nothing to write, buffers not examined
+  const hipError_t e = launch_append(cfg, params, k_cache, v_cache, seq_lens, k_new, v_new, in_dtype, n_new,
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
 
@@ -581,10 +655,7 @@ tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, u
   const tq_status st = check_cfg(cfg);
   if (st != TQ_OK) return st;
   if (bytes == nullptr || max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
-  const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
-  const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
-  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * (tq::kMaxGroup / 4) * 4;
-  *bytes = ((partial + 255) & ~255ull) + ((counters + 255) & ~255ull);
+  *bytes = workspace_need(cfg, max_seq_len);
   return TQ_OK;
 }
 
@@ -592,48 +663,37 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
                               const void* v_cache, const int32_t* seq_lens, int32_t max_seq_len,
                               const float* q, float* out, float* logits, void* workspace,
                               uint64_t workspace_bytes, void* stream) {
-  const tq_status st = check_cfg(cfg);
-  if (st != TQ_OK) return st;
-  if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr || q == nullptr ||
-      out == nullptr || workspace == nullptr)
-    return TQ_EINVAL;
-  if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
-      !aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256) || (logits && !aligned(logits, 4)))
-    return TQ_EINVAL;
-  if (max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
-  uint64_t need = 0;
-  tq_decode_workspace_bytes(cfg, max_seq_len, &need);
-  if (workspace_bytes < need) return TQ_EWORKSPACE;
-  const int splits = decode_splits(cfg, max_seq_len);
-  const uint64_t partial =
-      static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * decode_splits_bound(cfg, max_seq_len) * tq::kPartialStride * 4;
   tq::DecodeArgs a{};
-  a.tb = tables(cfg, params);
-  a.kc = static_cast<const uint8_t*>(k_cache);
-  a.vc = static_cast<const uint8_t*>(v_cache);
-  a.seq_lens = seq_lens;
-  a.q = q;
-  a.out = out;
-  a.logits = logits;
-  a.partials = static_cast<float*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + ((partial + 255) & ~255ull));
-  a.batch = cfg->batch;
-  a.n_q = cfg->n_q_heads;
-  a.n_kv = cfg->n_kv_heads;
-  a.group = cfg->n_q_heads / cfg->n_kv_heads;
-  a.max_ctx = cfg->max_ctx;
-  a.n_blocks = n_blocks(cfg);
-  a.chunk_blocks = decode_chunk_blocks(cfg, max_seq_len);
-  a.n_splits = splits;
-  a.k_codec = cfg->k_codec;
-  a.k_bits = cfg->k_bits;
-  a.v_codec = cfg->v_codec;
-  a.v_bits = cfg->v_bits;
-  a.sparse_v = cfg->sparse_v;
-  a.k_block_bytes = kBlock * k_record_bytes(cfg);
-  a.v_block_bytes = kBlock * v_record_bytes(cfg);
+  const tq_status st = prepare_decode(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits, workspace,
+                                      workspace_bytes, &a);
+  if (st != TQ_OK) return st;
   hipError_t e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
+}
+
+tq_status tq_append_decode(const tq_config* cfg, const void* params, void* k_cache, void* v_cache,
+                           const int32_t* seq_lens, int32_t max_seq_len, const void* k_new, const void* v_new,
+                           int32_t in_dtype, const float* q, float* out, float* logits, void* workspace,
+                           uint64_t workspace_bytes, void* stream) {
+  tq_status st = check_append(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, k_new, v_new, in_dtype, 1);
+  if (st != TQ_OK) return st;
+  tq::DecodeArgs a{};
+  st = prepare_decode(cfg, params, k_cache, v_cache, seq_lens, max_seq_len + 1, q, out, logits, workspace,
+                      workspace_bytes, &a);
+  if (st != TQ_OK) return st;
+  a.len_add = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mfma_path(cfg)) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.in_dtype = in_dtype;
+    hipError_t e = tq::launch_decode_mfma(a, s);
+    if (e != hipErrorNotSupported) return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
+  }
+  // codecs the matrix-core kernel does not serve: the two launches in order
+  hipError_t e = launch_append(cfg, params, k_cache, v_cache, seq_lens, k_new, v_new, in_dtype, 1, s);
+  if (e == hipSuccess) e = tq::launch_decode(a, s);
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
 

@@ -116,6 +116,12 @@ struct DecodeArgs {
   int32_t k_codec, k_bits, v_codec, v_bits;
   int32_t sparse_v;   // 0, or skip value work of blocks below 2^-sparse_v of the running maximum
   int64_t k_block_bytes, v_block_bytes;
+  // serving step: one new position per sequence at seq_lens[b], [batch][1][n_kv][d]
+  // in in_dtype, stored before it is attended to (null: plain decode)
+  const void* k_new;
+  const void* v_new;
+  int32_t in_dtype;
+  int32_t len_add;    // positions attended = min(seq_lens[b] + len_add, max_ctx)
 };
 
 struct DequantArgs {

@@ -70,9 +70,11 @@ def lib() -> ctypes.CDLL:
                                           _vp, ctypes.c_uint64, _vp]
         L.tq_dequantize.argtypes = [_cfgp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, _vp, _vp, ctypes.c_uint32, _vp]
+        L.tq_append_decode.argtypes = [_cfgp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32,
+                                       _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp]
         for fn in ("tq_cache_bytes", "tq_params_bytes", "tq_params_host", "tq_init_params",
                    "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention",
-                   "tq_dequantize"):
+                   "tq_dequantize", "tq_append_decode"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,6 +185,25 @@ def decode_attention(cfg: Config, params, k_cache, v_cache, seq_lens, max_seq_le
                                      _stream(stream)), "tq_decode_attention")
 
 
+def append_decode(cfg: Config, params, k_cache, v_cache, seq_lens, max_seq_len: int, k_new, v_new, q, out,
+                  workspace, logits=None, stream=None):
+    """One serving step: k_new, v_new [batch][1][n_kv][d] stored at position
+    seq_lens[b] of every sequence, then q decoded over seq_lens[b] + 1
+    positions.  seq_lens is not advanced."""
+    dt = _DTYPES[k_new.dtype]
+    assert v_new.dtype == k_new.dtype and k_new.is_contiguous() and v_new.is_contiguous()
+    assert tuple(k_new.shape) == (cfg.batch, 1, cfg.n_kv_heads, cfg.head_dim) == tuple(v_new.shape)
+    assert q.dtype == torch.float32 and q.is_contiguous()
+    assert tuple(q.shape) == (cfg.batch, cfg.n_q_heads, cfg.head_dim)
+    assert out.dtype == torch.float32 and out.shape == q.shape and out.is_contiguous()
+    if logits is not None:
+        assert logits.dtype == torch.float32 and tuple(logits.shape) == (cfg.batch, cfg.n_q_heads, cfg.max_ctx)
+    _check(lib().tq_append_decode(ctypes.byref(cfg), _ptr(params), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                  int(max_seq_len), _ptr(k_new), _ptr(v_new), dt, _ptr(q), _ptr(out), _ptr(logits),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_append_decode")
+
+
 def dequantize(cfg: Config, params, k_cache, v_cache, b: int, start: int, count: int, k_out=None,
                v_out=None, qjl=False, stream=None):
     for t in (k_out, v_out):
@@ -223,4 +244,15 @@ class KVLayer:
             out = torch.empty_like(q)
         decode_attention(self.cfg, self.params, self.k_cache, self.v_cache, self.seq_lens, self.max_len, q,
                          out, self.workspace, logits, stream)
+        return out
+
+    def step(self, k_new, v_new, q, out=None, logits=None, stream=None):
+        """Serving step: store one new position per sequence and decode q
+        over the lengths that include it (one launch on the matrix-core path)."""
+        if out is None:
+            out = torch.empty_like(q)
+        append_decode(self.cfg, self.params, self.k_cache, self.v_cache, self.seq_lens, self.max_len, k_new,
+                      v_new, q, out, self.workspace, logits, stream)
+        self.seq_lens += 1
+        self.max_len += 1
         return out

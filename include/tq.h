@@ -193,6 +193,25 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
                               const float* q, float* out, float* logits, void* workspace,
                               uint64_t workspace_bytes, void* stream);
 
+/* Serving step in one launch: append one new position per sequence (at
+ * seq_lens[b], as tq_quantize_append with n_new = 1) and decode q over the
+ * seq_lens[b] + 1 positions that then exist (as tq_decode_attention).  The
+ * cache bytes and the outputs equal those of the two calls in that order.
+ *   seq_lens     device int32[batch], lengths before the append; read only
+ *                (the caller advances them)
+ *   max_seq_len  host bound on seq_lens[b]; TQ_ECAPACITY if max_seq_len + 1
+ *                passes max_ctx
+ *   k_new, v_new device [batch][1][n_kv][d] in in_dtype
+ *   workspace    >= tq_decode_workspace_bytes(cfg, max_seq_len + 1)
+ * The matrix-core decode (the codecs tq_config.sparse_v names) stores the new
+ * record from inside the decode launch: the workgroups whose split holds the
+ * new position quantise and store it before they read the cache.  Other
+ * codecs run the append and the decode as two launches on the stream. */
+tq_status tq_append_decode(const tq_config* cfg, const void* params, void* k_cache, void* v_cache,
+                           const int32_t* seq_lens, int32_t max_seq_len, const void* k_new, const void* v_new,
+                           int32_t in_dtype, const float* q, float* out, float* logits, void* workspace,
+                           uint64_t workspace_bytes, void* stream);
+
 /* Dequantise positions [start, start+count) of sequence b.
  *   k_out, v_out  device fp32 [count][n_kv][d]; either may be NULL
  *   flags         TQ_DEQ_QJL: keys return x_tilde = x_hat + rho sqrt(pi/2)/m

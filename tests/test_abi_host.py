@@ -25,7 +25,7 @@ def tq():
 def test_every_declared_symbol_is_exported(tq):
     hdr = open(os.path.join(ROOT, "include", "tq.h")).read()
     names = set(re.findall(r"^(?:tq_status|const char\*)\s+(tq_\w+)\(", hdr, re.M))
-    assert len(names) == 9
+    assert len(names) == 10
     L = tq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -152,6 +152,23 @@ def test_decode_argument_checks(tq):
     assert call(maxlen=4097) == tq.EINVAL
     assert call(q=None) == tq.EINVAL
     assert call(ws=p(FAKE + 64)) == tq.EINVAL
+
+
+def test_append_decode_argument_checks(tq):
+    L = tq.lib()
+    cfg = _cfg(tq, max_ctx=256)
+    need = tq.decode_workspace_bytes(cfg, 256)
+    p = ctypes.c_void_p
+
+    def call(maxlen=100, dt=tq.F32, ws_bytes=need, k=p(FAKE), q=p(FAKE)):
+        return L.tq_append_decode(ctypes.byref(cfg), p(FAKE), p(FAKE), p(FAKE), p(FAKE), maxlen, k, p(FAKE), dt,
+                                  q, p(FAKE), None, p(FAKE), ws_bytes, None)
+    assert call(maxlen=256) == tq.ECAPACITY          # the new position would pass max_ctx
+    assert call(maxlen=-1) == tq.EINVAL
+    assert call(dt=7) == tq.EINVAL
+    assert call(k=None) == tq.EINVAL
+    assert call(q=None) == tq.EINVAL
+    assert call(maxlen=255, ws_bytes=tq.decode_workspace_bytes(cfg, 255) - 1) == tq.EWORKSPACE
 
 
 def test_workspace_bound_covers_every_shorter_length(tq):
