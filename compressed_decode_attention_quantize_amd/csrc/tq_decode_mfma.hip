@@ -322,47 +322,40 @@ __device__ __forceinline__ void merge_splits(const DecodeArgs& a, int b, int hq0
 
 // Serving step (a launch with a new position per sequence): the workgroups
 // whose split holds position len_in of (sequence b, KV head h) first store
-// that position's record, quantised by wavefront 0 exactly as the append
-// kernel quantises it (same per-group routine, S read from the parameter
-// image), and start their copies of the cache only afterwards.  With several
-// head groups per KV head each of them writes the same bytes.
+// that position's record -- wavefront 0 its key, wavefront 1 its value, with
+// the append path's one-position quantiser -- and start their copies of the
+// cache only afterwards.  With several head groups per KV head each of them
+// writes the same bytes.
 template <int KB, bool QJL, int VB>
-__device__ __forceinline__ void fused_append(const DecodeArgs& a, int b, int h, int len_in, int w, int lane) {
-  if (w == 0) {
+__device__ __forceinline__ void fused_append(const DecodeArgs& a, int b, int h, int len_in, int w, int lane,
+                                             float* r_lds) {
+  if (w < 2) {
     QuantArgs qa{};
     qa.tb = a.tb;
-    qa.kc = const_cast<uint8_t*>(a.kc);
-    qa.vc = const_cast<uint8_t*>(a.vc);
-    qa.seq_lens = a.seq_lens;
     qa.k_new = a.k_new;
     qa.v_new = a.v_new;
     qa.in_dtype = a.in_dtype;
-    qa.batch = a.batch;
-    qa.n_kv = a.n_kv;
-    qa.max_ctx = a.max_ctx;
-    qa.n_blocks = a.n_blocks;
-    qa.n_new = 1;
-    qa.groups_per_seq = 2;
     qa.k_codec = a.k_codec;
     qa.k_bits = a.k_bits;
     qa.v_codec = a.v_codec;
     qa.v_bits = a.v_bits;
-    qa.k_block_bytes = a.k_block_bytes;
-    qa.v_block_bytes = a.v_block_bytes;
-    qunit::Unit u;
-    u.b = b;
-    u.h = h;
-    u.t0 = len_in;
-    u.t1 = len_in + 1;
-    u.grp = len_in >> 5;
     const int64_t cslot = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks + len_in / kBlock;
-    u.kblk = qa.kc + cslot * a.k_block_bytes;
-    u.vblk = qa.vc + cslot * a.v_block_bytes;
-    qunit::quant_unit<(KB == 8 ? 0 : KB), VB, QJL, kD>(qa, u, a.tb.s, lane);
+    const int64_t in_idx = (static_cast<int64_t>(b) * a.n_kv + h) * kD;   // [batch][1][n_kv][d]
+    if (w == 0) {
+      qunit::token_keys<(KB == 8 ? 0 : KB), QJL, kD>(qa, in_idx, const_cast<uint8_t*>(a.kc) + cslot * a.k_block_bytes,
+                                                     len_in % kBlock, a.tb.s, r_lds, lane);
+    } else {
+      qunit::token_values<VB>(qa, in_idx, const_cast<uint8_t*>(a.vc) + cslot * a.v_block_bytes, len_in % kBlock, lane);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the record's stores have completed
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale vector-cache lines of the block
+  // The record's stores went through this compute unit's write-through vector
+  // cache; dropping that cache's lines as well (a workgroup-scope invalidate,
+  // not the device-wide one an agent-scope acquire issues) leaves no stale
+  // copy of the block that another workgroup on this unit fetched earlier.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int KB, bool QJL, int VB, int NG, bool FUSED>
@@ -425,6 +418,15 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   const int G = min(4, a.group - 4 * hg);  // query heads served here
   const int hq0 = h * a.group + 4 * hg;    // the first of them
   uint32_t* const counter = a.counters + (static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg;
+  // a scalar load: a vector load here would make the first wait for it also
+  // wait for every query and table load issued before it
+  typedef __attribute__((address_space(4))) const int cint;
+  const int len_in = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
+  if constexpr (FUSED) {
+    // before anything else, so that nothing of the decode is live across it
+    if (len_in < a.max_ctx && (len_in / kBlock) / a.chunk_blocks == split)
+      fused_append<KB, QJL, VB>(a, b, h, len_in, w, lane, reinterpret_cast<float*>(junk));
+  }
   // loads the set-up needs are issued first, before the sequence length they
   // do not depend on: this wave's query rows, the rotation signs, its slice
   // of the sketch table, the codebook coefficients
@@ -450,14 +452,6 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
     const cfloat* akp = (const cfloat*)(a.tb.ak);
 #pragma unroll
     for (int T = 0; T < NTK; ++T) ak[T] = akp[T];
-  }
-  // a scalar load: a vector load here would make the first wait for it also
-  // wait for every query and table load issued before it
-  typedef __attribute__((address_space(4))) const int cint;
-  const int len_in = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
-  if constexpr (FUSED) {
-    if (len_in < a.max_ctx && (len_in / kBlock) / a.chunk_blocks == split)
-      fused_append<KB, QJL, VB>(a, b, h, len_in, w, lane);
   }
   const int len = FUSED ? min(len_in + 1, a.max_ctx) : len_in;
   const int nblk_seq = (len + kBlock - 1) / kBlock;

@@ -74,11 +74,50 @@ __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_e
   const int64_t slot = (static_cast<int64_t>(u.b) * a.n_kv + u.h) * a.n_blocks + blk;
   u.kblk = a.kc + slot * a.k_block_bytes;
   u.vblk = a.vc + slot * a.v_block_bytes;
-  quant_unit<KB, VB, QJL>(a, u, s_lds, lane);
+  SRows sr;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) sr.p[mt] = s_lds + 16 * mt * kSRow;
+  quant_unit<KB, VB, QJL>(a, u, sr, lane);
+}
+
+// One new position per sequence (serving appends): two wavefronts per
+// (sequence, KV head), the even one for its key, the odd one for its value.
+template <int KB, int VB, bool QJL>
+__global__ __launch_bounds__(256) void token_kernel(QuantArgs a) {
+  __shared__ __attribute__((aligned(16))) float r_lds[2][kD];   // residuals of the two key wavefronts
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int unit = blockIdx.x * 2 + (wave >> 1);
+  if (unit >= a.batch * a.n_kv) return;
+  const int h = unit % a.n_kv;
+  const int b = unit / a.n_kv;
+  const int pos = a.seq_lens[b];
+  if (pos >= a.max_ctx) return;
+  const int64_t cslot = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks + pos / kBlock;
+  const int64_t in_idx = (static_cast<int64_t>(b) * a.n_kv + h) * kD;
+  if ((wave & 1) == 0) {
+    token_keys<KB, QJL, kD>(a, in_idx, a.kc + cslot * a.k_block_bytes, pos % kBlock, a.tb.s, r_lds[wave >> 1], lane);
+  } else {
+    token_values<VB>(a, in_idx, a.vc + cslot * a.v_block_bytes, pos % kBlock, lane);
+  }
+}
+
+template <int KB, bool QJL>
+hipError_t launch_token(const QuantArgs& a, hipStream_t stream) {
+  const dim3 grid((a.batch * a.n_kv + 1) / 2), blk(256);
+  switch (a.v_codec == POLAR ? a.v_bits : 0) {
+    case 0: hipLaunchKernelGGL((token_kernel<KB, 0, QJL>), grid, blk, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((token_kernel<KB, 2, QJL>), grid, blk, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((token_kernel<KB, 3, QJL>), grid, blk, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((token_kernel<KB, 4, QJL>), grid, blk, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <int KB, bool QJL>
 hipError_t launch_k(const QuantArgs& a, int grid, hipStream_t stream) {
+  if (a.n_new == 1) return launch_token<KB, QJL>(a, stream);
   const dim3 blk(64 * kWavesPerWg);
   switch (a.v_codec == POLAR ? a.v_bits : 0) {
     case 0: hipLaunchKernelGGL((quant_kernel<KB, 0, QJL>), dim3(grid), blk, 0, stream, a); break;

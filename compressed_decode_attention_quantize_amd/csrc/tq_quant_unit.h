@@ -283,9 +283,14 @@ struct Unit {
 };
 
 // --------------------------------------------------------------- kernel
-// s_rows: S with row j (sketch row j) at s_rows + j * SROW (LDS or global)
+// Where S sits: its rows 16 mt .. 16 mt + 15 start at p[mt], SROW floats
+// apart (shared memory or global)
+struct SRows {
+  const float* p[8];
+};
+
 template <int KB, int VB, bool QJL, int SROW = kSRow>
-__device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds, int lane) {
+__device__ void quant_unit(const QuantArgs& a, const Unit& u, const SRows& s_rows, int lane) {
   constexpr bool kPolar = KB > 0;
   const int p = lane & 15;
   const int g = lane >> 4;
@@ -390,7 +395,7 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
         uint32_t neg[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          const float4* srow = reinterpret_cast<const float4*>(s_lds + (16 * mt + p) * SROW + 16 * g);
+          const float4* srow = reinterpret_cast<const float4*>(s_rows.p[mt] + p * SROW + 16 * g);
           float4 aq[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -483,6 +488,185 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const float* s_lds
         *w = keep ? ((*w & keep) | (nw & ~keep)) : nw;
       }
     }
+  }
+}
+
+// ------------------------------------------------------------ one position
+// A single new position of one (sequence, KV head) per wavefront (the
+// serving step's append): lane l holds coordinates l and l + 64.  Codes,
+// radii and residual norms are those of quant_unit bit for bit (the same
+// FWHT stage order, fp64 norm tree, thresholds, binary search and residual);
+// the QJL sketch is a per-lane fp32 dot product over the coordinates in
+// order, so a sign can differ from quant_unit's only where the sketch value
+// is within rounding of zero (a sign bit set, -0 included, counts as
+// negative in both).
+
+__device__ __forceinline__ float token_in(const void* p, int64_t idx, int dtype) {
+  if (dtype == IN_F32) return static_cast<const float*>(p)[idx];
+  const uint16_t h = static_cast<const uint16_t*>(p)[idx];
+  if (dtype == IN_BF16) return __uint_as_float(static_cast<uint32_t>(h) << 16);
+  return f16_to_f32(h);
+}
+
+// the format's fp64 tree of squares over (lo = coordinate l, hi = l + 64):
+// level 64 in the lane, then levels 32 .. 1 across lanes; every lane gets it
+__device__ __forceinline__ double token_sumsq(float lo, float hi) {
+  double s = static_cast<double>(lo) * static_cast<double>(lo) + static_cast<double>(hi) * static_cast<double>(hi);
+  s += lane_xor<32>(s);
+  s += lane_xor<16>(s);
+  s += lane_xor<8>(s);
+  s += lane_xor<4>(s);
+  s += lane_xor<2>(s);
+  s += lane_xor<1>(s);
+  return __shfl(s, 0, 64);
+}
+
+// Keys of one position: POLAR (KB bits, QJL sketch if QJL), q8 or RAW.
+// in_idx: element offset of the vector in k_new; t: position in its block.
+// S: sketch row j at S + j * SROW.  r_lds: 128 floats of shared memory owned
+// by this wavefront (QJL only).
+template <int KB, bool QJL, int SROW>
+__device__ void token_keys(const QuantArgs& a, int64_t in_idx, uint8_t* kblk, int t, const float* S, float* r_lds,
+                           int lane) {
+  const float x0 = token_in(a.k_new, in_idx + lane, a.in_dtype);
+  const float x1 = token_in(a.k_new, in_idx + lane + 64, a.in_dtype);
+  const int slot = slot_of(t);
+  if constexpr (KB == 0) {
+    if (a.k_codec == RAW_F32) {
+      float* row = reinterpret_cast<float*>(kblk) + t * kD;
+      row[lane] = x0;
+      row[lane + 64] = x1;
+    } else if (a.k_codec == Q8_BLOCK32) {
+      // per 32-coordinate block: lanes 0..31 / 32..63 hold blocks 0 / 1 (lo) and 2 / 3 (hi)
+      float m0 = fabsf(x0), m1 = fabsf(x1);
+      m0 = fmaxf(m0, lane_xor<1>(m0));
+      m1 = fmaxf(m1, lane_xor<1>(m1));
+      m0 = fmaxf(m0, lane_xor<2>(m0));
+      m1 = fmaxf(m1, lane_xor<2>(m1));
+      m0 = fmaxf(m0, lane_xor<4>(m0));
+      m1 = fmaxf(m1, lane_xor<4>(m1));
+      m0 = fmaxf(m0, lane_xor<8>(m0));
+      m1 = fmaxf(m1, lane_xor<8>(m1));
+      m0 = fmaxf(m0, lane_xor<16>(m0));
+      m1 = fmaxf(m1, lane_xor<16>(m1));
+      const uint16_t s0 = norm_to_f16(m0 / 127.0f), s1 = norm_to_f16(m1 / 127.0f);
+      const float f0 = f16_to_f32(s0), f1 = f16_to_f32(s1);
+      const int k0 = (f0 > 0.0f) ? static_cast<int>(fminf(fmaxf(rintf(x0 / f0), -127.0f), 127.0f)) : 0;
+      const int k1 = (f1 > 0.0f) ? static_cast<int>(fminf(fmaxf(rintf(x1 / f1), -127.0f), 127.0f)) : 0;
+      int8_t* row = reinterpret_cast<int8_t*>(kblk) + t * kD;
+      row[lane] = static_cast<int8_t>(k0);
+      row[lane + 64] = static_cast<int8_t>(k1);
+      uint16_t* sc = reinterpret_cast<uint16_t*>(kblk + kBlock * kD) + t * (kD / 32);
+      if ((lane & 31) == 0) {
+        sc[lane >> 5] = s0;
+        sc[2 + (lane >> 5)] = s1;
+      }
+    }
+  } else {
+    float kthr[15], kc[16];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) kthr[j] = (j < (1 << KB) - 1) ? a.tb.kb[j] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kc[j] = (j < (1 << KB)) ? a.tb.ck[j] : 0.0f;
+    const float n = static_cast<float>(sqrt(token_sumsq(x0, x1)));
+    const uint16_t n16 = norm_to_f16(n);
+    const float nf = f16_to_f32(n16);
+    float lo = a.tb.dk[lane] * x0, hi = a.tb.dk[lane + 64] * x1;
+    wave_fwht128(lo, hi, lane);
+    float thr[15];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) thr[j] = kthr[j] * n;
+    bool blo[4] = {false, false, false, false}, bhi[4] = {false, false, false, false};
+    code_bits<KB>(lo, thr, blo);
+    code_bits<KB>(hi, thr, bhi);
+    // token-major plane words: word j holds coordinates 32 j .. 32 j + 31
+    uint32_t* planes = reinterpret_cast<uint32_t*>(kblk);
+    const int plane_words = (kD / 32) * kBlock;
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      const uint64_t ml = __ballot(blo[q]), mh = __ballot(bhi[q]);
+      const uint32_t wsel = (lane & 2) ? static_cast<uint32_t>(((lane & 1) ? mh : ml) >> 32)
+                                       : static_cast<uint32_t>((lane & 1) ? mh : ml);
+      // lane 0: word 0, lane 1: word 2, lane 2: word 1, lane 3: word 3
+      if (lane < 4) planes[q * plane_words + ((lane & 1) * 2 + (lane >> 1)) * kBlock + slot] = wsel;
+    }
+    uint8_t* after = kblk + 4 * KB * plane_words;
+    if constexpr (QJL) {
+      const float rlo = fmaf(-nf, centroid<KB>(kc, blo), lo);
+      const float rhi = fmaf(-nf, centroid<KB>(kc, bhi), hi);
+      const float rho = static_cast<float>(sqrt(token_sumsq(rlo, rhi) / static_cast<double>(kD)));
+      r_lds[lane] = rlo;
+      r_lds[lane + 64] = rhi;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // sketch rows lane and lane + 64
+      const float* s0 = S + lane * SROW;
+      const float* s1 = S + (lane + 64) * SROW;
+      float z0 = 0.0f, z1 = 0.0f;
+#pragma unroll 4
+      for (int i = 0; i < kD; i += 4) {
+        const float4 r4 = *reinterpret_cast<const float4*>(r_lds + i);
+        const float4 a4 = *reinterpret_cast<const float4*>(s0 + i);
+        const float4 b4 = *reinterpret_cast<const float4*>(s1 + i);
+        z0 = fmaf(a4.x, r4.x, z0);
+        z0 = fmaf(a4.y, r4.y, z0);
+        z0 = fmaf(a4.z, r4.z, z0);
+        z0 = fmaf(a4.w, r4.w, z0);
+        z1 = fmaf(b4.x, r4.x, z1);
+        z1 = fmaf(b4.y, r4.y, z1);
+        z1 = fmaf(b4.z, r4.z, z1);
+        z1 = fmaf(b4.w, r4.w, z1);
+      }
+      const uint64_t p0 = __ballot((__float_as_uint(z0) >> 31) == 0u);
+      const uint64_t p1 = __ballot((__float_as_uint(z1) >> 31) == 0u);
+      uint32_t* sgn = reinterpret_cast<uint32_t*>(after);
+      const uint32_t wsel = (lane & 2) ? static_cast<uint32_t>(((lane & 1) ? p1 : p0) >> 32)
+                                       : static_cast<uint32_t>((lane & 1) ? p1 : p0);
+      if (lane < 4) sgn[((lane & 1) * 2 + (lane >> 1)) * kBlock + slot] = wsel;
+      after += 4 * (kM / 32) * kBlock;
+      if (lane == 0) reinterpret_cast<uint16_t*>(after + 2 * kBlock)[slot] = norm_to_f16(rho);
+    }
+    if (lane == 0) reinterpret_cast<uint16_t*>(after)[slot] = n16;
+  }
+}
+
+// Values of one position: POLAR (VB bits) or RAW.  Coordinate-major words:
+// each lane rewrites the bit of this position in its two coordinates' words.
+template <int VB>
+__device__ void token_values(const QuantArgs& a, int64_t in_idx, uint8_t* vblk, int t, int lane) {
+  const float x0 = token_in(a.v_new, in_idx + lane, a.in_dtype);
+  const float x1 = token_in(a.v_new, in_idx + lane + 64, a.in_dtype);
+  if constexpr (VB == 0) {
+    if (a.v_codec == RAW_F32) {
+      float* row = reinterpret_cast<float*>(vblk) + t * kD;
+      row[lane] = x0;
+      row[lane + 64] = x1;
+    }
+  } else {
+    float vthr[15];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) vthr[j] = (j < (1 << VB) - 1) ? a.tb.vb[j] : 0.0f;
+    const float n = static_cast<float>(sqrt(token_sumsq(x0, x1)));
+    float lo = a.tb.dv[lane] * x0, hi = a.tb.dv[lane + 64] * x1;
+    wave_fwht128(lo, hi, lane);
+    float thr[15];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) thr[j] = vthr[j] * n;
+    bool blo[4] = {false, false, false, false}, bhi[4] = {false, false, false, false};
+    code_bits<VB>(lo, thr, blo);
+    code_bits<VB>(hi, thr, bhi);
+    uint32_t* planes = reinterpret_cast<uint32_t*>(vblk);
+    const int j = t >> 5, e = t & 31;
+    const uint32_t bitm = 1u << e;
+#pragma unroll
+    for (int q = 0; q < VB; ++q) {
+      uint32_t* w0 = planes + q * 4 * kD + j * kD + lane;
+      uint32_t* w1 = w0 + 64;
+      *w0 = (*w0 & ~bitm) | (blo[q] ? bitm : 0u);
+      *w1 = (*w1 & ~bitm) | (bhi[q] ? bitm : 0u);
+    }
+    if (lane == 0) reinterpret_cast<uint16_t*>(vblk + 4 * VB * 4 * kD)[slot_of(t)] = norm_to_f16(n);
   }
 }
 

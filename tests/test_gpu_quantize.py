@@ -104,20 +104,68 @@ def test_offset_append_keeps_other_positions(wname):
 
 
 def test_incremental_equals_one_shot():
+    """Appends of many sizes equal one append of everything: every field bit
+    for bit, except QJL sign bits, where the one-position appends (their own
+    kernel, a per-lane sketch sum) may differ from the 16-position tiles only
+    within the sign band; both caches are checked against the oracle."""
     w = synth.WORKLOADS["serving_b16_ctx8k"]
     ws = synth.with_ctx(w, 520, batch=3)
     cfg = tq.config_for(ws, seed=42, layer=0)
     A, B = tq.KVLayer(cfg, DEV), tq.KVLayer(cfg, DEV)
     k, v = synth.make_kv(ws, 520, seed=11, batch=3)
-    k, v = k.to(DEV), v.to(DEV)
-    A.append(k, v)
+    kd, vd = k.to(DEV), v.to(DEV)
+    A.append(kd, vd)
     pos = 0
     for n in (3, 29, 64, 1, 1, 200, 95, 127):
-        B.append(k[:, pos:pos + n].contiguous(), v[:, pos:pos + n].contiguous())
+        B.append(kd[:, pos:pos + n].contiguous(), vd[:, pos:pos + n].contiguous())
         pos += n
     torch.cuda.synchronize()
     assert pos == 520
-    assert torch.equal(A.k_cache, B.k_cache) and torch.equal(A.v_cache, B.v_cache)
+    assert torch.equal(A.v_cache, B.v_cache)
+    spec = spec_of(cfg)
+    GA = gpu_records(spec, A.k_cache, A.v_cache, [520] * 3)
+    GB = gpu_records(spec, B.k_cache, B.v_cache, [520] * 3)
+    for name in ("kcodes", "kn16", "rho16"):
+        assert np.array_equal(getattr(GA, name), getattr(GB, name)), name
+    P = oracle.Params(spec, 42, 0)
+    kn, vn = widen_np(k), widen_np(v)
+    R = oracle_quantize(spec, P, kn, vn, [520] * 3)
+    compare_records(spec, P, GA, R, [520] * 3, kn, "one shot")
+    compare_records(spec, P, GB, R, [520] * 3, kn, "incremental")
+
+
+@pytest.mark.parametrize("codecs", [(tq.POLAR_QJL, 3, tq.POLAR, 2), (tq.POLAR_QJL, 4, tq.POLAR, 4),
+                                    (tq.POLAR, 2, tq.POLAR, 3), (tq.Q8_BLOCK32, 8, tq.POLAR, 4),
+                                    (tq.RAW_F32, 32, tq.RAW_F32, 32), (tq.POLAR_QJL, 2, tq.RAW_F32, 32)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_single_position_appends_match_oracle(codecs, dtype):
+    """The one-position append (its own kernel): five sequences at ragged
+    lengths, 40 appends of one position each, against the oracle."""
+    kc_, kb_, vc_, vb_ = codecs
+    cfg = tq.make_config(n_q_heads=32, n_kv_heads=8, batch=5, max_ctx=400, k_codec=kc_, k_bits=kb_, v_codec=vc_,
+                         v_bits=vb_, seed=42, layer=2)
+    L = tq.KVLayer(cfg, DEV)
+    g = torch.Generator().manual_seed(kb_ * 10 + vb_)
+    n0 = [0, 31, 32, 127, 300]
+    k = (torch.randn((5, 340, 8, 128), generator=g) * 2.0).to(dtype)
+    v = torch.randn((5, 340, 8, 128), generator=g).to(dtype)
+    L.append(k[:, :300].to(DEV).contiguous(), v[:, :300].to(DEV).contiguous())
+    L.seq_lens.copy_(torch.tensor(n0, dtype=torch.int32, device=DEV))
+    L.max_len = 300
+    lens = list(n0)
+    for s in range(40):
+        idx = torch.tensor(lens)
+        kn = k[torch.arange(5), idx].unsqueeze(1).contiguous().to(DEV)
+        vn = v[torch.arange(5), idx].unsqueeze(1).contiguous().to(DEV)
+        L.append(kn, vn)
+        lens = [n + 1 for n in lens]
+    torch.cuda.synchronize()
+    spec = spec_of(cfg)
+    P = oracle.Params(spec, 42, 2)
+    kn_, vn_ = widen_np(k), widen_np(v)
+    R = oracle_quantize(spec, P, kn_, vn_, lens)
+    G = gpu_records(spec, L.k_cache, L.v_cache, lens)
+    print(compare_records(spec, P, G, R, lens, kn_, f"single {codecs}"))
 
 
 def test_capacity_and_noop():
