@@ -42,7 +42,6 @@ namespace tq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kHeadsPerThread = kMaxGroup / 2;
 
 // Recursive polar: (cos, sin) of the centroid angles, level 1 at [0][code],
 // level l >= 2 at [l][code].
@@ -69,10 +68,9 @@ __device__ __forceinline__ int tree_key_code(const uint32_t (&w)[3][4], const ui
 
 // dot[h] += <q_raw, u> over the subtree of level-6 node N6 (coordinates
 // 64 N6 .. 64 N6 + 63), its weight w6 being the root's cos or sin
-template <int N6>
+template <int N6, int HPT>
 __device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int nb1,
-                                              const TreeLds& tab, const float* qv, int hpar, int G,
-                                              float (&dot)[kHeadsPerThread]) {
+                                              const TreeLds& tab, const float* qv, int hpar, float (&dot)[HPT]) {
   const float2 c6 = tab.up[6][tree_key_code<0>(w, x, nb1, 2 + N6)];
 #pragma unroll 1
   for (int n5 = 2 * N6; n5 < 2 * N6 + 2; ++n5) {
@@ -98,12 +96,9 @@ __device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4
             const float2 cs = tab.l1[tree_key_code<2 + N6>(w, x, nb1, i & 31)];
             const float a0 = w1 * cs.x, a1 = w1 * cs.y;
 #pragma unroll
-            for (int u = 0; u < kHeadsPerThread; ++u) {
-              const int g = hpar + 2 * u;
-              if (g < G) {
-                const float2 q2 = *reinterpret_cast<const float2*>(qv + g * kD + 2 * i);
-                dot[u] = fmaf(q2.x, a0, fmaf(q2.y, a1, dot[u]));
-              }
+            for (int u = 0; u < HPT; ++u) {
+              const float2 q2 = *reinterpret_cast<const float2*>(qv + (hpar + 2 * u) * kD + 2 * i);
+              dot[u] = fmaf(q2.x, a0, fmaf(q2.y, a1, dot[u]));
             }
           }
         }
@@ -125,6 +120,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// HPT: query heads per thread, ceil(G / 2) rounded up to a power of two.  The
+// inner loops run over all HPT heads without a test: rows past the group
+// read shared memory that is allocated but holds no head, and their
+// accumulators are never written out (a branch per head per element made
+// every shared-memory read wait for its result).
+// TVB: bits of recursive polar values (0: other value codecs).
+template <int HPT, int TVB>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ float qv[kMaxGroup * kD];   // q (or q_raw) per head
   __shared__ float sq[kMaxGroup * kM];   // S q_raw / sqrt(d) per head
@@ -184,9 +186,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // accumulators: thread owns coordinate i = tid % 128 for heads g = tid/128 + 2u
   const int ci = tid & (kD - 1);
   const int hpar = tid >> 7;
-  float acc[kMaxGroup / 2];
+  float acc[HPT];
 #pragma unroll
-  for (int u = 0; u < kMaxGroup / 2; ++u) acc[u] = 0.0f;
+  for (int u = 0; u < HPT; ++u) acc[u] = 0.0f;
+
+  // recursive polar values: this coordinate's factor of each code at levels 2..7
+  float vf[6][TVB > 0 ? (1 << (TVB - 1)) : 1];
+  if constexpr (TVB > 0) {
+#pragma unroll
+    for (int l = 2; l <= 7; ++l)
+#pragma unroll
+      for (int c = 0; c < (1 << (TVB - 1)); ++c) {
+        const float2 cs = vtree.up[l][c];
+        vf[l - 2][c] = ((ci >> (l - 1)) & 1) ? cs.y : cs.x;
+      }
+  }
 
   const int blk0 = split * a.chunk_blocks;
   const int nblk_seq = (len + kBlock - 1) / kBlock;
@@ -204,21 +218,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // ------------------------------------------------------- logits
     {
       const int t = tid & (kBlock - 1);
-      float lg[kMaxGroup / 2];
+      float lg[HPT];
 #pragma unroll
-      for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = 0.0f;
+      for (int u = 0; u < HPT; ++u) lg[u] = 0.0f;
       if (t < n_t) {
         if (a.k_codec == POLAR || a.k_codec == POLAR_QJL) {
           const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
           const int plane_words = (kD / 32) * kBlock;
-          float cdot[kMaxGroup / 2], sdot[kMaxGroup / 2];
+          float cdot[HPT], sdot[HPT];
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) cdot[u] = sdot[u] = 0.0f;
+          for (int u = 0; u < HPT; ++u) cdot[u] = sdot[u] = 0.0f;
+#pragma unroll 1
           for (int j = 0; j < kD / 32; ++j) {
             uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
             for (int p = 0; p < 4; ++p)
               if (p < kbits) w[p] = planes[p * plane_words + j * kBlock + slot_of(t)];
+#pragma unroll 8
             for (int e = 0; e < 32; ++e) {
               int c = 0;
 #pragma unroll
@@ -226,28 +242,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
               const float cv = kcb[c];
               const int i = j * 32 + e;
 #pragma unroll
-              for (int u = 0; u < kMaxGroup / 2; ++u) {
-                const int g = hpar + 2 * u;
-                if (g < G) cdot[u] = fmaf(qv[g * kD + i], cv, cdot[u]);
-              }
+              for (int u = 0; u < HPT; ++u) cdot[u] = fmaf(qv[(hpar + 2 * u) * kD + i], cv, cdot[u]);
             }
           }
           const uint8_t* after = kb + 4 * kbits * plane_words;
           float rho = 0.0f;
           if (a.k_codec == POLAR_QJL) {
             const uint32_t* sg = reinterpret_cast<const uint32_t*>(after);
+#pragma unroll 1
             for (int j = 0; j < kM / 32; ++j) {
               const uint32_t w = sg[j * kBlock + slot_of(t)];
+#pragma unroll 8
               for (int e = 0; e < 32; ++e) {
                 const bool pos = (w >> e) & 1u;
                 const int r = j * 32 + e;
 #pragma unroll
-                for (int u = 0; u < kMaxGroup / 2; ++u) {
-                  const int g = hpar + 2 * u;
-                  if (g < G) {
-                    const float s = sq[g * kM + r];
-                    sdot[u] += pos ? s : -s;
-                  }
+                for (int u = 0; u < HPT; ++u) {
+                  const float s = sq[(hpar + 2 * u) * kM + r];
+                  sdot[u] += pos ? s : -s;
                 }
               }
             }
@@ -256,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           }
           const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(after)[slot_of(t)]);
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = alpha * n16 * cdot[u] + beta * rho * sdot[u];
+          for (int u = 0; u < HPT; ++u) lg[u] = alpha * n16 * cdot[u] + beta * rho * sdot[u];
         } else if (a.k_codec == POLAR_TREE) {
           const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
           const int sl = slot_of(t);
@@ -273,50 +285,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) x[k][j] = l1[(k * 2 + j) * kBlock + sl];
           const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
-          float dot[kHeadsPerThread] = {};
+          float dot[HPT] = {};
           const float2 c7 = ktree.up[7][tree_key_code<0>(w, x, nb1, 1)];
-          tree_half_dot<0>(c7.x, w, x, nb1, ktree, qv, hpar, G, dot);
-          tree_half_dot<1>(c7.y, w, x, nb1, ktree, qv, hpar, G, dot);
+          tree_half_dot<0, HPT>(c7.x, w, x, nb1, ktree, qv, hpar, dot);
+          tree_half_dot<1, HPT>(c7.y, w, x, nb1, ktree, qv, hpar, dot);
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = n16 * dot[u] * (1.0f / static_cast<float>(kD));
+          for (int u = 0; u < HPT; ++u) lg[u] = n16 * dot[u] * (1.0f / static_cast<float>(kD));
         } else if (a.k_codec == Q8_BLOCK32) {
           const int8_t* row = reinterpret_cast<const int8_t*>(kb) + t * kD;
           const uint16_t* sc = reinterpret_cast<const uint16_t*>(kb + kBlock * kD) + t * (kD / 32);
+#pragma unroll 1
           for (int blkq = 0; blkq < kD / 32; ++blkq) {
-            float part[kMaxGroup / 2];
+            float part[HPT];
 #pragma unroll
-            for (int u = 0; u < kMaxGroup / 2; ++u) part[u] = 0.0f;
+            for (int u = 0; u < HPT; ++u) part[u] = 0.0f;
+#pragma unroll 8
             for (int e = 0; e < 32; ++e) {
               const int i = blkq * 32 + e;
               const float kv = static_cast<float>(row[i]);
 #pragma unroll
-              for (int u = 0; u < kMaxGroup / 2; ++u) {
-                const int g = hpar + 2 * u;
-                if (g < G) part[u] = fmaf(qv[g * kD + i], kv, part[u]);
-              }
+              for (int u = 0; u < HPT; ++u) part[u] = fmaf(qv[(hpar + 2 * u) * kD + i], kv, part[u]);
             }
             const float s = f16_to_f32(sc[blkq]);
 #pragma unroll
-            for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] = fmaf(s, part[u], lg[u]);
+            for (int u = 0; u < HPT; ++u) lg[u] = fmaf(s, part[u], lg[u]);
           }
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] *= inv_sqrt_d;
+          for (int u = 0; u < HPT; ++u) lg[u] *= inv_sqrt_d;
         } else {
           const float* row = reinterpret_cast<const float*>(kb) + t * kD;
+#pragma unroll 8
           for (int i = 0; i < kD; ++i) {
             const float kv = row[i];
 #pragma unroll
-            for (int u = 0; u < kMaxGroup / 2; ++u) {
-              const int g = hpar + 2 * u;
-              if (g < G) lg[u] = fmaf(qv[g * kD + i], kv, lg[u]);
-            }
+            for (int u = 0; u < HPT; ++u) lg[u] = fmaf(qv[(hpar + 2 * u) * kD + i], kv, lg[u]);
           }
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) lg[u] *= inv_sqrt_d;
+          for (int u = 0; u < HPT; ++u) lg[u] *= inv_sqrt_d;
         }
       }
 #pragma unroll
-      for (int u = 0; u < kMaxGroup / 2; ++u) {
+      for (int u = 0; u < HPT; ++u) {
         const int g = hpar + 2 * u;
         if (g < G) {
           pt[g * kBlock + t] = (t < n_t) ? lg[u] : -INFINITY;
@@ -360,18 +369,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     // ----------------------------------------------------------- PV
 #pragma unroll
-    for (int u = 0; u < kMaxGroup / 2; ++u) {
-      const int g = hpar + 2 * u;
-      if (g < G) acc[u] *= scale[g];
-    }
+    for (int u = 0; u < HPT; ++u) acc[u] *= scale[hpar + 2 * u];
     if (a.v_codec == POLAR) {
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
+#pragma unroll 1
       for (int j = 0; j * 32 < n_t; ++j) {
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int p = 0; p < 4; ++p)
           if (p < vbits) w[p] = planes[p * 4 * kD + j * kD + ci];
         const int e_end = min(32, n_t - j * 32);
+#pragma unroll 4
         for (int e = 0; e < e_end; ++e) {
           int c = 0;
 #pragma unroll
@@ -379,36 +387,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           const float cv = vcb[c];
           const int t = j * 32 + e;
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) {
-            const int g = hpar + 2 * u;
-            if (g < G) acc[u] = fmaf(pt[g * kBlock + t], cv, acc[u]);
-          }
+          for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], cv, acc[u]);
         }
       }
-    } else if (a.v_codec == POLAR_TREE) {
+    } else if constexpr (TVB > 0) {
       // coordinate ci: its level-1 pair is slot 64 + ci / 2, its level-l
       // ancestor slot 2^(7 - l) + ci / 2^l; the factor is the sin of an
-      // ancestor's angle when ci lies in its right half, else the cos
+      // ancestor's angle when ci lies in its right half, else the cos.  The
+      // upper levels' factors of this coordinate sit in registers (vf) and
+      // are selected by the code bits; level 1 is a shared-memory lookup.
+      constexpr int nb1 = TVB - 1;
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
-      const int nb1 = vbits - 1;
       const uint32_t* l1 = planes + nb1 * 4 * kD;
+#pragma unroll 1
       for (int j = 0; j * 32 < n_t; ++j) {
-        uint32_t w[3][7] = {}, x[2];
+        uint32_t w[nb1][7], x[2];
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          if (p < nb1) {
-            w[p][0] = planes[(p * 4 + j) * kD + 64 + (ci >> 1)];
+        for (int p = 0; p < nb1; ++p) {
+          w[p][0] = planes[(p * 4 + j) * kD + 64 + (ci >> 1)];
 #pragma unroll
-            for (int l = 2; l <= 7; ++l) w[p][l - 1] = planes[(p * 4 + j) * kD + (1 << (7 - l)) + (ci >> l)];
-          }
+          for (int l = 2; l <= 7; ++l) w[p][l - 1] = planes[(p * 4 + j) * kD + (1 << (7 - l)) + (ci >> l)];
+        }
 #pragma unroll
         for (int k = 0; k < 2; ++k) x[k] = l1[(k * 4 + j) * (kD / 2) + (ci >> 1)];
         const int e_end = min(32, n_t - j * 32);
+#pragma unroll 4
         for (int e = 0; e < e_end; ++e) {
           int c = 0;
 #pragma unroll
-          for (int p = 0; p < 3; ++p)
-            if (p < nb1) c |= ((w[p][0] >> e) & 1u) << p;
+          for (int p = 0; p < nb1; ++p) c |= ((w[p][0] >> e) & 1u) << p;
           c |= ((x[0] >> e) & 1u) << nb1;
           c |= ((x[1] >> e) & 1u) << (nb1 + 1);
           const float2 cs1 = vtree.l1[c];
@@ -417,28 +424,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           for (int l = 2; l <= 7; ++l) {
             int cl = 0;
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-              if (p < nb1) cl |= ((w[p][l - 1] >> e) & 1u) << p;
-            const float2 cs = vtree.up[l][cl];
-            uval *= ((ci >> (l - 1)) & 1) ? cs.y : cs.x;
+            for (int p = 0; p < nb1; ++p) cl |= ((w[p][l - 1] >> e) & 1u) << p;
+            float f = vf[l - 2][0];
+#pragma unroll
+            for (int cc = 1; cc < (1 << nb1); ++cc) f = (cl == cc) ? vf[l - 2][cc] : f;
+            uval *= f;
           }
           const int t = j * 32 + e;
 #pragma unroll
-          for (int u = 0; u < kMaxGroup / 2; ++u) {
-            const int g = hpar + 2 * u;
-            if (g < G) acc[u] = fmaf(pt[g * kBlock + t], uval, acc[u]);
-          }
+          for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], uval, acc[u]);
         }
       }
     } else {
       const float* rows = reinterpret_cast<const float*>(vb);
+#pragma unroll 8
       for (int t = 0; t < n_t; ++t) {
         const float v = rows[t * kD + ci];
 #pragma unroll
-        for (int u = 0; u < kMaxGroup / 2; ++u) {
-          const int g = hpar + 2 * u;
-          if (g < G) acc[u] = fmaf(pt[g * kBlock + t], v, acc[u]);
-        }
+        for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], v, acc[u]);
       }
     }
     __syncthreads();
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // --------------------------------------------------------- partials
   const int64_t pstride = kPartialStride;
 #pragma unroll
-  for (int u = 0; u < kMaxGroup / 2; ++u) {
+  for (int u = 0; u < HPT; ++u) {
     const int g = hpar + 2 * u;
     if (g < G) {
       float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + g) * a.n_splits + split) * pstride;
@@ -463,12 +466,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   combine_splits(a, b, h, qv, kThreads);
 }
 
+template <int HPT>
+hipError_t launch_h(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.n_splits, a.n_kv, a.batch);
+  switch (a.v_codec == POLAR_TREE ? a.v_bits : 0) {
+    case 0: hipLaunchKernelGGL((decode_kernel<HPT, 0>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<HPT, 2>), grid, dim3(kThreads), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<HPT, 3>), grid, dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<HPT, 4>), grid, dim3(kThreads), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_splits, a.n_kv, a.batch);
-  hipLaunchKernelGGL(decode_kernel, grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  if (a.group <= 2) return launch_h<1>(a, stream);
+  if (a.group <= 4) return launch_h<2>(a, stream);
+  if (a.group <= 8) return launch_h<4>(a, stream);
+  return launch_h<8>(a, stream);
 }
 
 }  // namespace tq
