@@ -43,16 +43,21 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every unit and link libtq.so (always rebuilds)."""
+    """Compile every unit (in parallel) and link libtq.so (always rebuilds)."""
+    import concurrent.futures as cf
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    jobs = []
     for src, extra in UNITS:
         obj = os.path.join(BUILD, src + ".o")
-        cmd = [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
-        out = _run(cmd)
-        if verbose and out.strip():
-            print(out)
-        objs.append(obj)
+        jobs.append((obj, [HIPCC, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0")) or (os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as pool:
+        outs = list(pool.map(lambda j: _run(j[1]), jobs))
+    if verbose:
+        for out in outs:
+            if out.strip():
+                print(out)
+    objs = [obj for obj, _ in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

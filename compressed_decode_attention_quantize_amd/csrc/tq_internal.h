@@ -148,9 +148,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 int decode_mfma_groups(int k_codec);
 // Workgroups the automatic split count aims for: the matrix-core kernel fills
 // the 256 compute units of the target chip (512 / groups workgroups), the
-// VALU kernel runs about two 256-thread workgroups per compute unit.
+// VALU kernel runs about four 256-thread workgroups per compute unit (it is
+// latency-bound: more resident wavefronts hide more of it).
 constexpr int kMfmaUnitWorkgroups = 512;
-constexpr int kValuWorkgroups = 512;
+constexpr int kValuWorkgroups = 1024;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 // Append for tensors stored with the recursive polar codec (the other kernel
 // skips them).
