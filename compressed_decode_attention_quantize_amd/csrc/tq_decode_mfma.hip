@@ -16,7 +16,9 @@
 //    operation per 8 elements by leaving each bit where it lies and filling
 //    the other fields of its nibble (see expand_fp4_affine): the elements are
 //    affine in the signs, and the offset, one constant per head, is removed
-//    after the product.  Value words use the two-operation +/-1 form.
+//    after the product.  Value words take the same form; their offset
+//    depends on the probabilities of the step and is itself a matrix product
+//    (see the offset operand below).
 //  * The query side (q_raw = H D_K q and sq = S q_raw / sqrt d) is written as
 //    four base-32 fixed-point digits, integers in [-16, 16] that e4m3 holds
 //    exactly, with one E8M0 scale per digit (about 19 significant bits).  The
@@ -93,28 +95,16 @@ __device__ __forceinline__ uint32_t term_word(const uint32_t* w, int T) {
   return w[i0] ^ w[i1] ^ w[i2];
 }
 
-// 32 bits -> 32 fp4 elements of +/-1 (bit 1 -> +1.0 = 0x2, bit 0 -> -1.0 = 0xA);
-// element 8d + n holds bit 4n + d.  Dword d keeps bits 4n+3 of ~(w << (3-d))
-// (the sign bits) and ORs in 0x2 (magnitude 1): one shift and one v_bitop3
-// ((~a & c) | b, table 0xCE) per dword.
-__device__ __forceinline__ v8i expand_fp4(uint32_t w) {
-  constexpr uint32_t kSign = 0x88888888u, kOne = 0x22222222u;
-  v8i r;
-  r[0] = static_cast<int>(__builtin_amdgcn_bitop3_b32(w << 3, kOne, kSign, 0xCE));
-  r[1] = static_cast<int>(__builtin_amdgcn_bitop3_b32(w << 2, kOne, kSign, 0xCE));
-  r[2] = static_cast<int>(__builtin_amdgcn_bitop3_b32(w << 1, kOne, kSign, 0xCE));
-  r[3] = static_cast<int>(__builtin_amdgcn_bitop3_b32(w, kOne, kSign, 0xCE));
-  r[4] = r[5] = r[6] = r[7] = 0;
-  return r;
-}
-
 // 32 bits -> 32 fp4 elements with each bit used where it lies: element
 // 8d + n is nibble n of dword d and takes bit 4n + d of w into nibble field d,
 // the other fields fixed: d = 0 (mantissa) {4, 6}, d = 1 (low exponent bit)
 // {2, 4}, d = 2 (high exponent bit) {0, 2}, d = 3 (sign) {+1, -1}.  With
 // s = +1 for a set bit the element is 5 + s, 3 + s, 1 + s, -s: one AND(-OR) per
 // dword.  The matrix operand on the other side carries -1 on the d = 3
-// elements, and the offsets 5, 3, 1 are removed with one constant per head.
+// elements, and the offsets 5, 3, 1 are removed afterwards: for keys one
+// constant per head, for values the product of the step's probabilities with
+// a fixed operand (rows of all-one and all-zero words, whose mean is the
+// offset row 5, 3, 1, 0).
 // (w & m) | c as one v_and_or_b32; the mask rides in a scalar register and
 // the fill in a vector register (a three-operand instruction here takes no
 // literal), both set once outside the loops.
@@ -478,6 +468,12 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // Offset of the affine value operand: rows 0..7 of aoff are the all-one
+  // word, rows 8..15 the all-zero word, so lanes 0..31 of accO gather the
+  // all-one row's products and lanes 32..63 the all-zero row's; their mean
+  // is what every value row carries on top of its signed sum.
+  v4f accO = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u);
 
   {
     // The query set-up and the ring's first copies do not wait for the
@@ -753,8 +749,11 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
       float r1 = (p1 > 0.0f) ? p1 * h2f(vn >> 16) : 0.0f;
       const float pm = row_max16(fmaxf(r0, r1));
       const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
-      r0 = __builtin_amdgcn_ldexpf(r0, -s0);
-      r1 = __builtin_amdgcn_ldexpf(r1, -s0);
+      // k-slots 32wl + 2t + c meet the sign field of the affine value operand
+      // when t / 4 == 3: those digits carry the opposite sign
+      const float sgn = (t >= 12) ? -1.0f : 1.0f;
+      r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
+      r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
       uint32_t ebytes = 127u << 24;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -805,6 +804,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
           for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
+        accO *= fv;
       }
       // Sparse-V: a group block whose four wave references lie more than
       // tau_v below the running maximum for every head it serves holds only
@@ -835,8 +835,10 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
         for (int p = 0; p < VB; ++p)
           vw[p] = *reinterpret_cast<const uint32_t*>(vb + 4 * (p * 4 * kD + g4 * kD + 32 * wl + 16 * rr + t));
 #pragma unroll
-        for (int T = 0; T < NTV; ++T) accV[rr][T] = mfma_fp4_fp8(expand_fp4(term_word<VB>(vw, T)), Pv, accV[rr][T], scp);
+        for (int T = 0; T < NTV; ++T)
+          accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T)), Pv, accV[rr][T], scp);
       }
+      accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
     };
 
     // The barrier between part A of step i and part B: with three or more
@@ -891,12 +893,18 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
     if (t == 0) wred[w][g4] = ls;
     if (w == 0 && t == 0) mrun[g4] = m_a;
     const int hc = t >> 2;   // head of this lane's result column
+    // every term of column t carries the same offset, the code sum carries it
+    // times sum a_T
+    float avsum = 0.0f;
+#pragma unroll
+    for (int T = 0; T < NTV; ++T) avsum += av[T];
+    const float voff = avsum * 0.5f * (accO[0] + __shfl_xor(accO[0], 32, 64));
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s = 0.0f;
+        float s = -voff;
 #pragma unroll
         for (int T = 0; T < NTV; ++T) s = fmaf(av[T], accV[r][T][i], s);
         s += __shfl_xor(s, 1, 64);   // sum the 4 limb columns of head hc
@@ -949,7 +957,7 @@ template <int KB, bool QJL, int VB>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * ((a.group + 3) / 4));
-  constexpr int NG = (KB == 8) ? 1 : 2;   // as decode_mfma_groups
+  constexpr int NG = (KB == 8 || VB == 4) ? 1 : 2;   // as decode_mfma_groups
   if (a.k_new != nullptr)
     hipLaunchKernelGGL((decode_append_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
   else
@@ -969,9 +977,12 @@ hipError_t launch_v(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// q8 keys (large slots, three head groups per KV head at G = 12) run best as
-// two workgroups of one group per compute unit; the others as one of two.
-int decode_mfma_groups(int k_codec) { return k_codec == Q8_BLOCK32 ? 1 : 2; }
+// q8 keys (large slots, three head groups per KV head at G = 12) and
+// four-bit values (sixteen value products per step, every register in use)
+// run best as two workgroups of one group per compute unit; the others as
+// one workgroup of two groups (measured on the Llama-8B, 1M-context and
+// batched-serving layers).
+int decode_mfma_groups(int k_codec, int v_bits) { return (k_codec == Q8_BLOCK32 || v_bits == 4) ? 1 : 2; }
 
 bool decode_mfma_applies(int k_codec, int v_codec, int group) {
   return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL || k_codec == Q8_BLOCK32);

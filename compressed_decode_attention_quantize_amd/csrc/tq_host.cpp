@@ -442,7 +442,7 @@ bool mfma_path(const tq_config* c) {
 }
 
 int64_t target_workgroups(const tq_config* c) {
-  return mfma_path(c) ? tq::kMfmaUnitWorkgroups / tq::decode_mfma_groups(c->k_codec) : tq::kValuWorkgroups;
+  return mfma_path(c) ? tq::kMfmaUnitWorkgroups / tq::decode_mfma_groups(c->k_codec, c->v_bits) : tq::kValuWorkgroups;
 }
 
 // Independent (sequence, KV head, head group) units the splits multiply: the

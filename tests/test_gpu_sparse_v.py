@@ -107,12 +107,18 @@ def test_sparse_v_within_envelope(codec, heads, chunk):
     ref_out = ref_out.reshape(len(LENS), n_q, 128)
     assert np.max(np.abs(out_d - ref_out)) <= OUT_ABS
     vabs = [[np.abs(_values(spec, P, R, b, n, hk)) for hk in range(n_kv)] for b, n in enumerate(LENS)]
+    # The two decodes add different products into fp32 sums: each 128-position
+    # block adds once, and a sum may hold up to 6 times the weighted value mass
+    # (the value operand's elements reach 6 where the signs are +/-1), so they
+    # may differ by one rounding of that size per block on top of the skipped mass.
+    vmax = max(float(x.max()) for row in vabs for x in row)
+    rounding = 1e-5 + 6.0 * 2.0 ** -24 * (CTX / 128) * vmax
     changed = False
     for T in (2, 6, 10):
         out_s, lg_s = _decode(tq.make_config(decode_chunk=chunk, sparse_v=T, **base), caches, q)
         assert np.array_equal(np.nan_to_num(lg_s, nan=7.0), np.nan_to_num(lg_d, nan=7.0))
         env = _envelope(spec, vabs, ref_lg, T)
-        gap = np.abs(out_s - out_d) - (env * (1.0 + 1e-3) + 1e-5)
+        gap = np.abs(out_s - out_d) - (env * (1.0 + 1e-3) + rounding)
         assert gap.max() <= 0.0, f"T={T}: sparse-dense difference above the envelope by {gap.max():.3g}"
         assert np.max(np.abs(out_s - ref_out) - env) <= OUT_ABS
         changed |= not np.array_equal(out_s, out_d)
