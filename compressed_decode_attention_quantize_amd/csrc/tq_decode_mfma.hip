@@ -888,6 +888,9 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   // denominator per (wave, head); running max per head; the two groups'
   // weighted sums per coordinate (in the sketch buffer, free by now)
   float (*obuf)[4][kD] = reinterpret_cast<float (*)[4][kD]>(&sred[0][0]);
+  // the inverse rotation's signs, loaded before the exchange below so that
+  // their latency overlaps it
+  const float dva = a.tb.dv[lane], dvb = a.tb.dv[lane + 64];
   {
     const float ls = row_sum16(lsum);
     if (t == 0) wred[w][g4] = ls;
@@ -925,8 +928,8 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
     }
     wave_fwht128(lo, hi, lane);
     const float inv_d = 1.0f / static_cast<float>(kD);
-    lo *= a.tb.dv[lane] * inv_d;
-    hi *= a.tb.dv[lane + 64] * inv_d;
+    lo *= dva * inv_d;
+    hi *= dvb * inv_d;
     float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + hq0 + w) * a.n_splits + split) * kPartialStride;
     store_coherent(pp + lane, lo);
     store_coherent(pp + 64 + lane, hi);
