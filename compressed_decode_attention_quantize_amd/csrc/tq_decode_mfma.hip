@@ -956,16 +956,29 @@ __global__ __launch_bounds__(256 * NG, 2) void decode_append_kernel(DecodeArgs a
   decode_mfma_body<KB, QJL, VB, NG, true>(a);
 }
 
-template <int KB, bool QJL, int VB>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+template <int KB, bool QJL, int VB, int NG>
+hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * ((a.group + 3) / 4));
-  constexpr int NG = (KB == 8 || VB == 4) ? 1 : 2;   // as decode_mfma_groups
   if (a.k_new != nullptr)
     hipLaunchKernelGGL((decode_append_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
   else
     hipLaunchKernelGGL((decode_mfma_kernel<KB, QJL, VB, NG>), grid, dim3(256 * NG), 0, stream, a);
   return hipGetLastError();
+}
+
+// block groups per workgroup as the host chose them: one for q8 keys, one or
+// two for four-bit values, two otherwise
+template <int KB, bool QJL, int VB>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (KB == 8) {
+    return a.groups == 1 ? launch_g<KB, QJL, VB, 1>(a, stream) : hipErrorInvalidValue;
+  } else if constexpr (VB == 4) {
+    if (a.groups == 1) return launch_g<KB, QJL, VB, 1>(a, stream);
+    return a.groups == 2 ? launch_g<KB, QJL, VB, 2>(a, stream) : hipErrorInvalidValue;
+  } else {
+    return a.groups == 2 ? launch_g<KB, QJL, VB, 2>(a, stream) : hipErrorInvalidValue;
+  }
 }
 
 template <int KB, bool QJL>
@@ -979,13 +992,6 @@ hipError_t launch_v(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-// q8 keys (large slots, three head groups per KV head at G = 12) and
-// four-bit values (sixteen value products per step, every register in use)
-// run best as two workgroups of one group per compute unit; the others as
-// one workgroup of two groups (measured on the Llama-8B, 1M-context and
-// batched-serving layers).
-int decode_mfma_groups(int k_codec, int v_bits) { return (k_codec == Q8_BLOCK32 || v_bits == 4) ? 1 : 2; }
 
 bool decode_mfma_applies(int k_codec, int v_codec, int group) {
   return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL || k_codec == Q8_BLOCK32);

@@ -441,10 +441,6 @@ bool mfma_path(const tq_config* c) {
   return tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
 }
 
-int64_t target_workgroups(const tq_config* c) {
-  return mfma_path(c) ? tq::kMfmaUnitWorkgroups / tq::decode_mfma_groups(c->k_codec, c->v_bits) : tq::kValuWorkgroups;
-}
-
 // Independent (sequence, KV head, head group) units the splits multiply: the
 // matrix-core kernel serves up to four query heads per workgroup.
 int64_t split_units(const tq_config* c) {
@@ -452,14 +448,39 @@ int64_t split_units(const tq_config* c) {
   return static_cast<int64_t>(c->batch) * c->n_kv_heads * groups;
 }
 
-int decode_chunk_blocks(const tq_config* c, int32_t max_seq_len) {
+// Blocks per split when the grid aims at `target` workgroups.
+int chunk_blocks_for(const tq_config* c, int32_t max_seq_len, int64_t target) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return c->decode_chunk / kBlock;
-  // aim for the kernel's workgroup count over the whole grid
   const int64_t pairs = split_units(c);
-  const int64_t target = target_workgroups(c);
   const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
   return static_cast<int>(std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits));
+}
+
+// Block groups (of four wavefronts, one block each per step) per workgroup
+// of the matrix-core kernel.  q8 keys take one group: their large blocks leave
+// a two-group ring too shallow.  Four-bit values take one group once a
+// two-group workgroup would run 8 or more steps (two workgroups per compute
+// unit then hide each other's stalls; with fewer steps the doubled set-up and
+// merge cost more).  Measured with 4-bit keys and values, us per launch with
+// two groups / one group: 32K Llama shape 24.2 / 26.2, 16 x 8K 60.3 / 57.8,
+// 1M 394 / 356.  The choice only moves
+// to one group as the length grows, so the splits of a shorter call never
+// exceed those of a longer one.
+int mfma_groups(const tq_config* c, int32_t max_seq_len) {
+  if (c->k_codec == TQ_CODEC_Q8_BLOCK32) return 1;
+  if (c->v_bits != 4) return 2;
+  const int cb = chunk_blocks_for(c, max_seq_len, tq::kMfmaUnitWorkgroups / 2);
+  return (cb + 1) / 2 >= 8 ? 1 : 2;
+}
+
+int64_t target_workgroups(const tq_config* c, int32_t max_seq_len) {
+  return mfma_path(c) ? tq::kMfmaUnitWorkgroups / mfma_groups(c, max_seq_len) : tq::kValuWorkgroups;
+}
+
+int decode_chunk_blocks(const tq_config* c, int32_t max_seq_len) {
+  // aim for the kernel's workgroup count over the whole grid
+  return chunk_blocks_for(c, max_seq_len, target_workgroups(c, max_seq_len));
 }
 
 int decode_splits(const tq_config* c, int32_t max_seq_len) {
@@ -474,7 +495,7 @@ int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return (blocks + c->decode_chunk / kBlock - 1) / (c->decode_chunk / kBlock);
   const int64_t pairs = split_units(c);
-  const int64_t target = target_workgroups(c);
+  const int64_t target = target_workgroups(c, max_seq_len);   // no shorter call aims higher
   const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
   return static_cast<int>(std::min<int64_t>(blocks, want_splits));
 }
@@ -573,6 +594,7 @@ tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k
   a.n_blocks = n_blocks(cfg);
   a.chunk_blocks = decode_chunk_blocks(cfg, max_seq_len);
   a.n_splits = splits;
+  a.groups = mfma_path(cfg) ? mfma_groups(cfg, max_seq_len) : 1;
   a.k_codec = cfg->k_codec;
   a.k_bits = cfg->k_bits;
   a.v_codec = cfg->v_codec;

@@ -122,6 +122,7 @@ struct DecodeArgs {
   const void* v_new;
   int32_t in_dtype;
   int32_t len_add;    // positions attended = min(seq_lens[b] + len_add, max_ctx)
+  int32_t groups;     // matrix-core kernel: block groups of four wavefronts per workgroup (1 or 2)
 };
 
 struct DequantArgs {
@@ -145,7 +146,6 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Block groups (of four wavefronts) per workgroup of the matrix-core decode
 // kernel for a key codec: with one group two independent workgroups share a
 // compute unit, with two groups one workgroup of eight wavefronts fills it.
-int decode_mfma_groups(int k_codec, int v_bits);
 // Workgroups the automatic split count aims for: the matrix-core kernel fills
 // the 256 compute units of the target chip (512 / groups workgroups), the
 // VALU kernel runs about four 256-thread workgroups per compute unit (it is

@@ -172,11 +172,17 @@ def test_append_decode_argument_checks(tq):
 
 
 def test_workspace_bound_covers_every_shorter_length(tq):
-    for batch, kv in [(1, 8), (16, 8), (1, 2)]:
-        cfg = _cfg(tq, n_q_heads=4 * kv, n_kv_heads=kv, batch=batch, max_ctx=1 << 20)
-        top = tq.decode_workspace_bytes(cfg, 1 << 20)
-        for L_ in [1, 127, 128, 129, 5000, 8192, 32768, 65 * 128, 1 << 19, 1 << 20]:
-            assert tq.decode_workspace_bytes(cfg, L_) <= top
+    # a workspace sized for a length serves every shorter call: the bound is
+    # non-decreasing in the length, also across the length at which 4-bit
+    # values move from two block groups per workgroup to one (batch 1, 8 KV
+    # heads: 32 splits of at least 15 blocks, from 449 blocks on)
+    lens = [1, 127, 128, 129, 5000, 8192, 32768, 448 * 128, 448 * 128 + 1, 449 * 128, 449 * 128 + 1, 65 * 128 * 8,
+            1 << 19, 1 << 20]
+    for v_bits in (2, 4):
+        for batch, kv in [(1, 8), (16, 8), (1, 2)]:
+            cfg = _cfg(tq, n_q_heads=4 * kv, n_kv_heads=kv, batch=batch, max_ctx=1 << 20, v_bits=v_bits)
+            sizes = [tq.decode_workspace_bytes(cfg, L_) for L_ in sorted(lens)]
+            assert sizes == sorted(sizes), (v_bits, batch, kv, sizes)
 
 
 def test_dequantize_argument_checks(tq):
