@@ -15,8 +15,11 @@ quantize-append half of the metric is measured in its own timed region: the
 Also printed: the roofline of the decode kernel (algorithmic bytes per launch
 over its mean launch duration, from HIP events on the launch stream around the
 timed region), the HBM traffic per launch measured with rocprofv3 counters
-(from profiles/, when taken on the current kernel sources), and the oracle's
-CPU throughput on a bounded sample (single-threaded).
+(from profiles/, when taken on the current kernel sources), the median,
+minimum and maximum step time, the practical HBM read ceiling (a plain
+streaming read of 2 GiB on the same GPU) with the decode throughput as a
+fraction of it, and the oracle's CPU throughput on a bounded sample
+(single-threaded).
 """
 from __future__ import annotations
 
@@ -194,6 +197,27 @@ def serve_steps(args, w, layers, q, dev, tq, synth, seed, bytes_per_launch):
                       "decode_bytes_per_layer_step": bytes_per_launch}}
 
 
+def read_ceiling(tq, dev, nbytes=2 << 30, reps=10):
+    """The practical HBM read ceiling: a plain streaming read (tq_stream_read,
+    16-byte non-temporal loads) over 2 GiB, well past the 256 MB last-level
+    cache, timed with HIP events over `reps` back-to-back launches."""
+    import torch
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        tq.stream_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tq.stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf
+    return {"gbs": round(gbs, 1), "bytes": nbytes, "reps": reps, "kernel": "stream_read_kernel",
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,14 +330,16 @@ def main():
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    for _ in range(args.steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(stream)
+    for k_ in range(args.steps):
         step()
-    s1.record(stream)
+        marks[k_ + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = s0.elapsed_time(s1) / args.steps
+    step_ms = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = sorted(marks[k_].elapsed_time(marks[k_ + 1]) for k_ in range(args.steps))
+    ceiling = read_ceiling(tq, dev)
 
     # average duration of one decode launch: the timed region (HIP events on
     # the launch stream) holds only back-to-back decode launches
@@ -342,6 +368,11 @@ def main():
         "append_tokens_per_s": round(append_tok_s, 1),
         "append_ms_per_layer": round(append_s * 1e3, 4),
         "decode_us_per_layer": round(step_ms * 1e3 / n_layers, 3),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
+        "ms_per_step_max": round(per_step[-1], 4),
+        "hbm_read_ceiling": ceiling,
+        "frac_of_read_ceiling": round(value / ceiling["gbs"], 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": committed_traffic(w.name, n_layers),

@@ -30,6 +30,7 @@ UNITS = [
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
     ("tq_dequant.hip", []),
+    ("tq_stream.hip", []),
 ]
 
 

@@ -753,4 +753,12 @@ tq_status tq_dequantize(const tq_config* cfg, const void* params, const void* k_
   return tq::launch_dequantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
 
+tq_status tq_stream_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || !aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0)
+    return TQ_EINVAL;
+  if (bytes == 0) return TQ_OK;
+  return tq::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK
+                                                                                                   : TQ_EDEVICE;
+}
+
 }  // extern "C"

@@ -156,5 +156,6 @@ hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 // Append for tensors stored with the recursive polar codec (the other kernel
 // skips them).
 hipError_t launch_quantize_tree(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, uint64_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace tq

@@ -72,9 +72,10 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_int32, _vp, _vp, ctypes.c_uint32, _vp]
         L.tq_append_decode.argtypes = [_cfgp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32,
                                        _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp]
+        L.tq_stream_read.argtypes = [_vp, ctypes.c_uint64, _vp, _vp]
         for fn in ("tq_cache_bytes", "tq_params_bytes", "tq_params_host", "tq_init_params",
                    "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention",
-                   "tq_dequantize", "tq_append_decode"):
+                   "tq_dequantize", "tq_append_decode", "tq_stream_read"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -212,6 +213,15 @@ def dequantize(cfg: Config, params, k_cache, v_cache, b: int, start: int, count:
     _check(lib().tq_dequantize(ctypes.byref(cfg), _ptr(params), _ptr(k_cache), _ptr(v_cache), b, start,
                                count, _ptr(k_out), _ptr(v_out), DEQ_QJL if qjl else 0, _stream(stream)),
            "tq_dequantize")
+
+
+def stream_read(src, sink):
+    """Measurement helper (not part of the method): XOR every 32-bit word of
+    the device tensor src (a multiple of 16 bytes) into the device int32 sink
+    with a plain streaming read; the bench's practical HBM read ceiling."""
+    assert src.is_cuda and sink.is_cuda and sink.dtype == torch.int32
+    nbytes = src.numel() * src.element_size()
+    _check(lib().tq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream()), "tq_stream_read")
 
 
 # ------------------------------------------------------------ convenience

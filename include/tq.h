@@ -221,6 +221,19 @@ tq_status tq_dequantize(const tq_config* cfg, const void* params, const void* k_
                         const void* v_cache, int32_t b, int32_t start, int32_t count,
                         float* k_out, float* v_out, uint32_t flags, void* stream);
 
+/* Measurement helper, not part of the method: a plain streaming read of
+ * `bytes` of device memory (16-byte non-temporal loads over the whole grid),
+ * the practical HBM read ceiling that decode throughput is reported against
+ * beside the published peak.  XORs every 32-bit word of the range into *sink
+ * (XOR, so the result is exact whatever the schedule; the caller sets *sink
+ * first, e.g. to 0).
+ *   src    device, 16-byte aligned, read only
+ *   bytes  a multiple of 16 (0: nothing is launched)
+ *   sink   device uint32, 4-byte aligned
+ * Fails with TQ_EINVAL on a null pointer, misalignment or a ragged length;
+ * TQ_EDEVICE if the launch fails.  Asynchronous on `stream`. */
+tq_status tq_stream_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

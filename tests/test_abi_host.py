@@ -25,7 +25,7 @@ def tq():
 def test_every_declared_symbol_is_exported(tq):
     hdr = open(os.path.join(ROOT, "include", "tq.h")).read()
     names = set(re.findall(r"^(?:tq_status|const char\*)\s+(tq_\w+)\(", hdr, re.M))
-    assert len(names) == 10
+    assert len(names) == 11
     L = tq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -183,6 +183,18 @@ def test_workspace_bound_covers_every_shorter_length(tq):
             cfg = _cfg(tq, n_q_heads=4 * kv, n_kv_heads=kv, batch=batch, max_ctx=1 << 20, v_bits=v_bits)
             sizes = [tq.decode_workspace_bytes(cfg, L_) for L_ in sorted(lens)]
             assert sizes == sorted(sizes), (v_bits, batch, kv, sizes)
+
+
+def test_stream_read_argument_checks(tq):
+    # no launch happens for any of these: the checks run on the host
+    L = tq.lib()
+    p = ctypes.c_void_p
+    assert L.tq_stream_read(None, 16, p(FAKE), None) == tq.EINVAL
+    assert L.tq_stream_read(p(FAKE), 16, None, None) == tq.EINVAL
+    assert L.tq_stream_read(p(FAKE + 8), 16, p(FAKE), None) == tq.EINVAL   # src not 16-byte aligned
+    assert L.tq_stream_read(p(FAKE), 16, p(FAKE + 2), None) == tq.EINVAL   # sink not 4-byte aligned
+    assert L.tq_stream_read(p(FAKE), 24, p(FAKE), None) == tq.EINVAL       # ragged length
+    assert L.tq_stream_read(p(FAKE), 0, p(FAKE), None) == tq.OK            # nothing to read
 
 
 def test_dequantize_argument_checks(tq):
