@@ -42,7 +42,8 @@
 // each lane's operands whole 8-byte loads.
 //
 // Mapping: grid (split, KV head, sequence, head group); a workgroup is NG
-// groups of four waves (NG = 2: one workgroup per compute unit; NG = 1: two).
+// groups of four waves (NG = 2: one workgroup per compute unit; NG = 1: two;
+// the host picks NG per call).
 // Each step takes NG 128-position blocks, one per group, from a ring of
 // shared-memory slots that direct memory-to-shared-memory copies fill several
 // steps ahead.  Within a group, wave w computes the logits of its block's
