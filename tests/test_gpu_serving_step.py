@@ -106,3 +106,47 @@ def test_fused_steps_match_oracle(codec):
         rows = slice(b * cfg.n_q_heads, (b + 1) * cfg.n_q_heads)
         check_out(out[b], ref_out[rows], f"{codec} b={b}")
         check_logits(lg[b], ref_lg[rows], n, f"{codec} b={b}")
+
+
+def test_fused_step_one_group_layout():
+    """4-bit keys and values over splits long enough that the matrix-core
+    kernel runs one block group per workgroup (two workgroups per compute
+    unit): the fused step must still equal append then decode, step after
+    step.  The split count (16, against 8 with two groups) confirms the
+    layout."""
+    lens0 = [15000, 9000, 300, 14000]
+    cfg = tq.make_config(n_q_heads=32, n_kv_heads=8, batch=4, max_ctx=15104, k_codec=tq.POLAR_QJL, k_bits=4,
+                         v_codec=tq.POLAR, v_bits=4, seed=42, layer=3)
+    # the workspace holds one fp32 partial record (128 sums, max, denominator,
+    # 2 pad) per (sequence, query head, split): 8 more splits than the same
+    # shape with 2-bit values (always two groups, 8 splits) is 16
+    per_split = 4 * 32 * 132 * 4
+    cfg2 = tq.make_config(n_q_heads=32, n_kv_heads=8, batch=4, max_ctx=15104, k_codec=tq.POLAR_QJL, k_bits=4,
+                          v_codec=tq.POLAR, v_bits=2, seed=42, layer=3)
+    ws4 = tq.decode_workspace_bytes(cfg, max(lens0) + 1)
+    ws2 = tq.decode_workspace_bytes(cfg2, max(lens0) + 1)
+    assert ws4 - ws2 == 8 * per_split, (ws4, ws2)
+    A, B = tq.KVLayer(cfg, DEV), tq.KVLayer(cfg, DEV)
+    g = torch.Generator(device="cpu").manual_seed(77)
+    n0 = max(lens0)
+    k = torch.randn((cfg.batch, n0 + 3, cfg.n_kv_heads, 128), generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn((cfg.batch, n0 + 3, cfg.n_kv_heads, 128), generator=g).to(torch.bfloat16).to(DEV)
+    for L in (A, B):
+        L.append(k[:, :n0].contiguous(), v[:, :n0].contiguous())
+        L.seq_lens.copy_(torch.tensor(lens0, dtype=torch.int32, device=DEV))
+        L.max_len = n0
+    torch.cuda.synchronize()
+    lens = list(lens0)
+    for s in range(3):
+        print(f"[serving step, one group] step {s}", flush=True)
+        q = torch.randn((cfg.batch, cfg.n_q_heads, 128), generator=g).to(DEV)
+        idx = torch.tensor(lens, device=DEV)
+        kn = k[torch.arange(cfg.batch, device=DEV), idx].unsqueeze(1).contiguous()
+        vn = v[torch.arange(cfg.batch, device=DEV), idx].unsqueeze(1).contiguous()
+        oa = A.step(kn, vn, q)
+        B.append(kn, vn)
+        ob = B.decode(q)
+        torch.cuda.synchronize()
+        assert torch.equal(A.k_cache, B.k_cache) and torch.equal(A.v_cache, B.v_cache), f"step {s}: caches differ"
+        assert torch.equal(oa, ob), f"step {s}: outputs differ by {float((oa - ob).abs().max())}"
+        lens = [n + 1 for n in lens]
