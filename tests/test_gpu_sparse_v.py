@@ -32,6 +32,7 @@ CODECS = {
     "qjl3_v3": (tq.POLAR_QJL, 3, tq.POLAR, 3),
     "q8_v4": (tq.Q8_BLOCK32, 8, tq.POLAR, 4),
     "polar2_v2": (tq.POLAR, 2, tq.POLAR, 2),
+    "qjl4_v4": (tq.POLAR_QJL, 4, tq.POLAR, 4),
 }
 LENS = [3000, 1700]
 CTX = 3072
