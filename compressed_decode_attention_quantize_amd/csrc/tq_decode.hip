@@ -125,7 +125,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // read shared memory that is allocated but holds no head, and their
 // accumulators are never written out (a branch per head per element made
 // every shared-memory read wait for its result).
-// TVB: bits of recursive polar values (0: other value codecs).
+// TVB: bits of recursive polar values (0: other value codecs); the path
+// products of a word of positions are formed once per position in pp.
 template <int HPT, int TVB>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ float qv[kMaxGroup * kD];   // q (or q_raw) per head
@@ -133,6 +134,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ float pt[kMaxGroup * kBlock];  // logits, then p * value radius
   __shared__ float kcb[16], vcb[16];
   __shared__ TreeLds ktree, vtree;
+  // recursive polar values: per position of a 32-position word, the product
+  // of the level 2..7 factors on the path to each level-1 pair
+  __shared__ float pp[TVB > 0 ? 32 : 1][TVB > 0 ? kD / 2 : 1];
   __shared__ float m_run[kMaxGroup], l_run[kMaxGroup], scale[kMaxGroup];
   __shared__ int s_last;
 
@@ -190,17 +194,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < HPT; ++u) acc[u] = 0.0f;
 
-  // recursive polar values: this coordinate's factor of each code at levels 2..7
-  float vf[6][TVB > 0 ? (1 << (TVB - 1)) : 1];
-  if constexpr (TVB > 0) {
-#pragma unroll
-    for (int l = 2; l <= 7; ++l)
-#pragma unroll
-      for (int c = 0; c < (1 << (TVB - 1)); ++c) {
-        const float2 cs = vtree.up[l][c];
-        vf[l - 2][c] = ((ci >> (l - 1)) & 1) ? cs.y : cs.x;
-      }
-  }
 
   const int blk0 = split * a.chunk_blocks;
   const int nblk_seq = (len + kBlock - 1) / kBlock;
@@ -394,20 +387,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       // coordinate ci: its level-1 pair is slot 64 + ci / 2, its level-l
       // ancestor slot 2^(7 - l) + ci / 2^l; the factor is the sin of an
       // ancestor's angle when ci lies in its right half, else the cos.  The
-      // upper levels' factors of this coordinate sit in registers (vf) and
-      // are selected by the code bits; level 1 is a shared-memory lookup.
+      // product of the level 2..7 factors depends on the pair only: per word
+      // of 32 positions, thread (e, q) walks the level-4 subtree q of position
+      // 32 j + e top-down and leaves the products of its 8 pairs in pp (each
+      // node's angle looked up once per position), then thread ci forms
+      // u_ci = (cos or sin of its pair's angle) * pp[e][ci / 2].
       constexpr int nb1 = TVB - 1;
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
       const uint32_t* l1 = planes + nb1 * 4 * kD;
+      const int pe = tid & 31, pq = (tid >> 5) & 7;
 #pragma unroll 1
       for (int j = 0; j * 32 < n_t; ++j) {
-        uint32_t w[nb1][7], x[2];
+        // code of the upper slot sl for position 32 j + pe
+        auto node_code = [&](int sl) __attribute__((always_inline)) {
+          int c = 0;
 #pragma unroll
-        for (int p = 0; p < nb1; ++p) {
-          w[p][0] = planes[(p * 4 + j) * kD + 64 + (ci >> 1)];
+          for (int p = 0; p < nb1; ++p) c |= ((planes[(p * 4 + j) * kD + sl] >> pe) & 1u) << p;
+          return c;
+        };
+        __syncthreads();   // the previous word's pp has been read
+        {
+          const float2 c7 = vtree.up[7][node_code(1)];
+          float f = (pq >> 2) ? c7.y : c7.x;
+          const float2 c6 = vtree.up[6][node_code(2 + (pq >> 2))];
+          f *= ((pq >> 1) & 1) ? c6.y : c6.x;
+          const float2 c5 = vtree.up[5][node_code(4 + (pq >> 1))];
+          f *= (pq & 1) ? c5.y : c5.x;
+          const float2 c4 = vtree.up[4][node_code(8 + pq)];
 #pragma unroll
-          for (int l = 2; l <= 7; ++l) w[p][l - 1] = planes[(p * 4 + j) * kD + (1 << (7 - l)) + (ci >> l)];
+          for (int a3 = 0; a3 < 2; ++a3) {
+            const float f3 = f * (a3 ? c4.y : c4.x);
+            const float2 c3 = vtree.up[3][node_code(16 + 2 * pq + a3)];
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2) {
+              const float f2 = f3 * (a2 ? c3.y : c3.x);
+              const int n2 = 4 * pq + 2 * a3 + a2;   // level-2 node
+              const float2 c2 = vtree.up[2][node_code(32 + n2)];
+              pp[pe][2 * n2] = f2 * c2.x;
+              pp[pe][2 * n2 + 1] = f2 * c2.y;
+            }
+          }
         }
+        __syncthreads();
+        uint32_t w[nb1], x[2];
+#pragma unroll
+        for (int p = 0; p < nb1; ++p) w[p] = planes[(p * 4 + j) * kD + 64 + (ci >> 1)];
 #pragma unroll
         for (int k = 0; k < 2; ++k) x[k] = l1[(k * 4 + j) * (kD / 2) + (ci >> 1)];
         const int e_end = min(32, n_t - j * 32);
@@ -415,21 +439,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < e_end; ++e) {
           int c = 0;
 #pragma unroll
-          for (int p = 0; p < nb1; ++p) c |= ((w[p][0] >> e) & 1u) << p;
+          for (int p = 0; p < nb1; ++p) c |= ((w[p] >> e) & 1u) << p;
           c |= ((x[0] >> e) & 1u) << nb1;
           c |= ((x[1] >> e) & 1u) << (nb1 + 1);
           const float2 cs1 = vtree.l1[c];
-          float uval = (ci & 1) ? cs1.y : cs1.x;
-#pragma unroll
-          for (int l = 2; l <= 7; ++l) {
-            int cl = 0;
-#pragma unroll
-            for (int p = 0; p < nb1; ++p) cl |= ((w[p][l - 1] >> e) & 1u) << p;
-            float f = vf[l - 2][0];
-#pragma unroll
-            for (int cc = 1; cc < (1 << nb1); ++cc) f = (cl == cc) ? vf[l - 2][cc] : f;
-            uval *= f;
-          }
+          const float uval = ((ci & 1) ? cs1.y : cs1.x) * pp[e][ci >> 1];
           const int t = j * 32 + e;
 #pragma unroll
           for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], uval, acc[u]);
