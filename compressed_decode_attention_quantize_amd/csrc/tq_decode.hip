@@ -66,11 +66,11 @@ __device__ __forceinline__ int tree_key_code(const uint32_t (&w)[3][4], const ui
   return c;
 }
 
-// dot[h] += <q_raw, u> over the subtree of level-6 node N6 (coordinates
-// 64 N6 .. 64 N6 + 63), its weight w6 being the root's cos or sin
-template <int N6, int HPT>
+// dot[u] += <q_raw of head hb + HS u, u> over the subtree of level-6 node N6
+// (coordinates 64 N6 .. 64 N6 + 63), its weight w6 being the root's cos or sin
+template <int N6, int NH, int HS>
 __device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int nb1,
-                                              const TreeLds& tab, const float* qv, int hpar, float (&dot)[HPT]) {
+                                              const TreeLds& tab, const float* qv, int hb, float (&dot)[NH]) {
   const float2 c6 = tab.up[6][tree_key_code<0>(w, x, nb1, 2 + N6)];
 #pragma unroll 1
   for (int n5 = 2 * N6; n5 < 2 * N6 + 2; ++n5) {
@@ -96,8 +96,8 @@ __device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4
             const float2 cs = tab.l1[tree_key_code<2 + N6>(w, x, nb1, i & 31)];
             const float a0 = w1 * cs.x, a1 = w1 * cs.y;
 #pragma unroll
-            for (int u = 0; u < HPT; ++u) {
-              const float2 q2 = *reinterpret_cast<const float2*>(qv + (hpar + 2 * u) * kD + 2 * i);
+            for (int u = 0; u < NH; ++u) {
+              const float2 q2 = *reinterpret_cast<const float2*>(qv + (hb + HS * u) * kD + 2 * i);
               dot[u] = fmaf(q2.x, a0, fmaf(q2.y, a1, dot[u]));
             }
           }
@@ -209,7 +209,76 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const uint8_t* vb = a.vc + (slot0 + blk) * a.v_block_bytes;
 
     // ------------------------------------------------------- logits
-    {
+    if (a.k_codec == POLAR_TREE) {   // uniform
+      // Groups of up to four heads: thread (t, half) walks the half `hpar`
+      // of position t's tree (the root's left or right subtree) for every
+      // head, once for all of them; the right halves' sums reach the left
+      // halves through pt.  Larger groups: thread (t, hpar) walks the whole
+      // tree for its heads hpar + 2u (fewer registers per thread).
+      const int t = tid & (kBlock - 1);
+      constexpr int NH = HPT <= 2 ? 2 * HPT : HPT;   // heads per thread's sums
+      float dot[NH];
+#pragma unroll
+      for (int u = 0; u < NH; ++u) dot[u] = 0.0f;
+      float n16 = 0.0f;
+      if (t < n_t) {
+        const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
+        const int sl = slot_of(t);
+        const int nb1 = kbits - 1;
+        uint32_t w[3][4] = {}, x[2][2];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          if (p < nb1)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[p][j] = planes[(p * 4 + j) * kBlock + sl];
+        const uint32_t* l1 = planes + nb1 * 4 * kBlock;
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) x[k][j] = l1[(k * 2 + j) * kBlock + sl];
+        n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
+        const float2 c7 = ktree.up[7][tree_key_code<0>(w, x, nb1, 1)];
+        if constexpr (HPT <= 2) {
+          if (hpar == 0)
+            tree_half_dot<0, NH, 1>(c7.x, w, x, nb1, ktree, qv, 0, dot);
+          else
+            tree_half_dot<1, NH, 1>(c7.y, w, x, nb1, ktree, qv, 0, dot);
+        } else {
+          tree_half_dot<0, NH, 2>(c7.x, w, x, nb1, ktree, qv, hpar, dot);
+          tree_half_dot<1, NH, 2>(c7.y, w, x, nb1, ktree, qv, hpar, dot);
+        }
+      }
+      if constexpr (HPT > 2) {
+#pragma unroll
+        for (int u = 0; u < NH; ++u) {
+          const int g = hpar + 2 * u;
+          if (g < G) {
+            const float lgv = n16 * dot[u] * (1.0f / static_cast<float>(kD));
+            pt[g * kBlock + t] = (t < n_t) ? lgv : -INFINITY;
+            if (a.logits != nullptr && t < n_t)
+              a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g) * a.max_ctx + blk * kBlock + t] = lgv;
+          }
+        }
+      } else {
+      if (hpar == 1) {
+#pragma unroll
+        for (int g = 0; g < NH; ++g)
+          if (g < G) pt[g * kBlock + t] = dot[g];
+      }
+      __syncthreads();
+      if (hpar == 0) {
+#pragma unroll
+        for (int g = 0; g < NH; ++g) {
+          if (g < G) {
+            const float lgv = n16 * (dot[g] + pt[g * kBlock + t]) * (1.0f / static_cast<float>(kD));
+            pt[g * kBlock + t] = (t < n_t) ? lgv : -INFINITY;
+            if (a.logits != nullptr && t < n_t)
+              a.logits[(static_cast<int64_t>(b) * a.n_q + h * G + g) * a.max_ctx + blk * kBlock + t] = lgv;
+          }
+        }
+      }
+      }
+    } else {
       const int t = tid & (kBlock - 1);
       float lg[HPT];
 #pragma unroll
@@ -262,28 +331,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(after)[slot_of(t)]);
 #pragma unroll
           for (int u = 0; u < HPT; ++u) lg[u] = alpha * n16 * cdot[u] + beta * rho * sdot[u];
-        } else if (a.k_codec == POLAR_TREE) {
-          const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
-          const int sl = slot_of(t);
-          const int nb1 = kbits - 1;
-          uint32_t w[3][4] = {}, x[2][2];
-#pragma unroll
-          for (int p = 0; p < 3; ++p)
-            if (p < nb1)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) w[p][j] = planes[(p * 4 + j) * kBlock + sl];
-          const uint32_t* l1 = planes + nb1 * 4 * kBlock;
-#pragma unroll
-          for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) x[k][j] = l1[(k * 2 + j) * kBlock + sl];
-          const float n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
-          float dot[HPT] = {};
-          const float2 c7 = ktree.up[7][tree_key_code<0>(w, x, nb1, 1)];
-          tree_half_dot<0, HPT>(c7.x, w, x, nb1, ktree, qv, hpar, dot);
-          tree_half_dot<1, HPT>(c7.y, w, x, nb1, ktree, qv, hpar, dot);
-#pragma unroll
-          for (int u = 0; u < HPT; ++u) lg[u] = n16 * dot[u] * (1.0f / static_cast<float>(kD));
         } else if (a.k_codec == Q8_BLOCK32) {
           const int8_t* row = reinterpret_cast<const int8_t*>(kb) + t * kD;
           const uint16_t* sc = reinterpret_cast<const uint16_t*>(kb + kBlock * kD) + t * (kD / 32);
