@@ -97,3 +97,27 @@ def test_full_size_serving_steps():
             n = w.ctx + step + 1
             for b, h in pairs:
                 _check_pair(cfg, L, k, v, q, lg, out, b, h, n, f"serving step {step} b={b} kv={h}")
+
+
+def test_full_size_fused_serving_steps():
+    """The same 64 serving steps through the fused step (tq_append_decode:
+    the new position stored and attended to in one launch, the launch the
+    serving bench times): steps 0, 31 and 63 against the oracle on two
+    sampled (sequence, KV head) pairs, records included."""
+    wi, w = 2, synth.WORKLOADS["serving_b16_ctx8k"]
+    cfg = tq.config_for(w, seed=42, layer=0, max_ctx=w.ctx + w.steps)
+    L = tq.KVLayer(cfg, DEV)
+    n_tot = w.ctx + w.steps
+    k, v = synth.make_kv(w, n_tot, seed=1000 + wi, device=DEV)
+    L.append(k[:, :w.ctx].contiguous(), v[:, :w.ctx].contiguous())
+    pairs = [(6, 2), (15, 7)]
+    for step in range(w.steps):
+        q = synth.make_q(w, seed=5000 + step, device=DEV)
+        lg = torch.full((w.batch, w.n_q, cfg.max_ctx), float("nan"), device=DEV)
+        out = L.step(k[:, w.ctx + step:w.ctx + step + 1].contiguous(),
+                     v[:, w.ctx + step:w.ctx + step + 1].contiguous(), q, logits=lg)
+        if step in (0, 31, 63):
+            torch.cuda.synchronize()
+            n = w.ctx + step + 1
+            for b, h in pairs:
+                _check_pair(cfg, L, k, v, q, lg, out, b, h, n, f"fused serving step {step} b={b} kv={h}")
