@@ -121,3 +121,66 @@ def test_full_size_fused_serving_steps():
             n = w.ctx + step + 1
             for b, h in pairs:
                 _check_pair(cfg, L, k, v, q, lg, out, b, h, n, f"fused serving step {step} b={b} kv={h}")
+
+
+def test_full_size_sparse_v_1m():
+    """Sparse-V at the 1M-context workload in the benchmark's peaked setting
+    (one planted key per 1024 positions, skip distance T = 8): on two sampled
+    (sequence, KV head) pairs the sparse output stays within the mass of the
+    weights below 2^-T of the largest (the oracle's weights and dequantised
+    values) of the dense output, and within 2e-3 plus that mass of the
+    oracle; logits are the dense launch's bits."""
+    wi, w = 4, synth.WORKLOADS["long_b1_ctx1m"]
+    T = 8
+    k, v = synth.make_kv(w, w.ctx, seed=1000 + wi, device=DEV)
+    q = synth.make_q(w, seed=2000 + wi, device=DEV)
+    k, _ = synth.plant_focus_keys(w, k, q, seed=3000 + wi, every=1024)
+    outs, lgs, layer = [], [], None
+    for sv in (0, T):
+        cfg = tq.config_for(w, seed=42, layer=0, sparse_v=sv)
+        if layer is None:
+            layer = tq.KVLayer(cfg, DEV)
+            layer.append(k, v)
+        lg = torch.full((w.batch, w.n_q, cfg.max_ctx), float("nan"), device=DEV)
+        out = torch.empty_like(q)
+        tq.decode_attention(cfg, layer.params, layer.k_cache, layer.v_cache, layer.seq_lens, layer.max_len, q, out,
+                            torch.zeros(tq.decode_workspace_bytes(cfg, layer.max_len), dtype=torch.uint8, device=DEV),
+                            lg)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        lgs.append(lg.cpu().numpy())
+    assert np.array_equal(np.nan_to_num(lgs[0], nan=7.0), np.nan_to_num(lgs[1], nan=7.0))
+    assert not np.array_equal(outs[0], outs[1]), "no block was skipped on peaked data"
+    n = w.ctx
+    G = w.n_q // w.n_kv
+    for b, h in [(0, 5)]:
+        label = f"sparse-v 1M b={b} kv={h}"
+        sub, Gr = _sub_records(cfg, layer, b, h, n)
+        P = oracle.Params(sub, cfg.seed, cfg.layer)
+        kn = widen_np(k[b, :n, h])[:, None, :]
+        vn = widen_np(v[b, :n, h])[:, None, :]
+        R = oracle_quantize_threaded(sub, P, kn, vn, n)
+        qh = q[b, h * G:(h + 1) * G].cpu().numpy()
+        ref_out, ref_lg = _oracle_decode_threaded(sub, P, R, n, qh)
+        vabs = np.empty((n, 128))
+
+        def _deq(lo, hi):
+            for t in range(lo, hi):
+                vabs[t] = np.abs(oracle.dequant_polar(P.DV, P.cv16, R.vcodes[t], R.vn16[t]))
+
+        step = (n + THREADS - 1) // THREADS
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            for f in [ex.submit(_deq, s0, min(n, s0 + step)) for s0 in range(0, n, step)]:
+                f.result()
+        for g in range(G):
+            l = ref_lg[g, :n]
+            tol = 1e-3 * max(np.abs(l).max(), np.sqrt(np.mean(l * l)))
+            p = np.exp(l - l.max())
+            small = (l - l.max()) < -T * np.log(2.0) + 2.0 * tol
+            env = (p[small] @ vabs[small]) / p.sum()
+            d_s, d_d = outs[1][b, h * G + g], outs[0][b, h * G + g]
+            rounding = 1e-5 + 6.0 * 2.0 ** -24 * (n / 128) * float(vabs.max())
+            assert np.all(np.abs(d_s - d_d) <= env * (1.0 + 1e-3) + rounding), label
+            assert np.max(np.abs(d_s - ref_out[g]) - env) <= 2e-3, label
+        print(f"{label}: max |sparse - dense| = {np.abs(outs[1][b, h * G:(h + 1) * G] - outs[0][b, h * G:(h + 1) * G]).max():.2e}",
+              flush=True)
