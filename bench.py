@@ -255,7 +255,7 @@ def main():
             print(f"{k_}={v_}")
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
