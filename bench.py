@@ -130,15 +130,23 @@ def cpu_baseline(w, seed):
     reps = 3   # about 10 s of single-threaded work at the 32K Llama shape
     t_app = t_dec = 0.0
     lens = np.full(w.batch, w.ctx, np.int32)
-    for _ in range(reps):
-        R = oracle.Records(s)
-        t0 = time.perf_counter()
-        for b in range(w.batch):
-            oracle.quantize_into(s, P, R, kn[b], vn[b], b, 0)
-        t_app += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        oracle.decode(s, P, R, lens, q)
-        t_dec += time.perf_counter() - t0
+    # the oracle is single-threaded C; the calling thread is pinned to one
+    # host core while it runs
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    os.sched_setaffinity(0, {core})
+    try:
+        for _ in range(reps):
+            R = oracle.Records(s)
+            t0 = time.perf_counter()
+            for b in range(w.batch):
+                oracle.quantize_into(s, P, R, kn[b], vn[b], b, 0)
+            t_app += time.perf_counter() - t0
+            t0 = time.perf_counter()
+            oracle.decode(s, P, R, lens, q)
+            t_dec += time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, allowed)
     t_app /= reps
     t_dec /= reps
     sz = oracle.spec_sizes(s)
@@ -151,7 +159,22 @@ def cpu_baseline(w, seed):
                    f"({t_dec:.1f} s each), single-threaded C on the host"),
         "append_tokens_per_s": w.batch * w.ctx / t_app,
         "seconds": reps * (t_app + t_dec),
+        "pinned_core": core,
+        "host_cpus_allowed": len(allowed),
+        "nproc": os.cpu_count(),
+        "cpu_model": host_cpu_model(),
     }
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def serve_steps(args, w, layers, q, dev, tq, synth, seed, bytes_per_launch):
