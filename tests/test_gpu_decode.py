@@ -59,7 +59,9 @@ def _gpu_decode(cfg, kc, vc, lens, q, max_seq_len=None):
 
 
 @pytest.mark.parametrize("codec", list(CODECS))
-@pytest.mark.parametrize("heads", [(8, 2), (32, 8), (96, 8)])
+# groups of 4 and 12 (whole head groups of four), 1 (no sharing), 6 (a partial
+# head group) and 16 (the largest group)
+@pytest.mark.parametrize("heads", [(8, 2), (32, 8), (96, 8), (16, 16), (12, 2), (64, 4)])
 def test_decode_matches_oracle(codec, heads):
     kc_, kb_, vc_, vb_ = CODECS[codec]
     n_q, n_kv = heads

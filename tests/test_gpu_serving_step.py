@@ -43,7 +43,7 @@ def _prefill(L, k, v):
 
 
 @pytest.mark.parametrize("codec", list(CODECS))
-@pytest.mark.parametrize("heads", [(32, 8), (96, 8)])
+@pytest.mark.parametrize("heads", [(32, 8), (96, 8), (12, 2)])
 @pytest.mark.parametrize("chunk", [0, 128])
 def test_fused_step_equals_append_then_decode(codec, heads, chunk):
     print(f"[serving step] {codec} heads={heads} chunk={chunk}", flush=True)

@@ -115,7 +115,9 @@ def _oracle_cache(cfg, lens, seed):
 
 
 @pytest.mark.parametrize("pair", list(PAIRS))
-@pytest.mark.parametrize("heads", [(8, 2), (32, 8), (96, 8)])
+# groups of 4 and 12 (whole head groups of four), 1 (no sharing), 6 (a partial
+# head group) and 16 (the largest group)
+@pytest.mark.parametrize("heads", [(8, 2), (32, 8), (96, 8), (16, 16), (12, 2), (64, 4)])
 def test_tree_decode_matches_oracle(pair, heads):
     n_q, n_kv = heads
     lens = [300, 1, 129, 0]
