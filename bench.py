@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DECODE_KERNEL = "decode_mfma_kernel"   # name fragment of the timed decode kernel
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_llama8b_ctx32k_traffic.txt")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_mfma_*_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc", f)
                   for f in ("tq_decode_mfma.hip", "tq_device.h", "tq_internal.h")]
 
@@ -53,14 +53,13 @@ def committed_traffic(workload, layers):
     + WRITE_SIZE, scaled by what they read for a copy of known size), if the
     committed measurement was taken on this workload and the kernel sources
     have not changed since; else None."""
-    try:
-        with open(TRAFFIC_FILE) as fh:
+    import glob
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        with open(path) as fh:
             kv = dict(l.strip().split("=", 1) for l in fh if "=" in l and not l.startswith("#"))
-    except OSError:
-        return None
-    if kv.get("source_hash") != kernel_source_hash() or kv.get("workload") != workload:
-        return None
-    return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+        if kv.get("workload") == workload and kv.get("source_hash") == kernel_source_hash():
+            return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    return None
 
 
 def summarize_counters(fetch_csv, write_csv, copy_mib):
@@ -70,28 +69,26 @@ def summarize_counters(fetch_csv, write_csv, copy_mib):
     factor)."""
     import csv
 
-    def per_kernel(path, counter):
-        vals = {}
+    def dispatches(path, counter):
+        rows = []
         with open(path) as fh:
             for row in csv.DictReader(fh):
-                if row.get("Counter_Name") != counter:
-                    continue
-                name = row.get("Kernel_Name", "")
-                vals.setdefault(name, []).append(float(row["Counter_Value"]))
-        return vals
+                if row.get("Counter_Name") == counter:
+                    rows.append((int(row["Dispatch_Id"]), row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+        return sorted(rows)
 
     out = {}
     for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
-        vals = per_kernel(path, counter)
-        dec = [v for n, vs in vals.items() if DECODE_KERNEL in n for v in vs]
-        # the calibration copy: the dispatches whose counter is nearest the copy size
+        rows = dispatches(path, counter)
+        dec = sorted(v for _, n, v in rows if DECODE_KERNEL in n)
+        # the calibration copy: the run's last three dispatches (bench.py issues
+        # the three copies after everything else), all of one kernel
         want = copy_mib * 1024.0
-        cands = [v for n, vs in vals.items() if DECODE_KERNEL not in n for v in vs if v > 0.5 * want]
-        if not dec or not cands:
-            raise SystemExit(f"{path}: no {DECODE_KERNEL} or copy dispatches with {counter}")
-        dec.sort()
+        tail = rows[-3:]
+        if not dec or len(tail) < 3 or len({n for _, n, _ in tail}) != 1 or DECODE_KERNEL in tail[0][1]:
+            raise SystemExit(f"{path}: no {DECODE_KERNEL} dispatches or no trailing calibration copies with {counter}")
         med = dec[len(dec) // 2]
-        copy = sorted(cands, key=lambda v: abs(v - want))[0]
+        copy = sorted(v for _, _, v in tail)[1]
         factor = copy / want
         out[f"{tag}_kib_per_launch_raw"] = med
         out[f"{tag}_copy_kib"] = copy
