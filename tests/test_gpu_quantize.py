@@ -182,12 +182,11 @@ def test_capacity_and_noop():
     assert e.value.status == tq.ECAPACITY
 
 
-@pytest.mark.parametrize("wname", synth.ORDER)
-@pytest.mark.parametrize("qjl", [False, True])
+# the QJL-corrected reconstruction exists for QJL keys only
+@pytest.mark.parametrize("wname,qjl", [(n, False) for n in synth.ORDER] +
+                         [(n, True) for n in synth.ORDER if synth.WORKLOADS[n].k_codec == synth.POLAR_QJL])
 def test_dequantize_matches_oracle(wname, qjl):
     w = synth.WORKLOADS[wname]
-    if qjl and w.k_codec != synth.POLAR_QJL:
-        pytest.skip("QJL correction applies to QJL keys only")
     ws = synth.with_ctx(w, 200, batch=2)
     cfg = tq.config_for(ws, seed=42, layer=2)
     spec = spec_of(cfg)
