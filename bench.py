@@ -1,25 +1,33 @@
 """Benchmark of the TurboQuant KV-cache hot path on one MI355X.
 
-Default workload: the Llama-3.1-8B-shaped decode layer (32 query / 8 KV
-heads, head dim 128, batch 1, 32768 cached positions, bf16 K/V; keys 3-bit
-codes + 128-row QJL sketch, values 2-bit codes), over 32 distinct layer
-caches so that every decode reads HBM rather than the 256 MB Infinity Cache.
+Headline workload (the default): the long-context decode layer -- 32 query /
+8 KV heads, head dim 128, batch 1, 1,048,576 cached positions, bf16 K/V; keys
+3-bit codes + 128-row QJL sketch, values 3-bit codes -- over 4 distinct layer
+caches (3.96 GB, far above the 256 MB Infinity Cache), so that every decode
+reads HBM.
 
-A timed step is one decode pass over the 32 layer caches (one
+A timed step is one decode pass over the layer caches (one
 tq_decode_attention launch per layer).  `value` is the decode attention
 throughput in GB/s of algorithmic bytes: the packed K and V records of every
 attended position plus the query and output, divided by the step time.  The
-quantize-append half of the metric is measured in its own timed region: the
-32768-position prefill of each of the 32 layers, reported as tokens/s.
+quantize-append half of the metric is measured in its own timed region (the
+whole-context prefill of every layer after the first), reported as
+positions/s and against the fp32 roof of its sketch contraction.
 
-Also printed: the roofline of the decode kernel (algorithmic bytes per launch
-over its mean launch duration, from HIP events on the launch stream around the
-timed region), the HBM traffic per launch measured with rocprofv3 counters
-(from profiles/, when taken on the current kernel sources), the median,
-minimum and maximum step time, the practical HBM read ceiling (a plain
-streaming read of 2 GiB on the same GPU) with the decode throughput as a
-fraction of it, and the oracle's CPU throughput on a bounded sample
-(single-threaded).
+`configs` repeats the measurement for the other seeded workloads that fit
+the same contract: the Llama-3.1-8B-shaped 32K layer (32 layer caches), the
+Command-R+-shaped 128K layer with q8 keys (64 caches) and the batched serving
+workload (16 x 8K, 32 caches, 64 serving steps that each append one position
+per sequence and decode over it in one launch).
+
+Also printed: the roofline of the headline decode kernel (algorithmic bytes
+per launch over its mean launch duration, from HIP events on the launch
+stream around the timed region), the HBM traffic per launch measured with
+rocprofv3 counters (from profiles/, when taken on the current kernel
+sources), the median, minimum and maximum step time, the practical HBM read
+ceiling (a plain streaming read of 2 GiB on the same GPU) with the decode
+throughput as a fraction of it, and the oracle's CPU throughput on a bounded
+sample of the headline workload (single-threaded).
 """
 from __future__ import annotations
 
@@ -33,6 +41,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 (matrix and vector)
+HEADLINE = "long_b1_ctx1m"
+CONFIG_SET = ("llama8b_b1_ctx32k", "cmdr104b_b1_ctx128k", "serving_b16_ctx8k")
+# what the matrix-core decode computes in: packed codes enter the matrix
+# cores as fp4 (e2m1) operands against exact integer digits in fp8 (e4m3)
+# with one E8M0 scale per 32 k-slots; every sum accumulates in fp32
+DECODE_DTYPE = ("fp4 code operands x fp8 digit operands, fp32 accumulate (query: 4 base-32 digits per "
+                "32-slot E8M0 block, about 19 significant bits; p*radius: 3 digits, about 14 bits; "
+                "q8 keys: int8 x 3 base-128 int8 query digits, int32 accumulate)")
 DECODE_KERNEL = "decode_mfma_kernel"   # name fragment of the timed decode kernel
 TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_mfma_*_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc", f)
@@ -107,26 +124,28 @@ def algorithmic_decode_bytes(w, cfg, tq, lens):
     return recs * (krec + vrec) + qo, krec, vrec
 
 
-def cpu_baseline(w, seed):
-    """Oracle, single-threaded: quantise one layer's prefill (tokens/s) and
-    decode all query heads over it (GB/s of the same algorithmic bytes)."""
+def cpu_baseline(w, seed, n_pos):
+    """Oracle, single-threaded, on a bounded sample of workload w: quantise the
+    first n_pos positions of one layer (all KV heads; positions/s) and decode
+    every query head over them (GB/s of the sample's algorithmic bytes)."""
     import numpy as np
 
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import oracle
     from compressed_decode_attention_quantize_amd import synth
 
-    k, v = synth.make_kv(w, w.ctx, seed=seed)
-    q = synth.make_q(w, seed=seed + 1000).numpy()
+    ws = synth.with_ctx(w, n_pos)
+    k, v = synth.make_kv(ws, n_pos, seed=seed)
+    q = synth.make_q(ws, seed=seed + 1000).numpy()
     kn = k.to("cpu").float().numpy()
     vn = v.to("cpu").float().numpy()
     codec = {synth.RAW_F32: 0, synth.POLAR: 1, synth.POLAR_QJL: 2, synth.Q8_BLOCK32: 3}
-    s = oracle.make_spec(d=w.d, n_q=w.n_q, n_kv=w.n_kv, batch=w.batch, max_ctx=w.ctx, k_codec=codec[w.k_codec],
+    s = oracle.make_spec(d=w.d, n_q=w.n_q, n_kv=w.n_kv, batch=w.batch, max_ctx=n_pos, k_codec=codec[w.k_codec],
                          k_bits=w.k_bits, m=w.m, v_codec=codec[w.v_codec], v_bits=w.v_bits)
     P = oracle.Params(s, 42, 0)
-    reps = 3   # about 10 s of single-threaded work at the 32K Llama shape
+    reps = 3   # about 10 s of single-threaded work at 32768 positions of the 32/8-head shape
     t_app = t_dec = 0.0
-    lens = np.full(w.batch, w.ctx, np.int32)
+    lens = np.full(w.batch, n_pos, np.int32)
     # the oracle is single-threaded C; the calling thread is pinned to one
     # host core while it runs
     allowed = os.sched_getaffinity(0)
@@ -148,13 +167,14 @@ def cpu_baseline(w, seed):
     t_dec /= reps
     sz = oracle.spec_sizes(s)
     rec = sz["k_record"] + sz["v_record"]
-    dec_bytes = w.batch * w.ctx * w.n_kv * rec + 2 * w.batch * w.n_q * w.d * 4
+    dec_bytes = w.batch * n_pos * w.n_kv * rec + 2 * w.batch * w.n_q * w.d * 4
     return {
         "value": dec_bytes / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"one layer of {w.name}, {reps} times: oracle quantize of {w.batch * w.ctx} positions x "
-                   f"{w.n_kv} KV heads ({t_app:.1f} s each) then fp64 decode of all {w.n_q} query heads "
+        "sample": (f"the first {n_pos} positions of one layer of {w.name} (same shapes and input recipe), "
+                   f"{reps} times: oracle quantize of {w.batch * n_pos} positions x {w.n_kv} KV heads "
+                   f"({t_app:.1f} s each) then fp64 decode of all {w.n_q} query heads over them "
                    f"({t_dec:.1f} s each), single-threaded C on the host"),
-        "append_tokens_per_s": w.batch * w.ctx / t_app,
+        "append_tokens_per_s": w.batch * n_pos / t_app,
         "seconds": reps * (t_app + t_dec),
         "pinned_core": core,
         "host_cpus_allowed": len(allowed),
@@ -238,14 +258,163 @@ def read_ceiling(tq, dev, nbytes=2 << 30, reps=10):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def append_flop_per_position(w):
+    """Arithmetic of quantising one (position, KV head): the raw FWHT of the
+    key and of the value (d log2 d additions each) and, for QJL keys, the
+    m x d sketch contraction (2 m d)."""
+    import math
+    fwht = w.d * int(math.log2(w.d))
+    sketch = 2 * w.m * w.d if w.k_codec == "polar_qjl" else 0
+    key = fwht if w.k_codec in ("polar", "polar_qjl", "polar_tree") else 0
+    val = fwht if w.v_codec in ("polar", "polar_tree") else 0
+    return sketch + key + val
+
+
+def append_roofline(w, positions_per_s, krec, vrec):
+    """Binding roof of the append: the fp32 arithmetic roof when the sketch
+    contraction makes it compute-bound, else HBM (inputs read, records
+    written)."""
+    flop = append_flop_per_position(w) * w.n_kv
+    in_bytes = 2 * w.d * (4 if w.dtype == "f32" else 2)
+    nbytes = (in_bytes + krec + vrec) * w.n_kv
+    t_flop = flop / (FP32_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_flop >= t_hbm:
+        ach = positions_per_s * flop / 1e12
+        return {"bound": "fp32", "achieved": round(ach, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP32_PEAK_TFLOPS, 4), "flop_per_position": flop, "kernel": "quant_kernel"}
+    ach = positions_per_s * nbytes / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_position": nbytes, "kernel": "quant_kernel"}
+
+
+def build_layers(w, n_layers, args, dev, tq, room=0):
+    """The workload's layer caches (or the mixed-codec / recursive polar stack
+    the flags ask for)."""
+    policy = None
+    if args.policy:
+        from compressed_decode_attention_quantize_amd import presets
+        kt, vt, prot = (args.policy.split("/") + ["0"])[:3]
+        policy = presets.layer_policy(n_layers, kt, vt, int(prot))
+        layers = [tq.KVLayer(presets.config(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v),
+                                            policy[l], l), dev, zero=False)
+                  for l in range(n_layers)]
+    elif args.tree_bits:
+        tkb, tvb = (int(x) for x in args.tree_bits.split("/"))
+        layers = [tq.KVLayer(tq.make_config(w.d, w.n_q, w.n_kv, w.batch, w.ctx, tq.POLAR_TREE, tkb, 0,
+                                            tq.POLAR_TREE, tvb, 0, 42, l, args.sparse_v), dev, zero=False)
+                  for l in range(n_layers)]
+    else:
+        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v, max_ctx=w.ctx + room),
+                             dev, zero=False)
+                  for l in range(n_layers)]
+    return layers, policy
+
+
+def time_prefill(layers, k, v, stream):
+    """Whole-context append of every layer: one untimed (layer 0), the rest
+    timed back to back.  Returns seconds per layer."""
+    import torch
+    layers[0].append(k, v)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for L in layers[1:]:
+        L.append(k, v)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / max(1, len(layers) - 1)
+
+
+def time_decode(layers, q, steps, warmup, stream):
+    """Decode passes over the layer stack: `warmup` untimed, then `steps`
+    timed with HIP events on the launch stream.  Returns (mean ms per step,
+    sorted per-step ms, wall seconds)."""
+    import torch
+    outs = [torch.empty_like(q) for _ in layers]
+
+    def step():
+        for i, L in enumerate(layers):
+            L.decode(q, out=outs[i])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for k_ in range(steps):
+        step()
+        marks[k_ + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = marks[0].elapsed_time(marks[-1]) / steps
+    per_step = sorted(marks[k_].elapsed_time(marks[k_ + 1]) for k_ in range(steps))
+    return step_ms, per_step, wall
+
+
+def measure_config(name, args, dev, tq, synth):
+    """One workload of the configs table: prefill and decode timings (the
+    serving workload: fused serving steps) with their roofline fractions."""
+    import torch
+    w = synth.WORKLOADS[name]
+    wi = synth.ORDER.index(name)
+    seed = 1000 + wi
+    stream = torch.cuda.current_stream()
+    n_layers = w.layers
+    steps = w.steps if w.steps else args.steps
+    room = (args.warmup + steps) if w.steps else 0
+    layers, _ = build_layers(w, n_layers, argparse.Namespace(policy="", tree_bits="", sparse_v=0), dev, tq, room)
+    k, v = synth.make_kv(w, w.ctx, seed=seed, device=dev)
+    q = synth.make_q(w, seed=seed + 1000, device=dev)
+    app_s = time_prefill(layers, k, v, stream)
+    del k, v
+    cfg0 = layers[0].cfg
+    nbytes, krec, vrec = algorithmic_decode_bytes(w, cfg0, tq, [w.ctx] * w.batch)
+    pos_s = w.batch * w.ctx / app_s
+    res = {"workload": name, "batch": w.batch, "context": w.ctx, "n_q_heads": w.n_q, "n_kv_heads": w.n_kv,
+           "k_codec": f"{w.k_codec} b{w.k_bits} m{w.m}", "v_codec": f"{w.v_codec} b{w.v_bits}",
+           "layers": n_layers, "record_bytes": {"k": krec, "v": vrec},
+           "append_tokens_per_s": round(pos_s, 1), "append_ms_per_layer": round(app_s * 1e3, 4),
+           "append_roofline": append_roofline(w, pos_s, krec, vrec)}
+    if w.steps:
+        sargs = argparse.Namespace(steps=steps, warmup=args.warmup, serve="fused")
+        sv = serve_steps(sargs, w, layers, q, dev, tq, synth, seed, nbytes)["serve"]
+        us = sv["us_per_layer_step"]
+        # the decode of a step attends ctx + warmup + s + 1 positions, s = 0 .. steps - 1
+        mean_len = w.ctx + args.warmup + (steps + 1) / 2.0
+        step_bytes = algorithmic_decode_bytes(w, cfg0, tq, [mean_len] * w.batch)[0]
+        gbs = step_bytes / (us * 1e-6) / 1e9
+        res.update({"mode": "serving steps (tq_append_decode: append one position per sequence and decode, "
+                            "one launch per layer)", "steps": steps,
+                    "us_per_launch": us, "decode_bytes_per_launch": int(step_bytes),
+                    "gbs": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": sv["tokens_per_s"], "ms_per_step_all_layers": sv["ms_per_step_all_layers"]})
+    else:
+        step_ms, per_step, _ = time_decode(layers, q, args.steps, args.warmup, stream)
+        us = step_ms * 1e3 / n_layers
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res.update({"mode": "decode (tq_decode_attention, one launch per layer)", "steps": args.steps,
+                    "us_per_launch": round(us, 3), "decode_bytes_per_launch": nbytes,
+                    "gbs": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "ms_per_step_median": round(per_step[len(per_step) // 2], 4)})
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_b1_ctx32k")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--layers", type=int, default=0, help="layer caches to cycle (0 = workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="headline workload only")
+    ap.add_argument("--cpu-sample", type=int, default=32768, metavar="N",
+                    help="positions of the oracle's bounded CPU sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device three times (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -290,44 +459,22 @@ def main():
     w = synth.WORKLOADS[args.workload]
     n_layers = args.layers or w.layers
     data_seed = 1000 + wi
+    variant = bool(args.policy or args.tree_bits or args.sparse_v or args.focus_every or args.serve)
 
     # ------------------------------------------------ inputs and layer caches
     k, v = synth.make_kv(w, w.ctx, seed=data_seed, device=dev)
     q = synth.make_q(w, seed=data_seed + 1000, device=dev)
     if args.focus_every:
         k, _ = synth.plant_focus_keys(w, k, q, seed=data_seed + 2000, every=args.focus_every)
-    policy = None
-    if args.policy:
-        from compressed_decode_attention_quantize_amd import presets
-        kt, vt, prot = (args.policy.split("/") + ["0"])[:3]
-        policy = presets.layer_policy(n_layers, kt, vt, int(prot))
-        layers = [tq.KVLayer(presets.config(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v),
-                                            policy[l], l), dev, zero=False)
-                  for l in range(n_layers)]
-    elif args.tree_bits:
-        tkb, tvb = (int(x) for x in args.tree_bits.split("/"))
-        layers = [tq.KVLayer(tq.make_config(w.d, w.n_q, w.n_kv, w.batch, w.ctx, tq.POLAR_TREE, tkb, 0,
-                                            tq.POLAR_TREE, tvb, 0, 42, l, args.sparse_v), dev, zero=False)
-                  for l in range(n_layers)]
-    else:
-        room = (args.warmup + args.steps) if args.serve else 0   # serving steps append past the prefill
-        layers = [tq.KVLayer(tq.config_for(w, seed=42, layer=l, sparse_v=args.sparse_v, max_ctx=w.ctx + room), dev,
-                             zero=False)
-                  for l in range(n_layers)]
+    room = (args.warmup + args.steps) if args.serve else 0   # serving steps append past the prefill
+    layers, policy = build_layers(w, n_layers, args, dev, tq, room)
     torch.cuda.synchronize()
 
     # ------------------------------------------ append: prefill of every layer
     stream = torch.cuda.current_stream()
-    layers[0].append(k, v)          # warm-up launch (also fills layer 0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for L in layers[1:]:
-        L.append(k, v)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    append_s = e0.elapsed_time(e1) / 1e3 / max(1, n_layers - 1)
+    append_s = time_prefill(layers, k, v, stream)
     append_tok_s = w.batch * w.ctx / append_s
+    del k, v
 
     # --------------------------------------------------------------- decode
     lens = [w.ctx] * w.batch
@@ -336,29 +483,7 @@ def main():
     if policy is not None:   # mean over the stack's layers
         per_layer = [algorithmic_decode_bytes(w, L.cfg, tq, lens)[0] for L in layers]
         bytes_per_launch = sum(per_layer) // n_layers
-    outs = [torch.empty_like(q) for _ in layers]
-
-    def step(events=None):
-        for i, L in enumerate(layers):
-            if events is not None:
-                events[i][0].record(stream)
-            L.decode(q, out=outs[i])
-            if events is not None:
-                events[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record(stream)
-    for k_ in range(args.steps):
-        step()
-        marks[k_ + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = marks[0].elapsed_time(marks[-1]) / args.steps
-    per_step = sorted(marks[k_].elapsed_time(marks[k_ + 1]) for k_ in range(args.steps))
+    step_ms, per_step, wall = time_decode(layers, q, args.steps, args.warmup, stream)
     ceiling = read_ceiling(tq, dev)
 
     # average duration of one decode launch: the timed region (HIP events on
@@ -378,7 +503,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DECODE_DTYPE,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "context": w.ctx, "n_q_heads": w.n_q,
                    "n_kv_heads": w.n_kv, "head_dim": w.d, "k_codec": f"{w.k_codec} b{w.k_bits} m{w.m}",
@@ -387,6 +512,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "append_tokens_per_s": round(append_tok_s, 1),
         "append_ms_per_layer": round(append_s * 1e3, 4),
+        "append_roofline": append_roofline(w, append_tok_s, krec, vrec),
         "decode_us_per_layer": round(step_ms * 1e3 / n_layers, 3),
         "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
         "ms_per_step_min": round(per_step[0], 4),
@@ -411,23 +537,29 @@ def main():
         result["cache_bytes_total"] = packed
         result["compression_vs_fp16"] = round(fp16 / packed, 3)
         result["roofline"]["traffic"] = None
-        result.pop("append_tokens_per_s")
-        result.pop("append_ms_per_layer")
+        for key in ("append_tokens_per_s", "append_ms_per_layer", "append_roofline"):
+            result.pop(key)
     if args.tree_bits:
         result["metric"] = "decode attention HBM GB/s on packed KV, recursive polar codec; quantize-append tokens/s"
-        result["config"]["k_codec"] = f"polar_tree b{tkb}"
-        result["config"]["v_codec"] = f"polar_tree b{tvb}"
+        result["config"]["k_codec"] = f"polar_tree b{args.tree_bits.split('/')[0]}"
+        result["config"]["v_codec"] = f"polar_tree b{args.tree_bits.split('/')[1]}"
         result["roofline"]["traffic"] = None
         result["roofline"]["kernel"] = "decode_kernel"
+        result["dtype"] = "fp32"
+        result.pop("append_roofline")
     if args.sparse_v or args.focus_every:
         result["config"]["sparse_v"] = args.sparse_v
         result["config"]["focus_every"] = args.focus_every
         result["data"] = "synthetic, planted focus keys" if args.focus_every else "synthetic"
     if args.serve:
         result.update(serve_steps(args, w, layers, q, dev, tq, synth, data_seed, bytes_per_launch))
-    if not args.no_cpu_baseline and policy is None and not (args.sparse_v or args.focus_every or args.tree_bits
-                                                            or args.serve):
-        result["cpu_baseline"] = cpu_baseline(w, data_seed)
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not variant and not args.no_configs and args.workload == HEADLINE:
+        result["configs"] = {name: measure_config(name, args, dev, tq, synth) for name in CONFIG_SET}
+    if not args.no_cpu_baseline and not variant:
+        result["cpu_baseline"] = cpu_baseline(w, data_seed, min(args.cpu_sample, w.ctx))
     if args.copy_calibration:
         src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

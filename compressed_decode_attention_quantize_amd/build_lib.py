@@ -2,7 +2,10 @@
 
 Every HIP translation unit is compiled with packed-fp32 instructions turned
 off and with correctly rounded fp32 division/sqrt; the append kernel also
-with -ffp-contract=off (its arithmetic is fixed bit for bit by the format).
+with -ffp-contract=off (its arithmetic is fixed bit for bit by the format),
+as is the matrix-core decode unit, which inlines the one-position quantiser
+for the fused serving step (its decode code re-enables contraction with a
+pragma after that include).
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ UNITS = [
     ("tq_quant.hip", ["-ffp-contract=off"]),
     ("tq_quant_tree.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
-    ("tq_decode_mfma.hip", ["-fno-honor-nans"]),
+    ("tq_decode_mfma.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
     ("tq_dequant.hip", []),
     ("tq_stream.hip", []),
 ]

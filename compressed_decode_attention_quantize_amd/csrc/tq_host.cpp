@@ -502,13 +502,19 @@ int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
 
 // ------------------------------------------------------ entry helpers
 
-// partials [batch][n_q][splits][kPartialStride] fp32, then the completion
-// counters [batch][n_kv][kMaxGroup / 4] u32, each 256-byte aligned
+// The completion counters [batch][n_kv][kMaxGroup / 4] u32 come first, at a
+// fixed offset (they must stay where the previous call left them at zero,
+// whatever length this call decodes), then the partials
+// [batch][n_q][splits][kPartialStride] fp32; each part 256-byte aligned.
+uint64_t counters_bytes(const tq_config* cfg) {
+  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * (tq::kMaxGroup / 4) * 4;
+  return (counters + 255) & ~255ull;
+}
+
 uint64_t workspace_need(const tq_config* cfg, int32_t max_seq_len) {
   const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
   const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
-  const uint64_t counters = static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * (tq::kMaxGroup / 4) * 4;
-  return ((partial + 255) & ~255ull) + ((counters + 255) & ~255ull);
+  return counters_bytes(cfg) + ((partial + 255) & ~255ull);
 }
 
 tq_status check_append(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
@@ -572,8 +578,6 @@ tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k
     return TQ_EINVAL;
   if (max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
   const int splits = decode_splits(cfg, max_seq_len);
-  const uint64_t partial =
-      static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * decode_splits_bound(cfg, max_seq_len) * tq::kPartialStride * 4;
   if (workspace_bytes < workspace_need(cfg, max_seq_len)) return TQ_EWORKSPACE;
   tq::DecodeArgs& a = *out_args;
   a = tq::DecodeArgs{};
@@ -584,8 +588,8 @@ tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k
   a.q = q;
   a.out = out;
   a.logits = logits;
-  a.partials = static_cast<float*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + ((partial + 255) & ~255ull));
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(cfg));
   a.batch = cfg->batch;
   a.n_q = cfg->n_q_heads;
   a.n_kv = cfg->n_kv_heads;

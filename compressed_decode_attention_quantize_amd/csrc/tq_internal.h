@@ -110,7 +110,7 @@ struct DecodeArgs {
   float* out;
   float* logits;      // may be null
   float* partials;    // [batch][n_q][n_splits][kPartialStride]
-  uint32_t* counters; // [batch][n_kv]
+  uint32_t* counters; // [batch][n_kv][kMaxGroup / 4]
   int32_t batch, n_q, n_kv, group, max_ctx, n_blocks;
   int32_t chunk_blocks, n_splits;
   int32_t k_codec, k_bits, v_codec, v_bits;

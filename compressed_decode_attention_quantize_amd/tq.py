@@ -11,8 +11,6 @@ import os
 
 import torch
 
-from . import synth
-
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 ABI_VERSION = 1
@@ -22,8 +20,10 @@ RAW_F32, POLAR, POLAR_QJL, Q8_BLOCK32, POLAR_TREE = range(5)
 F32, BF16, F16 = range(3)
 DEQ_QJL = 1
 
-CODEC_IDS = {synth.RAW_F32: RAW_F32, synth.POLAR: POLAR, synth.POLAR_QJL: POLAR_QJL,
-             synth.Q8_BLOCK32: Q8_BLOCK32, synth.POLAR_TREE: POLAR_TREE}
+FORMAT_VERSION = 1
+# codec names of a workload description (its k_codec / v_codec fields)
+CODEC_IDS = {"raw_f32": RAW_F32, "polar": POLAR, "polar_qjl": POLAR_QJL, "q8_block32": Q8_BLOCK32,
+             "polar_tree": POLAR_TREE}
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
@@ -117,7 +117,7 @@ def make_config(head_dim=128, n_q_heads=8, n_kv_heads=2, batch=1, max_ctx=1024, 
                   qjl_m, v_codec, v_bits, decode_chunk, seed, layer, sparse_v)
 
 
-def config_for(w: "synth.Workload", seed=42, layer=0, max_ctx=None, batch=None,
+def config_for(w, seed=42, layer=0, max_ctx=None, batch=None,
                decode_chunk=0, sparse_v=0) -> Config:
     return make_config(w.d, w.n_q, w.n_kv, w.batch if batch is None else batch,
                        w.ctx if max_ctx is None else max_ctx, CODEC_IDS[w.k_codec], w.k_bits, w.m,

@@ -42,6 +42,11 @@ extern "C" {
 #endif
 
 #define TQ_ABI_VERSION 1u
+/* Version of the packed cache and parameter-image format described at
+ * tq_cache_bytes and tq_params_host.  A cache written under one format
+ * version is read back (decode, dequantize, a resumed append) only by a
+ * library of the same version. */
+#define TQ_FORMAT_VERSION 1u
 #define TQ_BLOCK_TOKENS 128   /* positions per cache block */
 
 typedef enum {
@@ -105,7 +110,9 @@ typedef struct tq_config {
 /* Text for a status code (static storage). */
 const char* tq_status_string(tq_status s);
 
-/* Sizes in bytes of the K and V caches for cfg (host, pure).  Layout of one
+/* Sizes in bytes of the K and V caches for cfg (host, pure); the memory
+ * figures of the leviatan.io page's "Benchmarks de memoire" section are these
+ * sizes in closed form.  Layout of one
  * cache: [batch][n_kv][ceil(max_ctx/128)][block]; block = 128 positions of one
  * (sequence, KV head):
  *   K POLAR / POLAR_QJL (b bits, m rows): b code planes u32[d/32][128] (bit e
@@ -151,6 +158,12 @@ tq_status tq_init_params(const tq_config* cfg, void* params, uint64_t bytes, voi
 
 /* Quantise n_new new positions per sequence and store them at positions
  * seq_lens[b] .. seq_lens[b]+n_new-1 of every sequence b.
+ * The operation is the compression step of the wis-web.com reader article on
+ * TurboQuant in a llama.cpp fork (its three-step description: Walsh-Hadamard
+ * rotation, radius + angle with the angle's law known in advance, then the
+ * 1-bit QJL corrector of the residual), with the problem statement's fp16
+ * norms, fixed codebooks and m = 128 sign rows; the "K in q8_0" codec is the
+ * same article's asymmetric configuration.
  *   params    device, from tq_init_params for the same cfg
  *   k_cache, v_cache  device, tq_cache_bytes each, 16-byte aligned
  *   seq_lens  device int32[batch]; read only (the caller advances it)
@@ -173,10 +186,19 @@ tq_status tq_quantize_append(const tq_config* cfg, const void* params, void* k_c
                              const void* k_new, const void* v_new, int32_t in_dtype,
                              int32_t n_new, void* stream);
 
-/* Workspace for tq_decode_attention with sequences up to max_seq_len. */
+/* Workspace for tq_decode_attention with sequences up to max_seq_len (host,
+ * pure): completion counters at a fixed offset, then the split partials.
+ * A workspace sized for max_seq_len serves every call with a shorter bound,
+ * in any order. */
 tq_status tq_decode_workspace_bytes(const tq_config* cfg, int32_t max_seq_len, uint64_t* bytes);
 
 /* Decode attention: one query per sequence over positions [0, seq_lens[b]).
+ * The operation is the attention read straight from the compressed cache
+ * that the leviatan.io page ("TurboQuant : 6x moins de cache, jusqu'a 8x plus
+ * rapide", sections "Acceleration jusqu'a 8x du calcul d'attention" and
+ * "Comparaison 4-bit vs 32-bit") times against a 32-bit cache, and that the
+ * wis-web.com article runs as flash attention ("-fa on"); its logit is the
+ * problem statement's QJL-corrected inner-product estimator.
  *   q        device fp32 [batch][n_q][d]
  *   out      device fp32 [batch][n_q][d]
  *   logits   device fp32 [batch][n_q][max_ctx] or NULL: pre-softmax scaled
@@ -193,7 +215,9 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
                               const float* q, float* out, float* logits, void* workspace,
                               uint64_t workspace_bytes, void* stream);
 
-/* Serving step in one launch: append one new position per sequence (at
+/* Serving step in one launch (the batched-serving workload's step: one new
+ * position per sequence appended, then one decode query per sequence, as the
+ * wis-web.com article's llama-server runs it).  Append one new position per sequence (at
  * seq_lens[b], as tq_quantize_append with n_new = 1) and decode q over the
  * seq_lens[b] + 1 positions that then exist (as tq_decode_attention).  The
  * cache bytes and the outputs equal those of the two calls in that order.
@@ -212,7 +236,10 @@ tq_status tq_append_decode(const tq_config* cfg, const void* params, void* k_cac
                            int32_t in_dtype, const float* q, float* out, float* logits, void* workspace,
                            uint64_t workspace_bytes, void* stream);
 
-/* Dequantise positions [start, start+count) of sequence b.
+/* Dequantise positions [start, start+count) of sequence b: the inverse of
+ * the append's steps (codebook centroid times radius, inverse rotation; the
+ * wis-web.com article's PolarQuant paragraph), optionally with the QJL
+ * correction of the problem statement's estimator, written out as a vector.
  *   k_out, v_out  device fp32 [count][n_kv][d]; either may be NULL
  *   flags         TQ_DEQ_QJL: keys return x_tilde = x_hat + rho sqrt(pi/2)/m
  *                 R^T S^T sign, whose inner product with q is the estimator

@@ -258,3 +258,11 @@ def test_tree_config_validation(tq):
     cfg = tq.make_config(k_codec=tq.POLAR_TREE, k_bits=3)
     cfg.qjl_m = 128
     assert tq.lib().tq_cache_bytes(ctypes.byref(cfg), ctypes.byref(k), ctypes.byref(v)) == tq.EINVAL
+
+
+def test_format_version_matches_header(tq):
+    """The binding's format version is the header's TQ_FORMAT_VERSION."""
+    import re
+    with open(os.path.join(ROOT, "include", "tq.h")) as fh:
+        m = re.search(r"#define TQ_FORMAT_VERSION (\d+)u", fh.read())
+    assert m and int(m.group(1)) == tq.FORMAT_VERSION

@@ -138,9 +138,9 @@ def test_workspace_counters_return_to_zero_and_repeat():
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
-    # the counters live after the partials, 256-byte aligned; they must all be zero again
-    n_cnt = 2 * 8 * 4
-    assert torch.count_nonzero(ws[-256:][:n_cnt]) == 0
+    # the counters [batch][n_kv][4] u32 open the workspace; they must all be zero again
+    n_cnt = 2 * 8 * 4 * 4
+    assert torch.count_nonzero(ws[:n_cnt]) == 0
 
 
 def test_logits_equal_dequantised_qjl_inner_products():
@@ -185,3 +185,33 @@ def test_end_to_end_tiny_workload_full_size(wi, wname):
     check_logits(lg.cpu().numpy()[0], ref_lg, w.ctx, wname, skip=skip)
     check_out(out[0], ref_out, wname)
     print(st)
+
+
+@pytest.mark.parametrize("k_bits,v_bits,lengths", [
+    (3, 2, (4096, 2048, 4096, 1, 4096)),
+    # 4-bit values: 448 blocks run two block groups per workgroup, 449 one
+    (4, 4, (449 * 128 + 1, 448 * 128, 449 * 128 + 1, 300, 449 * 128 + 1)),
+])
+def test_workspace_reuse_across_lengths(k_bits, v_bits, lengths):
+    """One workspace sized for the longest call serves calls of every shorter
+    length in any order: each output equals (bit for bit) a decode of the same
+    length on a freshly zeroed workspace."""
+    n_max = max(lengths)
+    cfg = tq.make_config(n_q_heads=32, n_kv_heads=8, batch=1, max_ctx=n_max, k_codec=tq.POLAR_QJL, k_bits=k_bits,
+                         v_codec=tq.POLAR, v_bits=v_bits, seed=42, layer=0)
+    L = tq.KVLayer(cfg, DEV)
+    g = torch.Generator(device=DEV).manual_seed(17)
+    k = torch.randn((1, n_max, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((1, n_max, 8, 128), generator=g, device=DEV).to(torch.bfloat16)
+    L.append(k, v)
+    q = torch.randn((1, 32, 128), generator=g, device=DEV)
+    ws = torch.zeros(tq.decode_workspace_bytes(cfg, n_max), dtype=torch.uint8, device=DEV)
+    for n in lengths:
+        seq = torch.tensor([n], dtype=torch.int32, device=DEV)
+        out = torch.empty_like(q)
+        tq.decode_attention(cfg, L.params, L.k_cache, L.v_cache, seq, n, q, out, ws)
+        fresh = torch.empty_like(q)
+        tq.decode_attention(cfg, L.params, L.k_cache, L.v_cache, seq, n, q, fresh,
+                            torch.zeros(tq.decode_workspace_bytes(cfg, n), dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh), f"length {n} on the shared workspace"

@@ -1,8 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (one prefill append of the whole context, then decode), on
-sampled (sequence, KV head) pairs that the oracle recomputes from the same
-inputs: every record of the pair bit-exact (counted sign exceptions), the
-pair's query heads' logits and outputs to the bars."""
+benchmark times (one prefill append of the whole context, then decode): the
+records of every (sequence, KV head) bit-exact against the oracle (counted
+sign exceptions inside the band), and on sampled pairs the query heads'
+logits and outputs to the bars."""
 import concurrent.futures as cf
 
 import numpy as np
@@ -36,6 +36,31 @@ def _oracle_decode_threaded(sub, P, R, n, qh):
         futs = [ex.submit(oracle.decode, sub, P, R, [n], qh[None], [(0, g)], True) for g in range(G)]
         res = [f.result() for f in futs]
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
+def _check_all_records(cfg, layer, k, v, lens, label):
+    """Records of every (sequence, KV head) of the layer against the oracle,
+    one sequence at a time (the oracle quantises in parallel chunks)."""
+    kb, vb = tq.cache_bytes(cfg)
+    kseq, vseq = kb // cfg.batch, vb // cfg.batch
+    sub = spec_of(cfg, batch=1)
+    P = oracle.Params(sub, cfg.seed, cfg.layer)
+    tot = dict(records=0, sign_mismatch=0, sign_total=0)
+    for b in range(cfg.batch):
+        n = int(lens[b])
+        kc = layer.k_cache[b * kseq:(b + 1) * kseq].cpu().numpy()
+        vc = layer.v_cache[b * vseq:(b + 1) * vseq].cpu().numpy()
+        Gr = oracle.unpack_cache(sub, kc, vc, np.array([n], np.int32))
+        kn = widen_np(k[b, :n])
+        vn = widen_np(v[b, :n])
+        R = oracle_quantize_threaded(sub, P, kn, vn, n)
+        st = compare_records(sub, P, Gr, R, [n], kn[None], f"{label} b={b}")
+        for key in tot:
+            tot[key] += st[key]
+        del Gr, R
+    print(f"{label}: every record of {cfg.batch} x {cfg.n_kv_heads} (sequence, KV head) pairs bit-exact: {tot}",
+          flush=True)
+    return tot
 
 
 def _check_pair(cfg, layer, k, v, q, lg, out, b, h, n, label):
@@ -76,10 +101,25 @@ def test_full_size_prefill_then_decode(wi, wname):
     _check_pair(cfg, L, k, v, q, lg, out, 0, h, w.ctx, f"{wname} kv={h}")
 
 
+@pytest.mark.parametrize("wi,wname", [(i, n) for i, n in enumerate(synth.ORDER) if n != "serving_b16_ctx8k"])
+def test_full_size_records_every_head(wi, wname):
+    """The prefill of the benchmark's launch configuration: the records of
+    every KV head of the workload against the oracle."""
+    w = synth.WORKLOADS[wname]
+    print(f"[fullsize records] {wname}", flush=True)
+    cfg = tq.config_for(w, seed=42, layer=0)
+    L = tq.KVLayer(cfg, DEV)
+    k, v = synth.make_kv(w, w.ctx, seed=1000 + wi, device=DEV)
+    L.append(k, v)
+    torch.cuda.synchronize()
+    _check_all_records(cfg, L, k, v, [w.ctx] * w.batch, wname)
+
+
 def test_full_size_serving_steps():
     """Batched serving: 16 x 8192 prefill, then 64 steps of one appended
     position per sequence followed by decode; steps 0, 31 and 63 checked on
-    two sampled (sequence, KV head) pairs."""
+    two sampled (sequence, KV head) pairs, and at step 63 the records of
+    every (sequence, KV head)."""
     wi, w = 2, synth.WORKLOADS["serving_b16_ctx8k"]
     cfg = tq.config_for(w, seed=42, layer=0, max_ctx=w.ctx + w.steps)
     L = tq.KVLayer(cfg, DEV)
@@ -97,13 +137,16 @@ def test_full_size_serving_steps():
             n = w.ctx + step + 1
             for b, h in pairs:
                 _check_pair(cfg, L, k, v, q, lg, out, b, h, n, f"serving step {step} b={b} kv={h}")
+            if step == w.steps - 1:
+                _check_all_records(cfg, L, k, v, [n] * w.batch, f"serving step {step}")
 
 
 def test_full_size_fused_serving_steps():
     """The same 64 serving steps through the fused step (tq_append_decode:
     the new position stored and attended to in one launch, the launch the
     serving bench times): steps 0, 31 and 63 against the oracle on two
-    sampled (sequence, KV head) pairs, records included."""
+    sampled (sequence, KV head) pairs, records included, and at step 63 the
+    records of every (sequence, KV head)."""
     wi, w = 2, synth.WORKLOADS["serving_b16_ctx8k"]
     cfg = tq.config_for(w, seed=42, layer=0, max_ctx=w.ctx + w.steps)
     L = tq.KVLayer(cfg, DEV)
@@ -121,6 +164,8 @@ def test_full_size_fused_serving_steps():
             n = w.ctx + step + 1
             for b, h in pairs:
                 _check_pair(cfg, L, k, v, q, lg, out, b, h, n, f"fused serving step {step} b={b} kv={h}")
+            if step == w.steps - 1:
+                _check_all_records(cfg, L, k, v, [n] * w.batch, f"fused serving step {step}")
 
 
 def test_full_size_sparse_v_1m():

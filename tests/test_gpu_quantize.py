@@ -258,3 +258,159 @@ def test_append_every_codec(codec):
     R = oracle_quantize(spec, P, kn, vn, [300, 300])
     G = gpu_records(spec, L.k_cache, L.v_cache, [300, 300])
     print(compare_records(spec, P, G, R, [300, 300], kn, codec))
+
+
+# ------------------------------------------------------------------ edge cases
+
+def _tie_rows(D, bounds, sign=1.0):
+    """Rows x whose rotated vector y = H (D . x) holds a coordinate equal to
+    fp32(B_j n) for every positive boundary B_j (a tie, which the format sends
+    to the lower cell; sign -1 mirrors it onto -B_j).  x' = D . x is
+    (a, 0, 1, -1, 0, ...) for B_j < 1 (y_0 = a exactly, n^2 = a^2 + 2) and
+    (a, 1, ..., 1, 0, ...) with K ones otherwise (y_0 = a + K through the
+    FWHT's own rounding, computed with the oracle's fp32 transform); a starts
+    at the real root of y_0 / n = B_j and is walked over consecutive fp32
+    values until y_0 == fp32(B_j n) holds exactly."""
+    rows = []
+    D = np.asarray(D, np.float32)
+    for B in np.asarray(bounds, np.float32):
+        if B <= 0:
+            continue
+
+        def row(a):
+            xp = np.zeros(128, np.float32)
+            xp[0] = a
+            if B < 1.0:
+                xp[2], xp[3] = 1.0, -1.0
+            else:
+                xp[1:(2 if B < 1.35 else 8)] = 1.0
+            return xp
+
+        lo, hi = (0.0, 1e6) if B < 1.0 else (-1e6, 1.0)   # the branch where y_0 / n increases with a
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            xm = row(mid).astype(np.float64)
+            if xm.sum() / np.sqrt((xm * xm).sum()) < float(B):
+                lo = mid
+            else:
+                hi = mid
+        a = np.float32(hi)
+        found = None
+        for _ in range(20000):
+            xp = row(a)
+            y0 = oracle.fwht_f32(xp)[0]
+            n = np.float32(np.sqrt(oracle.tree_sumsq(xp)))
+            thr = np.float32(B * n)
+            if y0 == thr:
+                found = xp
+                break
+            a = np.nextafter(a, np.float32(np.inf) if y0 < thr else np.float32(-np.inf), dtype=np.float32)
+        assert found is not None, f"no exact tie found for boundary {B}"
+        rows.append(D * (np.float32(sign) * found))
+    return rows
+
+
+def _q8_rows():
+    """q8 blocks: a zero block, exact multiples of s = 2^-4 with the block
+    amax at 127 s, exact half-way points (k + 1/2) s (round half to even)."""
+    rng = np.random.default_rng(99)
+    rows = []
+    x = rng.standard_normal(128).astype(np.float32)
+    x[32:64] = 0.0                                                  # zero block
+    x[64:96] = (rng.integers(-127, 128, 32) * 2.0 ** -4).astype(np.float32)
+    x[64 + 7] = np.float32(127 * 2.0 ** -4)                         # block amax -> +127
+    x[96:128] = ((rng.integers(-120, 120, 32) + 0.5) * 2.0 ** -4).astype(np.float32)
+    x[96 + 3] = np.float32(-127 * 2.0 ** -4)                        # amax -> -127, s = 2^-4
+    rows.append(x)
+    y = np.zeros(128, np.float32)
+    y[:32] = (np.arange(-16, 16) * 2.0 ** -3).astype(np.float32)
+    y[5] = np.float32(127 * 2.0 ** -3)
+    rows.append(y)
+    return rows
+
+
+def _special_rows(P, spec):
+    """The edge cases of the format, one row per position (keys, values)."""
+    rng = np.random.default_rng(7)
+    base = [np.zeros(128, np.float32), np.full(128, -0.0, np.float32),
+            (rng.standard_normal(128) * 1e4).astype(np.float32),          # norm > 65504: radius saturates
+            np.full(128, 1e4, np.float32),
+            (rng.standard_normal(128) * 3e-6).astype(np.float32),        # fp16-subnormal radius
+            (rng.standard_normal(128) * 1e-30).astype(np.float32),       # radius rounds to zero
+            np.eye(128, dtype=np.float32)[5] * 2.5,
+            np.ones(128, np.float32)]
+    kb = P.kbounds if spec.k_codec in (oracle.POLAR, oracle.POLAR_QJL) else np.zeros(0, np.float32)
+    keys = base + _tie_rows(P.DK, kb) + _tie_rows(P.DK, kb, -1.0)
+    if spec.k_codec == oracle.Q8_BLOCK32:
+        keys += _q8_rows()
+    vals = base + _tie_rows(P.DV, P.vbounds) + _tie_rows(P.DV, P.vbounds, -1.0)
+    n = max(len(keys), len(vals))
+    keys += [rng.standard_normal(128).astype(np.float32) for _ in range(n - len(keys))]
+    vals += [rng.standard_normal(128).astype(np.float32) for _ in range(n - len(vals))]
+    return np.stack(keys), np.stack(vals)
+
+
+SPECIAL_CODECS = {
+    "qjl2_v2": (tq.POLAR_QJL, 2, tq.POLAR, 2),
+    "qjl3_v3": (tq.POLAR_QJL, 3, tq.POLAR, 3),
+    "qjl4_v4": (tq.POLAR_QJL, 4, tq.POLAR, 4),
+    "polar3_v2": (tq.POLAR, 3, tq.POLAR, 2),
+    "q8_v2": (tq.Q8_BLOCK32, 8, tq.POLAR, 2),
+    "q8_v4": (tq.Q8_BLOCK32, 8, tq.POLAR, 4),
+}
+
+
+@pytest.mark.parametrize("path", ["tile", "one_position", "fused_step"])
+@pytest.mark.parametrize("codec", list(SPECIAL_CODECS))
+def test_append_special_vectors(codec, path):
+    """Zero and signed-zero vectors (codes 0, radii 0, every sign bit 1),
+    exact ties y_i == fp32(B_j n) on every boundary of both signs (lower
+    cell), a norm past 65504 (radius saturates), fp16-subnormal and
+    underflowing radii, one-hot and constant rows, q8 zero blocks, exact
+    multiples (amax -> +-127) and exact half-way points: every field of the
+    records bit-exact against the oracle through the 16-position tile
+    kernel (one append of every row), the one-position kernel (one append
+    per row) and the fused serving step (one step per row)."""
+    kc_, kb_, vc_, vb_ = SPECIAL_CODECS[codec]
+    cfg = tq.make_config(n_q_heads=8, n_kv_heads=2, batch=1, max_ctx=128, k_codec=kc_, k_bits=kb_,
+                         v_codec=vc_, v_bits=vb_, seed=42, layer=6)
+    spec = spec_of(cfg)
+    P = oracle.Params(spec, 42, 6)
+    xk, xv = _special_rows(P, spec)
+    n = xk.shape[0]
+    # two KV heads: head 0 the rows, head 1 the rows in reverse order
+    k = np.stack([xk, xk[::-1]], axis=1)[None].copy()
+    v = np.stack([xv, xv[::-1]], axis=1)[None].copy()
+    print(f"[special] {codec} {path} rows={n}", flush=True)
+    L = tq.KVLayer(cfg, DEV)
+    kd, vd = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+    if path == "tile":
+        L.append(kd, vd)
+    elif path == "one_position":
+        for t in range(n):
+            L.append(kd[:, t:t + 1].contiguous(), vd[:, t:t + 1].contiguous())
+    else:
+        g = torch.Generator().manual_seed(3)
+        for t in range(n):
+            q = torch.randn((1, 8, 128), generator=g).to(DEV)
+            out = L.step(kd[:, t:t + 1].contiguous(), vd[:, t:t + 1].contiguous(), q)
+            # the fused step equals a decode of the cache it leaves behind
+            ref = torch.empty_like(q)
+            tq.decode_attention(cfg, L.params, L.k_cache, L.v_cache, L.seq_lens, L.max_len, q, ref,
+                                torch.zeros_like(L.workspace))
+            torch.cuda.synchronize()
+            assert torch.equal(torch.nan_to_num(out, nan=7.0), torch.nan_to_num(ref, nan=7.0)), f"step {t}"
+    torch.cuda.synchronize()
+    R = oracle_quantize(spec, P, k, v, [n])
+    G = gpu_records(spec, L.k_cache, L.v_cache, [n])
+    st = compare_records(spec, P, G, R, [n], k, f"{codec} {path}")
+    if spec.k_codec == oracle.POLAR_QJL:
+        for h, t in ((0, 0), (0, 1), (1, n - 1), (1, n - 2)):   # the zero rows of either head
+            i = R.rec_index(0, t, h)
+            assert np.all(G.signs[i] == 1) and G.rho16[i] == 0 and G.kn16[i] == 0
+            assert np.all(G.kcodes[i] == 0)
+    if spec.v_codec == oracle.POLAR:
+        for h, t in ((0, 0), (0, 1), (1, n - 1), (1, n - 2)):
+            i = R.rec_index(0, t, h)
+            assert G.vn16[i] == 0 and np.all(G.vcodes[i] == 0)
+    print(st)
