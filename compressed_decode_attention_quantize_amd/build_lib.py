@@ -34,6 +34,7 @@ UNITS = [
     ("tq_decode_mfma.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
     ("tq_dequant.hip", []),
     ("tq_stream.hip", []),
+    ("tq_scratch.hip", []),
 ]
 
 

@@ -565,20 +565,28 @@ hipError_t launch_append(const tq_config* cfg, const void* params, void* k_cache
 }
 
 // Checks and kernel arguments of a decode over lengths up to max_seq_len.
-tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
-                         const int32_t* seq_lens, int32_t max_seq_len, const float* q, float* out, float* logits,
-                         void* workspace, uint64_t workspace_bytes, tq::DecodeArgs* out_args) {
+// Argument checks of a decode (no workspace involved).
+tq_status check_decode(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, int32_t max_seq_len, const float* q, float* out, float* logits) {
   const tq_status st = check_cfg(cfg);
   if (st != TQ_OK) return st;
   if (params == nullptr || k_cache == nullptr || v_cache == nullptr || seq_lens == nullptr || q == nullptr ||
-      out == nullptr || workspace == nullptr)
+      out == nullptr)
     return TQ_EINVAL;
   if (!aligned(params, 256) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(seq_lens, 4) ||
-      !aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 256) || (logits && !aligned(logits, 4)))
+      !aligned(q, 16) || !aligned(out, 16) || (logits && !aligned(logits, 4)))
     return TQ_EINVAL;
   if (max_seq_len < 0 || max_seq_len > cfg->max_ctx) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+// Kernel arguments of a decode over lengths up to max_seq_len (arguments
+// already checked): the completion counters at `counters` (counters_bytes
+// of them, zero between calls), the rest of the workspace at `rest`.
+void fill_decode_args(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, int32_t max_seq_len, const float* q, float* out, float* logits,
+                      uint32_t* counters, uint8_t* rest, tq::DecodeArgs* out_args) {
   const int splits = decode_splits(cfg, max_seq_len);
-  if (workspace_bytes < workspace_need(cfg, max_seq_len)) return TQ_EWORKSPACE;
   tq::DecodeArgs& a = *out_args;
   a = tq::DecodeArgs{};
   a.tb = tables(cfg, params);
@@ -588,8 +596,8 @@ tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k
   a.q = q;
   a.out = out;
   a.logits = logits;
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(cfg));
+  a.counters = counters;
+  a.partials = reinterpret_cast<float*>(rest);
   a.batch = cfg->batch;
   a.n_q = cfg->n_q_heads;
   a.n_kv = cfg->n_kv_heads;
@@ -606,6 +614,20 @@ tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k
   a.sparse_v = cfg->sparse_v;
   a.k_block_bytes = kBlock * k_record_bytes(cfg);
   a.v_block_bytes = kBlock * v_record_bytes(cfg);
+}
+
+// Checks and kernel arguments of a decode on a caller's workspace: counters
+// at offset 0, the partials after them.
+tq_status prepare_decode(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, int32_t max_seq_len, const float* q, float* out, float* logits,
+                         void* workspace, uint64_t workspace_bytes, tq::DecodeArgs* out_args) {
+  const tq_status st = check_decode(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits);
+  if (st != TQ_OK) return st;
+  if (workspace == nullptr || !aligned(workspace, 256)) return TQ_EINVAL;
+  if (workspace_bytes < workspace_need(cfg, max_seq_len)) return TQ_EWORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  fill_decode_args(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits,
+                   reinterpret_cast<uint32_t*>(ws), ws + counters_bytes(cfg), out_args);
   return TQ_OK;
 }
 
@@ -695,6 +717,28 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
   if (st != TQ_OK) return st;
   hipError_t e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
+}
+
+tq_status tq_decode_attention_noalloc(const tq_config* cfg, const void* params, const void* k_cache,
+                                      const void* v_cache, const int32_t* seq_lens, int32_t max_seq_len,
+                                      const float* q, float* out, float* logits, void* stream) {
+  tq_status st = check_decode(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits);
+  if (st != TQ_OK) return st;
+  // the same layout as a caller's workspace, with the counters in a region of
+  // fixed size that calls of every configuration share
+  if (counters_bytes(cfg) > tq::kScratchCounterBytes ||
+      workspace_need(cfg, max_seq_len) - counters_bytes(cfg) > tq::kScratchBytes - tq::kScratchCounterBytes)
+    return TQ_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ptr = nullptr;
+  if (tq::scratch_workspace(&ptr, s) != hipSuccess) return TQ_EDEVICE;
+  uint8_t* base = static_cast<uint8_t*>(ptr);
+  tq::DecodeArgs a{};
+  fill_decode_args(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits,
+                   reinterpret_cast<uint32_t*>(base), base + tq::kScratchCounterBytes, &a);
+  hipError_t e = tq::launch_decode_mfma(a, s);
+  if (e == hipErrorNotSupported) e = tq::launch_decode(a, s);
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
 

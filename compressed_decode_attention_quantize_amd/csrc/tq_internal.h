@@ -153,6 +153,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 constexpr int kMfmaUnitWorkgroups = 512;
 constexpr int kValuWorkgroups = 1024;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+// The library's own decode workspace (tq_decode_attention_noalloc): counters
+// in the first kScratchCounterBytes (zero between calls), the partials after
+// them.  Device address of the current device's copy; set up on first use.
+constexpr uint64_t kScratchBytes = 8ull << 20;
+constexpr uint64_t kScratchCounterBytes = 64ull << 10;
+hipError_t scratch_workspace(void** out, hipStream_t stream);
 // Append for tensors stored with the recursive polar codec (the other kernel
 // skips them).
 hipError_t launch_quantize_tree(const QuantArgs& a, hipStream_t stream);

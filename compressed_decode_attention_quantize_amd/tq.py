@@ -70,12 +70,13 @@ def lib() -> ctypes.CDLL:
                                           _vp, ctypes.c_uint64, _vp]
         L.tq_dequantize.argtypes = [_cfgp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, _vp, _vp, ctypes.c_uint32, _vp]
+        L.tq_decode_attention_noalloc.argtypes = [_cfgp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp]
         L.tq_append_decode.argtypes = [_cfgp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32,
                                        _vp, _vp, _vp, _vp, ctypes.c_uint64, _vp]
         L.tq_stream_read.argtypes = [_vp, ctypes.c_uint64, _vp, _vp]
         for fn in ("tq_cache_bytes", "tq_params_bytes", "tq_params_host", "tq_init_params",
                    "tq_quantize_append", "tq_decode_workspace_bytes", "tq_decode_attention",
-                   "tq_dequantize", "tq_append_decode", "tq_stream_read"):
+                   "tq_dequantize", "tq_append_decode", "tq_stream_read", "tq_decode_attention_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,6 +185,20 @@ def decode_attention(cfg: Config, params, k_cache, v_cache, seq_lens, max_seq_le
                                      _ptr(seq_lens), int(max_seq_len), _ptr(q), _ptr(out), _ptr(logits),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)), "tq_decode_attention")
+
+
+def decode_attention_noalloc(cfg: Config, params, k_cache, v_cache, seq_lens, max_seq_len: int, q, out, logits=None,
+                             stream=None):
+    """tq_decode_attention on the library's own per-GPU scratch array instead
+    of a caller workspace (no device allocation anywhere in the call)."""
+    assert q.dtype == torch.float32 and q.is_contiguous()
+    assert tuple(q.shape) == (cfg.batch, cfg.n_q_heads, cfg.head_dim)
+    assert out.dtype == torch.float32 and out.shape == q.shape and out.is_contiguous()
+    if logits is not None:
+        assert logits.dtype == torch.float32 and tuple(logits.shape) == (cfg.batch, cfg.n_q_heads, cfg.max_ctx)
+    _check(lib().tq_decode_attention_noalloc(ctypes.byref(cfg), _ptr(params), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(seq_lens), int(max_seq_len), _ptr(q), _ptr(out), _ptr(logits),
+                                             _stream(stream)), "tq_decode_attention_noalloc")
 
 
 def append_decode(cfg: Config, params, k_cache, v_cache, seq_lens, max_seq_len: int, k_new, v_new, q, out,

@@ -215,6 +215,23 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
                               const float* q, float* out, float* logits, void* workspace,
                               uint64_t workspace_bytes, void* stream);
 
+/* tq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The library uses its own file-scope
+ * device array instead: 8 MiB per GPU, held until the process ends, found
+ * once per device on the first call (which also clears its completion
+ * counters with a small kernel on `stream`).  The first 64 KiB hold the
+ * counters (batch * n_kv_heads <= 4096), the rest the split partials; a call
+ * that needs more returns TQ_EWORKSPACE before any launch.  No allocation,
+ * free or allocating library routine is called.  `stream` must belong to the
+ * current device.  Every call on one GPU shares that GPU's array: calls that
+ * may overlap on one GPU (different streams, different threads) race and
+ * must be serialised by the caller.  Arguments and results otherwise as
+ * tq_decode_attention. */
+tq_status tq_decode_attention_noalloc(const tq_config* cfg, const void* params, const void* k_cache,
+                                      const void* v_cache, const int32_t* seq_lens, int32_t max_seq_len,
+                                      const float* q, float* out, float* logits, void* stream);
+
 /* Serving step in one launch (the batched-serving workload's step: one new
  * position per sequence appended, then one decode query per sequence, as the
  * wis-web.com article's llama-server runs it).  Append one new position per sequence (at

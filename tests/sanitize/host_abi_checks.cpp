@@ -22,6 +22,7 @@ hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t) { return hipErrorN
 hipError_t launch_dequantize(const DequantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quantize_tree(const QuantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_stream_read(const void*, uint64_t, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
+hipError_t scratch_workspace(void**, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace tq
 
 extern "C" hipError_t hipMemcpyAsync(void*, const void*, size_t, hipMemcpyKind, hipStream_t) {
@@ -102,6 +103,8 @@ int main() {
     EXPECT(tq_decode_attention(&c, dev, dev, dev, lens, 700, nullptr, fdev, nullptr, dev, need, nullptr) ==
            TQ_EINVAL);
     EXPECT(tq_decode_attention(&c, dev, dev, dev, lens, 700, fdev, fdev, nullptr, dev, need, nullptr) == TQ_EDEVICE);
+    EXPECT(tq_decode_attention_noalloc(&c, dev, dev, dev, lens, 700, fdev, fdev, nullptr, nullptr) == TQ_EDEVICE);
+    EXPECT(tq_decode_attention_noalloc(&c, dev, dev, dev, lens, 1001, fdev, fdev, nullptr, nullptr) == TQ_EINVAL);
     EXPECT(tq_append_decode(&c, dev, dev, dev, lens, 1000, dev, dev, TQ_BF16, fdev, fdev, nullptr, dev, need,
                             nullptr) == TQ_ECAPACITY);
     // dequantize

@@ -25,7 +25,7 @@ def tq():
 def test_every_declared_symbol_is_exported(tq):
     hdr = open(os.path.join(ROOT, "include", "tq.h")).read()
     names = set(re.findall(r"^(?:tq_status|const char\*)\s+(tq_\w+)\(", hdr, re.M))
-    assert len(names) == 11
+    assert len(names) == 12
     L = tq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -266,3 +266,21 @@ def test_format_version_matches_header(tq):
     with open(os.path.join(ROOT, "include", "tq.h")) as fh:
         m = re.search(r"#define TQ_FORMAT_VERSION (\d+)u", fh.read())
     assert m and int(m.group(1)) == tq.FORMAT_VERSION
+
+
+def test_noalloc_size_limits_checked_on_the_host(tq):
+    """The no-allocation decode rejects configurations whose counters or
+    partials do not fit the library's scratch array, before any HIP call."""
+    L = tq.lib()
+    fake = ctypes.c_void_p(1 << 20)   # aligned; never dereferenced by the host checks
+    big_partials = tq.make_config(n_q_heads=64, n_kv_heads=8, batch=512, max_ctx=256)
+    assert L.tq_decode_attention_noalloc(ctypes.byref(big_partials), fake, fake, fake, fake, 256, fake, fake, None,
+                                         None) == tq.EWORKSPACE
+    big_counters = tq.make_config(n_q_heads=16, n_kv_heads=16, batch=257, max_ctx=128)
+    assert L.tq_decode_attention_noalloc(ctypes.byref(big_counters), fake, fake, fake, fake, 128, fake, fake, None,
+                                         None) == tq.EWORKSPACE
+    cfg = tq.make_config()
+    assert L.tq_decode_attention_noalloc(ctypes.byref(cfg), fake, fake, fake, fake, cfg.max_ctx + 1, fake, fake,
+                                         None, None) == tq.EINVAL
+    assert L.tq_decode_attention_noalloc(ctypes.byref(cfg), None, fake, fake, fake, 10, fake, fake, None,
+                                         None) == tq.EINVAL
