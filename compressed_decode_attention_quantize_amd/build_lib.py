@@ -32,6 +32,7 @@ UNITS = [
     ("tq_quant_tree.hip", ["-ffp-contract=off"]),
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
+    ("tq_decode_reg.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
     ("tq_dequant.hip", []),
     ("tq_stream.hip", []),
     ("tq_scratch.hip", []),

@@ -437,14 +437,20 @@ tq::Tables tables(const tq_config* c, const void* params) {
   return t;
 }
 
+// Register-streamed matrix-core decode (POLAR / POLAR_QJL keys, POLAR values).
+bool reg_path(const tq_config* c) {
+  return tq::decode_reg_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
+}
+
+// Ring-staged matrix-core decode: the other codecs it serves (q8 keys).
 bool mfma_path(const tq_config* c) {
-  return tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
+  return !reg_path(c) && tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
 }
 
 // Independent (sequence, KV head, head group) units the splits multiply: the
 // matrix-core kernel serves up to four query heads per workgroup.
 int64_t split_units(const tq_config* c) {
-  const int64_t groups = mfma_path(c) ? (c->n_q_heads / c->n_kv_heads + 3) / 4 : 1;
+  const int64_t groups = (mfma_path(c) || reg_path(c)) ? (c->n_q_heads / c->n_kv_heads + 3) / 4 : 1;
   return static_cast<int64_t>(c->batch) * c->n_kv_heads * groups;
 }
 
@@ -475,6 +481,7 @@ int mfma_groups(const tq_config* c, int32_t max_seq_len) {
 }
 
 int64_t target_workgroups(const tq_config* c, int32_t max_seq_len) {
+  if (reg_path(c)) return tq::kRegWorkgroups;
   return mfma_path(c) ? tq::kMfmaUnitWorkgroups / mfma_groups(c, max_seq_len) : tq::kValuWorkgroups;
 }
 
@@ -511,10 +518,22 @@ uint64_t counters_bytes(const tq_config* cfg) {
   return (counters + 255) & ~255ull;
 }
 
-uint64_t workspace_need(const tq_config* cfg, int32_t max_seq_len) {
+// Query operands of the register-streamed decode: one kQopsStride record per
+// (sequence, KV head, head group), after the counters.
+uint64_t qops_bytes(const tq_config* cfg) {
+  if (!reg_path(cfg)) return 0;
+  const uint64_t groups = (cfg->n_q_heads / cfg->n_kv_heads + 3) / 4;
+  return static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * groups * tq::kQopsStride;
+}
+
+uint64_t partials_bytes(const tq_config* cfg, int32_t max_seq_len) {
   const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
   const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
-  return counters_bytes(cfg) + ((partial + 255) & ~255ull);
+  return (partial + 255) & ~255ull;
+}
+
+uint64_t workspace_need(const tq_config* cfg, int32_t max_seq_len) {
+  return counters_bytes(cfg) + qops_bytes(cfg) + partials_bytes(cfg, max_seq_len);
 }
 
 tq_status check_append(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
@@ -597,7 +616,8 @@ void fill_decode_args(const tq_config* cfg, const void* params, const void* k_ca
   a.out = out;
   a.logits = logits;
   a.counters = counters;
-  a.partials = reinterpret_cast<float*>(rest);
+  a.qops = reg_path(cfg) ? reinterpret_cast<uint32_t*>(rest) : nullptr;
+  a.partials = reinterpret_cast<float*>(rest + qops_bytes(cfg));
   a.batch = cfg->batch;
   a.n_q = cfg->n_q_heads;
   a.n_kv = cfg->n_kv_heads;
@@ -715,7 +735,8 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
   const tq_status st = prepare_decode(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits, workspace,
                                       workspace_bytes, &a);
   if (st != TQ_OK) return st;
-  hipError_t e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
+  hipError_t e = tq::launch_decode_reg(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
@@ -737,7 +758,8 @@ tq_status tq_decode_attention_noalloc(const tq_config* cfg, const void* params, 
   tq::DecodeArgs a{};
   fill_decode_args(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits,
                    reinterpret_cast<uint32_t*>(base), base + tq::kScratchCounterBytes, &a);
-  hipError_t e = tq::launch_decode_mfma(a, s);
+  hipError_t e = tq::launch_decode_reg(a, s);
+  if (e == hipErrorNotSupported) e = tq::launch_decode_mfma(a, s);
   if (e == hipErrorNotSupported) e = tq::launch_decode(a, s);
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
 }
@@ -754,12 +776,13 @@ tq_status tq_append_decode(const tq_config* cfg, const void* params, void* k_cac
   if (st != TQ_OK) return st;
   a.len_add = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mfma_path(cfg)) {
+  if (reg_path(cfg) || mfma_path(cfg)) {
     a.k_new = k_new;
     a.v_new = v_new;
     a.in_dtype = in_dtype;
-    hipError_t e = tq::launch_decode_mfma(a, s);
+    hipError_t e = reg_path(cfg) ? tq::launch_decode_reg(a, s) : tq::launch_decode_mfma(a, s);
     if (e != hipErrorNotSupported) return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
+    a.k_new = a.v_new = nullptr;
   }
   // codecs the matrix-core kernel does not serve: the two launches in order
   hipError_t e = launch_append(cfg, params, k_cache, v_cache, seq_lens, k_new, v_new, in_dtype, 1, s);
