@@ -19,6 +19,10 @@ bool decode_mfma_applies(int k_codec, int v_codec, int group) {
   return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL || k_codec == Q8_BLOCK32);
 }
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
+bool decode_reg_applies(int k_codec, int v_codec, int group) {
+  return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL);
+}
+hipError_t launch_decode_reg(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_dequantize(const DequantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quantize_tree(const QuantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_stream_read(const void*, uint64_t, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
