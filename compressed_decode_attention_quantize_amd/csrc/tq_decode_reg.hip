@@ -44,24 +44,38 @@ struct KeyOps {
 };
 
 // ------------------------------------------------------------- query prep
-// One workgroup per (sequence, KV head, head group); wave g takes query head
-// 4 hg + g (zero past the group).  q_raw = H D_K q in registers; the sketch
-// S q_raw / sqrt d as (S H D_K / sqrt d) q from the table; then base-32 digits
-// with one E8M0 exponent per 32 k-slots (the operand layout of
+// One workgroup of eight waves per (sequence, KV head, head group) of four
+// query heads (zero past the group).  Waves 0..3 rotate head w's query
+// (q_raw = H D_K q); every wave loads its 16-coordinate slice of the sketch
+// table and forms its share of (S H D_K / sqrt d) q for the four heads (the
+// eight shares of a row are added in wave order), so the table's loads are
+// in flight together and no wave walks all 128 coordinates.  Then base-32
+// digits with one E8M0 exponent per 32 k-slots (the operand layout of
 // v_mfma_scale_f32_16x16x128_f8f6f4: k-slot k stands for coordinate or sketch
 // row pos_of_slot(k); the k-slots that meet the sign field of the affine key
-// operand carry the value with its sign flipped), written as each decode
-// lane's 32 operand bytes and scale byte.
+// operand carry the value with its sign flipped), one (operand set, head)
+// pair per wave at a time, written as each decode lane's 32 operand bytes
+// and scale byte.
+constexpr int kPrepThreads = 512;
+// The logit's constant factors travel in the query digits: log2(e) / sqrt d
+// (softmax in base 2, scale 1/sqrt d) times 1/d for the code term (the raw
+// FWHT's d) and sqrt(pi/2)/m for the sketch term (the estimator's constant);
+// a logit is then n16 * code + rho16 * sketch.
+constexpr float kCodeScale = 1.4426950408889634f * 0.08838834764831845f / 128.0f;
+constexpr float kSketchScale = 1.4426950408889634f * 0.08838834764831845f * 1.2533141373155003f / 128.0f;
+
 template <int KB, bool QJL>
-__global__ __launch_bounds__(kRegThreads) void qprep_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kPrepThreads) void qprep_kernel(DecodeArgs a) {
   using KO = KeyOps<KB>;
   constexpr int NSETS = KO::code_sets + (QJL ? 1 : 0);
+  constexpr int kWavesP = kPrepThreads / 64;
+  constexpr int kCpw = kD / kWavesP;   // table coordinates per wave
   __shared__ __attribute__((aligned(16))) uint8_t alimb[NSETS][16 * 128];   // [set][row = 4g + j][k]
   __shared__ uint8_t aexp[NSETS][4][16];                                   // [set][k / 32][row]
   __shared__ float cconst[NSETS][4];
   __shared__ float qr[4][kD];     // rotated query per head
   __shared__ float qs[4][kD];     // the query per head (before rotation)
-  __shared__ __attribute__((aligned(16))) float sred[4][4][kM];   // [wave][head][row]: partial sketch sums
+  __shared__ __attribute__((aligned(16))) float sred[kWavesP][4][kM];   // [wave][head][row]: partial sketch sums
   const int nhg = (a.group + 3) >> 2;
   const int u = blockIdx.x;                  // (b * n_kv + h) * nhg + hg
   const int hg = u % nhg;
@@ -71,45 +85,41 @@ __global__ __launch_bounds__(kRegThreads) void qprep_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int G = min(4, a.group - 4 * hg);
   const int hq0 = h * a.group + 4 * hg;
-  const bool live = w < G;
-  const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
-  const float q0 = live ? qp[lane] : 0.0f, q1 = live ? qp[lane + 64] : 0.0f;
-  // this wave's slice of the sketch table: coordinates [32 w, 32 w + 32),
-  // sketch rows 2 lane, 2 lane + 1 (all its loads in flight together)
-  float2 st2[32];
+  float2 st2[kCpw];
   if constexpr (QJL) {
 #pragma unroll
-    for (int c = 0; c < 32; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (32 * w + c) * kM + 2 * lane);
+    for (int c = 0; c < kCpw; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * w + c) * kM + 2 * lane);
   }
-  float lo = q0 * a.tb.dk[lane], hi = q1 * a.tb.dk[lane + 64];
-  qs[w][lane] = q0;
-  qs[w][lane + 64] = q1;
-  wave_fwht128(lo, hi, lane);
-  qr[w][lane] = lo;
-  qr[w][lane + 64] = hi;
+  if (w < 4) {
+    const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
+    const float q0 = (w < G) ? qp[lane] : 0.0f, q1 = (w < G) ? qp[lane + 64] : 0.0f;
+    float lo = q0 * a.tb.dk[lane], hi = q1 * a.tb.dk[lane + 64];
+    qs[w][lane] = q0;
+    qs[w][lane + 64] = q1;
+    wave_fwht128(lo, hi, lane);
+    qr[w][lane] = lo;
+    qr[w][lane + 64] = hi;
+  }
   __syncthreads();
   if constexpr (QJL) {
-    // (S H D_K / sqrt d) q over this wave's 32 coordinates, for every head;
-    // the four partial sums of a row are added in wave order below
     float acc[4][2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
+    for (int c = 0; c < kCpw; ++c) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float x = qs[g][32 * w + c];
+        const float x = qs[g][kCpw * w + c];
         acc[g][0] = fmaf(st2[c].x, x, acc[g][0]);
         acc[g][1] = fmaf(st2[c].y, x, acc[g][1]);
       }
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g][2 * lane]) = make_float2(acc[g][0], acc[g][1]);
-    __syncthreads();
   }
 
-  // digits of u at k-slots 2 lane, 2 lane + 1 into operand set `set`, head w
-  auto write_digits = [&](int set, float u0, float u1) __attribute__((always_inline)) {
+  // digits of u at k-slots 2 lane, 2 lane + 1 into operand set `set`, head g
+  auto write_digits = [&](int set, int g, float u0, float u1) __attribute__((always_inline)) {
     const int k0 = 2 * lane;
     const int fld = (k0 & 31) >> 3;
     if (fld == 3) {
@@ -128,30 +138,39 @@ __global__ __launch_bounds__(kRegThreads) void qprep_kernel(DecodeArgs a) {
       t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
       r0 = (r0 - d0) * 32.0f;
       r1 = (r1 - d1) * 32.0f;
-      *reinterpret_cast<uint16_t*>(&alimb[set][(4 * w + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
-      if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * w + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
+      *reinterpret_cast<uint16_t*>(&alimb[set][(4 * g + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
+      if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
     }
     const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
     const float c = wave_sum64(__builtin_amdgcn_ldexpf(wf * (t0 + t1), s0));
-    if (lane == 0) cconst[set][w] = c;
+    if (lane == 0) cconst[set][g] = c;
   };
-  const float x0 = qr[w][pos_of_slot(2 * lane)], x1 = qr[w][pos_of_slot(2 * lane + 1)];
-#pragma unroll
-  for (int s = 0; s < KO::code_sets; ++s) {
-    const float coef = KO::chain ? a.tb.ak[s] : 1.0f;
-    write_digits(s, coef * x0, coef * x1);
+  const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
+  // the code sets: (set, head) pairs spread over the waves
+  for (int job = w; job < KO::code_sets * 4; job += kWavesP) {
+    const int s = job >> 2, g = job & 3;
+    const float coef = (KO::chain ? a.tb.ak[s] : 1.0f) * kCodeScale;
+    write_digits(s, g, coef * qr[g][r0], coef * qr[g][r1]);
   }
   if constexpr (QJL) {
-    const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
-    const float u0 = ((sred[0][w][r0] + sred[1][w][r0]) + sred[2][w][r0]) + sred[3][w][r0];
-    const float u1 = ((sred[0][w][r1] + sred[1][w][r1]) + sred[2][w][r1]) + sred[3][w][r1];
-    write_digits(KO::code_sets, u0, u1);
+    __syncthreads();   // every wave's sketch shares are in shared memory
+    // the sketch set: head w - 4 on waves 4..7
+    if (w >= 4) {
+      const int g = w - 4;
+      float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kWavesP; ++c) {
+        u0 += sred[c][g][r0];
+        u1 += sred[c][g][r1];
+      }
+      write_digits(KO::code_sets, g, kSketchScale * u0, kSketchScale * u1);
+    }
   }
   __syncthreads();
 
   // lane L of the decode waves: row L % 16, k = 64 (e / 16) + 16 (L / 16) + e % 16
   uint32_t* out = a.qops + static_cast<int64_t>(u) * (kQopsStride / 4);
-  for (int s = w; s < NSETS; s += 4) {
+  for (int s = w; s < NSETS; s += kWavesP) {
     const int t = lane & 15, g4 = lane >> 4;
     const uint4 l4 = *reinterpret_cast<const uint4*>(&alimb[s][t * 128 + 16 * g4]);
     const uint4 h4 = *reinterpret_cast<const uint4*>(&alimb[s][t * 128 + 64 + 16 * g4]);
@@ -289,36 +308,39 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const int so = 4 * (g4 * kBlock + 32 * w + 2 * t);   // key words of this lane (and value words)
   const int sn = 2 * (32 * w + 2 * t);                 // its two fp16 per-slot fields
   constexpr int kNT = 2;   // streaming loads (read once)
-  auto load = [&](R& B, int blk, __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv) __attribute__((always_inline)) {
-    const int kb0 = blk * F::kBytes, vb0 = blk * F::vBytes;
+  // The block index is clamped to the resource's last block (blocks past the
+  // split re-read that block, unused), so every address lies inside the
+  // (sequence, KV head)'s cache; the block's base travels in the scalar
+  // offset and each lane's offset inside the block is a constant register.
+  auto load = [&](R& B, int blk, int nvalid, __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv)
+      __attribute__((always_inline)) {
+    const int bc = __builtin_amdgcn_readfirstlane(min(blk, nvalid - 1));
+    const int kb0 = bc * F::kBytes, vb0 = bc * F::vBytes;
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsk, kb0 + p * 2048 + so, 0, kNT);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsk, so, kb0 + p * 2048, kNT);
       B.kp[p] = make_uint2(x[0], x[1]);
     }
     if constexpr (QJL) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsk, kb0 + KB * 2048 + so, 0, kNT);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsk, so, kb0 + KB * 2048, kNT);
       B.ks = make_uint2(x[0], x[1]);
-      B.kr = __builtin_amdgcn_raw_buffer_load_b32(rsk, kb0 + F::kNorms + 256 + sn, 0, kNT);
+      B.kr = __builtin_amdgcn_raw_buffer_load_b32(rsk, sn, kb0 + F::kNorms + 256, kNT);
     }
-    B.kn = __builtin_amdgcn_raw_buffer_load_b32(rsk, kb0 + F::kNorms + sn, 0, kNT);
+    B.kn = __builtin_amdgcn_raw_buffer_load_b32(rsk, sn, kb0 + F::kNorms, kNT);
 #pragma unroll
     for (int p = 0; p < VB; ++p) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsv, vb0 + p * 2048 + so, 0, kNT);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsv, so, vb0 + p * 2048, kNT);
       B.vp[p] = make_uint2(x[0], x[1]);
     }
-    B.vn = __builtin_amdgcn_raw_buffer_load_b32(rsv, vb0 + 2048 * VB + sn, 0, kNT);
+    B.vn = __builtin_amdgcn_raw_buffer_load_b32(rsv, sn, vb0 + 2048 * VB, kNT);
   };
   // kSets register sets: blocks i + 1 .. i + kSets - 1 are in flight while
   // block i is worked on
   R buf0, buf1, buf2;
-  load(buf0, blk0, rk0, rv0);
-  load(buf1, blk0 + 1, rk0, rv0);
-  if constexpr (kSets == 3) load(buf2, blk0 + 2, rk0, rv0);
+  load(buf0, blk0, a.n_blocks, rk0, rv0);
+  load(buf1, blk0 + 1, a.n_blocks, rk0, rv0);
+  if constexpr (kSets == 3) load(buf2, blk0 + 2, a.n_blocks, rk0, rv0);
 
-  const float inv_sqrt_d = 0.08838834764831845f;
-  const float alpha2 = kLog2e * inv_sqrt_d / static_cast<float>(kD);
-  const float beta2 = kLog2e * inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);
   float m_a = -INFINITY, m_b = -INFINITY;   // running reference of head g4 (denominator) / head t / 4 (column)
   float m_top = -INFINITY;                  // Sparse-V: largest step reference of head t / 4 so far
   const bool sparse_v = a.sparse_v > 0;
@@ -335,7 +357,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // One step: logits of this wave's 32 positions for the four heads, its
   // reference and the digits of p * radius; one barrier; the running
   // references and the weighted sum of the block's values for this wave's 32
-  // coordinates; then the register set is refilled two blocks ahead.
+  // coordinates; then the register set is refilled kSets blocks ahead.
   auto step = [&](R& B, int i) __attribute__((always_inline)) {
     wait_vm<(kSets - 1) * F::loads>();   // this set has landed (the later sets' loads may still be in flight)
     const int blk = blk0 + i;
@@ -351,10 +373,10 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       for (int p = 0; p < KB; ++p) wd[p] = c ? B.kp[p].y : B.kp[p].x;
       float code;
       if constexpr (KO::chain) {
-        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        v4f acc = v4f{-cq, 0.0f, 0.0f, 0.0f};   // the affine operands' offset, removed up front
 #pragma unroll
         for (int T = 0; T < NTK; ++T) acc = mfma_fp8_fp4(Aq[T], expand_fp4_affine(term_word<KB>(wd, T)), acc, scq[T]);
-        code = ((acc[0] + acc[1]) + (acc[2] + acc[3])) - cq;
+        code = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       } else {
         v4f dT[NTK];
 #pragma unroll
@@ -366,13 +388,13 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       }
       float qj = 0.0f;
       if constexpr (QJL) {
-        const v4f dQ = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? B.ks.y : B.ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
-        qj = ((dQ[0] + dQ[1]) + (dQ[2] + dQ[3])) - csq;
+        const v4f dQ = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? B.ks.y : B.ks.x), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+        qj = (dQ[0] + dQ[1]) + (dQ[2] + dQ[3]);
       }
       const int tok = pos_of_slot(32 * w + 2 * t + c);
       const float nk = h2f(c ? (B.kn >> 16) : B.kn);
       const float rho = QJL ? h2f(c ? (B.kr >> 16) : B.kr) : 0.0f;
-      const float l2 = fmaf(__fmul_rn(alpha2, nk), code, QJL ? __fmul_rn(__fmul_rn(beta2, rho), qj) : 0.0f);
+      const float l2 = fmaf(nk, code, QJL ? __fmul_rn(rho, qj) : 0.0f);
       const bool valid = (tok < n_t) && (g4 < G);
       if (a.logits != nullptr && valid)
         a.logits[(static_cast<int64_t>(b) * a.n_q + hq0 + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
@@ -468,8 +490,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       }
       accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
     }
-    // refill this register set kSets blocks ahead (zero past the split)
-    load(B, blk + kSets, rk, rv);
+    // refill this register set kSets blocks ahead
+    load(B, blk + kSets, blk1, rk, rv);
   };
 
   if (n_iter > 0) {   // uniform over the workgroup
@@ -556,7 +578,7 @@ __global__ __launch_bounds__(kRegThreads, 2) void decode_reg_append_kernel(Decod
 template <int KB, bool QJL, int VB>
 hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   const int nhg = (a.group + 3) / 4;
-  hipLaunchKernelGGL((qprep_kernel<KB, QJL>), dim3(a.batch * a.n_kv * nhg), dim3(kRegThreads), 0, stream, a);
+  hipLaunchKernelGGL((qprep_kernel<KB, QJL>), dim3(a.batch * a.n_kv * nhg), dim3(kPrepThreads), 0, stream, a);
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * nhg);
   if (a.k_new != nullptr)

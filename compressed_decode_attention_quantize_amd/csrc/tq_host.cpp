@@ -460,7 +460,10 @@ int chunk_blocks_for(const tq_config* c, int32_t max_seq_len, int64_t target) {
   if (c->decode_chunk > 0) return c->decode_chunk / kBlock;
   const int64_t pairs = split_units(c);
   const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
-  return static_cast<int>(std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits));
+  const int64_t chunk = std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits);
+  // the register-streamed kernel's per-split costs (query operands, the
+  // first loads' latency, partials, merge) want a few steps to spread over
+  return static_cast<int>(reg_path(c) ? std::max<int64_t>(chunk, tq::kRegMinChunkBlocks) : chunk);
 }
 
 // Block groups (of four wavefronts, one block each per step) per workgroup

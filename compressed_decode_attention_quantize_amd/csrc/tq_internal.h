@@ -165,8 +165,9 @@ hipError_t launch_decode_reg(const DecodeArgs& a, hipStream_t stream);
 // VALU kernel runs about four 256-thread workgroups per compute unit (it is
 // latency-bound: more resident wavefronts hide more of it).
 constexpr int kMfmaUnitWorkgroups = 512;
-// register-streamed decode: 256-thread workgroups, several per compute unit
+// register-streamed decode: 256-thread workgroups, two per compute unit
 constexpr int kRegWorkgroups = 512;
+constexpr int kRegMinChunkBlocks = 8;   // fewest blocks per split it is given
 constexpr int kValuWorkgroups = 1024;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 // The library's own decode workspace (tq_decode_attention_noalloc): counters
