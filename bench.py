@@ -50,10 +50,13 @@ CONFIG_SET = ("llama8b_b1_ctx32k", "cmdr104b_b1_ctx128k", "serving_b16_ctx8k")
 DECODE_DTYPE = ("fp4 code operands x fp8 digit operands, fp32 accumulate (query: 4 base-32 digits per "
                 "32-slot E8M0 block, about 19 significant bits; p*radius: 3 digits, about 14 bits; "
                 "q8 keys: int8 x 3 base-128 int8 query digits, int32 accumulate)")
-DECODE_KERNEL = "decode_mfma_kernel"   # name fragment of the timed decode kernel
-TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_mfma_*_traffic.txt")
+# name fragment of the dominant decode kernel (POLAR / POLAR_QJL keys; each
+# decode call runs a small query-prep kernel before it)
+DECODE_KERNEL = "decode_reg_kernel"
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_reg_*_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc", f)
-                  for f in ("tq_decode_mfma.hip", "tq_device.h", "tq_internal.h")]
+                  for f in ("tq_decode_reg.hip", "tq_mfma_ops.h", "tq_quant_unit.h", "tq_device.h",
+                            "tq_internal.h")]
 
 
 def kernel_source_hash():
@@ -408,7 +411,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the clocks and caches settle within a few tens of ms)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--layers", type=int, default=0, help="layer caches to cycle (0 = workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

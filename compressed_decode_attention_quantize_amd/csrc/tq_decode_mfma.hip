@@ -264,7 +264,8 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   // all-one row's products and lanes 32..63 the all-zero row's; their mean
   // is what every value row carries on top of its signed sum.
   v4f accO = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u);
+  const Fp4Fill kf = fp4_fill();
+  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u, kf);
 
   {
     // The query set-up and the ring's first copies do not wait for the
@@ -497,8 +498,8 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
         for (int p = 0; p < KB; ++p) wd[p] = c ? kp[p].y : kp[p].x;
 #pragma unroll
         for (int T = 0; T < NTK; ++T)
-          dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4_affine(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
-        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? ks.y : ks.x), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
+          dT[c][T] = mfma_fp8_fp4(Aq, expand_fp4_affine(term_word<KB>(wd, T), kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq);
+        if (QJL) dQ[c] = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? ks.y : ks.x, kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scsq);
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -627,7 +628,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
           vw[p] = *reinterpret_cast<const uint32_t*>(vb + 4 * (p * 4 * kD + g4 * kD + 32 * wl + 16 * rr + t));
 #pragma unroll
         for (int T = 0; T < NTV; ++T)
-          accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T)), Pv, accV[rr][T], scp);
+          accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
       }
       accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
     };

@@ -14,20 +14,25 @@
 //    (one 8-byte load per plane) and the value words of k-block g4 for
 //    coordinates 32w + 2t, 32w + 2t + 1 (row t of the value product stands
 //    for coordinate 32w + 2t + rr in its pass rr, so that those two words are
-//    one 8-byte load too).  Each block's loads are issued three steps before
-//    the step that uses them, into one of three register sets.
+//    one 8-byte load too).  A block's key and value loads are issued about
+//    three steps before the step that uses them, into one of three register
+//    sets (two with 4-bit values).
 //  * The query side is prepared once per (sequence, KV head, head group) by
-//    qprep_kernel and read as ready-made operands: no sketch table, rotation
-//    or digit formation in the decode workgroups.
-//  * With at most four terms per key code (2- and 3-bit keys) the codebook
-//    coefficients are folded into the query digits (one operand per term),
-//    so a column's terms accumulate in one matrix instruction chain instead
-//    of being summed and weighted afterwards.
+//    qprep_kernel; a workgroup copies those ready-made operands to shared
+//    memory once and reads each right before its product: no sketch table,
+//    rotation or digit formation in the decode workgroups.
+//  * With at most four terms per key code (2- and 3-bit keys, values of 2 or
+//    3 bits) the codebook coefficients are folded into the query digits (one
+//    operand per term), so a column's terms accumulate in one matrix
+//    instruction chain instead of being summed and weighted afterwards.
 //  * A workgroup is one group of four waves taking one 128-position block per
-//    step (one barrier per step), and several workgroups share a compute
-//    unit, so their steps interleave.
+//    step with one barrier per step, software-pipelined over two blocks: step
+//    i forms the logits of block i and, around the barrier, the probability
+//    digits, running references and weighted values of block i - 1.  Two
+//    workgroups share a compute unit, so their steps interleave.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "tq_mfma_ops.h"
 
@@ -35,11 +40,25 @@ namespace tq {
 namespace {
 
 constexpr int kRegThreads = 256;
+// A running or step reference with no valid position behind it: finite, so
+// that differences and exponentials of it need no special case (it converts
+// to a huge negative shift, 2^shift = 0).
+constexpr float kNoRef = -1e30f;
 
-template <int KB>
+// a * b, 0 for a = 0 whatever b (the cache words of slots past the length are
+// arbitrary)
+__device__ __forceinline__ float mul_zero_wins(float a, float b) { return (a > 0.0f) ? a * b : 0.0f; }
+// float -> int of a shift that is at most a few units above zero, clamped
+// below (an absent reference gives a large negative value)
+__device__ __forceinline__ int shift_of(float x) { return static_cast<int>(fmaxf(x, -1073741824.0f)); }
+
+// CHAIN: one query operand per code term (at most four terms); with 4-bit
+// values the decode keeps one operand and weights the terms itself (the four
+// operands would not fit in its registers).
+template <int KB, int VB>
 struct KeyOps {
   static constexpr int nt = NTerms<KB>::n;
-  static constexpr bool chain = nt <= 4;      // one operand per code term
+  static constexpr bool chain = nt <= 4 && VB < 4;
   static constexpr int code_sets = chain ? nt : 1;
 };
 
@@ -64,9 +83,9 @@ constexpr int kPrepThreads = 512;
 constexpr float kCodeScale = 1.4426950408889634f * 0.08838834764831845f / 128.0f;
 constexpr float kSketchScale = 1.4426950408889634f * 0.08838834764831845f * 1.2533141373155003f / 128.0f;
 
-template <int KB, bool QJL>
+template <int KB, bool QJL, int VB>
 __global__ __launch_bounds__(kPrepThreads) void qprep_kernel(DecodeArgs a) {
-  using KO = KeyOps<KB>;
+  using KO = KeyOps<KB, VB>;
   constexpr int NSETS = KO::code_sets + (QJL ? 1 : 0);
   constexpr int kWavesP = kPrepThreads / 64;
   constexpr int kCpw = kD / kWavesP;   // table coordinates per wave
@@ -215,19 +234,23 @@ struct RegFmt {
   static constexpr int loads = KB + (QJL ? 3 : 1) + VB + 1;   // vector loads per step and wave
 };
 
-template <int KB, bool QJL, int VB, bool FUSED>
+// AUX: the variant that also writes logits and skips value work (Sparse-V);
+// the plain variant has neither in its step.
+template <int KB, bool QJL, int VB, bool FUSED, bool AUX>
 __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
-  // three register sets, except in the serving step with QJL keys and 4-bit
-  // values, where the quantiser's registers leave room for two within 256
-  constexpr int kSets = (FUSED && QJL && VB == 4) ? 2 : 3;
-  using KO = KeyOps<KB>;
+  // three register sets, two with 4-bit values (three would not fit in 256)
+  constexpr int kSets = (VB == 4) ? 2 : 3;
+  using KO = KeyOps<KB, VB>;
   using F = RegFmt<KB, QJL, VB>;
   using R = StepRegs<KB, QJL, VB>;
   constexpr int NTK = KO::nt;
   constexpr int NCS = KO::code_sets;
   constexpr int NTV = NTerms<VB>::n;
   constexpr int kWaves = kRegThreads / 64;
-  __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * 128];   // [parity][col][k]: digits of p * radius
+  // [parity][col][k]: digits of p * radius; rows padded to 144 bytes so that
+  // the 16 rows one 16-byte read instruction gathers fall on distinct banks
+  constexpr int kPRow = 144;
+  __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * kPRow];
   __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];        // [parity][k / 32][col]
   __shared__ float rwb[2][kWaves][4];       // [parity][wave][head]: each wave's step reference
   __shared__ float wred[kWaves][4];
@@ -264,24 +287,22 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   }
 
   // ------------------------------------------------ query operands (ready-made)
+  // The fp8 operands (NCS code sets, then the sketch set) wait in shared
+  // memory in lane order and are read right before each product: held in
+  // registers through the loop they would take 8 per set.
+  constexpr int NQS = NCS + (QJL ? 1 : 0);
+  __shared__ uint4 qlds[NQS * 2 * 64];
   const uint32_t* qo = a.qops + ((static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg) * (kQopsStride / 4);
-  v8i Aq[NCS];
+  for (int e = tid; e < NQS * 2 * 64; e += kRegThreads) qlds[e] = *reinterpret_cast<const uint4*>(qo + 4 * e);
+  auto qop = [&](int set) __attribute__((always_inline)) {
+    const uint4 l4 = qlds[(2 * set) * 64 + lane];
+    const uint4 h4 = qlds[(2 * set + 1) * 64 + lane];
+    return v8i{(int)l4.x, (int)l4.y, (int)l4.z, (int)l4.w, (int)h4.x, (int)h4.y, (int)h4.z, (int)h4.w};
+  };
   int scq[NCS];
 #pragma unroll
-  for (int s = 0; s < NCS; ++s) {
-    const uint4 l4 = *reinterpret_cast<const uint4*>(qo + (2 * s) * 256 + 4 * lane);
-    const uint4 h4 = *reinterpret_cast<const uint4*>(qo + (2 * s + 1) * 256 + 4 * lane);
-    Aq[s] = v8i{(int)l4.x, (int)l4.y, (int)l4.z, (int)l4.w, (int)h4.x, (int)h4.y, (int)h4.z, (int)h4.w};
-    scq[s] = static_cast<int>(qo[kQopsScaleWord + s * 64 + lane]);
-  }
-  v8i Asq = Aq[0];
-  int scsq = 127;
-  if constexpr (QJL) {
-    const uint4 l4 = *reinterpret_cast<const uint4*>(qo + (2 * NCS) * 256 + 4 * lane);
-    const uint4 h4 = *reinterpret_cast<const uint4*>(qo + (2 * NCS + 1) * 256 + 4 * lane);
-    Asq = v8i{(int)l4.x, (int)l4.y, (int)l4.z, (int)l4.w, (int)h4.x, (int)h4.y, (int)h4.z, (int)h4.w};
-    scsq = static_cast<int>(qo[kQopsScaleWord + NCS * 64 + lane]);
-  }
+  for (int s = 0; s < NCS; ++s) scq[s] = static_cast<int>(qo[kQopsScaleWord + s * 64 + lane]);
+  const int scsq = QJL ? static_cast<int>(qo[kQopsScaleWord + NCS * 64 + lane]) : 127;
   const float cq = reinterpret_cast<const float*>(qo)[kQopsConstWord + g4];
   const float csq = QJL ? reinterpret_cast<const float*>(qo)[kQopsConstWord + 4 + g4] : 0.0f;
   float ak[NTK], av[NTV];
@@ -299,7 +320,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const uint8_t* kbase = a.kc + slot0_idx * a.k_block_bytes;
   const uint8_t* vbase = a.vc + slot0_idx * a.v_block_bytes;
-  // the first two blocks are requested before the length is known: over the
+  // the first kSets blocks are requested before the length is known: over the
   // whole cache of this (sequence, KV head); later ones only within the split
   const __amdgpu_buffer_rsrc_t rk0 = block_rsrc(kbase, F::kBytes, a.n_blocks);
   const __amdgpu_buffer_rsrc_t rv0 = block_rsrc(vbase, F::vBytes, a.n_blocks);
@@ -312,10 +333,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // split re-read that block, unused), so every address lies inside the
   // (sequence, KV head)'s cache; the block's base travels in the scalar
   // offset and each lane's offset inside the block is a constant register.
-  auto load = [&](R& B, int blk, int nvalid, __amdgpu_buffer_rsrc_t rsk, __amdgpu_buffer_rsrc_t rsv)
-      __attribute__((always_inline)) {
-    const int bc = __builtin_amdgcn_readfirstlane(min(blk, nvalid - 1));
-    const int kb0 = bc * F::kBytes, vb0 = bc * F::vBytes;
+  auto load_k = [&](R& B, int blk, int nvalid, __amdgpu_buffer_rsrc_t rsk) __attribute__((always_inline)) {
+    const int kb0 = __builtin_amdgcn_readfirstlane(min(blk, nvalid - 1)) * F::kBytes;
 #pragma unroll
     for (int p = 0; p < KB; ++p) {
       const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsk, so, kb0 + p * 2048, kNT);
@@ -327,6 +346,9 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       B.kr = __builtin_amdgcn_raw_buffer_load_b32(rsk, sn, kb0 + F::kNorms + 256, kNT);
     }
     B.kn = __builtin_amdgcn_raw_buffer_load_b32(rsk, sn, kb0 + F::kNorms, kNT);
+  };
+  auto load_v = [&](R& B, int blk, int nvalid, __amdgpu_buffer_rsrc_t rsv) __attribute__((always_inline)) {
+    const int vb0 = __builtin_amdgcn_readfirstlane(min(blk, nvalid - 1)) * F::vBytes;
 #pragma unroll
     for (int p = 0; p < VB; ++p) {
       const auto x = __builtin_amdgcn_raw_buffer_load_b64(rsv, so, vb0 + p * 2048, kNT);
@@ -334,16 +356,31 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     }
     B.vn = __builtin_amdgcn_raw_buffer_load_b32(rsv, sn, vb0 + 2048 * VB, kNT);
   };
-  // kSets register sets: blocks i + 1 .. i + kSets - 1 are in flight while
-  // block i is worked on
+  // Register set s holds the key words of block j and the value words of
+  // block j' with j = j' = s (mod kSets): the keys of block i and the values
+  // of block i - 1 are used in step i, then refilled with blocks i + kSets and
+  // i - 1 + kSets.
   R buf0, buf1, buf2;
-  load(buf0, blk0, a.n_blocks, rk0, rv0);
-  load(buf1, blk0 + 1, a.n_blocks, rk0, rv0);
-  if constexpr (kSets == 3) load(buf2, blk0 + 2, a.n_blocks, rk0, rv0);
+  load_k(buf0, blk0, a.n_blocks, rk0);
+  load_v(buf0, blk0, a.n_blocks, rv0);
+  load_k(buf1, blk0 + 1, a.n_blocks, rk0);
+  load_v(buf1, blk0 + 1, a.n_blocks, rv0);
+  if constexpr (kSets == 3) {
+    load_k(buf2, blk0 + 2, a.n_blocks, rk0);
+    load_v(buf2, blk0 + 2, a.n_blocks, rv0);
+  }
 
-  float m_a = -INFINITY, m_b = -INFINITY;   // running reference of head g4 (denominator) / head t / 4 (column)
+  lds_barrier();   // the query operands are in shared memory (the loads above stay in flight)
+
+  // The optional logits go through a buffer over this (sequence, head
+  // group)'s rows: a lane with no logit to store takes an offset past its end
+  // and the store is dropped (no branch in the step).
+  const __amdgpu_buffer_rsrc_t rlg = __builtin_amdgcn_make_buffer_rsrc(
+      a.logits != nullptr ? a.logits + (static_cast<int64_t>(b) * a.n_q + hq0) * a.max_ctx : a.logits,
+      static_cast<short>(0), a.logits != nullptr ? G * a.max_ctx * 4 : 0, 0x00020000);
+
+  float m_a = kNoRef, m_b = kNoRef;   // running reference of head g4 (denominator) / head t / 4 (column)
   float m_top = -INFINITY;                  // Sparse-V: largest step reference of head t / 4 so far
-  const bool sparse_v = a.sparse_v > 0;
   const float tau_v = static_cast<float>(a.sparse_v);
   float lsum = 0.0f;
   v4f accV[2][NTV];
@@ -352,73 +389,96 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
 #pragma unroll
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   v4f accO = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u);
+  const Fp4Fill kf = fp4_fill();
+  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u, kf);
+  float lgp[2] = {-INFINITY, -INFINITY};   // this lane's two logits of the block before
 
-  // One step: logits of this wave's 32 positions for the four heads, its
-  // reference and the digits of p * radius; one barrier; the running
-  // references and the weighted sum of the block's values for this wave's 32
-  // coordinates; then the register set is refilled kSets blocks ahead.
-  auto step = [&](R& B, int i) __attribute__((always_inline)) {
-    wait_vm<(kSets - 1) * F::loads>();   // this set has landed (the later sets' loads may still be in flight)
-    const int blk = blk0 + i;
-    const int n_t = min(kBlock, len - blk * kBlock);
-    float lg2[2];
-    // column group c = slots 32 w + 2 t + c: its matrix products, then its
-    // logit (one column group at a time keeps the unchained sums' registers
-    // to one group's)
+  // Step i is two halves around one barrier, each pairing matrix work with
+  // independent vector work: (1) the key products of block i with the
+  // probability digits of block i - 1 (written to shared memory); (2) after
+  // the barrier, the logits of block i, then block i - 1's running references
+  // and value products.  CUR: block i exists; PREV: block i - 1 does.
+  auto step = [&](R& Bk, R& Bv, int i, auto cur_c, auto prev_c) __attribute__((always_inline)) {
+    constexpr bool CUR = decltype(cur_c)::value;
+    constexpr bool PREV = decltype(prev_c)::value;
+    // no instruction moves across a step boundary (hoisting the next step's
+    // products into this one's runs out of registers)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(kSets - 1) * F::loads>();   // block i's keys and block i - 1's values have landed
+    // ---- (1a) key products of block i: column group c = slots 32 w + 2 t + c
+    float code2[2] = {0.0f, 0.0f}, qj2[2] = {0.0f, 0.0f};
+    if constexpr (CUR) {
+      if constexpr (KO::chain && VB < 4) {   // both column groups' chains side by side
+        uint32_t wd0[KB], wd1[KB];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t wd[KB];
+        for (int p = 0; p < KB; ++p) {
+          wd0[p] = Bk.kp[p].x;
+          wd1[p] = Bk.kp[p].y;
+        }
+        v4f acc0 = v4f{-cq, 0.0f, 0.0f, 0.0f}, acc1 = acc0;   // the affine operands' offset, removed up front
 #pragma unroll
-      for (int p = 0; p < KB; ++p) wd[p] = c ? B.kp[p].y : B.kp[p].x;
-      float code;
-      if constexpr (KO::chain) {
-        v4f acc = v4f{-cq, 0.0f, 0.0f, 0.0f};   // the affine operands' offset, removed up front
-#pragma unroll
-        for (int T = 0; T < NTK; ++T) acc = mfma_fp8_fp4(Aq[T], expand_fp4_affine(term_word<KB>(wd, T)), acc, scq[T]);
-        code = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        for (int T = 0; T < NTK; ++T) {
+          const v8i A = qop(T);
+          acc0 = mfma_fp8_fp4(A, expand_fp4_affine(term_word<KB>(wd0, T), kf), acc0, scq[T]);
+          acc1 = mfma_fp8_fp4(A, expand_fp4_affine(term_word<KB>(wd1, T), kf), acc1, scq[T]);
+        }
+        code2[0] = (acc0[0] + acc0[1]) + (acc0[2] + acc0[3]);
+        code2[1] = (acc1[0] + acc1[1]) + (acc1[2] + acc1[3]);
       } else {
-        v4f dT[NTK];
+        // one column group at a time (fewer live registers)
 #pragma unroll
-        for (int T = 0; T < NTK; ++T)
-          dT[T] = mfma_fp8_fp4(Aq[0], expand_fp4_affine(term_word<KB>(wd, T)), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq[0]);
-        code = -cq;
+        for (int c = 0; c < 2; ++c) {
+          uint32_t wd[KB];
 #pragma unroll
-        for (int T = 0; T < NTK; ++T) code = fmaf(ak[T], (dT[T][0] + dT[T][1]) + (dT[T][2] + dT[T][3]), code);
+          for (int p = 0; p < KB; ++p) wd[p] = c ? Bk.kp[p].y : Bk.kp[p].x;
+          if constexpr (KO::chain) {
+            v4f acc = v4f{-cq, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int T = 0; T < NTK; ++T) acc = mfma_fp8_fp4(qop(T), expand_fp4_affine(term_word<KB>(wd, T), kf), acc, scq[T]);
+            code2[c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+          } else {
+            v4f dT[NTK];
+            const v8i A = qop(0);
+#pragma unroll
+            for (int T = 0; T < NTK; ++T)
+              dT[T] = mfma_fp8_fp4(A, expand_fp4_affine(term_word<KB>(wd, T), kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq[0]);
+            float code = -cq;
+#pragma unroll
+            for (int T = 0; T < NTK; ++T) code = fmaf(ak[T], (dT[T][0] + dT[T][1]) + (dT[T][2] + dT[T][3]), code);
+            code2[c] = code;
+          }
+        }
       }
-      float qj = 0.0f;
       if constexpr (QJL) {
-        const v4f dQ = mfma_fp8_fp4(Asq, expand_fp4_affine(c ? B.ks.y : B.ks.x), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
-        qj = (dQ[0] + dQ[1]) + (dQ[2] + dQ[3]);
+        const v8i As = qop(NCS);
+        const v4f dQ0 = mfma_fp8_fp4(As, expand_fp4_affine(Bk.ks.x, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+        const v4f dQ1 = mfma_fp8_fp4(As, expand_fp4_affine(Bk.ks.y, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+        qj2[0] = (dQ0[0] + dQ0[1]) + (dQ0[2] + dQ0[3]);
+        qj2[1] = (dQ1[0] + dQ1[1]) + (dQ1[2] + dQ1[3]);
       }
-      const int tok = pos_of_slot(32 * w + 2 * t + c);
-      const float nk = h2f(c ? (B.kn >> 16) : B.kn);
-      const float rho = QJL ? h2f(c ? (B.kr >> 16) : B.kr) : 0.0f;
-      const float l2 = fmaf(nk, code, QJL ? __fmul_rn(rho, qj) : 0.0f);
-      const bool valid = (tok < n_t) && (g4 < G);
-      if (a.logits != nullptr && valid)
-        a.logits[(static_cast<int64_t>(b) * a.n_q + hq0 + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
-      lg2[c] = valid ? l2 : -INFINITY;
     }
-    // this wave's reference per head (row g4): the integer ceiling of its
-    // step maximum; p <= 1 against it
-    const int par = i & 1;
-    uint8_t* const pl = &plimb[par][0];
-    uint8_t* const pe = &pexp[par][0][0];
-    const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
-    const float rw = (mloc == -INFINITY) ? -INFINITY : ceilf(mloc);
-    if (t == 0) rwb[par][w][g4] = rw;
-    const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - rw);
-    const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - rw);
-    {
-      float r0 = (p0 > 0.0f) ? p0 * h2f(B.vn) : 0.0f;
-      float r1 = (p1 > 0.0f) ? p1 * h2f(B.vn >> 16) : 0.0f;
+    // ---- (1b) block i - 1: this wave's reference per head (row g4) is the
+    // integer ceiling of its step maximum (p <= 1 against it); the digits of
+    // p * radius go to shared memory
+    const int pj = (i - 1) & 1;
+    float rw = -INFINITY, ps = 0.0f;
+    if constexpr (PREV) {
+      uint8_t* const pl = &plimb[pj][0];
+      uint8_t* const pe = &pexp[pj][0][0];
+      const float mloc = row_max16(fmaxf(lgp[0], lgp[1]));
+      rw = fmaxf(ceilf(mloc), kNoRef);
+      rwb[pj][w][g4] = rw;   // every lane of the row stores the same value
+      const float p0 = __builtin_amdgcn_exp2f(lgp[0] - rw);   // exp2(-inf) = 0 for slots without a logit
+      const float p1 = __builtin_amdgcn_exp2f(lgp[1] - rw);
+      float r0 = mul_zero_wins(p0, h2f(Bv.vn));
+      float r1 = mul_zero_wins(p1, h2f(Bv.vn >> 16));
       const float pm = row_max16(fmaxf(r0, r1));
-      const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
+      // r 2^-s0 < 16; s0 in [-103, 124] (pm < 2^128; pm below 2^-100 is taken
+      // as 2^-100), so every digit's E8M0 byte s0 - 5 j + 127 lies in [14, 251]
+      const int s0 = max(exponent_of(pm), -100) - 3;
       const float sgn = (t >= 12) ? -1.0f : 1.0f;   // k-slots on the value operand's sign field
       r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
       r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
-      uint32_t ebytes = 127u << 24;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int pk = 0;   // the fourth digit row stays zero
@@ -429,87 +489,140 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
             r0 = (r0 - d0) * 32.0f;
             r1 = (r1 - d1) * 32.0f;
           }
-          ebytes |= static_cast<uint32_t>(min(max(s0 - 5 * j + 127, 1), 254)) << (8 * j);
         }
-        *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * 128 + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
+        *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * kPRow + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
       }
-      if (t == 0) *reinterpret_cast<uint32_t*>(&pe[16 * w + 4 * g4]) = ebytes;
+      // bytes s0 + 127, s0 + 122, s0 + 117, 127 (no byte carries into the next)
+      const uint32_t ebytes = static_cast<uint32_t>(s0 * 0x010101 + (0x7f000000 + 127 + (122 << 8) + (117 << 16)));
+      *reinterpret_cast<uint32_t*>(&pe[16 * w + 4 * g4]) = ebytes;   // the same from every lane of the row
+      ps = p0 + p1;
     }
-    const float ps = p0 + p1;
-    lds_barrier();
+    if constexpr (CUR && PREV) {
+      // this half's key products and digit work: each matrix instruction is
+      // issued with a few vector ones after it
+      constexpr int kMat = 2 * NTK + (QJL ? 2 : 0);
+#pragma unroll
+      for (int k = 0; k < kMat; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six vector ones
+      }
+    }
+    if constexpr (PREV) lds_barrier();
 
-    // running references of head g4 (denominator) and head t / 4 (column)
-    const int hb = t >> 2;
-    float ra = rwb[par][0][g4], rb = rwb[par][0][hb];
+    // ---- (2a) logits of block i
+    if constexpr (CUR) {
+      const int blk = blk0 + i;
+      const int n_t = min(kBlock, len - blk * kBlock);
 #pragma unroll
-    for (int u = 1; u < kWaves; ++u) {
-      ra = fmaxf(ra, rwb[par][u][g4]);
-      rb = fmaxf(rb, rwb[par][u][hb]);
-    }
-    const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
-    const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
-    const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_a - mn_a));
-    const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_b - mn_b));
-    lsum = lsum * fh + ((rw == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(ps, static_cast<int>(rw - mn_a)));
-    m_a = mn_a;
-    m_b = mn_b;
-    if (__any(fv != 1.0f)) {   // rescale only when some head's reference moved
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-        for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
-      accO *= fv;
-    }
-    bool skip = false;
-    if (sparse_v) {
-      // every weight of the block below 2^-tau of the largest one so far, for
-      // every head of the group: the value work is skipped (the weights stay
-      // in the denominator)
-      m_top = fmaxf(m_top, rb);
-      skip = __all((rb == -INFINITY) || (rb < m_top - tau_v));
-    }
-    if (!skip) {
-      v8i Pv;
-      {
-        const uint4 lo = *reinterpret_cast<const uint4*>(&pl[t * 128 + 16 * g4]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&pl[t * 128 + 64 + 16 * g4]);
-        Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int c = 0; c < 2; ++c) {
+        const int tok = pos_of_slot(32 * w + 2 * t + c);
+        const float nk = h2f(c ? (Bk.kn >> 16) : Bk.kn);
+        const float rho = QJL ? h2f(c ? (Bk.kr >> 16) : Bk.kr) : 0.0f;
+        float l2 = fmaf(nk, code2[c], QJL ? __fmul_rn(rho, qj2[c]) : 0.0f);
+        // computed on every lane: used only where valid, the products feeding it
+        // would otherwise be sunk into a divergent branch
+        asm volatile("" : "+v"(l2));
+        const bool valid = (tok < n_t) && (g4 < G);
+        if constexpr (AUX) {   // (no logits: an empty buffer, every store dropped)
+          const int lo = valid ? (g4 * a.max_ctx + blk * kBlock + tok) * 4 : -1;   // -1: past the buffer's end
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fmul_rn(l2, kLn2)), rlg, lo, 0, 0);
+        }
+        lgp[c] = valid ? l2 : -INFINITY;
       }
-      // k-block g4 holds wave g4's positions: its digits carry 2^(its reference - the running one)
-      const float rk_ = rwb[par][g4][hb];
-      const int adj = (rk_ == -INFINITY) ? 0 : static_cast<int>(rk_ - m_b);
-      const int scp = min(max(static_cast<int>(pe[16 * g4 + t]) + adj, 1), 254);
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        uint32_t vw[VB];
-#pragma unroll
-        for (int p = 0; p < VB; ++p) vw[p] = rr ? B.vp[p].y : B.vp[p].x;
-#pragma unroll
-        for (int T = 0; T < NTV; ++T)
-          accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T)), Pv, accV[rr][T], scp);
-      }
-      accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
     }
-    // refill this register set kSets blocks ahead
-    load(B, blk + kSets, blk1, rk, rv);
+    // ---- (2b) block i - 1: running references of head g4 (denominator) and
+    // head t / 4 (column), then its value products
+    if constexpr (PREV) {
+      const int hb = t >> 2;
+      float ra = rwb[pj][0][g4], rb = rwb[pj][0][hb];
+#pragma unroll
+      for (int u = 1; u < kWaves; ++u) {
+        ra = fmaxf(ra, rwb[pj][u][g4]);
+        rb = fmaxf(rb, rwb[pj][u][hb]);
+      }
+      const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
+      const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
+      const float fh = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_a - mn_a));
+      const float fv = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_b - mn_b));
+      lsum = fmaf(lsum, fh, __builtin_amdgcn_ldexpf(ps, shift_of(rw - mn_a)));
+      m_a = mn_a;
+      m_b = mn_b;
+      if (__any(fv != 1.0f)) {   // rescale only when some head's reference moved
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
+        accO *= fv;
+      }
+      bool skip = false;
+      if (AUX && a.sparse_v > 0) {
+        // every weight of the block below 2^-tau of the largest one so far, for
+        // every head of the group: the value work is skipped (the weights stay
+        // in the denominator)
+        m_top = fmaxf(m_top, rb);
+        skip = __all(rb < m_top - tau_v);   // a block with no position has rb = kNoRef
+      }
+      if (!skip) {
+        const uint8_t* const pl = &plimb[pj][0];
+        const uint4 lo = *reinterpret_cast<const uint4*>(&pl[t * kPRow + 16 * g4]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&pl[t * kPRow + 64 + 16 * g4]);
+        const v8i Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        // k-block g4 holds wave g4's positions: its digits carry 2^(its reference - the running one)
+        const int adj = shift_of(rwb[pj][g4][hb] - m_b);   // an empty k-block gives the smallest scale (its digits are 0)
+        const int scp = min(max(static_cast<int>(pexp[pj][g4][t]) + adj, 1), 254);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          uint32_t vw[VB];
+#pragma unroll
+          for (int p = 0; p < VB; ++p) vw[p] = rr ? Bv.vp[p].y : Bv.vp[p].x;
+#pragma unroll
+          for (int T = 0; T < NTV; ++T)
+            accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
+        }
+        accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
+      }
+    }
+    // ---- refills: keys kSets blocks past block i, values kSets past block i - 1
+    if constexpr (CUR) load_k(Bk, blk0 + i + kSets, blk1, rk);
+    if constexpr (PREV) load_v(Bv, blk0 + i - 1 + kSets, blk1, rv);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  using Y = std::true_type;
+  using N = std::false_type;
   if (n_iter > 0) {   // uniform over the workgroup
-    int i = 0;
+    step(buf0, buf1, 0, Y{}, N{});
+    int i = 1;
     if constexpr (kSets == 3) {
       for (; i + 3 <= n_iter; i += 3) {
-        step(buf0, i);
-        step(buf1, i + 1);
-        step(buf2, i + 2);
+        step(buf1, buf0, i, Y{}, Y{});
+        step(buf2, buf1, i + 1, Y{}, Y{});
+        step(buf0, buf2, i + 2, Y{}, Y{});
       }
-      if (i < n_iter) step(buf0, i);
-      if (i + 1 < n_iter) step(buf1, i + 1);
+      // i = 1 (mod 3); the last step has no block i
+      if (i < n_iter) {
+        step(buf1, buf0, i, Y{}, Y{});
+        if (i + 1 < n_iter) {
+          step(buf2, buf1, i + 1, Y{}, Y{});
+          step(buf0, buf2, i + 2, N{}, Y{});
+        } else {
+          step(buf2, buf1, i + 1, N{}, Y{});
+        }
+      } else {
+        step(buf1, buf0, i, N{}, Y{});
+      }
     } else {
       for (; i + 2 <= n_iter; i += 2) {
-        step(buf0, i);
-        step(buf1, i + 1);
+        step(buf1, buf0, i, Y{}, Y{});
+        step(buf0, buf1, i + 1, Y{}, Y{});
       }
-      if (i < n_iter) step(buf0, i);
+      // i odd
+      if (i < n_iter) {
+        step(buf1, buf0, i, Y{}, Y{});
+        step(buf0, buf1, i + 1, N{}, Y{});
+      } else {
+        step(buf1, buf0, i, N{}, Y{});
+      }
     }
   }
 
@@ -518,7 +631,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   {
     const float ls = row_sum16(lsum);
     if (t == 0) wred[w][g4] = ls;
-    if (w == 0 && t == 0) mrun[g4] = m_a;
+    if (w == 0 && t == 0) mrun[g4] = (m_a == kNoRef) ? -INFINITY : m_a;
     const int hc = t >> 2;
     float avsum = 0.0f;
 #pragma unroll
@@ -565,26 +678,34 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   merge_splits(a, b, hq0, G, counter, w, lane);
 }
 
-template <int KB, bool QJL, int VB>
+template <int KB, bool QJL, int VB, bool AUX>
 __global__ __launch_bounds__(kRegThreads, 2) void decode_reg_kernel(DecodeArgs a) {
-  decode_reg_body<KB, QJL, VB, false>(a);
+  decode_reg_body<KB, QJL, VB, false, AUX>(a);
 }
 
-template <int KB, bool QJL, int VB>
+template <int KB, bool QJL, int VB, bool AUX>
 __global__ __launch_bounds__(kRegThreads, 2) void decode_reg_append_kernel(DecodeArgs a) {
-  decode_reg_body<KB, QJL, VB, true>(a);
+  decode_reg_body<KB, QJL, VB, true, AUX>(a);
 }
 
 template <int KB, bool QJL, int VB>
 hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   const int nhg = (a.group + 3) / 4;
-  hipLaunchKernelGGL((qprep_kernel<KB, QJL>), dim3(a.batch * a.n_kv * nhg), dim3(kPrepThreads), 0, stream, a);
+  hipLaunchKernelGGL((qprep_kernel<KB, QJL, VB>), dim3(a.batch * a.n_kv * nhg), dim3(kPrepThreads), 0, stream, a);
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * nhg);
-  if (a.k_new != nullptr)
-    hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB>), grid, dim3(kRegThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB>), grid, dim3(kRegThreads), 0, stream, a);
+  const bool aux = a.sparse_v > 0 || a.logits != nullptr;
+  if (a.k_new != nullptr) {
+    if (aux)
+      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, true>), grid, dim3(kRegThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, false>), grid, dim3(kRegThreads), 0, stream, a);
+  } else {
+    if (aux)
+      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, true>), grid, dim3(kRegThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, false>), grid, dim3(kRegThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -610,6 +731,8 @@ hipError_t launch_decode_reg(const DecodeArgs& a, hipStream_t stream) {
   const int64_t span = (static_cast<int64_t>(a.n_blocks) + 4) * std::max(a.k_block_bytes, a.v_block_bytes);
   if (span >= (int64_t{1} << 31) || static_cast<int64_t>(a.n_splits) * kPartialStride * 4 >= (int64_t{1} << 31))
     return hipErrorNotSupported;
+  // the logits of four heads of one sequence are addressed with 32-bit offsets
+  if (a.logits != nullptr && int64_t{16} * a.max_ctx >= (int64_t{1} << 31)) return hipErrorNotSupported;
   if (a.k_codec == POLAR_QJL) {
     switch (a.k_bits) {
       case 2: return launch_k<2, true>(a, stream);

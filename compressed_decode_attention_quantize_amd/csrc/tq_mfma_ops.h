@@ -48,20 +48,29 @@ __device__ __forceinline__ uint32_t term_word(const uint32_t* w, int T) {
 // constant per head, for values the product of the step's probabilities with
 // a fixed operand (rows of all-one and all-zero words, whose mean is the
 // offset row 5, 3, 1, 0).
-// (w & m) | c as one v_and_or_b32; the mask rides in a scalar register and
-// the fill in a vector register (a three-operand instruction here takes no
-// literal), both set once outside the loops.
-__device__ __forceinline__ int and_or(uint32_t w, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
-  return static_cast<int>(r);
+// The masks (scalar registers) and fills (vector registers) of the
+// expansion, made once per kernel so that each dword is one v_and_or_b32 (its
+// three-operand form takes no literal; with literals the compiler splits it
+// in two).  The empty asm statements only hide the values from constant
+// folding and emit nothing: every instruction that writes an operand stays
+// visible to the compiler, which pads the matrix instructions' operand
+// hazards.
+struct Fp4Fill {
+  uint32_t m0, m1, m3;   // 0x11111111, 0x22222222, 0x88888888
+  uint32_t c0, c1, c3;   // 0x66666666, 0x44444444, 0x22222222
+};
+__device__ __forceinline__ Fp4Fill fp4_fill() {
+  Fp4Fill k{0x11111111u, 0x22222222u, 0x88888888u, 0x66666666u, 0x44444444u, 0x22222222u};
+  asm volatile("" : "+s"(k.m0), "+s"(k.m1), "+s"(k.m3));
+  asm volatile("" : "+v"(k.c0), "+v"(k.c1), "+v"(k.c3));
+  return k;
 }
-__device__ __forceinline__ v8i expand_fp4_affine(uint32_t w) {
+__device__ __forceinline__ v8i expand_fp4_affine(uint32_t w, const Fp4Fill& k) {
   v8i r;
-  r[0] = and_or(w, 0x11111111u, 0x66666666u);
-  r[1] = and_or(w, 0x22222222u, 0x44444444u);
+  r[0] = static_cast<int>((w & k.m0) | k.c0);
+  r[1] = static_cast<int>((w & k.m1) | k.c1);
   r[2] = static_cast<int>(w & 0x44444444u);
-  r[3] = and_or(w, 0x88888888u, 0x22222222u);
+  r[3] = static_cast<int>((w & k.m3) | k.c3);
   r[4] = r[5] = r[6] = r[7] = 0;
   return r;
 }

@@ -17,7 +17,7 @@ def _write(path, counter, rows):
 
 
 def test_calibration_copy_is_the_trailing_dispatches(tmp_path):
-    dec = "void tq::decode_mfma_kernel<3, true, 2, 2>(tq::DecodeArgs)"
+    dec = "void tq::(anonymous namespace)::decode_reg_kernel<3, true, 3, false>(tq::DecodeArgs)"
     # a decoy whose count lies nearer the 256 MiB copy size than the copy's own
     fetch = [("reduce_kernel", 163911.0)] + [(dec, 13824.0)] * 5 + [("copyBuffer", 131083.5)] * 3
     write = [("reduce_kernel", 9.0)] + [(dec, 632.25)] * 5 + [("copyBuffer", 262144.0)] * 3
@@ -32,7 +32,7 @@ def test_calibration_copy_is_the_trailing_dispatches(tmp_path):
 
 
 def test_summary_refuses_a_run_without_trailing_copies(tmp_path):
-    dec = "void tq::decode_mfma_kernel<3, true, 2, 2>(tq::DecodeArgs)"
+    dec = "void tq::(anonymous namespace)::decode_reg_kernel<3, true, 3, false>(tq::DecodeArgs)"
     f, w = tmp_path / "f.csv", tmp_path / "w.csv"
     _write(f, "FETCH_SIZE", [(dec, 1.0)] * 4)
     _write(w, "WRITE_SIZE", [(dec, 1.0)] * 4)
