@@ -17,10 +17,9 @@
 //    one 8-byte load too).  A block's key and value loads are issued about
 //    three steps before the step that uses them, into one of three register
 //    sets (two with 4-bit values).
-//  * The query side is prepared once per (sequence, KV head, head group) by
-//    qprep_kernel; a workgroup copies those ready-made operands to shared
-//    memory once and reads each right before its product: no sketch table,
-//    rotation or digit formation in the decode workgroups.
+//  * Each workgroup forms its query operands (rotation, sketch, digits) in
+//    shared memory while its first blocks' loads are in flight, and reads
+//    each operand right before its product: no separate launch for them.
 //  * With at most four terms per key code (2- and 3-bit keys, values of 2 or
 //    3 bits) the codebook coefficients are folded into the query digits (one
 //    operand per term), so a column's terms accumulate in one matrix
@@ -62,155 +61,49 @@ struct KeyOps {
   static constexpr int code_sets = chain ? nt : 1;
 };
 
-// ------------------------------------------------------------- query prep
-// One workgroup of eight waves per (sequence, KV head, head group) of four
-// query heads (zero past the group).  Waves 0..3 rotate head w's query
-// (q_raw = H D_K q); every wave loads its 16-coordinate slice of the sketch
-// table and forms its share of (S H D_K / sqrt d) q for the four heads (the
-// eight shares of a row are added in wave order), so the table's loads are
-// in flight together and no wave walks all 128 coordinates.  Then base-32
-// digits with one E8M0 exponent per 32 k-slots (the operand layout of
-// v_mfma_scale_f32_16x16x128_f8f6f4: k-slot k stands for coordinate or sketch
-// row pos_of_slot(k); the k-slots that meet the sign field of the affine key
-// operand carry the value with its sign flipped), one (operand set, head)
-// pair per wave at a time, written as each decode lane's 32 operand bytes
-// and scale byte.
-constexpr int kPrepThreads = 512;
+// ------------------------------------------------------------ query side
 // The logit's constant factors travel in the query digits: log2(e) / sqrt d
 // (softmax in base 2, scale 1/sqrt d) times 1/d for the code term (the raw
 // FWHT's d) and sqrt(pi/2)/m for the sketch term (the estimator's constant);
 // a logit is then n16 * code + rho16 * sketch.
 constexpr float kCodeScale = 1.4426950408889634f * 0.08838834764831845f / 128.0f;
 constexpr float kSketchScale = 1.4426950408889634f * 0.08838834764831845f * 1.2533141373155003f / 128.0f;
+constexpr int kARow = 144;   // bytes per operand row in shared memory (128 k-slots, padded against bank conflicts)
 
-template <int KB, bool QJL, int VB>
-__global__ __launch_bounds__(kPrepThreads) void qprep_kernel(DecodeArgs a) {
-  using KO = KeyOps<KB, VB>;
-  constexpr int NSETS = KO::code_sets + (QJL ? 1 : 0);
-  constexpr int kWavesP = kPrepThreads / 64;
-  constexpr int kCpw = kD / kWavesP;   // table coordinates per wave
-  __shared__ __attribute__((aligned(16))) uint8_t alimb[NSETS][16 * 128];   // [set][row = 4g + j][k]
-  __shared__ uint8_t aexp[NSETS][4][16];                                   // [set][k / 32][row]
-  __shared__ float cconst[NSETS][4];
-  __shared__ float qr[4][kD];     // rotated query per head
-  __shared__ float qs[4][kD];     // the query per head (before rotation)
-  __shared__ __attribute__((aligned(16))) float sred[kWavesP][4][kM];   // [wave][head][row]: partial sketch sums
-  const int nhg = (a.group + 3) >> 2;
-  const int u = blockIdx.x;                  // (b * n_kv + h) * nhg + hg
-  const int hg = u % nhg;
-  const int h = (u / nhg) % a.n_kv;
-  const int b = u / (nhg * a.n_kv);
-  const int w = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int G = min(4, a.group - 4 * hg);
-  const int hq0 = h * a.group + 4 * hg;
-  float2 st2[kCpw];
-  if constexpr (QJL) {
-#pragma unroll
-    for (int c = 0; c < kCpw; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * w + c) * kM + 2 * lane);
+// Digits of u at k-slots 2 lane, 2 lane + 1 into operand `op` ([row][k]
+// bytes, rows 4 g + j), its E8M0 bytes `ex` ([k / 32][row]) and, on lane 0,
+// the operand's affine offset for head g (the sum of the digit-exact values
+// times the fixed nibble-field offsets 5, 3, 1, 0 of the key operand).
+// Base-32 digits with one exponent per 32 k-slots; the k-slots that meet the
+// sign field of the affine key operand carry the value with its sign flipped
+// (the operand layout of v_mfma_scale_f32_16x16x128_f8f6f4: k-slot k stands
+// for coordinate or sketch row pos_of_slot(k)).
+__device__ __forceinline__ void write_digits(uint8_t* op, uint8_t* ex, float* cconst, int g, float u0, float u1,
+                                             int lane) {
+  const int k0 = 2 * lane;
+  const int fld = (k0 & 31) >> 3;
+  if (fld == 3) {
+    u0 = -u0;
+    u1 = -u1;
   }
-  if (w < 4) {
-    const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
-    const float q0 = (w < G) ? qp[lane] : 0.0f, q1 = (w < G) ? qp[lane + 64] : 0.0f;
-    float lo = q0 * a.tb.dk[lane], hi = q1 * a.tb.dk[lane + 64];
-    qs[w][lane] = q0;
-    qs[w][lane + 64] = q1;
-    wave_fwht128(lo, hi, lane);
-    qr[w][lane] = lo;
-    qr[w][lane + 64] = hi;
+  const float m = row_max16(fmaxf(fabsf(u0), fabsf(u1)));
+  const int s0 = (m >= 1e-30f) ? exponent_of(m) - 3 : 0;   // |u| 2^-s0 < 16
+  float r0 = __builtin_amdgcn_ldexpf(u0, -s0), r1 = __builtin_amdgcn_ldexpf(u1, -s0);
+  float t0 = 0.0f, t1 = 0.0f;   // digit-exact values, in units of 2^s0
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+    t0 = fmaf(d0, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t0);
+    t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
+    r0 = (r0 - d0) * 32.0f;
+    r1 = (r1 - d1) * 32.0f;
+    *reinterpret_cast<uint16_t*>(&op[(4 * g + j) * kARow + k0]) = static_cast<uint16_t>(pk & 0xffff);
+    if ((k0 & 31) == 0) ex[(k0 >> 5) * 16 + 4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
   }
-  __syncthreads();
-  if constexpr (QJL) {
-    float acc[4][2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kCpw; ++c) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float x = qs[g][kCpw * w + c];
-        acc[g][0] = fmaf(st2[c].x, x, acc[g][0]);
-        acc[g][1] = fmaf(st2[c].y, x, acc[g][1]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g][2 * lane]) = make_float2(acc[g][0], acc[g][1]);
-  }
-
-  // digits of u at k-slots 2 lane, 2 lane + 1 into operand set `set`, head g
-  auto write_digits = [&](int set, int g, float u0, float u1) __attribute__((always_inline)) {
-    const int k0 = 2 * lane;
-    const int fld = (k0 & 31) >> 3;
-    if (fld == 3) {
-      u0 = -u0;
-      u1 = -u1;
-    }
-    const float m = row_max16(fmaxf(fabsf(u0), fabsf(u1)));
-    const int s0 = (m >= 1e-30f) ? exponent_of(m) - 3 : 0;   // |u| 2^-s0 < 16
-    float r0 = __builtin_amdgcn_ldexpf(u0, -s0), r1 = __builtin_amdgcn_ldexpf(u1, -s0);
-    float t0 = 0.0f, t1 = 0.0f;   // digit-exact values, in units of 2^s0
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
-      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
-      t0 = fmaf(d0, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t0);
-      t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
-      r0 = (r0 - d0) * 32.0f;
-      r1 = (r1 - d1) * 32.0f;
-      *reinterpret_cast<uint16_t*>(&alimb[set][(4 * g + j) * 128 + k0]) = static_cast<uint16_t>(pk & 0xffff);
-      if ((k0 & 31) == 0) aexp[set][k0 >> 5][4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
-    }
-    const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
-    const float c = wave_sum64(__builtin_amdgcn_ldexpf(wf * (t0 + t1), s0));
-    if (lane == 0) cconst[set][g] = c;
-  };
-  const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
-  // the code sets: (set, head) pairs spread over the waves
-  for (int job = w; job < KO::code_sets * 4; job += kWavesP) {
-    const int s = job >> 2, g = job & 3;
-    const float coef = (KO::chain ? a.tb.ak[s] : 1.0f) * kCodeScale;
-    write_digits(s, g, coef * qr[g][r0], coef * qr[g][r1]);
-  }
-  if constexpr (QJL) {
-    __syncthreads();   // every wave's sketch shares are in shared memory
-    // the sketch set: head w - 4 on waves 4..7
-    if (w >= 4) {
-      const int g = w - 4;
-      float u0 = 0.0f, u1 = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kWavesP; ++c) {
-        u0 += sred[c][g][r0];
-        u1 += sred[c][g][r1];
-      }
-      write_digits(KO::code_sets, g, kSketchScale * u0, kSketchScale * u1);
-    }
-  }
-  __syncthreads();
-
-  // lane L of the decode waves: row L % 16, k = 64 (e / 16) + 16 (L / 16) + e % 16
-  uint32_t* out = a.qops + static_cast<int64_t>(u) * (kQopsStride / 4);
-  for (int s = w; s < NSETS; s += kWavesP) {
-    const int t = lane & 15, g4 = lane >> 4;
-    const uint4 l4 = *reinterpret_cast<const uint4*>(&alimb[s][t * 128 + 16 * g4]);
-    const uint4 h4 = *reinterpret_cast<const uint4*>(&alimb[s][t * 128 + 64 + 16 * g4]);
-    *reinterpret_cast<uint4*>(out + (2 * s) * 256 + 4 * lane) = l4;
-    *reinterpret_cast<uint4*>(out + (2 * s + 1) * 256 + 4 * lane) = h4;
-    out[kQopsScaleWord + s * 64 + lane] = aexp[s][g4][t];
-  }
-  if (threadIdx.x < 4) {
-    float cq = 0.0f;
-    if constexpr (KO::chain) {
-#pragma unroll
-      for (int s = 0; s < KO::code_sets; ++s) cq += cconst[s][threadIdx.x];
-    } else {
-      float aksum = 0.0f;
-#pragma unroll
-      for (int T = 0; T < KO::nt; ++T) aksum += a.tb.ak[T];
-      cq = cconst[0][threadIdx.x] * aksum;
-    }
-    reinterpret_cast<float*>(out)[kQopsConstWord + threadIdx.x] = cq;
-    reinterpret_cast<float*>(out)[kQopsConstWord + 4 + threadIdx.x] = QJL ? cconst[NSETS - 1][threadIdx.x] : 0.0f;
-  }
+  const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
+  const float c = wave_sum64(__builtin_amdgcn_ldexpf(wf * (t0 + t1), s0));
+  if (lane == 0) cconst[g] = c;
 }
 
 // ---------------------------------------------------------------- decode
@@ -280,36 +173,30 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const int hq0 = h * a.group + 4 * hg;
   uint32_t* const counter = a.counters + (static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg;
   typedef __attribute__((address_space(4))) const int cint;
+  typedef __attribute__((address_space(4))) const float cfloat;
   const int len_in = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
   if constexpr (FUSED) {
     if (len_in < a.max_ctx && (len_in / kBlock) / a.chunk_blocks == split)
       fused_append<KB, QJL, VB>(a, b, h, len_in, w, lane, r_lds);
   }
 
-  // ------------------------------------------------ query operands (ready-made)
-  // The fp8 operands (NCS code sets, then the sketch set) wait in shared
-  // memory in lane order and are read right before each product: held in
-  // registers through the loop they would take 8 per set.
-  constexpr int NQS = NCS + (QJL ? 1 : 0);
-  __shared__ uint4 qlds[NQS * 2 * 64];
-  const uint32_t* qo = a.qops + ((static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg) * (kQopsStride / 4);
-  for (int e = tid; e < NQS * 2 * 64; e += kRegThreads) qlds[e] = *reinterpret_cast<const uint4*>(qo + 4 * e);
-  auto qop = [&](int set) __attribute__((always_inline)) {
-    const uint4 l4 = qlds[(2 * set) * 64 + lane];
-    const uint4 h4 = qlds[(2 * set + 1) * 64 + lane];
-    return v8i{(int)l4.x, (int)l4.y, (int)l4.z, (int)l4.w, (int)h4.x, (int)h4.y, (int)h4.z, (int)h4.w};
-  };
-  int scq[NCS];
-#pragma unroll
-  for (int s = 0; s < NCS; ++s) scq[s] = static_cast<int>(qo[kQopsScaleWord + s * 64 + lane]);
-  const int scsq = QJL ? static_cast<int>(qo[kQopsScaleWord + NCS * 64 + lane]) : 127;
-  const float cq = reinterpret_cast<const float*>(qo)[kQopsConstWord + g4];
-  const float csq = QJL ? reinterpret_cast<const float*>(qo)[kQopsConstWord + 4 + g4] : 0.0f;
   float ak[NTK], av[NTV];
 #pragma unroll
-  for (int T = 0; T < NTK; ++T) ak[T] = a.tb.ak[T];
+  for (int T = 0; T < NTK; ++T) ak[T] = ((cfloat*)(a.tb.ak))[T];   // scalar loads
 #pragma unroll
-  for (int T = 0; T < NTV; ++T) av[T] = a.tb.av[T];
+  for (int T = 0; T < NTV; ++T) av[T] = ((cfloat*)(a.tb.av))[T];
+
+  // the query side's loads go first: waits for them then leave the cache
+  // loads below in flight (vector memory counts complete in issue order)
+  constexpr int kCpw = kD / kWaves;   // sketch-table coordinates per wave
+  float2 st2[QJL ? kCpw : 1];
+  if constexpr (QJL) {
+#pragma unroll
+    for (int c = 0; c < kCpw; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * w + c) * kM + 2 * lane);
+  }
+  const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
+  const float pq0 = (w < G) ? qp[lane] : 0.0f, pq1 = (w < G) ? qp[lane + 64] : 0.0f;
+  const float pdk0 = a.tb.dk[lane], pdk1 = a.tb.dk[lane + 64];
 
   // ------------------------------------------------------------- streaming
   const int len = FUSED ? min(len_in + 1, a.max_ctx) : len_in;
@@ -369,8 +256,90 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     load_k(buf2, blk0 + 2, a.n_blocks, rk0);
     load_v(buf2, blk0 + 2, a.n_blocks, rv0);
   }
+  __builtin_amdgcn_sched_barrier(0);   // (issued before the query-side work below)
 
-  lds_barrier();   // the query operands are in shared memory (the loads above stay in flight)
+  // ------------------------------------------------ query operands
+  // Formed here while the first blocks' loads are in flight, into shared
+  // memory, and read right before each product (held in registers through
+  // the loop they would take 8 per set).  Wave w rotates head w's query
+  // (q_raw = H D_K q), takes a 32-coordinate slice of the sketch table for
+  // its share of (S H D_K / sqrt d) q for the four heads, then forms head w's
+  // digits for every operand set: the code sets (with the codebook
+  // coefficient folded in when chained), then the sketch set.
+  constexpr int NQS = NCS + (QJL ? 1 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t alimb[NQS][16 * kARow];   // [set][row = 4 g + j][k]
+  __shared__ __attribute__((aligned(4))) uint8_t aexp[NQS][4 * 16];        // [set][k / 32][row]
+  __shared__ float cconst[NQS][4];
+  __shared__ float qr[4][kD];                                               // rotated query per head
+  __shared__ float qs[QJL ? 4 : 1][kD];                                     // the query per head
+  __shared__ __attribute__((aligned(16))) float sred[QJL ? kWaves : 1][4][kM];   // partial sketch sums
+  {
+    {
+      float lo = pq0 * pdk0, hi = pq1 * pdk1;
+      const float q0 = pq0, q1 = pq1;
+      if constexpr (QJL) {
+        qs[w][lane] = q0;
+        qs[w][lane + 64] = q1;
+      }
+      wave_fwht128(lo, hi, lane);
+      qr[w][lane] = lo;
+      qr[w][lane + 64] = hi;
+    }
+    lds_barrier();   // (shared memory only: the cache loads stay in flight)
+    if constexpr (QJL) {
+      float acc[4][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kCpw; ++c) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float x = qs[g][kCpw * w + c];
+          acc[g][0] = fmaf(st2[c].x, x, acc[g][0]);
+          acc[g][1] = fmaf(st2[c].y, x, acc[g][1]);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g][2 * lane]) = make_float2(acc[g][0], acc[g][1]);
+    }
+    const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
+#pragma unroll
+    for (int s = 0; s < NCS; ++s) {
+      const float coef = (KO::chain ? ak[s] : 1.0f) * kCodeScale;
+      write_digits(alimb[s], aexp[s], cconst[s], w, coef * qr[w][r0], coef * qr[w][r1], lane);
+    }
+    if constexpr (QJL) {
+      lds_barrier();   // every wave's sketch shares are in shared memory
+      float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kWaves; ++c) {
+        u0 += sred[c][w][r0];
+        u1 += sred[c][w][r1];
+      }
+      write_digits(alimb[NCS], aexp[NCS], cconst[NCS], w, kSketchScale * u0, kSketchScale * u1, lane);
+    }
+  }
+  lds_barrier();   // the operands are in shared memory (the cache loads above stay in flight)
+  auto qop = [&](int set) __attribute__((always_inline)) {
+    const uint4 l4 = *reinterpret_cast<const uint4*>(&alimb[set][t * kARow + 16 * g4]);
+    const uint4 h4 = *reinterpret_cast<const uint4*>(&alimb[set][t * kARow + 64 + 16 * g4]);
+    return v8i{(int)l4.x, (int)l4.y, (int)l4.z, (int)l4.w, (int)h4.x, (int)h4.y, (int)h4.z, (int)h4.w};
+  };
+  int scq[NCS];
+#pragma unroll
+  for (int s = 0; s < NCS; ++s) scq[s] = aexp[s][16 * g4 + t];
+  const int scsq = QJL ? static_cast<int>(aexp[NQS - 1][16 * g4 + t]) : 127;
+  float cq = 0.0f;
+  if constexpr (KO::chain) {
+#pragma unroll
+    for (int s = 0; s < NCS; ++s) cq += cconst[s][g4];
+  } else {
+    float aksum = 0.0f;
+#pragma unroll
+    for (int T = 0; T < NTK; ++T) aksum += ak[T];
+    cq = cconst[0][g4] * aksum;
+  }
+  const float csq = QJL ? cconst[NQS - 1][g4] : 0.0f;
 
   // The optional logits go through a buffer over this (sequence, head
   // group)'s rows: a lane with no logit to store takes an offset past its end
@@ -691,7 +660,6 @@ __global__ __launch_bounds__(kRegThreads, 2) void decode_reg_append_kernel(Decod
 template <int KB, bool QJL, int VB>
 hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   const int nhg = (a.group + 3) / 4;
-  hipLaunchKernelGGL((qprep_kernel<KB, QJL, VB>), dim3(a.batch * a.n_kv * nhg), dim3(kPrepThreads), 0, stream, a);
   const int n_units = a.n_splits * a.n_kv * a.batch;
   dim3 grid(((n_units + 7) / 8) * 8 * nhg);
   const bool aux = a.sparse_v > 0 || a.logits != nullptr;
@@ -726,7 +694,7 @@ bool decode_reg_applies(int k_codec, int v_codec, int group) {
 }
 
 hipError_t launch_decode_reg(const DecodeArgs& a, hipStream_t stream) {
-  if (!decode_reg_applies(a.k_codec, a.v_codec, a.group) || a.qops == nullptr) return hipErrorNotSupported;
+  if (!decode_reg_applies(a.k_codec, a.v_codec, a.group)) return hipErrorNotSupported;
   // block byte offsets (up to n_blocks + 2 blocks) are 32-bit buffer offsets
   const int64_t span = (static_cast<int64_t>(a.n_blocks) + 4) * std::max(a.k_block_bytes, a.v_block_bytes);
   if (span >= (int64_t{1} << 31) || static_cast<int64_t>(a.n_splits) * kPartialStride * 4 >= (int64_t{1} << 31))

@@ -521,14 +521,6 @@ uint64_t counters_bytes(const tq_config* cfg) {
   return (counters + 255) & ~255ull;
 }
 
-// Query operands of the register-streamed decode: one kQopsStride record per
-// (sequence, KV head, head group), after the counters.
-uint64_t qops_bytes(const tq_config* cfg) {
-  if (!reg_path(cfg)) return 0;
-  const uint64_t groups = (cfg->n_q_heads / cfg->n_kv_heads + 3) / 4;
-  return static_cast<uint64_t>(cfg->batch) * cfg->n_kv_heads * groups * tq::kQopsStride;
-}
-
 uint64_t partials_bytes(const tq_config* cfg, int32_t max_seq_len) {
   const uint64_t splits = decode_splits_bound(cfg, max_seq_len);
   const uint64_t partial = static_cast<uint64_t>(cfg->batch) * cfg->n_q_heads * splits * tq::kPartialStride * 4;
@@ -536,7 +528,7 @@ uint64_t partials_bytes(const tq_config* cfg, int32_t max_seq_len) {
 }
 
 uint64_t workspace_need(const tq_config* cfg, int32_t max_seq_len) {
-  return counters_bytes(cfg) + qops_bytes(cfg) + partials_bytes(cfg, max_seq_len);
+  return counters_bytes(cfg) + partials_bytes(cfg, max_seq_len);
 }
 
 tq_status check_append(const tq_config* cfg, const void* params, const void* k_cache, const void* v_cache,
@@ -619,8 +611,7 @@ void fill_decode_args(const tq_config* cfg, const void* params, const void* k_ca
   a.out = out;
   a.logits = logits;
   a.counters = counters;
-  a.qops = reg_path(cfg) ? reinterpret_cast<uint32_t*>(rest) : nullptr;
-  a.partials = reinterpret_cast<float*>(rest + qops_bytes(cfg));
+  a.partials = reinterpret_cast<float*>(rest);
   a.batch = cfg->batch;
   a.n_q = cfg->n_q_heads;
   a.n_kv = cfg->n_kv_heads;

@@ -12,16 +12,6 @@ constexpr int kM = 128;        // QJL sketch rows served by the kernels
 constexpr int kBlock = 128;    // positions per cache block
 constexpr int kMaxGroup = 16;  // largest GQA group
 constexpr int kPartialStride = kD + 4;  // floats per split partial: acc[128], m, l, 2 pad (16-byte rows)
-// Query operands of one (sequence, KV head, group of four query heads), as the
-// query-prep kernel leaves them for the register-streamed decode kernel: up to
-// kQopsSets fp8 matrix operands (the key code terms, then the sketch), each
-// as two 1 KB halves of 64 lanes x 16 bytes, then one E8M0 scale word per set
-// and lane, then per head the offsets of the affine key operands.
-constexpr int kQopsSets = 5;
-constexpr int kQopsScaleWord = kQopsSets * 2 * 64 * 4;            // uint32 index of the scale words
-constexpr int kQopsConstWord = kQopsScaleWord + kQopsSets * 64;  // 4 code offsets, then 4 sketch offsets
-constexpr int kQopsStride = ((kQopsConstWord + 8) * 4 + 255) / 256 * 256;   // bytes per group, 256-aligned
-
 // Slot of position t inside its 128-position block for the per-position
 // fields of POLAR keys (code words, sign words, radius, residual norm) and
 // for the radius of POLAR values: a fixed permutation inside each group of
@@ -120,7 +110,6 @@ struct DecodeArgs {
   float* logits;      // may be null
   float* partials;    // [batch][n_q][n_splits][kPartialStride]
   uint32_t* counters; // [batch][n_kv][kMaxGroup / 4]
-  uint32_t* qops;     // [batch][n_kv][head groups] x kQopsStride bytes (register-streamed decode)
   int32_t batch, n_q, n_kv, group, max_ctx, n_blocks;
   int32_t chunk_blocks, n_splits;
   int32_t k_codec, k_bits, v_codec, v_bits;
@@ -153,8 +142,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // returns hipErrorNotSupported for other configurations.
 bool decode_mfma_applies(int k_codec, int v_codec, int group);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-// Register-streamed matrix-core decode (query prep, then decode) for POLAR /
-// POLAR_QJL keys with POLAR values and G <= 16; hipErrorNotSupported otherwise.
+// Register-streamed matrix-core decode for POLAR / POLAR_QJL keys with POLAR
+// values and G <= 16; hipErrorNotSupported otherwise.
 bool decode_reg_applies(int k_codec, int v_codec, int group);
 hipError_t launch_decode_reg(const DecodeArgs& a, hipStream_t stream);
 // Block groups (of four wavefronts) per workgroup of the matrix-core decode
