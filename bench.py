@@ -45,13 +45,13 @@ FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 (matrix and vector)
 HEADLINE = "long_b1_ctx1m"
 CONFIG_SET = ("llama8b_b1_ctx32k", "cmdr104b_b1_ctx128k", "serving_b16_ctx8k")
 # what the matrix-core decode computes in: packed codes enter the matrix
-# cores as fp4 (e2m1) operands against exact integer digits in fp8 (e4m3)
-# with one E8M0 scale per 32 k-slots; every sum accumulates in fp32
-DECODE_DTYPE = ("fp4 code operands x fp8 digit operands, fp32 accumulate (query: 4 base-32 digits per "
-                "32-slot E8M0 block, about 19 significant bits; p*radius: 3 digits, about 14 bits; "
-                "q8 keys: int8 x 3 base-128 int8 query digits, int32 accumulate)")
-# name fragment of the dominant decode kernel (POLAR / POLAR_QJL keys; each
-# decode call runs a small query-prep kernel before it)
+# cores as fp4 (e2m1) operands against exact digits in fp6 (e2m3, the query)
+# or fp8 (e4m3, p * radius) with one E8M0 scale per 32 k-slots; every sum
+# accumulates in fp32
+DECODE_DTYPE = ("fp4 code operands x fp6 (query) and fp8 (p*radius) digit operands, fp32 accumulate (query: "
+                "4 base-16 digits per 32-slot E8M0 block, about 15 significant bits; p*radius: 3 base-32 digits, "
+                "about 14 bits; q8 keys: int8 x 3 base-128 int8 query digits, int32 accumulate)")
+# name fragment of the dominant decode kernel (POLAR / POLAR_QJL keys)
 DECODE_KERNEL = "decode_reg_kernel"
 TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_reg_*_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "compressed_decode_attention_quantize_amd", "csrc", f)

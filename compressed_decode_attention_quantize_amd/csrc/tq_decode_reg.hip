@@ -5,8 +5,10 @@
 // The arithmetic is the matrix-core form of the estimator, softmax and
 // rotated-frame weighted sum (wis-web.com reader, TurboQuant article, the
 // PolarQuant and QJL paragraphs; see tq_decode_mfma.hip for the operand
-// algebra): code planes become fp4 operands with one and-or per dword, the
-// query and p * radius enter as exact base-32 fp8 digits with E8M0 scales.
+// algebra): code planes become fp4 operands with one and-or per dword; the
+// query enters as exact base-16 digits in fp6 (so that its products with the
+// fp4 codes run at the matrix cores' 4-pass rate), p * radius as exact
+// base-32 fp8 digits, both with E8M0 scales.
 // What differs is the data flow:
 //
 //  * No cache byte is read twice and none is staged: lane (t, g4) of wave w
@@ -68,42 +70,78 @@ struct KeyOps {
 // a logit is then n16 * code + rho16 * sketch.
 constexpr float kCodeScale = 1.4426950408889634f * 0.08838834764831845f / 128.0f;
 constexpr float kSketchScale = 1.4426950408889634f * 0.08838834764831845f * 1.2533141373155003f / 128.0f;
-constexpr int kARow = 144;   // bytes per operand row in shared memory (128 k-slots, padded against bank conflicts)
+// Query operand rows in shared memory: 128 k-slots of fp6 (e2m3) digits,
+// packed 6 bits per k-slot from bit 0 (96 bytes), padded to 104 bytes so
+// that the 16 rows one 8-byte read instruction gathers fall on distinct banks.
+// Lane (t, g4) of a product reads row t, k-slots 32 g4 .. 32 g4 + 31: the
+// fp6 operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 (contiguous 32
+// k-slots per group of 16 lanes, one E8M0 scale each).
+constexpr int kARow = 104;
 
-// Digits of u at k-slots 2 lane, 2 lane + 1 into operand `op` ([row][k]
-// bytes, rows 4 g + j), its E8M0 bytes `ex` ([k / 32][row]) and, on lane 0,
-// the operand's affine offset for head g (the sum of the digit-exact values
-// times the fixed nibble-field offsets 5, 3, 1, 0 of the key operand).
-// Base-32 digits with one exponent per 32 k-slots; the k-slots that meet the
-// sign field of the affine key operand carry the value with its sign flipped
-// (the operand layout of v_mfma_scale_f32_16x16x128_f8f6f4: k-slot k stands
-// for coordinate or sketch row pos_of_slot(k)).
-__device__ __forceinline__ void write_digits(uint8_t* op, uint8_t* ex, float* cconst, int g, float u0, float u1,
-                                             int lane) {
-  const int k0 = 2 * lane;
-  const int fld = (k0 & 31) >> 3;
-  if (fld == 3) {
-    u0 = -u0;
-    u1 = -u1;
-  }
-  const float m = row_max16(fmaxf(fabsf(u0), fabsf(u1)));
-  const int s0 = (m >= 1e-30f) ? exponent_of(m) - 3 : 0;   // |u| 2^-s0 < 16
-  float r0 = __builtin_amdgcn_ldexpf(u0, -s0), r1 = __builtin_amdgcn_ldexpf(u1, -s0);
-  float t0 = 0.0f, t1 = 0.0f;   // digit-exact values, in units of 2^s0
+// Query digits of one (operand set, head) job, formed by a half-wave: lane l
+// (0 .. 31) holds the values x (already divided by the job's coefficient
+// coef) of k-slots 4 l .. 4 l + 3, which occupy 3 whole bytes of each operand
+// row.  Digit j of value v = coef x is an integer n_j in [-8, 8] standing for
+// n_j / 8 (exact in fp6 e2m3 as sign and magnitude: code |n_j|, sign in bit
+// 5), with v = 2^s0 sum_j (n_j / 8) 16^-j; s0 is taken per 32 k-slots so that
+// their largest |v| 2^-s0 lies in [0.5, 1), and each remainder again lies in
+// [-1, 1].  Writes operand rows 4 g + j of `op` (kARow bytes each; each quad
+// of lanes gathers its 12 bytes and stores them as 3 aligned words), their
+// E8M0 bytes 2^(s0 - 4 j) into `ex` ([k / 32][row]) and, into cc[g], the
+// operand's affine offset for head g (the sum of the digit-exact values
+// times the fixed nibble-field offsets 5, 3, 1, 0 of the key operand).  The
+// k-slots that meet the sign field of the affine key operand carry the value
+// with its sign flipped (k-slot k stands for coordinate or sketch row
+// pos_of_slot(k)).
+struct DigitLane {
+  uint32_t psel;   // byte selector of this lane's word (own 3 bytes, then the next lane's)
+  int pofs;        // byte offset of that word inside a row
+  int l;           // lane within the half-wave
+};
+__device__ __forceinline__ DigitLane digit_lane(int lane) {
+  const int l = lane & 31, i = min(l & 3, 2);
+  return DigitLane{(i == 0) ? 0x04020100u : (i == 1) ? 0x05040201u : 0x06050402u, 12 * (l >> 2) + 4 * i, l};
+}
+__device__ __forceinline__ void write_digits(uint8_t* op, uint8_t* ex, float* cc, int g, float4 x, float coef,
+                                             const DigitLane& dl) {
+  const int l = dl.l;
+  const int fld = (l & 7) >> 1;
+  float m = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+  m *= fabsf(coef);   // the largest |v| of these 32 k-slots
+  const int s0 = (m >= 1e-30f) ? exponent_of(m) + 1 : 0;
+  float sc = __builtin_amdgcn_ldexpf(coef, 3 - s0);   // v 2^(3 - s0) = 8 v 2^-s0, in [-8, 8]
+  if (fld == 3) sc = -sc;
+  float r[4] = {x.x * sc, x.y * sc, x.z * sc, x.w * sc};
+  const float r0[4] = {r[0], r[1], r[2], r[3]};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float d0 = rintf(r0), d1 = rintf(r1);   // integers in [-16, 16]: exact in e4m3
-    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
-    t0 = fmaf(d0, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t0);
-    t1 = fmaf(d1, __builtin_amdgcn_ldexpf(1.0f, -5 * j), t1);
-    r0 = (r0 - d0) * 32.0f;
-    r1 = (r1 - d1) * 32.0f;
-    *reinterpret_cast<uint16_t*>(&op[(4 * g + j) * kARow + k0]) = static_cast<uint16_t>(pk & 0xffff);
-    if ((k0 & 31) == 0) ex[(k0 >> 5) * 16 + 4 * g + j] = static_cast<uint8_t>(min(max(s0 - 5 * j + 127, 1), 254));
+    uint32_t v = 0;   // fp6 codes of the 4 k-slots, k-slot 4 l + i at bits 6 i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float n = rintf(r[i]);
+      r[i] = (r[i] - n) * 16.0f;   // exact
+      const uint32_t c = static_cast<uint32_t>(fabsf(n)) | ((__float_as_uint(n) >> 26) & 0x20u);
+      v |= c << (6 * i);
+    }
+    // lane i of a quad stores the word made of bytes 4 i' .. 4 i' + 3 of the
+    // quad's 12 (i' = min(i, 2); lane 3 repeats lane 2's word)
+    const uint32_t nxt = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xF9, 0xF, 0xF, false));
+    const uint32_t slf = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xA4, 0xF, 0xF, false));
+    *reinterpret_cast<uint32_t*>(&op[(4 * g + j) * kARow + dl.pofs]) = __builtin_amdgcn_perm(nxt, slf, dl.psel);
   }
+  // the exponent of digit l & 3 of the 32 k-slots (lanes l and l + 4 store the same)
+  ex[(l >> 3) * 16 + 4 * g + (l & 3)] = static_cast<uint8_t>(min(max(s0 - 4 * (l & 3) + 127, 1), 254));
+  // digit-exact value of k-slot i in units of 2^(s0 - 3): r0 - r4 16^-4 (exact)
+  float tv = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tv += fmaf(r[i], -1.52587890625e-05f, r0[i]);
   const float wf = (fld == 0) ? 5.0f : (fld == 1) ? 3.0f : (fld == 2) ? 1.0f : 0.0f;
-  const float c = wave_sum64(__builtin_amdgcn_ldexpf(wf * (t0 + t1), s0));
-  if (lane == 0) cconst[g] = c;
+  float s = row_sum16(__builtin_amdgcn_ldexpf(wf * tv, s0 - 3));
+  s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x142, 0xA, 0xF, false));   // rows 1, 3: + rows 0, 2
+  if (l & 16) cc[g] = s;
 }
 
 // ---------------------------------------------------------------- decode
@@ -188,15 +226,16 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
 
   // the query side's loads go first: waits for them then leave the cache
   // loads below in flight (vector memory counts complete in issue order)
+  // (the rotation's operands first: its wait then leaves the table in flight)
+  const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
+  const float pq0 = (w < G) ? qp[lane] : 0.0f, pq1 = (w < G) ? qp[lane + 64] : 0.0f;
+  const float pdk0 = a.tb.dk[lane], pdk1 = a.tb.dk[lane + 64];
   constexpr int kCpw = kD / kWaves;   // sketch-table coordinates per wave
   float2 st2[QJL ? kCpw : 1];
   if constexpr (QJL) {
 #pragma unroll
     for (int c = 0; c < kCpw; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * w + c) * kM + 2 * lane);
   }
-  const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
-  const float pq0 = (w < G) ? qp[lane] : 0.0f, pq1 = (w < G) ? qp[lane + 64] : 0.0f;
-  const float pdk0 = a.tb.dk[lane], pdk1 = a.tb.dk[lane + 64];
 
   // ------------------------------------------------------------- streaming
   const int len = FUSED ? min(len_in + 1, a.max_ctx) : len_in;
@@ -262,17 +301,18 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // Formed here while the first blocks' loads are in flight, into shared
   // memory, and read right before each product (held in registers through
   // the loop they would take 8 per set).  Wave w rotates head w's query
-  // (q_raw = H D_K q), takes a 32-coordinate slice of the sketch table for
-  // its share of (S H D_K / sqrt d) q for the four heads, then forms head w's
-  // digits for every operand set: the code sets (with the codebook
-  // coefficient folded in when chained), then the sketch set.
+  // (q_raw = H D_K q) and takes a 32-coordinate slice of the sketch table for
+  // its share of (S H D_K / sqrt d) q for the four heads; then each half of
+  // wave w forms head w's digits for one operand set at a time: the code
+  // sets two at a time (with the codebook coefficient folded in when
+  // chained), then the sketch set.  Both vectors are kept in k-slot order.
   constexpr int NQS = NCS + (QJL ? 1 : 0);
   __shared__ __attribute__((aligned(16))) uint8_t alimb[NQS][16 * kARow];   // [set][row = 4 g + j][k]
   __shared__ __attribute__((aligned(4))) uint8_t aexp[NQS][4 * 16];        // [set][k / 32][row]
   __shared__ float cconst[NQS][4];
-  __shared__ float qr[4][kD];                                               // rotated query per head
-  __shared__ float qs[QJL ? 4 : 1][kD];                                     // the query per head
-  __shared__ __attribute__((aligned(16))) float sred[QJL ? kWaves : 1][4][kM];   // partial sketch sums
+  __shared__ __attribute__((aligned(16))) float qr[4][kD];                  // rotated query per head, by k-slot
+  __shared__ __attribute__((aligned(16))) float qs[QJL ? 4 : 1][kD];       // the query per head
+  __shared__ __attribute__((aligned(16))) float sred[QJL ? kWaves : 1][4][kM];   // partial sketch sums, by k-slot
   {
     {
       float lo = pq0 * pdk0, hi = pq1 * pdk1;
@@ -282,48 +322,65 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
         qs[w][lane + 64] = q1;
       }
       wave_fwht128(lo, hi, lane);
-      qr[w][lane] = lo;
-      qr[w][lane + 64] = hi;
+      qr[w][slot_of(lane)] = lo;
+      qr[w][slot_of(lane + 64)] = hi;
     }
-    lds_barrier();   // (shared memory only: the cache loads stay in flight)
+    const DigitLane dl = digit_lane(lane);
+    const int half = lane >> 5;
     if constexpr (QJL) {
+      lds_barrier();   // every head's query is in shared memory (the cache loads stay in flight)
       float acc[4][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kCpw; ++c) {
+      for (int c4 = 0; c4 < kCpw; c4 += 4) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float x = qs[g][kCpw * w + c];
-          acc[g][0] = fmaf(st2[c].x, x, acc[g][0]);
-          acc[g][1] = fmaf(st2[c].y, x, acc[g][1]);
+          const float4 x = *reinterpret_cast<const float4*>(&qs[g][kCpw * w + c4]);
+          acc[g][0] = fmaf(st2[c4].x, x.x, acc[g][0]);
+          acc[g][1] = fmaf(st2[c4].y, x.x, acc[g][1]);
+          acc[g][0] = fmaf(st2[c4 + 1].x, x.y, acc[g][0]);
+          acc[g][1] = fmaf(st2[c4 + 1].y, x.y, acc[g][1]);
+          acc[g][0] = fmaf(st2[c4 + 2].x, x.z, acc[g][0]);
+          acc[g][1] = fmaf(st2[c4 + 2].y, x.z, acc[g][1]);
+          acc[g][0] = fmaf(st2[c4 + 3].x, x.w, acc[g][0]);
+          acc[g][1] = fmaf(st2[c4 + 3].y, x.w, acc[g][1]);
         }
       }
+      const int k0 = slot_of(2 * lane), k1 = slot_of(2 * lane + 1);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) *reinterpret_cast<float2*>(&sred[w][g][2 * lane]) = make_float2(acc[g][0], acc[g][1]);
+      for (int g = 0; g < 4; ++g) {
+        sred[w][g][k0] = acc[g][0];
+        sred[w][g][k1] = acc[g][1];
+      }
     }
-    const int r0 = pos_of_slot(2 * lane), r1 = pos_of_slot(2 * lane + 1);
+    // (head w's rotated query was written by this wave: no barrier)
+    const float4 xr = *reinterpret_cast<const float4*>(&qr[w][4 * dl.l]);
 #pragma unroll
-    for (int s = 0; s < NCS; ++s) {
-      const float coef = (KO::chain ? ak[s] : 1.0f) * kCodeScale;
-      write_digits(alimb[s], aexp[s], cconst[s], w, coef * qr[w][r0], coef * qr[w][r1], lane);
+    for (int s2 = 0; s2 < NCS; s2 += 2) {
+      const int s = min(s2 + half, NCS - 1);   // (an odd last set is formed by both halves)
+      const float coef = (KO::chain ? ((s == s2) ? ak[s2] : ak[min(s2 + 1, NCS - 1)]) : 1.0f) * kCodeScale;
+      write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, w, xr, coef, dl);
     }
     if constexpr (QJL) {
       lds_barrier();   // every wave's sketch shares are in shared memory
-      float u0 = 0.0f, u1 = 0.0f;
+      float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
       for (int c = 0; c < kWaves; ++c) {
-        u0 += sred[c][w][r0];
-        u1 += sred[c][w][r1];
+        const float4 y = *reinterpret_cast<const float4*>(&sred[c][w][4 * dl.l]);
+        u.x += y.x;
+        u.y += y.y;
+        u.z += y.z;
+        u.w += y.w;
       }
-      write_digits(alimb[NCS], aexp[NCS], cconst[NCS], w, kSketchScale * u0, kSketchScale * u1, lane);
+      write_digits(alimb[NCS], aexp[NCS], cconst[NCS], w, u, kSketchScale, dl);   // (both halves: the same job)
     }
   }
   lds_barrier();   // the operands are in shared memory (the cache loads above stay in flight)
   auto qop = [&](int set) __attribute__((always_inline)) {
-    const uint4 l4 = *reinterpret_cast<const uint4*>(&alimb[set][t * kARow + 16 * g4]);
-    const uint4 h4 = *reinterpret_cast<const uint4*>(&alimb[set][t * kARow + 64 + 16 * g4]);
-    return v8i{(int)l4.x, (int)l4.y, (int)l4.z, (int)l4.w, (int)h4.x, (int)h4.y, (int)h4.z, (int)h4.w};
+    const uint2* rp = reinterpret_cast<const uint2*>(&alimb[set][t * kARow + 24 * g4]);
+    const uint2 x = rp[0], y = rp[1], z = rp[2];
+    return v8i{(int)x.x, (int)x.y, (int)y.x, (int)y.y, (int)z.x, (int)z.y, 0, 0};
   };
   int scq[NCS];
 #pragma unroll
@@ -388,8 +445,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
 #pragma unroll
         for (int T = 0; T < NTK; ++T) {
           const v8i A = qop(T);
-          acc0 = mfma_fp8_fp4(A, expand_fp4_affine(term_word<KB>(wd0, T), kf), acc0, scq[T]);
-          acc1 = mfma_fp8_fp4(A, expand_fp4_affine(term_word<KB>(wd1, T), kf), acc1, scq[T]);
+          acc0 = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd0, T), kf), acc0, scq[T]);
+          acc1 = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd1, T), kf), acc1, scq[T]);
         }
         code2[0] = (acc0[0] + acc0[1]) + (acc0[2] + acc0[3]);
         code2[1] = (acc1[0] + acc1[1]) + (acc1[2] + acc1[3]);
@@ -403,14 +460,14 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
           if constexpr (KO::chain) {
             v4f acc = v4f{-cq, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int T = 0; T < NTK; ++T) acc = mfma_fp8_fp4(qop(T), expand_fp4_affine(term_word<KB>(wd, T), kf), acc, scq[T]);
+            for (int T = 0; T < NTK; ++T) acc = mfma_fp6_fp4(qop(T), expand_fp4_affine(term_word<KB>(wd, T), kf), acc, scq[T]);
             code2[c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
           } else {
             v4f dT[NTK];
             const v8i A = qop(0);
 #pragma unroll
             for (int T = 0; T < NTK; ++T)
-              dT[T] = mfma_fp8_fp4(A, expand_fp4_affine(term_word<KB>(wd, T), kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq[0]);
+              dT[T] = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd, T), kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq[0]);
             float code = -cq;
 #pragma unroll
             for (int T = 0; T < NTK; ++T) code = fmaf(ak[T], (dT[T][0] + dT[T][1]) + (dT[T][2] + dT[T][3]), code);
@@ -420,8 +477,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       }
       if constexpr (QJL) {
         const v8i As = qop(NCS);
-        const v4f dQ0 = mfma_fp8_fp4(As, expand_fp4_affine(Bk.ks.x, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
-        const v4f dQ1 = mfma_fp8_fp4(As, expand_fp4_affine(Bk.ks.y, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+        const v4f dQ0 = mfma_fp6_fp4(As, expand_fp4_affine(Bk.ks.x, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+        const v4f dQ1 = mfma_fp6_fp4(As, expand_fp4_affine(Bk.ks.y, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
         qj2[0] = (dQ0[0] + dQ0[1]) + (dQ0[2] + dQ0[3]);
         qj2[1] = (dQ1[0] + dQ1[1]) + (dQ1[2] + dQ1[3]);
       }

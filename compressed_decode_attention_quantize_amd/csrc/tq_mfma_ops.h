@@ -81,6 +81,10 @@ __device__ __forceinline__ int exponent_of(float x) {   // floor(log2 x), x > 0 
 
 __device__ __forceinline__ float h2f(uint32_t bits16) { return __half2float(__ushort_as_half(static_cast<uint16_t>(bits16))); }
 
+// fp6 (e2m3) digits x fp4 code operand: both at most 6 bits, the 4-pass rate
+__device__ __forceinline__ v4f mfma_fp6_fp4(const v8i& a, const v8i& b, const v4f& c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 2, 4, 0, sa, 0, 127);
+}
 __device__ __forceinline__ v4f mfma_fp8_fp4(const v8i& a, const v8i& b, const v4f& c, int sa) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 127);
 }
