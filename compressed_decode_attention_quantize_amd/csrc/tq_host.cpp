@@ -454,12 +454,16 @@ int64_t split_units(const tq_config* c) {
   return static_cast<int64_t>(c->batch) * c->n_kv_heads * groups;
 }
 
-// Blocks per split when the grid aims at `target` workgroups.
+// Blocks per split when the grid aims at `target` workgroups, the number the
+// chip holds at once: the split count rounds down, so that a grid never has a
+// few workgroups left for a second round (with three head groups per KV head,
+// 22 splits x 24 units would be 528 workgroups of the same length for 512
+// places: the last 16 would start when the first finish, doubling the launch).
 int chunk_blocks_for(const tq_config* c, int32_t max_seq_len, int64_t target) {
   const int blocks = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
   if (c->decode_chunk > 0) return c->decode_chunk / kBlock;
   const int64_t pairs = split_units(c);
-  const int64_t want_splits = std::max<int64_t>(1, (target + pairs - 1) / pairs);
+  const int64_t want_splits = std::max<int64_t>(1, target / pairs);
   const int64_t chunk = std::max<int64_t>(1, (blocks + want_splits - 1) / want_splits);
   // the register-streamed kernel's per-split costs (query operands, the
   // first loads' latency, partials, merge) want a few steps to spread over
