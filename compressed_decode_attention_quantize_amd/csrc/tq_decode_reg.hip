@@ -31,6 +31,9 @@
 //    i forms the logits of block i and, around the barrier, the probability
 //    digits, running references and weighted values of block i - 1.  Two
 //    workgroups share a compute unit, so their steps interleave.
+//  * Sparse-V (the wis-web.com article's third finding): the variant that
+//    votes on blocks requests a block's value words only after its vote, so
+//    the value bytes of a skipped block stay in HBM.
 
 #include <algorithm>
 #include <type_traits>
@@ -155,6 +158,11 @@ struct StepRegs {
   uint32_t kr;     // fp16 residual norms
   uint2 vp[VB];    // value planes: coordinates 32w + 2t, + 1 of k-block g4
   uint32_t vn;     // fp16 value radii of the two slots
+  // with the value request after the vote: the probabilities of the two
+  // slots of the block whose values the set holds, and whether they were
+  // requested (its vote kept the block)
+  float pp0, pp1;
+  bool vreq;
 };
 
 template <int KB, bool QJL, int VB>
@@ -165,12 +173,17 @@ struct RegFmt {
   static constexpr int loads = KB + (QJL ? 3 : 1) + VB + 1;   // vector loads per step and wave
 };
 
-// AUX: the variant that also writes logits and skips value work (Sparse-V);
-// the plain variant has neither in its step.
+// AUX: the variant that also writes logits and skips the value work of
+// blocks whose weights are negligible (Sparse-V; with 2- and 3-bit values it
+// also never requests their value words); the plain variant has neither in
+// its step.
 template <int KB, bool QJL, int VB, bool FUSED, bool AUX>
 __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // three register sets, two with 4-bit values (three would not fit in 256)
   constexpr int kSets = (VB == 4) ? 2 : 3;
+  // the logits / Sparse-V variant requests a block's values only after its
+  // vote (three register sets needed)
+  constexpr bool kLag = AUX && kSets == 3;
   using KO = KeyOps<KB, VB>;
   using F = RegFmt<KB, QJL, VB>;
   using R = StepRegs<KB, QJL, VB>;
@@ -183,7 +196,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   constexpr int kPRow = 144;
   __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * kPRow];
   __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];        // [parity][k / 32][col]
-  __shared__ float rwb[2][kWaves][4];       // [parity][wave][head]: each wave's step reference
+  __shared__ float rwb[4][kWaves][4];       // [block mod 4 (mod 2)][wave][head]: each wave's step reference
   __shared__ float wred[kWaves][4];
   __shared__ float mrun[4];
   __shared__ __attribute__((aligned(16))) float obuf[4][kD];
@@ -288,12 +301,12 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // i - 1 + kSets.
   R buf0, buf1, buf2;
   load_k(buf0, blk0, a.n_blocks, rk0);
-  load_v(buf0, blk0, a.n_blocks, rv0);
+  if constexpr (!kLag) load_v(buf0, blk0, a.n_blocks, rv0);
   load_k(buf1, blk0 + 1, a.n_blocks, rk0);
-  load_v(buf1, blk0 + 1, a.n_blocks, rv0);
+  if constexpr (!kLag) load_v(buf1, blk0 + 1, a.n_blocks, rv0);
   if constexpr (kSets == 3) {
     load_k(buf2, blk0 + 2, a.n_blocks, rk0);
-    load_v(buf2, blk0 + 2, a.n_blocks, rv0);
+    if constexpr (!kLag) load_v(buf2, blk0 + 2, a.n_blocks, rv0);
   }
   __builtin_amdgcn_sched_barrier(0);   // (issued before the query-side work below)
 
@@ -419,6 +432,184 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u, kf);
   float lgp[2] = {-INFINITY, -INFINITY};   // this lane's two logits of the block before
 
+  // ---- the pieces of a step
+  // (1a) key products of the block in Bk: column group c = slots 32 w + 2 t + c
+  auto key_products = [&](R& Bk, float (&code2)[2], float (&qj2)[2]) __attribute__((always_inline)) {
+    if constexpr (KO::chain && VB < 4) {   // both column groups' chains side by side
+      uint32_t wd0[KB], wd1[KB];
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        wd0[p] = Bk.kp[p].x;
+        wd1[p] = Bk.kp[p].y;
+      }
+      v4f acc0 = v4f{-cq, 0.0f, 0.0f, 0.0f}, acc1 = acc0;   // the affine operands' offset, removed up front
+#pragma unroll
+      for (int T = 0; T < NTK; ++T) {
+        const v8i A = qop(T);
+        acc0 = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd0, T), kf), acc0, scq[T]);
+        acc1 = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd1, T), kf), acc1, scq[T]);
+      }
+      code2[0] = (acc0[0] + acc0[1]) + (acc0[2] + acc0[3]);
+      code2[1] = (acc1[0] + acc1[1]) + (acc1[2] + acc1[3]);
+    } else {
+      // one column group at a time (fewer live registers)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint32_t wd[KB];
+#pragma unroll
+        for (int p = 0; p < KB; ++p) wd[p] = c ? Bk.kp[p].y : Bk.kp[p].x;
+        if constexpr (KO::chain) {
+          v4f acc = v4f{-cq, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int T = 0; T < NTK; ++T) acc = mfma_fp6_fp4(qop(T), expand_fp4_affine(term_word<KB>(wd, T), kf), acc, scq[T]);
+          code2[c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        } else {
+          v4f dT[NTK];
+          const v8i A = qop(0);
+#pragma unroll
+          for (int T = 0; T < NTK; ++T)
+            dT[T] = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd, T), kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq[0]);
+          float code = -cq;
+#pragma unroll
+          for (int T = 0; T < NTK; ++T) code = fmaf(ak[T], (dT[T][0] + dT[T][1]) + (dT[T][2] + dT[T][3]), code);
+          code2[c] = code;
+        }
+      }
+    }
+    if constexpr (QJL) {
+      const v8i As = qop(NCS);
+      const v4f dQ0 = mfma_fp6_fp4(As, expand_fp4_affine(Bk.ks.x, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+      const v4f dQ1 = mfma_fp6_fp4(As, expand_fp4_affine(Bk.ks.y, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
+      qj2[0] = (dQ0[0] + dQ0[1]) + (dQ0[2] + dQ0[3]);
+      qj2[1] = (dQ1[0] + dQ1[1]) + (dQ1[2] + dQ1[3]);
+    }
+  };
+  // (1b) this wave's reference per head (row g4) for the logits in lgp: the
+  // integer ceiling of its step maximum (p <= 1 against it), and the
+  // probabilities of its two slots
+  auto wave_ref = [&](float& rw, float& p0, float& p1) __attribute__((always_inline)) {
+    const float mloc = row_max16(fmaxf(lgp[0], lgp[1]));
+    rw = fmaxf(ceilf(mloc), kNoRef);
+    p0 = __builtin_amdgcn_exp2f(lgp[0] - rw);   // exp2(-inf) = 0 for slots without a logit
+    p1 = __builtin_amdgcn_exp2f(lgp[1] - rw);
+  };
+  // digits of p * radius (radii in vn) to shared memory
+  auto p_digits = [&](uint8_t* pl, uint8_t* pe, float p0, float p1, uint32_t vn) __attribute__((always_inline)) {
+    float r0 = mul_zero_wins(p0, h2f(vn));
+    float r1 = mul_zero_wins(p1, h2f(vn >> 16));
+    const float pm = row_max16(fmaxf(r0, r1));
+    // r 2^-s0 < 16; s0 in [-103, 124] (pm < 2^128; pm below 2^-100 is taken
+    // as 2^-100), so every digit's E8M0 byte s0 - 5 j + 127 lies in [14, 251]
+    const int s0 = max(exponent_of(pm), -100) - 3;
+    const float sgn = (t >= 12) ? -1.0f : 1.0f;   // k-slots on the value operand's sign field
+    r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
+    r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int pk = 0;   // the fourth digit row stays zero
+      if (j < 3) {
+        const float d0 = rintf(r0), d1 = rintf(r1);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
+        if (j < 2) {
+          r0 = (r0 - d0) * 32.0f;
+          r1 = (r1 - d1) * 32.0f;
+        }
+      }
+      *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * kPRow + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
+    }
+    // bytes s0 + 127, s0 + 122, s0 + 117, 127 (no byte carries into the next)
+    const uint32_t ebytes = static_cast<uint32_t>(s0 * 0x010101 + (0x7f000000 + 127 + (122 << 8) + (117 << 16)));
+    *reinterpret_cast<uint32_t*>(&pe[16 * w + 4 * g4]) = ebytes;   // the same from every lane of the row
+  };
+  // (2a) logits of block i
+  auto logits = [&](R& Bk, int i, const float (&code2)[2], const float (&qj2)[2]) __attribute__((always_inline)) {
+    const int blk = blk0 + i;
+    const int n_t = min(kBlock, len - blk * kBlock);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int tok = pos_of_slot(32 * w + 2 * t + c);
+      const float nk = h2f(c ? (Bk.kn >> 16) : Bk.kn);
+      const float rho = QJL ? h2f(c ? (Bk.kr >> 16) : Bk.kr) : 0.0f;
+      float l2 = fmaf(nk, code2[c], QJL ? __fmul_rn(rho, qj2[c]) : 0.0f);
+      // computed on every lane: used only where valid, the products feeding it
+      // would otherwise be sunk into a divergent branch
+      asm volatile("" : "+v"(l2));
+      const bool valid = (tok < n_t) && (g4 < G);
+      if constexpr (AUX) {   // (no logits: an empty buffer, every store dropped)
+        const int lo = valid ? (g4 * a.max_ctx + blk * kBlock + tok) * 4 : -1;   // -1: past the buffer's end
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fmul_rn(l2, kLn2)), rlg, lo, 0, 0);
+      }
+      lgp[c] = valid ? l2 : -INFINITY;
+    }
+  };
+  // (2b) the block's running references: head g4 (denominator) and head t / 4
+  // (column) from every wave's reference in rwr; returns the block's
+  // reference of head t / 4
+  auto merge_refs = [&](const float (*rwr)[4], float rw, float ps) __attribute__((always_inline)) {
+    const int hb = t >> 2;
+    float ra = rwr[0][g4], rb = rwr[0][hb];
+#pragma unroll
+    for (int u = 1; u < kWaves; ++u) {
+      ra = fmaxf(ra, rwr[u][g4]);
+      rb = fmaxf(rb, rwr[u][hb]);
+    }
+    const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
+    const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
+    const float fh = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_a - mn_a));
+    const float fv = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_b - mn_b));
+    lsum = fmaf(lsum, fh, __builtin_amdgcn_ldexpf(ps, shift_of(rw - mn_a)));
+    m_a = mn_a;
+    m_b = mn_b;
+    if (__any(fv != 1.0f)) {   // rescale only when some head's reference moved
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
+      accO *= fv;
+    }
+    return rb;
+  };
+  // Sparse-V: every weight of the block below 2^-tau of the largest one so
+  // far, for every head of the group (the same verdict in every wave: they
+  // merge the same references); its value work is skipped, its weights stay
+  // in the denominator
+  auto sparse_skip = [&](float rb) __attribute__((always_inline)) {
+    if (!AUX || a.sparse_v <= 0) return false;
+    m_top = fmaxf(m_top, rb);
+    return static_cast<bool>(__all(rb < m_top - tau_v));   // a block with no position has rb = kNoRef
+  };
+  // value products of the block whose digits are in pl / pe and whose value
+  // words are in Bv; rwr: every wave's reference of that block
+  auto value_products = [&](const uint8_t* pl, const uint8_t* pe, const float (*rwr)[4], R& Bv)
+      __attribute__((always_inline)) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(&pl[t * kPRow + 16 * g4]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&pl[t * kPRow + 64 + 16 * g4]);
+    const v8i Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    // k-block g4 holds wave g4's positions: its digits carry 2^(its reference - the running one)
+    const int adj = shift_of(rwr[g4][t >> 2] - m_b);   // an empty k-block gives the smallest scale (its digits are 0)
+    const int scp = min(max(static_cast<int>(pe[16 * g4 + t]) + adj, 1), 254);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      uint32_t vw[VB];
+#pragma unroll
+      for (int p = 0; p < VB; ++p) vw[p] = rr ? Bv.vp[p].y : Bv.vp[p].x;
+#pragma unroll
+      for (int T = 0; T < NTV; ++T)
+        accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
+    }
+    accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
+  };
+  // each matrix instruction of a step's first half issued with a few vector
+  // ones after it
+  auto interleave = [&](auto n_mat) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < decltype(n_mat)::value; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six vector ones
+    }
+  };
+  using KMat = std::integral_constant<int, 2 * NTK + (QJL ? 2 : 0)>;
+
   // Step i is two halves around one barrier, each pairing matrix work with
   // independent vector work: (1) the key products of block i with the
   // probability digits of block i - 1 (written to shared memory); (2) after
@@ -431,182 +622,23 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     // products into this one's runs out of registers)
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<(kSets - 1) * F::loads>();   // block i's keys and block i - 1's values have landed
-    // ---- (1a) key products of block i: column group c = slots 32 w + 2 t + c
     float code2[2] = {0.0f, 0.0f}, qj2[2] = {0.0f, 0.0f};
-    if constexpr (CUR) {
-      if constexpr (KO::chain && VB < 4) {   // both column groups' chains side by side
-        uint32_t wd0[KB], wd1[KB];
-#pragma unroll
-        for (int p = 0; p < KB; ++p) {
-          wd0[p] = Bk.kp[p].x;
-          wd1[p] = Bk.kp[p].y;
-        }
-        v4f acc0 = v4f{-cq, 0.0f, 0.0f, 0.0f}, acc1 = acc0;   // the affine operands' offset, removed up front
-#pragma unroll
-        for (int T = 0; T < NTK; ++T) {
-          const v8i A = qop(T);
-          acc0 = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd0, T), kf), acc0, scq[T]);
-          acc1 = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd1, T), kf), acc1, scq[T]);
-        }
-        code2[0] = (acc0[0] + acc0[1]) + (acc0[2] + acc0[3]);
-        code2[1] = (acc1[0] + acc1[1]) + (acc1[2] + acc1[3]);
-      } else {
-        // one column group at a time (fewer live registers)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          uint32_t wd[KB];
-#pragma unroll
-          for (int p = 0; p < KB; ++p) wd[p] = c ? Bk.kp[p].y : Bk.kp[p].x;
-          if constexpr (KO::chain) {
-            v4f acc = v4f{-cq, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int T = 0; T < NTK; ++T) acc = mfma_fp6_fp4(qop(T), expand_fp4_affine(term_word<KB>(wd, T), kf), acc, scq[T]);
-            code2[c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-          } else {
-            v4f dT[NTK];
-            const v8i A = qop(0);
-#pragma unroll
-            for (int T = 0; T < NTK; ++T)
-              dT[T] = mfma_fp6_fp4(A, expand_fp4_affine(term_word<KB>(wd, T), kf), v4f{0.0f, 0.0f, 0.0f, 0.0f}, scq[0]);
-            float code = -cq;
-#pragma unroll
-            for (int T = 0; T < NTK; ++T) code = fmaf(ak[T], (dT[T][0] + dT[T][1]) + (dT[T][2] + dT[T][3]), code);
-            code2[c] = code;
-          }
-        }
-      }
-      if constexpr (QJL) {
-        const v8i As = qop(NCS);
-        const v4f dQ0 = mfma_fp6_fp4(As, expand_fp4_affine(Bk.ks.x, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
-        const v4f dQ1 = mfma_fp6_fp4(As, expand_fp4_affine(Bk.ks.y, kf), v4f{-csq, 0.0f, 0.0f, 0.0f}, scsq);
-        qj2[0] = (dQ0[0] + dQ0[1]) + (dQ0[2] + dQ0[3]);
-        qj2[1] = (dQ1[0] + dQ1[1]) + (dQ1[2] + dQ1[3]);
-      }
-    }
-    // ---- (1b) block i - 1: this wave's reference per head (row g4) is the
-    // integer ceiling of its step maximum (p <= 1 against it); the digits of
-    // p * radius go to shared memory
+    if constexpr (CUR) key_products(Bk, code2, qj2);
     const int pj = (i - 1) & 1;
     float rw = -INFINITY, ps = 0.0f;
     if constexpr (PREV) {
-      uint8_t* const pl = &plimb[pj][0];
-      uint8_t* const pe = &pexp[pj][0][0];
-      const float mloc = row_max16(fmaxf(lgp[0], lgp[1]));
-      rw = fmaxf(ceilf(mloc), kNoRef);
+      float p0, p1;
+      wave_ref(rw, p0, p1);
       rwb[pj][w][g4] = rw;   // every lane of the row stores the same value
-      const float p0 = __builtin_amdgcn_exp2f(lgp[0] - rw);   // exp2(-inf) = 0 for slots without a logit
-      const float p1 = __builtin_amdgcn_exp2f(lgp[1] - rw);
-      float r0 = mul_zero_wins(p0, h2f(Bv.vn));
-      float r1 = mul_zero_wins(p1, h2f(Bv.vn >> 16));
-      const float pm = row_max16(fmaxf(r0, r1));
-      // r 2^-s0 < 16; s0 in [-103, 124] (pm < 2^128; pm below 2^-100 is taken
-      // as 2^-100), so every digit's E8M0 byte s0 - 5 j + 127 lies in [14, 251]
-      const int s0 = max(exponent_of(pm), -100) - 3;
-      const float sgn = (t >= 12) ? -1.0f : 1.0f;   // k-slots on the value operand's sign field
-      r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
-      r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int pk = 0;   // the fourth digit row stays zero
-        if (j < 3) {
-          const float d0 = rintf(r0), d1 = rintf(r1);
-          pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
-          if (j < 2) {
-            r0 = (r0 - d0) * 32.0f;
-            r1 = (r1 - d1) * 32.0f;
-          }
-        }
-        *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * kPRow + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
-      }
-      // bytes s0 + 127, s0 + 122, s0 + 117, 127 (no byte carries into the next)
-      const uint32_t ebytes = static_cast<uint32_t>(s0 * 0x010101 + (0x7f000000 + 127 + (122 << 8) + (117 << 16)));
-      *reinterpret_cast<uint32_t*>(&pe[16 * w + 4 * g4]) = ebytes;   // the same from every lane of the row
+      p_digits(&plimb[pj][0], &pexp[pj][0][0], p0, p1, Bv.vn);
       ps = p0 + p1;
     }
-    if constexpr (CUR && PREV) {
-      // this half's key products and digit work: each matrix instruction is
-      // issued with a few vector ones after it
-      constexpr int kMat = 2 * NTK + (QJL ? 2 : 0);
-#pragma unroll
-      for (int k = 0; k < kMat; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six vector ones
-      }
-    }
+    if constexpr (CUR && PREV) interleave(KMat{});
     if constexpr (PREV) lds_barrier();
-
-    // ---- (2a) logits of block i
-    if constexpr (CUR) {
-      const int blk = blk0 + i;
-      const int n_t = min(kBlock, len - blk * kBlock);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int tok = pos_of_slot(32 * w + 2 * t + c);
-        const float nk = h2f(c ? (Bk.kn >> 16) : Bk.kn);
-        const float rho = QJL ? h2f(c ? (Bk.kr >> 16) : Bk.kr) : 0.0f;
-        float l2 = fmaf(nk, code2[c], QJL ? __fmul_rn(rho, qj2[c]) : 0.0f);
-        // computed on every lane: used only where valid, the products feeding it
-        // would otherwise be sunk into a divergent branch
-        asm volatile("" : "+v"(l2));
-        const bool valid = (tok < n_t) && (g4 < G);
-        if constexpr (AUX) {   // (no logits: an empty buffer, every store dropped)
-          const int lo = valid ? (g4 * a.max_ctx + blk * kBlock + tok) * 4 : -1;   // -1: past the buffer's end
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fmul_rn(l2, kLn2)), rlg, lo, 0, 0);
-        }
-        lgp[c] = valid ? l2 : -INFINITY;
-      }
-    }
-    // ---- (2b) block i - 1: running references of head g4 (denominator) and
-    // head t / 4 (column), then its value products
+    if constexpr (CUR) logits(Bk, i, code2, qj2);
     if constexpr (PREV) {
-      const int hb = t >> 2;
-      float ra = rwb[pj][0][g4], rb = rwb[pj][0][hb];
-#pragma unroll
-      for (int u = 1; u < kWaves; ++u) {
-        ra = fmaxf(ra, rwb[pj][u][g4]);
-        rb = fmaxf(rb, rwb[pj][u][hb]);
-      }
-      const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
-      const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
-      const float fh = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_a - mn_a));
-      const float fv = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_b - mn_b));
-      lsum = fmaf(lsum, fh, __builtin_amdgcn_ldexpf(ps, shift_of(rw - mn_a)));
-      m_a = mn_a;
-      m_b = mn_b;
-      if (__any(fv != 1.0f)) {   // rescale only when some head's reference moved
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-          for (int T = 0; T < NTV; ++T) accV[rr][T] *= fv;
-        accO *= fv;
-      }
-      bool skip = false;
-      if (AUX && a.sparse_v > 0) {
-        // every weight of the block below 2^-tau of the largest one so far, for
-        // every head of the group: the value work is skipped (the weights stay
-        // in the denominator)
-        m_top = fmaxf(m_top, rb);
-        skip = __all(rb < m_top - tau_v);   // a block with no position has rb = kNoRef
-      }
-      if (!skip) {
-        const uint8_t* const pl = &plimb[pj][0];
-        const uint4 lo = *reinterpret_cast<const uint4*>(&pl[t * kPRow + 16 * g4]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&pl[t * kPRow + 64 + 16 * g4]);
-        const v8i Pv = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        // k-block g4 holds wave g4's positions: its digits carry 2^(its reference - the running one)
-        const int adj = shift_of(rwb[pj][g4][hb] - m_b);   // an empty k-block gives the smallest scale (its digits are 0)
-        const int scp = min(max(static_cast<int>(pexp[pj][g4][t]) + adj, 1), 254);
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          uint32_t vw[VB];
-#pragma unroll
-          for (int p = 0; p < VB; ++p) vw[p] = rr ? Bv.vp[p].y : Bv.vp[p].x;
-#pragma unroll
-          for (int T = 0; T < NTV; ++T)
-            accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
-        }
-        accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
-      }
+      const float rb = merge_refs(rwb[pj], rw, ps);
+      if (!sparse_skip(rb)) value_products(&plimb[pj][0], &pexp[pj][0][0], rwb[pj], Bv);
     }
     // ---- refills: keys kSets blocks past block i, values kSets past block i - 1
     if constexpr (CUR) load_k(Bk, blk0 + i + kSets, blk1, rk);
@@ -614,40 +646,121 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Sparse-V that skips the value bytes too (the logits / Sparse-V variant
+  // with three register sets): a block's value words are requested only once
+  // its vote is known and used two steps later.  Step i: the key products of
+  // block i and the reference of block i - 1; the digits of block i - 3;
+  // barrier; the logits of block i; the vote on block i - 1 and its value
+  // request; the value products of block i - 3.  Set s = i mod 3 holds the
+  // keys of block i and the values, probabilities and vote of block i - 3.
+  // CUR: block i exists; PREV: block i - 1 does; OLD: block i - 3 does.
+  auto step_lag = [&](R& Bc, R& Bn, R& Bm, int i, auto cur_c, auto prev_c, auto old_c) __attribute__((always_inline)) {
+    constexpr bool CUR = decltype(cur_c)::value;
+    constexpr bool PREV = decltype(prev_c)::value;
+    constexpr bool OLD = decltype(old_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    // block i's keys (and block i - 3's values) have landed: issued after
+    // them are the keys of blocks i + 1 and i + 2 and, unless its vote
+    // skipped it, the values of block i - 2 (in set Bm); in the last steps
+    // every load is waited for
+    if (CUR || PREV) {
+      if (Bm.vreq) wait_vm<2 * (F::loads - VB - 1) + VB + 1>();
+      else wait_vm<2 * (F::loads - VB - 1)>();
+    } else {
+      wait_vm<0>();
+    }
+    float code2[2] = {0.0f, 0.0f}, qj2[2] = {0.0f, 0.0f};
+    if constexpr (CUR) key_products(Bc, code2, qj2);
+    float rw = -INFINITY, ps = 0.0f;
+    if constexpr (PREV) {
+      wave_ref(rw, Bn.pp0, Bn.pp1);
+      rwb[(i - 1) & 3][w][g4] = rw;
+      ps = Bn.pp0 + Bn.pp1;
+    }
+    const int pj = i & 1;
+    if constexpr (OLD) {
+      if (Bc.vreq) p_digits(&plimb[pj][0], &pexp[pj][0][0], Bc.pp0, Bc.pp1, Bc.vn);
+    }
+    if constexpr (CUR && PREV) interleave(KMat{});
+    if constexpr (PREV || OLD) lds_barrier();
+    if constexpr (CUR) logits(Bc, i, code2, qj2);
+    if constexpr (PREV) {
+      const float rb = merge_refs(rwb[(i - 1) & 3], rw, ps);
+      Bn.vreq = !sparse_skip(rb);
+      if (Bn.vreq) load_v(Bn, blk0 + i - 1, blk1, rv);
+    }
+    if constexpr (OLD) {
+      if (Bc.vreq) value_products(&plimb[pj][0], &pexp[pj][0][0], rwb[(i - 3) & 3], Bc);
+    }
+    if constexpr (CUR) load_k(Bc, blk0 + i + kSets, blk1, rk);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   using Y = std::true_type;
   using N = std::false_type;
   if (n_iter > 0) {   // uniform over the workgroup
-    step(buf0, buf1, 0, Y{}, N{});
-    int i = 1;
-    if constexpr (kSets == 3) {
+    if constexpr (kLag) {
+      buf0.vreq = buf1.vreq = buf2.vreq = false;
+      // steps 0 .. n_iter + 2; set i mod 3 is (keys of i, values of i - 3)
+      step_lag(buf0, buf2, buf1, 0, Y{}, N{}, N{});
+      if (n_iter > 1) step_lag(buf1, buf0, buf2, 1, Y{}, Y{}, N{});
+      else step_lag(buf1, buf0, buf2, 1, N{}, Y{}, N{});
+      if (n_iter > 2) step_lag(buf2, buf1, buf0, 2, Y{}, Y{}, N{});
+      else if (n_iter == 2) step_lag(buf2, buf1, buf0, 2, N{}, Y{}, N{});
+      int i = 3;
       for (; i + 3 <= n_iter; i += 3) {
-        step(buf1, buf0, i, Y{}, Y{});
-        step(buf2, buf1, i + 1, Y{}, Y{});
-        step(buf0, buf2, i + 2, Y{}, Y{});
+        step_lag(buf0, buf2, buf1, i, Y{}, Y{}, Y{});
+        step_lag(buf1, buf0, buf2, i + 1, Y{}, Y{}, Y{});
+        step_lag(buf2, buf1, buf0, i + 2, Y{}, Y{}, Y{});
       }
-      // i = 1 (mod 3); the last step has no block i
-      if (i < n_iter) {
-        step(buf1, buf0, i, Y{}, Y{});
-        if (i + 1 < n_iter) {
+      // the rest: steps i .. n_iter + 2 (i = 0 mod 3, i >= 3; at most 5 steps)
+      auto tail = [&](R& Bc, R& Bn, R& Bm, int j) __attribute__((always_inline)) {
+        if (j < n_iter) {
+          step_lag(Bc, Bn, Bm, j, Y{}, Y{}, Y{});
+        } else if (j == n_iter) {
+          step_lag(Bc, Bn, Bm, j, N{}, Y{}, Y{});
+        } else if (j <= n_iter + 2) {
+          step_lag(Bc, Bn, Bm, j, N{}, N{}, Y{});
+        }
+      };
+      tail(buf0, buf2, buf1, i);
+      tail(buf1, buf0, buf2, i + 1);
+      tail(buf2, buf1, buf0, i + 2);
+      tail(buf0, buf2, buf1, i + 3);
+      tail(buf1, buf0, buf2, i + 4);
+    } else {
+      step(buf0, buf1, 0, Y{}, N{});
+      int i = 1;
+      if constexpr (kSets == 3) {
+        for (; i + 3 <= n_iter; i += 3) {
+          step(buf1, buf0, i, Y{}, Y{});
           step(buf2, buf1, i + 1, Y{}, Y{});
-          step(buf0, buf2, i + 2, N{}, Y{});
+          step(buf0, buf2, i + 2, Y{}, Y{});
+        }
+        // i = 1 (mod 3); the last step has no block i
+        if (i < n_iter) {
+          step(buf1, buf0, i, Y{}, Y{});
+          if (i + 1 < n_iter) {
+            step(buf2, buf1, i + 1, Y{}, Y{});
+            step(buf0, buf2, i + 2, N{}, Y{});
+          } else {
+            step(buf2, buf1, i + 1, N{}, Y{});
+          }
         } else {
-          step(buf2, buf1, i + 1, N{}, Y{});
+          step(buf1, buf0, i, N{}, Y{});
         }
       } else {
-        step(buf1, buf0, i, N{}, Y{});
-      }
-    } else {
-      for (; i + 2 <= n_iter; i += 2) {
-        step(buf1, buf0, i, Y{}, Y{});
-        step(buf0, buf1, i + 1, Y{}, Y{});
-      }
-      // i odd
-      if (i < n_iter) {
-        step(buf1, buf0, i, Y{}, Y{});
-        step(buf0, buf1, i + 1, N{}, Y{});
-      } else {
-        step(buf1, buf0, i, N{}, Y{});
+        for (; i + 2 <= n_iter; i += 2) {
+          step(buf1, buf0, i, Y{}, Y{});
+          step(buf0, buf1, i + 1, Y{}, Y{});
+        }
+        // i odd
+        if (i < n_iter) {
+          step(buf1, buf0, i, Y{}, Y{});
+          step(buf0, buf1, i + 1, N{}, Y{});
+        } else {
+          step(buf1, buf0, i, N{}, Y{});
+        }
       }
     }
   }
