@@ -196,19 +196,27 @@ __device__ __forceinline__ void code_bits(float y, const float (&thr)[15], bool 
     bit[k] = y > cand[0];
   }
 }
+// The centroid of a code.  The codebook is antisymmetric (centroid
+// 2^B - 1 - c is minus centroid c, exactly: the host mirrors the positive
+// half), so the top bit is the sign and the other bits, complemented for a
+// negative code, pick the magnitude among the positive half: B - 1 levels of
+// selects over 2^(B-1) values instead of B levels over 2^B.
 template <int B>
 __device__ __forceinline__ float centroid(const float (&cv)[16], const bool (&bit)[4]) {
-  float cand[1 << B];
+  constexpr int H = 1 << (B - 1);
+  const bool pos = bit[B - 1];
+  float cand[H];
 #pragma unroll
-  for (int m = 0; m < (1 << B); ++m) cand[m] = cv[m];
+  for (int m = 0; m < H; ++m) cand[m] = cv[H + m];
 #pragma unroll
-  for (int j = 0; j < B; ++j) {
-    const int half = 1 << (B - 1 - j);
+  for (int j = 0; j < B - 1; ++j) {
+    const bool up = bit[j] == pos;   // bit j of the code's mirror image in the positive half
+    const int half = 1 << (B - 2 - j);
 #pragma unroll
-    for (int m = 0; m < (1 << (B - 1)); ++m)
-      if (m < half) cand[m] = bit[j] ? cand[2 * m + 1] : cand[2 * m];
+    for (int m = 0; m < H / 2; ++m)
+      if (m < half) cand[m] = up ? cand[2 * m + 1] : cand[2 * m];
   }
-  return cand[0];
+  return pos ? cand[0] : -cand[0];
 }
 
 // ----------------------------------------------------------------- loads
