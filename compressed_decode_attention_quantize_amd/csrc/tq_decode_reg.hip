@@ -20,8 +20,8 @@
 //    three steps before the step that uses them, into one of three register
 //    sets (two with 4-bit values).
 //  * Each workgroup forms its query operands (rotation, sketch, digits) in
-//    shared memory while its first blocks' loads are in flight, and reads
-//    each operand right before its product: no separate launch for them.
+//    shared memory while its first blocks' loads are in flight, then keeps
+//    them in registers through the loop: no separate launch for them.
 //  * With at most four terms per key code (2- and 3-bit keys, values of 2 or
 //    3 bits) the codebook coefficients are folded into the query digits (one
 //    operand per term), so a column's terms accumulate in one matrix
@@ -311,14 +311,14 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   __builtin_amdgcn_sched_barrier(0);   // (issued before the query-side work below)
 
   // ------------------------------------------------ query operands
-  // Formed here while the first blocks' loads are in flight, into shared
-  // memory, and read right before each product (held in registers through
-  // the loop they would take 8 per set).  Wave w rotates head w's query
-  // (q_raw = H D_K q) and takes a 32-coordinate slice of the sketch table for
-  // its share of (S H D_K / sqrt d) q for the four heads; then each half of
-  // wave w forms head w's digits for one operand set at a time: the code
-  // sets two at a time (with the codebook coefficient folded in when
-  // chained), then the sketch set.  Both vectors are kept in k-slot order.
+  // Formed here while the first blocks' loads are in flight, in shared
+  // memory, then read once into registers (6 words per set).  Wave w rotates
+  // head w's query (q_raw = H D_K q) and takes a 32-coordinate slice of the
+  // sketch table for its share of (S H D_K / sqrt d) q for the four heads;
+  // then each half of wave w forms head w's digits for one operand set at a
+  // time: the code sets two at a time (with the codebook coefficient folded
+  // in when chained), then the sketch set.  Both vectors are kept in k-slot
+  // order.
   constexpr int NQS = NCS + (QJL ? 1 : 0);
   __shared__ __attribute__((aligned(16))) uint8_t alimb[NQS][16 * kARow];   // [set][row = 4 g + j][k]
   __shared__ __attribute__((aligned(4))) uint8_t aexp[NQS][4 * 16];        // [set][k / 32][row]
@@ -390,11 +390,15 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     }
   }
   lds_barrier();   // the operands are in shared memory (the cache loads above stay in flight)
-  auto qop = [&](int set) __attribute__((always_inline)) {
+  // the operands stay in registers through the loop (6 words per set)
+  v8i qreg[NQS];
+#pragma unroll
+  for (int set = 0; set < NQS; ++set) {
     const uint2* rp = reinterpret_cast<const uint2*>(&alimb[set][t * kARow + 24 * g4]);
     const uint2 x = rp[0], y = rp[1], z = rp[2];
-    return v8i{(int)x.x, (int)x.y, (int)y.x, (int)y.y, (int)z.x, (int)z.y, 0, 0};
-  };
+    qreg[set] = v8i{(int)x.x, (int)x.y, (int)y.x, (int)y.y, (int)z.x, (int)z.y, 0, 0};
+  }
+  auto qop = [&](int set) __attribute__((always_inline)) { return qreg[set]; };
   int scq[NCS];
 #pragma unroll
   for (int s = 0; s < NCS; ++s) scq[s] = aexp[s][16 * g4 + t];
