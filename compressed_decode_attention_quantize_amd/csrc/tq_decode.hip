@@ -35,6 +35,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -51,49 +53,48 @@ struct TreeLds {
 };
 
 // code of an angle slot of one key from its word J (slot / 32, a constant
-// at every call) and bit e: w[p][J] for the b - 1 shared planes, x[k][J - 2]
-// for the two extra level-1 planes
-template <int J>
-__device__ __forceinline__ int tree_key_code(const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int nb1, int e) {
+// at every call) and bit e: w[p][J] for the NB1 = b - 1 shared planes,
+// x[k][J - 2] for the two extra level-1 planes
+template <int NB1, int J>
+__device__ __forceinline__ int tree_key_code(const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int e) {
   int c = 0;
 #pragma unroll
-  for (int p = 0; p < 3; ++p)
-    if (p < nb1) c |= ((w[p][J] >> e) & 1u) << p;
+  for (int p = 0; p < NB1; ++p) c |= ((w[p][J] >> e) & 1u) << p;
   if constexpr (J >= 2) {
-    c |= ((x[0][J - 2] >> e) & 1u) << nb1;
-    c |= ((x[1][J - 2] >> e) & 1u) << (nb1 + 1);
+    c |= ((x[0][J - 2] >> e) & 1u) << NB1;
+    c |= ((x[1][J - 2] >> e) & 1u) << (NB1 + 1);
   }
   return c;
 }
 
 // dot[u] += <q_raw of head hb + HS u, u> over the subtree of level-6 node N6
 // (coordinates 64 N6 .. 64 N6 + 63), its weight w6 being the root's cos or sin
-template <int N6, int NH, int HS>
-__device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4], const uint32_t (&x)[2][2], int nb1,
+template <int NB1, int N6, int NH, int HS>
+__device__ __forceinline__ void tree_half_dot(float w6, const uint32_t (&w)[3][4], const uint32_t (&x)[2][2],
                                               const TreeLds& tab, const float* qv, int hb, float (&dot)[NH]) {
-  const float2 c6 = tab.up[6][tree_key_code<0>(w, x, nb1, 2 + N6)];
+  const float2 c6 = tab.up[6][tree_key_code<NB1, 0>(w, x, 2 + N6)];
 #pragma unroll 1
   for (int n5 = 2 * N6; n5 < 2 * N6 + 2; ++n5) {
     const float w5 = w6 * ((n5 & 1) ? c6.y : c6.x);
-    const float2 c5 = tab.up[5][tree_key_code<0>(w, x, nb1, 4 + n5)];
+    const float2 c5 = tab.up[5][tree_key_code<NB1, 0>(w, x, 4 + n5)];
 #pragma unroll 1
     for (int n4 = 2 * n5; n4 < 2 * n5 + 2; ++n4) {
       const float w4 = w5 * ((n4 & 1) ? c5.y : c5.x);
-      const float2 c4 = tab.up[4][tree_key_code<0>(w, x, nb1, 8 + n4)];
+      const float2 c4 = tab.up[4][tree_key_code<NB1, 0>(w, x, 8 + n4)];
 #pragma unroll 1
       for (int n3 = 2 * n4; n3 < 2 * n4 + 2; ++n3) {
         const float w3 = w4 * ((n3 & 1) ? c4.y : c4.x);
-        const float2 c3 = tab.up[3][tree_key_code<0>(w, x, nb1, 16 + n3)];
+        const float2 c3 = tab.up[3][tree_key_code<NB1, 0>(w, x, 16 + n3)];
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
           const int n2 = 2 * n3 + b2;
           const float w2 = w3 * (b2 ? c3.y : c3.x);
-          const float2 c2 = tab.up[2][tree_key_code<1>(w, x, nb1, n2)];   // slot 32 + n2
+          const float2 c2 = tab.up[2][tree_key_code<NB1, 1>(w, x, n2)];   // slot 32 + n2
 #pragma unroll
           for (int b1 = 0; b1 < 2; ++b1) {
             const int i = 2 * n2 + b1;   // level-1 pair, slot 64 + i (word 2 + N6)
             const float w1 = w2 * (b1 ? c2.y : c2.x);
-            const float2 cs = tab.l1[tree_key_code<2 + N6>(w, x, nb1, i & 31)];
+            const float2 cs = tab.l1[tree_key_code<NB1, 2 + N6>(w, x, i & 31)];
             const float a0 = w1 * cs.x, a1 = w1 * cs.y;
 #pragma unroll
             for (int u = 0; u < NH; ++u) {
@@ -224,28 +225,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       if (t < n_t) {
         const uint32_t* planes = reinterpret_cast<const uint32_t*>(kb);
         const int sl = slot_of(t);
-        const int nb1 = kbits - 1;
-        uint32_t w[3][4] = {}, x[2][2];
+        // the walk with the plane count a constant (2-, 3- and 4-bit keys)
+        auto walk = [&](auto nb1_c) __attribute__((always_inline)) {
+          constexpr int NB1 = decltype(nb1_c)::value;
+          uint32_t w[3][4] = {}, x[2][2];
 #pragma unroll
-        for (int p = 0; p < 3; ++p)
-          if (p < nb1)
+          for (int p = 0; p < NB1; ++p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) w[p][j] = planes[(p * 4 + j) * kBlock + sl];
-        const uint32_t* l1 = planes + nb1 * 4 * kBlock;
+          const uint32_t* l1 = planes + NB1 * 4 * kBlock;
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+          for (int k = 0; k < 2; ++k)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) x[k][j] = l1[(k * 2 + j) * kBlock + sl];
-        n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
-        const float2 c7 = ktree.up[7][tree_key_code<0>(w, x, nb1, 1)];
-        if constexpr (HPT <= 2) {
-          if (hpar == 0)
-            tree_half_dot<0, NH, 1>(c7.x, w, x, nb1, ktree, qv, 0, dot);
-          else
-            tree_half_dot<1, NH, 1>(c7.y, w, x, nb1, ktree, qv, 0, dot);
-        } else {
-          tree_half_dot<0, NH, 2>(c7.x, w, x, nb1, ktree, qv, hpar, dot);
-          tree_half_dot<1, NH, 2>(c7.y, w, x, nb1, ktree, qv, hpar, dot);
+            for (int j = 0; j < 2; ++j) x[k][j] = l1[(k * 2 + j) * kBlock + sl];
+          n16 = f16_to_f32(reinterpret_cast<const uint16_t*>(l1 + 4 * kBlock)[sl]);
+          const float2 c7 = ktree.up[7][tree_key_code<NB1, 0>(w, x, 1)];
+          if constexpr (HPT <= 2) {
+            if (hpar == 0)
+              tree_half_dot<NB1, 0, NH, 1>(c7.x, w, x, ktree, qv, 0, dot);
+            else
+              tree_half_dot<NB1, 1, NH, 1>(c7.y, w, x, ktree, qv, 0, dot);
+          } else {
+            tree_half_dot<NB1, 0, NH, 2>(c7.x, w, x, ktree, qv, hpar, dot);
+            tree_half_dot<NB1, 1, NH, 2>(c7.y, w, x, ktree, qv, hpar, dot);
+          }
+        };
+        switch (kbits) {   // uniform
+          case 2: walk(std::integral_constant<int, 1>{}); break;
+          case 3: walk(std::integral_constant<int, 2>{}); break;
+          default: walk(std::integral_constant<int, 3>{}); break;
         }
       }
       if constexpr (HPT > 2) {
