@@ -188,12 +188,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // accumulators: thread owns coordinate i = tid % 128 for heads g = tid/128 + 2u
+  // accumulators: thread (coordinate ci = tid % 128, hpar = tid / 128) sums
+  // the positions t = hpar (mod 2) of every block for every head g < 2 HPT
+  // (each value coordinate formed once); the two halves are added at the end
   const int ci = tid & (kD - 1);
   const int hpar = tid >> 7;
-  float acc[HPT];
+  constexpr int NHA = 2 * HPT;
+  float acc[NHA];
 #pragma unroll
-  for (int u = 0; u < HPT; ++u) acc[u] = 0.0f;
+  for (int g = 0; g < NHA; ++g) acc[g] = 0.0f;
 
 
   const int blk0 = split * a.chunk_blocks;
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     // ----------------------------------------------------------- PV
 #pragma unroll
-    for (int u = 0; u < HPT; ++u) acc[u] *= scale[hpar + 2 * u];
+    for (int g = 0; g < NHA; ++g) acc[g] *= scale[g];
     if (a.v_codec == POLAR) {
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
 #pragma unroll 1
@@ -428,14 +431,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           if (p < vbits) w[p] = planes[p * 4 * kD + j * kD + ci];
         const int e_end = min(32, n_t - j * 32);
 #pragma unroll 4
-        for (int e = 0; e < e_end; ++e) {
+        for (int e = hpar; e < e_end; e += 2) {
           int c = 0;
 #pragma unroll
           for (int p = 0; p < 4; ++p) c |= ((w[p] >> e) & 1u) << p;
           const float cv = vcb[c];
           const int t = j * 32 + e;
 #pragma unroll
-          for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], cv, acc[u]);
+          for (int g = 0; g < NHA; ++g) acc[g] = fmaf(pt[g * kBlock + t], cv, acc[g]);
         }
       }
     } else if constexpr (TVB > 0) {
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int k = 0; k < 2; ++k) x[k] = l1[(k * 4 + j) * (kD / 2) + (ci >> 1)];
         const int e_end = min(32, n_t - j * 32);
 #pragma unroll 4
-        for (int e = 0; e < e_end; ++e) {
+        for (int e = hpar; e < e_end; e += 2) {
           int c = 0;
 #pragma unroll
           for (int p = 0; p < nb1; ++p) c |= ((w[p] >> e) & 1u) << p;
@@ -501,29 +504,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           const float uval = ((ci & 1) ? cs1.y : cs1.x) * pp[e][ci >> 1];
           const int t = j * 32 + e;
 #pragma unroll
-          for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], uval, acc[u]);
+          for (int g = 0; g < NHA; ++g) acc[g] = fmaf(pt[g * kBlock + t], uval, acc[g]);
         }
       }
     } else {
       const float* rows = reinterpret_cast<const float*>(vb);
 #pragma unroll 8
-      for (int t = 0; t < n_t; ++t) {
+      for (int t = hpar; t < n_t; t += 2) {
         const float v = rows[t * kD + ci];
 #pragma unroll
-        for (int u = 0; u < HPT; ++u) acc[u] = fmaf(pt[(hpar + 2 * u) * kBlock + t], v, acc[u]);
+        for (int g = 0; g < NHA; ++g) acc[g] = fmaf(pt[g * kBlock + t], v, acc[g]);
       }
     }
     __syncthreads();
   }
 
   // --------------------------------------------------------- partials
+  // the two halves of the positions: thread (ci, hpar) keeps heads hpar + 2 u
+  // and takes the other half's sums for them through pt (free by now)
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) pt[(1 - hpar + 2 * u) * kBlock + ci] = acc[1 - hpar + 2 * u];
+  __syncthreads();
   const int64_t pstride = kPartialStride;
 #pragma unroll
   for (int u = 0; u < HPT; ++u) {
     const int g = hpar + 2 * u;
     if (g < G) {
       float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + g) * a.n_splits + split) * pstride;
-      store_coherent(pp + ci, acc[u]);
+      store_coherent(pp + ci, acc[g] + pt[g * kBlock + ci]);
       if (ci == 0) {
         store_coherent(pp + kD, m_run[g]);
         store_coherent(pp + kD + 1, l_run[g]);
