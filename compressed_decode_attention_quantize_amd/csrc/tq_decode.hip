@@ -194,9 +194,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int ci = tid & (kD - 1);
   const int hpar = tid >> 7;
   constexpr int NHA = 2 * HPT;
-  float acc[NHA];
+  // recursive polar values: thread (level-1 pair i = tid % 64, quarter
+  // qq = tid / 64) sums coordinates 2 i, 2 i + 1 over the positions
+  // t = qq (mod 4), acc[c NHA + g] for coordinate 2 i + c
+  constexpr int NACC = TVB > 0 ? 2 * NHA : NHA;
+  const int vpi = tid & 63, vqq = tid >> 6;
+  float acc[NACC];
 #pragma unroll
-  for (int g = 0; g < NHA; ++g) acc[g] = 0.0f;
+  for (int g = 0; g < NACC; ++g) acc[g] = 0.0f;
 
 
   const int blk0 = split * a.chunk_blocks;
@@ -420,36 +425,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
     // ----------------------------------------------------------- PV
 #pragma unroll
-    for (int g = 0; g < NHA; ++g) acc[g] *= scale[g];
-    if (a.v_codec == POLAR) {
-      const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
-#pragma unroll 1
-      for (int j = 0; j * 32 < n_t; ++j) {
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          if (p < vbits) w[p] = planes[p * 4 * kD + j * kD + ci];
-        const int e_end = min(32, n_t - j * 32);
-#pragma unroll 4
-        for (int e = hpar; e < e_end; e += 2) {
-          int c = 0;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) c |= ((w[p] >> e) & 1u) << p;
-          const float cv = vcb[c];
-          const int t = j * 32 + e;
-#pragma unroll
-          for (int g = 0; g < NHA; ++g) acc[g] = fmaf(pt[g * kBlock + t], cv, acc[g]);
-        }
-      }
-    } else if constexpr (TVB > 0) {
+    for (int g = 0; g < NACC; ++g) acc[g] *= scale[g % NHA];
+    if constexpr (TVB > 0) {
       // coordinate ci: its level-1 pair is slot 64 + ci / 2, its level-l
       // ancestor slot 2^(7 - l) + ci / 2^l; the factor is the sin of an
       // ancestor's angle when ci lies in its right half, else the cos.  The
       // product of the level 2..7 factors depends on the pair only: per word
       // of 32 positions, thread (e, q) walks the level-4 subtree q of position
       // 32 j + e top-down and leaves the products of its 8 pairs in pp (each
-      // node's angle looked up once per position), then thread ci forms
-      // u_ci = (cos or sin of its pair's angle) * pp[e][ci / 2].
+      // node's angle looked up once per position), then thread (pair i,
+      // quarter) looks up its pair's angle once per position and forms
+      // u_2i = cos * pp[e][i], u_2i+1 = sin * pp[e][i].
       constexpr int nb1 = TVB - 1;
       const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
       const uint32_t* l1 = planes + nb1 * 4 * kD;
@@ -487,24 +473,50 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           }
         }
         __syncthreads();
+        // pair vpi's code words; positions 32 j + e, e = vqq (mod 4)
         uint32_t w[nb1], x[2];
 #pragma unroll
-        for (int p = 0; p < nb1; ++p) w[p] = planes[(p * 4 + j) * kD + 64 + (ci >> 1)];
+        for (int p = 0; p < nb1; ++p) w[p] = planes[(p * 4 + j) * kD + 64 + vpi];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) x[k] = l1[(k * 4 + j) * (kD / 2) + (ci >> 1)];
+        for (int k = 0; k < 2; ++k) x[k] = l1[(k * 4 + j) * (kD / 2) + vpi];
         const int e_end = min(32, n_t - j * 32);
-#pragma unroll 4
-        for (int e = hpar; e < e_end; e += 2) {
+#pragma unroll 2
+        for (int e = vqq; e < e_end; e += 4) {
           int c = 0;
 #pragma unroll
           for (int p = 0; p < nb1; ++p) c |= ((w[p] >> e) & 1u) << p;
           c |= ((x[0] >> e) & 1u) << nb1;
           c |= ((x[1] >> e) & 1u) << (nb1 + 1);
           const float2 cs1 = vtree.l1[c];
-          const float uval = ((ci & 1) ? cs1.y : cs1.x) * pp[e][ci >> 1];
+          const float pv = pp[e][vpi];
+          const float u0 = cs1.x * pv, u1 = cs1.y * pv;
           const int t = j * 32 + e;
 #pragma unroll
-          for (int g = 0; g < NHA; ++g) acc[g] = fmaf(pt[g * kBlock + t], uval, acc[g]);
+          for (int g = 0; g < NHA; ++g) {
+            const float pg = pt[g * kBlock + t];
+            acc[g] = fmaf(pg, u0, acc[g]);
+            acc[NHA + g] = fmaf(pg, u1, acc[NHA + g]);
+          }
+        }
+      }
+    } else if (a.v_codec == POLAR) {
+      const uint32_t* planes = reinterpret_cast<const uint32_t*>(vb);
+#pragma unroll 1
+      for (int j = 0; j * 32 < n_t; ++j) {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          if (p < vbits) w[p] = planes[p * 4 * kD + j * kD + ci];
+        const int e_end = min(32, n_t - j * 32);
+#pragma unroll 4
+        for (int e = hpar; e < e_end; e += 2) {
+          int c = 0;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) c |= ((w[p] >> e) & 1u) << p;
+          const float cv = vcb[c];
+          const int t = j * 32 + e;
+#pragma unroll
+          for (int g = 0; g < NHA; ++g) acc[g] = fmaf(pt[g * kBlock + t], cv, acc[g]);
         }
       }
     } else {
@@ -520,18 +532,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   // --------------------------------------------------------- partials
-  // the two halves of the positions: thread (ci, hpar) keeps heads hpar + 2 u
-  // and takes the other half's sums for them through pt (free by now)
+  // the sums per head and coordinate end in pt[g][coordinate] (free by now;
+  // NHA <= kMaxGroup rows): the threads that hold parts of the positions add
+  // theirs in turn, then thread (ci, hpar) stores heads hpar + 2 u
+  static_assert(NHA <= kMaxGroup, "one row of pt per head");
+  if constexpr (TVB > 0) {
+#pragma unroll 1
+    for (int q4 = 3; q4 >= 0; --q4) {   // quarter 3 writes, 2, 1, 0 add
+      if (vqq == q4) {
 #pragma unroll
-  for (int u = 0; u < HPT; ++u) pt[(1 - hpar + 2 * u) * kBlock + ci] = acc[1 - hpar + 2 * u];
-  __syncthreads();
+        for (int g = 0; g < NHA; ++g) {
+          float* r = &pt[g * kBlock + 2 * vpi];
+          r[0] = (q4 == 3) ? acc[g] : r[0] + acc[g];
+          r[1] = (q4 == 3) ? acc[NHA + g] : r[1] + acc[NHA + g];
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    if (hpar == 1) {
+#pragma unroll
+      for (int g = 0; g < NHA; ++g) pt[g * kBlock + ci] = acc[g];
+    }
+    __syncthreads();
+    if (hpar == 0) {
+#pragma unroll
+      for (int g = 0; g < NHA; ++g) pt[g * kBlock + ci] += acc[g];
+    }
+    __syncthreads();
+  }
   const int64_t pstride = kPartialStride;
 #pragma unroll
   for (int u = 0; u < HPT; ++u) {
     const int g = hpar + 2 * u;
     if (g < G) {
       float* pp = a.partials + ((static_cast<int64_t>(b) * a.n_q + h * G + g) * a.n_splits + split) * pstride;
-      store_coherent(pp + ci, acc[g] + pt[g * kBlock + ci]);
+      store_coherent(pp + ci, pt[g * kBlock + ci]);
       if (ci == 0) {
         store_coherent(pp + kD, m_run[g]);
         store_coherent(pp + kD + 1, l_run[g]);
