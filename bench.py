@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 (matrix and vector)
+FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix
 HEADLINE = "long_b1_ctx1m"
 CONFIG_SET = ("llama8b_b1_ctx32k", "cmdr104b_b1_ctx128k", "serving_b16_ctx8k")
 # what the matrix-core decode computes in: packed codes enter the matrix
@@ -274,9 +275,13 @@ def append_flop_per_position(w):
 
 
 def append_roofline(w, positions_per_s, krec, vrec):
-    """Binding roof of the append: the fp32 arithmetic roof when the sketch
-    contraction makes it compute-bound, else HBM (inputs read, records
-    written)."""
+    """Binding roof of the append: the m x d sketch contraction at fp32
+    accuracy when it makes the append compute-bound, else HBM (inputs read,
+    records written).  The contraction runs on the fp16 matrix instruction as
+    three products of split operands (hi hi + lo hi + hi lo, fp32
+    accumulate): `achieved` and `frac` count its fp32-equivalent flops
+    against the fp32 roof (what an fp32 kernel could reach at most), and
+    `fp16_matrix` the fp16 products actually issued against the fp16 roof."""
     flop = append_flop_per_position(w) * w.n_kv
     in_bytes = 2 * w.d * (4 if w.dtype == "f32" else 2)
     nbytes = (in_bytes + krec + vrec) * w.n_kv
@@ -284,8 +289,14 @@ def append_roofline(w, positions_per_s, krec, vrec):
     t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
     if t_flop >= t_hbm:
         ach = positions_per_s * flop / 1e12
-        return {"bound": "fp32", "achieved": round(ach, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / FP32_PEAK_TFLOPS, 4), "flop_per_position": flop, "kernel": "quant_kernel"}
+        sketch = 2 * w.m * w.d * w.n_kv if w.k_codec == "polar_qjl" else 0   # the contraction's share of `flop`
+        f16 = 3 * positions_per_s * sketch / 1e12
+        return {"bound": "fp32-equivalent", "achieved": round(ach, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP32_PEAK_TFLOPS, 4), "flop_per_position": flop,
+                "arith": "sketch S r as three fp16 matrix products of split operands, fp32 accumulate",
+                "fp16_matrix": {"achieved": round(f16, 2), "peak": FP16_PEAK_TFLOPS,
+                                "frac": round(f16 / FP16_PEAK_TFLOPS, 4)},
+                "kernel": "quant_kernel"}
     ach = positions_per_s * nbytes / 1e9
     return {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_position": nbytes, "kernel": "quant_kernel"}

@@ -19,9 +19,12 @@
 //     in-lane add/sub: stages and levels keep the format's order (stages
 //     h = 1..64, tree levels 64..1) and pairing, so the rotated values and
 //     the norms are bit-identical to any engine that follows the format;
-//   * the residual of a tile, r[16 positions][128], is already the A operand
-//     of the fp32 matrix instruction, so the sketch S r of 16 positions is
-//     256 MFMA 16x16x4 against S^T staged once per workgroup in LDS;
+//   * the residual of a tile, r[16 positions][128], is already the B operand
+//     of the fp16 matrix instruction (8 of a lane's coordinates per
+//     instruction), so the sketch S r of 16 positions is 96 MFMA 16x16x32:
+//     S staged once per workgroup in LDS as fp16 high and low parts, the
+//     residual split the same way, hi hi + lo hi + hi lo (products exact in
+//     fp32, far inside the sign band the format allows);
 //   * code bits come from a binary search over the sorted boundaries and
 //     are shifted into in-lane words (an add with the compare mask as carry);
 //     key bit-planes (token-major words) take them as they are, value
@@ -43,7 +46,9 @@ using namespace qunit;
 
 template <int KB, int VB, bool QJL>
 __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(4))) void quant_kernel(QuantArgs a) {
-  __shared__ float s_lds[QJL ? kM * kSRow : 1];   // S, row j = sketch row, padded rows
+  // S as fp16 high and low parts, row j = sketch row, padded rows
+  __shared__ __attribute__((aligned(16))) _Float16 s_hi[QJL ? kM * kSRowH : 8];
+  __shared__ __attribute__((aligned(16))) _Float16 s_lo[QJL ? kM * kSRowH : 8];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -51,7 +56,19 @@ __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_e
     const float4* src = reinterpret_cast<const float4*>(a.tb.s);
     for (int i = threadIdx.x; i < kM * kD / 4; i += blockDim.x) {
       const int row = i / (kD / 4), c4 = i % (kD / 4);
-      *reinterpret_cast<float4*>(s_lds + row * kSRow + 4 * c4) = src[i];
+      const float4 f = src[i];
+      const float x[4] = {f.x, f.y, f.z, f.w};
+      _Float16 h[4], l[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[k] = static_cast<_Float16>(x[k]);
+        l[k] = static_cast<_Float16>(x[k] - static_cast<float>(h[k]));
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s_hi[row * kSRowH + 4 * c4 + k] = h[k];
+        s_lo[row * kSRowH + 4 * c4 + k] = l[k];
+      }
     }
     __syncthreads();
   }
@@ -74,10 +91,7 @@ __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_e
   const int64_t slot = (static_cast<int64_t>(u.b) * a.n_kv + u.h) * a.n_blocks + blk;
   u.kblk = a.kc + slot * a.k_block_bytes;
   u.vblk = a.vc + slot * a.v_block_bytes;
-  SRows sr;
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) sr.p[mt] = s_lds + 16 * mt * kSRow;
-  quant_unit<KB, VB, QJL>(a, u, sr, lane);
+  quant_unit<KB, VB, QJL>(a, u, SHalves{s_hi, s_lo}, lane);
 }
 
 // One new position per sequence (serving appends): two wavefronts per

@@ -19,14 +19,19 @@ namespace tq {
 namespace qunit {
 
 constexpr int kWavesPerWg = 8;
-constexpr int kSRow = kD + 4;   // padded LDS row of S (floats): conflict-free 16-byte reads
+// padded LDS row of the sketch halves (fp16 high and low parts of S): 16-byte
+// reads of 16 rows fall on distinct banks
+constexpr int kSRowH = kD + 8;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint16_t norm_to_f16(float n) {
   return __half_as_ushort(__float2half_rn(fminf(n, 65504.0f)));
 }
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+// floor(log2 x) of a positive finite x (subnormals give -127)
+__device__ __forceinline__ int exponent_of_f(float x) { return static_cast<int>((__float_as_uint(x) >> 23) & 0xffu) - 127; }
 
 // ---------------------------------------------------------------- exchanges
 // xswap<LB>(a, b): afterwards, in every lane, a holds the value whose lane
@@ -291,14 +296,16 @@ struct Unit {
 };
 
 // --------------------------------------------------------------- kernel
-// Where S sits: its rows 16 mt .. 16 mt + 15 start at p[mt], SROW floats
-// apart (shared memory or global)
-struct SRows {
-  const float* p[8];
+// The sketch S in shared memory as two fp16 tables, S = hi + lo (hi = S
+// rounded to fp16, lo = the remainder rounded to fp16), rows kSRowH halves
+// apart in natural coordinate order.
+struct SHalves {
+  const _Float16* hi;
+  const _Float16* lo;
 };
 
-template <int KB, int VB, bool QJL, int SROW = kSRow>
-__device__ void quant_unit(const QuantArgs& a, const Unit& u, const SRows& s_rows, int lane) {
+template <int KB, int VB, bool QJL>
+__device__ void quant_unit(const QuantArgs& a, const Unit& u, const SHalves& sh, int lane) {
   constexpr bool kPolar = KB > 0;
   const int p = lane & 15;
   const int g = lane >> 4;
@@ -397,25 +404,43 @@ __device__ void quant_unit(const QuantArgs& a, const Unit& u, const SRows& s_row
       if constexpr (QJL) {
         const double sr = tree_sumsq<5>(v);
         const float rho = static_cast<float>(sqrt(sr / static_cast<double>(kD)));
-        // sketch Z = S R: rows = sketch rows, columns = the tile's positions.
-        // neg[w] collects, in this lane, the signs of its position's rows
-        // 32 w + 16 (mt & 1) + 4 g + i at bit 16 (mt & 1) + i.
+        // sketch Z = S R: rows = sketch rows, columns = the tile's positions,
+        // on the fp16 matrix instruction with both factors split into fp16
+        // high and low parts (hi hi + lo hi + hi lo: products exact in fp32,
+        // the dropped lo lo and the splits' remainders below 2^-21 of each
+        // term), the residual first scaled by a power of two to |r| < 1 (the
+        // signs do not change).  Instruction b of a row tile takes, from lane
+        // group g, the 8 coordinates this lane holds in registers 8 b .. 8 b
+        // + 7: coordinates 16 g + 8 (b & 1) + 64 (b >> 1) + i, in natural
+        // order in the tables.  neg[w] collects, in this lane, the signs of
+        // its position's rows 32 w + 16 (mt & 1) + 4 g + i at bit
+        // 16 (mt & 1) + i.
+        const float rn = static_cast<float>(sqrt(sr));
+        const int re = (rn > 0.0f) ? exponent_of_f(rn) + 1 : 0;
+        v8h rh[4], rl[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = __builtin_amdgcn_ldexpf(v[8 * b + i], -re);
+            const _Float16 hx = static_cast<_Float16>(x);
+            rh[b][i] = hx;
+            rl[b][i] = static_cast<_Float16>(x - static_cast<float>(hx));
+          }
         uint32_t neg[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          const float4* srow = reinterpret_cast<const float4*>(s_rows.p[mt] + p * SROW + 16 * g);
-          float4 aq[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            aq[i] = srow[i];
-            aq[4 + i] = srow[16 + i];   // coordinates 64 + 16 g + ...
-          }
+          const _Float16* shi = sh.hi + (16 * mt + p) * kSRowH + 16 * g;
+          const _Float16* slo = sh.lo + (16 * mt + p) * kSRowH + 16 * g;
           v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int s = 0; s < 32; ++s) {
-            const float4 q4 = aq[s >> 2];
-            const float av = (s & 3) == 0 ? q4.x : (s & 3) == 1 ? q4.y : (s & 3) == 2 ? q4.z : q4.w;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, v[s], acc, 0, 0, 0);
+          for (int b = 0; b < 4; ++b) {
+            const int c0 = 8 * (b & 1) + 64 * (b >> 1);
+            const v8h ah = *reinterpret_cast<const v8h*>(shi + c0);
+            const v8h al = *reinterpret_cast<const v8h*>(slo + c0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rh[b], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rh[b], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rl[b], acc, 0, 0, 0);
           }
           // acc[i]: sketch row 16 mt + 4 g + i of position p; a zero sum is +0
 #pragma unroll
