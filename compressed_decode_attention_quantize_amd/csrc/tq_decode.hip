@@ -26,9 +26,13 @@
 //   logits  thread = (position t, head parity); keys are token-major planes,
 //           so a thread reads its position's words directly;
 //   softmax one wavefront per head, wave-reduced max and sum;
-//   PV      thread = (coordinate i, head parity); values are coordinate-major
-//           planes, so a thread reads the 4 words of its coordinate and walks
-//           the block's positions bit by bit.
+//   PV      thread = (coordinate i, position parity) for every head: values
+//           are coordinate-major planes, so a thread reads the words of its
+//           coordinate and walks every other position of the block bit by
+//           bit, decoding each value coordinate once; recursive polar values
+//           take thread = (level-1 pair, quarter of the positions) instead,
+//           one angle lookup per pair and position for both coordinates.
+//           The partial sums meet in shared memory at the end of the split.
 // Partials (m, l, acc) go to the workspace; the last workgroup of each
 // (sequence, KV head) (device-scope counter) merges them by log-sum-exp
 // rescaling, applies the inverse rotation and writes the output.
