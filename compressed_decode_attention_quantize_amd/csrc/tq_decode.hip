@@ -208,9 +208,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   for (int g = 0; g < NACC; ++g) acc[g] = 0.0f;
 
 
-  const int blk0 = split * a.chunk_blocks;
+  const int blk0 = split_first_block(a, split);
   const int nblk_seq = (len + kBlock - 1) / kBlock;
-  const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
+  const int blk1 = min(blk0 + split_block_count(a, split), nblk_seq);
   const int64_t slot0 = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const float alpha = inv_sqrt_d / static_cast<float>(kD);                       // (1/sqrt d)(1/d)
   const float beta = inv_sqrt_d * 1.2533141373155003f / static_cast<float>(kM);  // sqrt(pi/2)/m/sqrt d

@@ -205,7 +205,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   const int len_in = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
   if constexpr (FUSED) {
     // before anything else, so that nothing of the decode is live across it
-    if (len_in < a.max_ctx && (len_in / kBlock) / a.chunk_blocks == split)
+    if (len_in < a.max_ctx && split_of_block(a, len_in / kBlock) == split)
       fused_append<KB, QJL, VB>(a, b, h, len_in, w, lane, reinterpret_cast<float*>(junk));
   }
   // loads the set-up needs are issued first, before the sequence length they
@@ -236,8 +236,8 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   }
   const int len = FUSED ? min(len_in + 1, a.max_ctx) : len_in;
   const int nblk_seq = (len + kBlock - 1) / kBlock;
-  const int blk0 = split * a.chunk_blocks;
-  const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
+  const int blk0 = split_first_block(a, split);
+  const int blk1 = min(blk0 + split_block_count(a, split), nblk_seq);
   const int n_iter = max(0, (blk1 - blk0 + NG - 1) / NG);   // steps of NG blocks
   const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const float inv_sqrt_d = 0.08838834764831845f;

@@ -209,17 +209,22 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const int t = lane & 15;
   const int g4 = lane >> 4;
   // Workgroup -> (split, KV head, sequence, head group); the head groups of
-  // one (split, KV head, sequence) get ids 8 apart (one XCD, one L2)
+  // one (split, KV head, sequence) get ids 8 apart (one XCD, one L2).  Units
+  // are split-major, so the workgroups dispatched first are the low splits,
+  // which the host may make longer (the first workgroup of a compute unit
+  // runs ahead of the second).
   const int nhg = (a.group + 3) >> 2;
-  const int n_units = a.n_splits * a.n_kv * a.batch;
+  const int pairs = a.n_kv * a.batch;
+  const int n_units = a.n_splits * pairs;
   const int id = blockIdx.x;
   const int kx = id >> 3;
   const int unit = (kx / nhg) * 8 + (id & 7);
   if (unit >= n_units) return;
   const int hg = kx - (kx / nhg) * nhg;
-  const int split = unit % a.n_splits;
-  const int h = (unit / a.n_splits) % a.n_kv;
-  const int b = unit / (a.n_splits * a.n_kv);
+  const int split = unit / pairs;
+  const int pair = unit - split * pairs;
+  const int h = pair % a.n_kv;
+  const int b = pair / a.n_kv;
   const int G = min(4, a.group - 4 * hg);
   const int hq0 = h * a.group + 4 * hg;
   uint32_t* const counter = a.counters + (static_cast<int64_t>(b) * a.n_kv + h) * nhg + hg;
@@ -227,7 +232,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   typedef __attribute__((address_space(4))) const float cfloat;
   const int len_in = min(*((cint*)(a.seq_lens) + b), a.max_ctx);
   if constexpr (FUSED) {
-    if (len_in < a.max_ctx && (len_in / kBlock) / a.chunk_blocks == split)
+    if (len_in < a.max_ctx && split_of_block(a, len_in / kBlock) == split)
       fused_append<KB, QJL, VB>(a, b, h, len_in, w, lane, r_lds);
   }
 
@@ -253,8 +258,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // ------------------------------------------------------------- streaming
   const int len = FUSED ? min(len_in + 1, a.max_ctx) : len_in;
   const int nblk_seq = (len + kBlock - 1) / kBlock;
-  const int blk0 = split * a.chunk_blocks;
-  const int blk1 = min(blk0 + a.chunk_blocks, nblk_seq);
+  const int blk0 = split_first_block(a, split);
+  const int blk1 = min(blk0 + split_block_count(a, split), nblk_seq);
   const int n_iter = max(0, blk1 - blk0);
   const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const uint8_t* kbase = a.kc + slot0_idx * a.k_block_bytes;

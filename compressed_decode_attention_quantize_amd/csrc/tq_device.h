@@ -25,6 +25,21 @@ __device__ inline void block_fwht128(float* buf, int rows, int nthreads) {
   __syncthreads();
 }
 
+// Block range of a split: splits [0, n_long) take long_blocks blocks each,
+// the later ones chunk_blocks.
+__device__ __forceinline__ int split_first_block(const DecodeArgs& a, int split) {
+  return (split < a.n_long) ? split * a.long_blocks
+                            : a.n_long * a.long_blocks + (split - a.n_long) * a.chunk_blocks;
+}
+__device__ __forceinline__ int split_block_count(const DecodeArgs& a, int split) {
+  return (split < a.n_long) ? a.long_blocks : a.chunk_blocks;
+}
+// The split whose range holds block blk.
+__device__ __forceinline__ int split_of_block(const DecodeArgs& a, int blk) {
+  const int lb = a.n_long * a.long_blocks;
+  return (blk < lb) ? blk / a.long_blocks : a.n_long + (blk - lb) / a.chunk_blocks;
+}
+
 // Max / sum over the 16 lanes of a row (DPP: xor 1, xor 2, half-row mirror,
 // row mirror); every lane of the row ends with the result.
 __device__ __forceinline__ float row_max16(float x) {

@@ -503,6 +503,29 @@ int decode_splits(const tq_config* c, int32_t max_seq_len) {
   return (blocks + cb - 1) / cb;
 }
 
+// Register-streamed decode with two workgroups per compute unit: the first
+// dispatch round (one workgroup per unit) holds the low splits (the kernel
+// numbers its units split-major), and a unit's first workgroup runs ahead of
+// its second, so those splits take about kRegLongSplitPermille / 1000 times
+// the blocks of the later ones and both finish together.  Sets a's split
+// ranges; the split count and so the workspace stay as decode_splits says.
+void set_split_ranges(const tq_config* c, int32_t max_seq_len, tq::DecodeArgs* a) {
+  a->long_blocks = 0;
+  a->n_long = 0;
+  if (!reg_path(c) || c->decode_chunk > 0) return;
+  const int64_t units = split_units(c);
+  const int64_t S = a->n_splits;
+  const int64_t n_long = tq::kComputeUnits / units;
+  if (n_long < 1 || n_long >= S) return;   // one round: every split equal
+  const int64_t B = std::max(1, (max_seq_len + kBlock - 1) / kBlock);
+  const int64_t P = tq::kRegLongSplitPermille;
+  const int64_t shrt = std::max<int64_t>(1, B * 1000 / (n_long * P + (S - n_long) * 1000));
+  const int64_t lng = std::max<int64_t>(shrt, (B - (S - n_long) * shrt + n_long - 1) / n_long);
+  a->chunk_blocks = static_cast<int32_t>(shrt);
+  a->long_blocks = static_cast<int32_t>(lng);
+  a->n_long = static_cast<int32_t>(n_long);
+}
+
 // Largest split count of any call with lengths up to max_seq_len (the
 // automatic chunking is not monotonic in the length), for workspace sizing.
 int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
@@ -624,6 +647,7 @@ void fill_decode_args(const tq_config* cfg, const void* params, const void* k_ca
   a.n_blocks = n_blocks(cfg);
   a.chunk_blocks = decode_chunk_blocks(cfg, max_seq_len);
   a.n_splits = splits;
+  set_split_ranges(cfg, max_seq_len, &a);
   a.groups = mfma_path(cfg) ? mfma_groups(cfg, max_seq_len) : 1;
   a.k_codec = cfg->k_codec;
   a.k_bits = cfg->k_bits;

@@ -112,6 +112,9 @@ struct DecodeArgs {
   uint32_t* counters; // [batch][n_kv][kMaxGroup / 4]
   int32_t batch, n_q, n_kv, group, max_ctx, n_blocks;
   int32_t chunk_blocks, n_splits;
+  // splits [0, n_long) take long_blocks blocks each, the later ones
+  // chunk_blocks (n_long = 0: every split takes chunk_blocks)
+  int32_t long_blocks, n_long;
   int32_t k_codec, k_bits, v_codec, v_bits;
   int32_t sparse_v;   // 0, or skip value work of blocks below 2^-sparse_v of the running maximum
   int64_t k_block_bytes, v_block_bytes;
@@ -157,6 +160,16 @@ constexpr int kMfmaUnitWorkgroups = 512;
 // register-streamed decode: 256-thread workgroups, two per compute unit
 constexpr int kRegWorkgroups = 512;
 constexpr int kRegMinChunkBlocks = 8;   // fewest blocks per split it is given
+// With two register-streamed workgroups per compute unit, the one dispatched
+// first runs ahead of the other (it wins issue arbitration): the splits whose
+// workgroups go out in the first dispatch round (one per compute unit) are
+// given about this many times the blocks of the later ones, so that both
+// finish together.  Per mille.
+#ifndef TQ_REG_LONG_SPLIT_PERMILLE
+#define TQ_REG_LONG_SPLIT_PERMILLE 1400
+#endif
+constexpr int kRegLongSplitPermille = TQ_REG_LONG_SPLIT_PERMILLE;
+constexpr int kComputeUnits = 256;   // workgroups of the first dispatch round
 constexpr int kValuWorkgroups = 1024;
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 // The library's own decode workspace (tq_decode_attention_noalloc): counters
