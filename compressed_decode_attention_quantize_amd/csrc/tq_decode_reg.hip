@@ -49,9 +49,11 @@ constexpr int kRegThreads = 256;
 // to a huge negative shift, 2^shift = 0).
 constexpr float kNoRef = -1e30f;
 
-// a * b, 0 for a = 0 whatever b (the cache words of slots past the length are
-// arbitrary)
-__device__ __forceinline__ float mul_zero_wins(float a, float b) { return (a > 0.0f) ? a * b : 0.0f; }
+// a * b for a >= 0 and b an fp16 radius, 0 for a = 0 whatever b (the cache
+// words of slots past the length are arbitrary): 0 x inf and 0 x NaN give a
+// quiet NaN, which the maximum with 0 drops (IEEE maxNum, the kernel's IEEE
+// mode); negative garbage gives 0 as well
+__device__ __forceinline__ float mul_zero_wins(float a, float b) { return __builtin_fmaxf(a * b, 0.0f); }
 // float -> int of a shift that is at most a few units above zero, clamped
 // below (an absent reference gives a large negative value)
 __device__ __forceinline__ int shift_of(float x) { return static_cast<int>(fmaxf(x, -1073741824.0f)); }
@@ -194,9 +196,12 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // [parity][col][k]: digits of p * radius; rows padded to 144 bytes so that
   // the 16 rows one 16-byte read instruction gathers fall on distinct banks
   constexpr int kPRow = 144;
-  __shared__ __attribute__((aligned(16))) uint8_t plimb[2][16 * kPRow];
-  __shared__ __attribute__((aligned(4))) uint8_t pexp[2][4][16];        // [parity][k / 32][col]
-  __shared__ float rwb[4][kWaves][4];       // [block mod 4 (mod 2)][wave][head]: each wave's step reference
+  // digit buffers: block j's digits go to buffer j mod kSets (the index of the
+  // register set that holds its values), so every address in the unrolled
+  // step is a constant offset; the voting variant uses j mod 2
+  __shared__ __attribute__((aligned(16))) uint8_t plimb[kSets][16 * kPRow];
+  __shared__ __attribute__((aligned(4))) uint8_t pexp[kSets][4][16];        // [buffer][k / 32][col]
+  __shared__ float rwb[4][kWaves][4];       // [block mod kSets (voting: mod 4)][wave][head]: each wave's step reference
   __shared__ float wred[kWaves][4];
   __shared__ float mrun[4];
   __shared__ __attribute__((aligned(16))) float obuf[4][kD];
@@ -332,6 +337,11 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   __shared__ __attribute__((aligned(16))) float qs[QJL ? 4 : 1][kD];       // the query per head
   __shared__ __attribute__((aligned(16))) float sred[QJL ? kWaves : 1][4][kM];   // partial sketch sums, by k-slot
   {
+    // the fourth digit row of every digit buffer holds zeros throughout
+    for (int o = tid; o < kSets * 4 * (kPRow / 4); o += kRegThreads) {
+      const int pb = o / (4 * (kPRow / 4)), rg = (o / (kPRow / 4)) % 4, dw = o % (kPRow / 4);
+      reinterpret_cast<uint32_t*>(&plimb[pb][(4 * rg + 3) * kPRow])[dw] = 0u;
+    }
     {
       float lo = pq0 * pdk0, hi = pq1 * pdk1;
       const float q0 = pq0, q1 = pq1;
@@ -513,16 +523,14 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     const float sgn = (t >= 12) ? -1.0f : 1.0f;   // k-slots on the value operand's sign field
     r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
     r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
+    int pk = static_cast<int>(vn);   // (the high half of each packed word is not stored)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int pk = 0;   // the fourth digit row stays zero
-      if (j < 3) {
-        const float d0 = rintf(r0), d1 = rintf(r1);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, 0, false);
-        if (j < 2) {
-          r0 = (r0 - d0) * 32.0f;
-          r1 = (r1 - d1) * 32.0f;
-        }
+    for (int j = 0; j < 3; ++j) {   // (the fourth digit row is zero from the start)
+      const float d0 = rintf(r0), d1 = rintf(r1);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(d0, d1, pk, false);
+      if (j < 2) {
+        r0 = (r0 - d0) * 32.0f;
+        r1 = (r1 - d1) * 32.0f;
       }
       *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * kPRow + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
     }
@@ -624,16 +632,16 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // probability digits of block i - 1 (written to shared memory); (2) after
   // the barrier, the logits of block i, then block i - 1's running references
   // and value products.  CUR: block i exists; PREV: block i - 1 does.
-  auto step = [&](R& Bk, R& Bv, int i, auto cur_c, auto prev_c) __attribute__((always_inline)) {
+  auto step = [&](R& Bk, R& Bv, int i, auto cur_c, auto prev_c, auto set_c) __attribute__((always_inline)) {
     constexpr bool CUR = decltype(cur_c)::value;
     constexpr bool PREV = decltype(prev_c)::value;
+    constexpr int pj = decltype(set_c)::value;   // Bv's register set = block (i - 1) mod kSets
     // no instruction moves across a step boundary (hoisting the next step's
     // products into this one's runs out of registers)
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<(kSets - 1) * F::loads>();   // block i's keys and block i - 1's values have landed
     float code2[2] = {0.0f, 0.0f}, qj2[2] = {0.0f, 0.0f};
     if constexpr (CUR) key_products(Bk, code2, qj2);
-    const int pj = (i - 1) & 1;
     float rw = -INFINITY, ps = 0.0f;
     if constexpr (PREV) {
       float p0, p1;
@@ -738,37 +746,40 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       tail(buf0, buf2, buf1, i + 3);
       tail(buf1, buf0, buf2, i + 4);
     } else {
-      step(buf0, buf1, 0, Y{}, N{});
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      using S2 = std::integral_constant<int, 2>;
+      step(buf0, buf1, 0, Y{}, N{}, S1{});   // (no block -1: its buffer is not used)
       int i = 1;
       if constexpr (kSets == 3) {
         for (; i + 3 <= n_iter; i += 3) {
-          step(buf1, buf0, i, Y{}, Y{});
-          step(buf2, buf1, i + 1, Y{}, Y{});
-          step(buf0, buf2, i + 2, Y{}, Y{});
+          step(buf1, buf0, i, Y{}, Y{}, S0{});
+          step(buf2, buf1, i + 1, Y{}, Y{}, S1{});
+          step(buf0, buf2, i + 2, Y{}, Y{}, S2{});
         }
         // i = 1 (mod 3); the last step has no block i
         if (i < n_iter) {
-          step(buf1, buf0, i, Y{}, Y{});
+          step(buf1, buf0, i, Y{}, Y{}, S0{});
           if (i + 1 < n_iter) {
-            step(buf2, buf1, i + 1, Y{}, Y{});
-            step(buf0, buf2, i + 2, N{}, Y{});
+            step(buf2, buf1, i + 1, Y{}, Y{}, S1{});
+            step(buf0, buf2, i + 2, N{}, Y{}, S2{});
           } else {
-            step(buf2, buf1, i + 1, N{}, Y{});
+            step(buf2, buf1, i + 1, N{}, Y{}, S1{});
           }
         } else {
-          step(buf1, buf0, i, N{}, Y{});
+          step(buf1, buf0, i, N{}, Y{}, S0{});
         }
       } else {
         for (; i + 2 <= n_iter; i += 2) {
-          step(buf1, buf0, i, Y{}, Y{});
-          step(buf0, buf1, i + 1, Y{}, Y{});
+          step(buf1, buf0, i, Y{}, Y{}, S0{});
+          step(buf0, buf1, i + 1, Y{}, Y{}, S1{});
         }
         // i odd
         if (i < n_iter) {
-          step(buf1, buf0, i, Y{}, Y{});
-          step(buf0, buf1, i + 1, N{}, Y{});
+          step(buf1, buf0, i, Y{}, Y{}, S0{});
+          step(buf0, buf1, i + 1, N{}, Y{}, S1{});
         } else {
-          step(buf1, buf0, i, N{}, Y{});
+          step(buf1, buf0, i, N{}, Y{}, S0{});
         }
       }
     }
