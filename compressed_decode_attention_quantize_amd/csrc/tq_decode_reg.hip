@@ -179,8 +179,14 @@ struct RegFmt {
 // blocks whose weights are negligible (Sparse-V; with 2- and 3-bit values it
 // also never requests their value words); the plain variant has neither in
 // its step.
-template <int KB, bool QJL, int VB, bool FUSED, bool AUX>
+// NG: block groups of four waves per workgroup.  With two, one workgroup of
+// eight waves fills a compute unit: its groups take alternate blocks of the
+// split (one block each per step, in lock step through the same barriers),
+// share one query set-up and merge in shared memory before the split's
+// partial leaves the workgroup (not with logits or Sparse-V).
+template <int KB, bool QJL, int VB, bool FUSED, bool AUX, int NG>
 __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
+  static_assert(NG == 1 || (NG == 2 && !AUX), "two block groups: not with logits or Sparse-V");
   // three register sets, two with 4-bit values (three would not fit in 256)
   constexpr int kSets = (VB == 4) ? 2 : 3;
   // the logits / Sparse-V variant requests a block's values only after its
@@ -192,25 +198,27 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   constexpr int NTK = KO::nt;
   constexpr int NCS = KO::code_sets;
   constexpr int NTV = NTerms<VB>::n;
-  constexpr int kWaves = kRegThreads / 64;
+  constexpr int kWaves = 4 * NG;
   // [parity][col][k]: digits of p * radius; rows padded to 144 bytes so that
   // the 16 rows one 16-byte read instruction gathers fall on distinct banks
   constexpr int kPRow = 144;
   // digit buffers: block j's digits go to buffer j mod kSets (the index of the
   // register set that holds its values), so every address in the unrolled
   // step is a constant offset; the voting variant uses j mod 2
-  __shared__ __attribute__((aligned(16))) uint8_t plimb[kSets][16 * kPRow];
-  __shared__ __attribute__((aligned(4))) uint8_t pexp[kSets][4][16];        // [buffer][k / 32][col]
+  __shared__ __attribute__((aligned(16))) uint8_t plimb[NG][kSets][16 * kPRow];
+  __shared__ __attribute__((aligned(4))) uint8_t pexp[NG][kSets][4][16];        // [group][buffer][k / 32][col]
   __shared__ float rwb[4][kWaves][4];       // [block mod kSets (voting: mod 4)][wave][head]: each wave's step reference
   __shared__ float wred[kWaves][4];
-  __shared__ float mrun[4];
-  __shared__ __attribute__((aligned(16))) float obuf[4][kD];
+  __shared__ float mrun[NG][4];
+  __shared__ __attribute__((aligned(16))) float obuf[NG][4][kD];
   __shared__ __attribute__((aligned(16))) float r_lds[kD];   // the serving step's key residual
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gr = w >> 2;   // block group
+  const int wl = w & 3;    // wave within the group
   const int t = lane & 15;
   const int g4 = lane >> 4;
   // Workgroup -> (split, KV head, sequence, head group); the head groups of
@@ -265,7 +273,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const int nblk_seq = (len + kBlock - 1) / kBlock;
   const int blk0 = split_first_block(a, split);
   const int blk1 = min(blk0 + split_block_count(a, split), nblk_seq);
-  const int n_iter = max(0, blk1 - blk0);
+  const int n_iter = max(0, (blk1 - blk0 + NG - 1) / NG);   // steps; group gr takes blocks blk0 + NG i + gr
+  auto bk = [&](int i) __attribute__((always_inline)) { return blk0 + NG * i + gr; };
   const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const uint8_t* kbase = a.kc + slot0_idx * a.k_block_bytes;
   const uint8_t* vbase = a.vc + slot0_idx * a.v_block_bytes;
@@ -275,8 +284,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const __amdgpu_buffer_rsrc_t rv0 = block_rsrc(vbase, F::vBytes, a.n_blocks);
   const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase, F::kBytes, blk1);
   const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase, F::vBytes, blk1);
-  const int so = 4 * (g4 * kBlock + 32 * w + 2 * t);   // key words of this lane (and value words)
-  const int sn = 2 * (32 * w + 2 * t);                 // its two fp16 per-slot fields
+  const int so = 4 * (g4 * kBlock + 32 * wl + 2 * t);   // key words of this lane (and value words)
+  const int sn = 2 * (32 * wl + 2 * t);                 // its two fp16 per-slot fields
   constexpr int kNT = 2;   // streaming loads (read once)
   // The block index is clamped to the resource's last block (blocks past the
   // split re-read that block, unused), so every address lies inside the
@@ -310,13 +319,13 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // of block i - 1 are used in step i, then refilled with blocks i + kSets and
   // i - 1 + kSets.
   R buf0, buf1, buf2;
-  load_k(buf0, blk0, a.n_blocks, rk0);
-  if constexpr (!kLag) load_v(buf0, blk0, a.n_blocks, rv0);
-  load_k(buf1, blk0 + 1, a.n_blocks, rk0);
-  if constexpr (!kLag) load_v(buf1, blk0 + 1, a.n_blocks, rv0);
+  load_k(buf0, bk(0), a.n_blocks, rk0);
+  if constexpr (!kLag) load_v(buf0, bk(0), a.n_blocks, rv0);
+  load_k(buf1, bk(1), a.n_blocks, rk0);
+  if constexpr (!kLag) load_v(buf1, bk(1), a.n_blocks, rv0);
   if constexpr (kSets == 3) {
-    load_k(buf2, blk0 + 2, a.n_blocks, rk0);
-    if constexpr (!kLag) load_v(buf2, blk0 + 2, a.n_blocks, rv0);
+    load_k(buf2, bk(2), a.n_blocks, rk0);
+    if constexpr (!kLag) load_v(buf2, bk(2), a.n_blocks, rv0);
   }
   __builtin_amdgcn_sched_barrier(0);   // (issued before the query-side work below)
 
@@ -338,11 +347,11 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   __shared__ __attribute__((aligned(16))) float sred[QJL ? kWaves : 1][4][kM];   // partial sketch sums, by k-slot
   {
     // the fourth digit row of every digit buffer holds zeros throughout
-    for (int o = tid; o < kSets * 4 * (kPRow / 4); o += kRegThreads) {
+    for (int o = tid; o < NG * kSets * 4 * (kPRow / 4); o += 64 * kWaves) {
       const int pb = o / (4 * (kPRow / 4)), rg = (o / (kPRow / 4)) % 4, dw = o % (kPRow / 4);
-      reinterpret_cast<uint32_t*>(&plimb[pb][(4 * rg + 3) * kPRow])[dw] = 0u;
+      reinterpret_cast<uint32_t*>(&plimb[pb / kSets][pb % kSets][(4 * rg + 3) * kPRow])[dw] = 0u;
     }
-    {
+    if (w < 4) {   // waves 0..3: head w
       float lo = pq0 * pdk0, hi = pq1 * pdk1;
       const float q0 = pq0, q1 = pq1;
       if constexpr (QJL) {
@@ -382,26 +391,33 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
         sred[w][g][k1] = acc[g][1];
       }
     }
-    // (head w's rotated query was written by this wave: no barrier)
-    const float4 xr = *reinterpret_cast<const float4*>(&qr[w][4 * dl.l]);
+    if (w < 4) {
+      // (head w's rotated query was written by this wave: no barrier)
+      const float4 xr = *reinterpret_cast<const float4*>(&qr[w][4 * dl.l]);
 #pragma unroll
-    for (int s2 = 0; s2 < NCS; s2 += 2) {
-      const int s = min(s2 + half, NCS - 1);   // (an odd last set is formed by both halves)
-      const float coef = (KO::chain ? ((s == s2) ? ak[s2] : ak[min(s2 + 1, NCS - 1)]) : 1.0f) * kCodeScale;
-      write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, w, xr, coef, dl);
+      for (int s2 = 0; s2 < NCS; s2 += 2) {
+        const int s = min(s2 + half, NCS - 1);   // (an odd last set is formed by both halves)
+        const float coef = (KO::chain ? ((s == s2) ? ak[s2] : ak[min(s2 + 1, NCS - 1)]) : 1.0f) * kCodeScale;
+        write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, w, xr, coef, dl);
+      }
     }
     if constexpr (QJL) {
       lds_barrier();   // every wave's sketch shares are in shared memory
-      float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      // head hd's sketch digits: waves 0..3, or with two groups waves 4..7
+      // (while waves 0..3 form the code digits above)
+      const int hd = w - 4 * (NG - 1);
+      if (hd >= 0) {
+        float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-      for (int c = 0; c < kWaves; ++c) {
-        const float4 y = *reinterpret_cast<const float4*>(&sred[c][w][4 * dl.l]);
-        u.x += y.x;
-        u.y += y.y;
-        u.z += y.z;
-        u.w += y.w;
+        for (int c = 0; c < kWaves; ++c) {
+          const float4 y = *reinterpret_cast<const float4*>(&sred[c][hd][4 * dl.l]);
+          u.x += y.x;
+          u.y += y.y;
+          u.z += y.z;
+          u.w += y.w;
+        }
+        write_digits(alimb[NCS], aexp[NCS], cconst[NCS], hd, u, kSketchScale, dl);   // (both halves: the same job)
       }
-      write_digits(alimb[NCS], aexp[NCS], cconst[NCS], w, u, kSketchScale, dl);   // (both halves: the same job)
     }
   }
   lds_barrier();   // the operands are in shared memory (the cache loads above stay in flight)
@@ -532,19 +548,19 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
         r0 = (r0 - d0) * 32.0f;
         r1 = (r1 - d1) * 32.0f;
       }
-      *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * kPRow + 32 * w + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
+      *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * kPRow + 32 * wl + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
     }
     // bytes s0 + 127, s0 + 122, s0 + 117, 127 (no byte carries into the next)
     const uint32_t ebytes = static_cast<uint32_t>(s0 * 0x010101 + (0x7f000000 + 127 + (122 << 8) + (117 << 16)));
-    *reinterpret_cast<uint32_t*>(&pe[16 * w + 4 * g4]) = ebytes;   // the same from every lane of the row
+    *reinterpret_cast<uint32_t*>(&pe[16 * wl + 4 * g4]) = ebytes;   // the same from every lane of the row
   };
   // (2a) logits of block i
   auto logits = [&](R& Bk, int i, const float (&code2)[2], const float (&qj2)[2]) __attribute__((always_inline)) {
-    const int blk = blk0 + i;
-    const int n_t = min(kBlock, len - blk * kBlock);
+    const int blk = bk(i);
+    const int n_t = (blk < blk1) ? min(kBlock, len - blk * kBlock) : 0;   // (a group's block past the split: none)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int tok = pos_of_slot(32 * w + 2 * t + c);
+      const int tok = pos_of_slot(32 * wl + 2 * t + c);
       const float nk = h2f(c ? (Bk.kn >> 16) : Bk.kn);
       const float rho = QJL ? h2f(c ? (Bk.kr >> 16) : Bk.kr) : 0.0f;
       float l2 = fmaf(nk, code2[c], QJL ? __fmul_rn(rho, qj2[c]) : 0.0f);
@@ -560,13 +576,13 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     }
   };
   // (2b) the block's running references: head g4 (denominator) and head t / 4
-  // (column) from every wave's reference in rwr; returns the block's
-  // reference of head t / 4
+  // (column) from the references of the group's waves in rwr (indexed by
+  // wave within the group); returns the block's reference of head t / 4
   auto merge_refs = [&](const float (*rwr)[4], float rw, float ps) __attribute__((always_inline)) {
     const int hb = t >> 2;
     float ra = rwr[0][g4], rb = rwr[0][hb];
 #pragma unroll
-    for (int u = 1; u < kWaves; ++u) {
+    for (int u = 1; u < 4; ++u) {
       ra = fmaxf(ra, rwr[u][g4]);
       rb = fmaxf(rb, rwr[u][hb]);
     }
@@ -647,19 +663,19 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       float p0, p1;
       wave_ref(rw, p0, p1);
       rwb[pj][w][g4] = rw;   // every lane of the row stores the same value
-      p_digits(&plimb[pj][0], &pexp[pj][0][0], p0, p1, Bv.vn);
+      p_digits(&plimb[gr][pj][0], &pexp[gr][pj][0][0], p0, p1, Bv.vn);
       ps = p0 + p1;
     }
     if constexpr (CUR && PREV) interleave(KMat{});
     if constexpr (PREV) lds_barrier();
     if constexpr (CUR) logits(Bk, i, code2, qj2);
     if constexpr (PREV) {
-      const float rb = merge_refs(rwb[pj], rw, ps);
-      if (!sparse_skip(rb)) value_products(&plimb[pj][0], &pexp[pj][0][0], rwb[pj], Bv);
+      const float rb = merge_refs(rwb[pj] + 4 * gr, rw, ps);
+      if (!sparse_skip(rb)) value_products(&plimb[gr][pj][0], &pexp[gr][pj][0][0], rwb[pj] + 4 * gr, Bv);
     }
     // ---- refills: keys kSets blocks past block i, values kSets past block i - 1
-    if constexpr (CUR) load_k(Bk, blk0 + i + kSets, blk1, rk);
-    if constexpr (PREV) load_v(Bv, blk0 + i - 1 + kSets, blk1, rv);
+    if constexpr (CUR) load_k(Bk, bk(i + kSets), blk1, rk);
+    if constexpr (PREV) load_v(Bv, bk(i - 1 + kSets), blk1, rv);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -696,7 +712,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     }
     const int pj = i & 1;
     if constexpr (OLD) {
-      if (Bc.vreq) p_digits(&plimb[pj][0], &pexp[pj][0][0], Bc.pp0, Bc.pp1, Bc.vn);
+      if (Bc.vreq) p_digits(&plimb[0][pj][0], &pexp[0][pj][0][0], Bc.pp0, Bc.pp1, Bc.vn);
     }
     if constexpr (CUR && PREV) interleave(KMat{});
     if constexpr (PREV || OLD) lds_barrier();
@@ -704,12 +720,12 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     if constexpr (PREV) {
       const float rb = merge_refs(rwb[(i - 1) & 3], rw, ps);
       Bn.vreq = !sparse_skip(rb);
-      if (Bn.vreq) load_v(Bn, blk0 + i - 1, blk1, rv);
+      if (Bn.vreq) load_v(Bn, bk(i - 1), blk1, rv);
     }
     if constexpr (OLD) {
-      if (Bc.vreq) value_products(&plimb[pj][0], &pexp[pj][0][0], rwb[(i - 3) & 3], Bc);
+      if (Bc.vreq) value_products(&plimb[0][pj][0], &pexp[0][pj][0][0], rwb[(i - 3) & 3], Bc);
     }
-    if constexpr (CUR) load_k(Bc, blk0 + i + kSets, blk1, rk);
+    if constexpr (CUR) load_k(Bc, bk(i + kSets), blk1, rk);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -790,7 +806,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   {
     const float ls = row_sum16(lsum);
     if (t == 0) wred[w][g4] = ls;
-    if (w == 0 && t == 0) mrun[g4] = (m_a == kNoRef) ? -INFINITY : m_a;
+    if (wl == 0 && t == 0) mrun[gr][g4] = (m_a == kNoRef) ? -INFINITY : m_a;
     const int hc = t >> 2;
     float avsum = 0.0f;
 #pragma unroll
@@ -808,16 +824,34 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
         s += __shfl_xor(s, 2, 64);
         v[r][i] = s;
       }
-    // result row 4 g4 + i of pass r is coordinate 32 w + 8 g4 + 2 i + r
+    // result row 4 g4 + i of pass r is coordinate 32 wl + 8 g4 + 2 i + r
     if (hc < G && (t & 3) == 0) {
-      float* o = &obuf[hc][32 * w + 8 * g4];
+      float* o = &obuf[gr][hc][32 * wl + 8 * g4];
       *reinterpret_cast<float4*>(o) = make_float4(v[0][0], v[1][0], v[0][1], v[1][1]);
       *reinterpret_cast<float4*>(o + 4) = make_float4(v[0][2], v[1][2], v[0][3], v[1][3]);
     }
   }
   __syncthreads();
   if (w < G) {
-    float lo = obuf[w][lane], hi = obuf[w][lane + 64];
+    float lo = obuf[0][w][lane], hi = obuf[0][w][lane + 64];
+    float mh = mrun[0][w], lh = 0.0f;   // the split's reference (log2 units) and denominator of head w
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lh += wred[u][w];
+    if constexpr (NG == 2) {
+      // the two groups' sums, each against its own running reference, brought
+      // to the larger one (powers of two)
+      const float m1 = mrun[1][w];
+      float l1 = 0.0f;
+#pragma unroll
+      for (int u = 4; u < 8; ++u) l1 += wred[u][w];
+      const float mx = fmaxf(mh, m1);
+      const float f0 = (mh == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, shift_of(mh - mx));
+      const float f1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, shift_of(m1 - mx));
+      lo = fmaf(obuf[1][w][lane], f1, lo * f0);
+      hi = fmaf(obuf[1][w][lane + 64], f1, hi * f0);
+      lh = fmaf(l1, f1, lh * f0);
+      mh = mx;
+    }
     wave_fwht128(lo, hi, lane);
     const float inv_d = 1.0f / static_cast<float>(kD);
     lo *= dva * inv_d;
@@ -826,25 +860,22 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     store_coherent(pp + lane, lo);
     store_coherent(pp + 64 + lane, hi);
     if (lane == 0) {
-      float l = 0.0f;
-#pragma unroll
-      for (int u = 0; u < kWaves; ++u) l += wred[u][w];
-      store_coherent(pp + kD, mrun[w] * kLn2);
-      store_coherent(pp + kD + 1, l);
+      store_coherent(pp + kD, mh * kLn2);
+      store_coherent(pp + kD + 1, lh);
     }
   }
   if (!arrive_last(counter, a.n_splits, &s_last)) return;
   merge_splits(a, b, hq0, G, counter, w, lane);
 }
 
-template <int KB, bool QJL, int VB, bool AUX>
-__global__ __launch_bounds__(kRegThreads, 2) void decode_reg_kernel(DecodeArgs a) {
-  decode_reg_body<KB, QJL, VB, false, AUX>(a);
+template <int KB, bool QJL, int VB, bool AUX, int NG>
+__global__ __launch_bounds__(kRegThreads * NG, 2) void decode_reg_kernel(DecodeArgs a) {
+  decode_reg_body<KB, QJL, VB, false, AUX, NG>(a);
 }
 
-template <int KB, bool QJL, int VB, bool AUX>
-__global__ __launch_bounds__(kRegThreads, 2) void decode_reg_append_kernel(DecodeArgs a) {
-  decode_reg_body<KB, QJL, VB, true, AUX>(a);
+template <int KB, bool QJL, int VB, bool AUX, int NG>
+__global__ __launch_bounds__(kRegThreads * NG, 2) void decode_reg_append_kernel(DecodeArgs a) {
+  decode_reg_body<KB, QJL, VB, true, AUX, NG>(a);
 }
 
 template <int KB, bool QJL, int VB>
@@ -855,14 +886,18 @@ hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   const bool aux = a.sparse_v > 0 || a.logits != nullptr;
   if (a.k_new != nullptr) {
     if (aux)
-      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, true>), grid, dim3(kRegThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, true, 1>), grid, dim3(kRegThreads), 0, stream, a);
+    else if (a.groups == 2)
+      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, false, 2>), grid, dim3(2 * kRegThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, false>), grid, dim3(kRegThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_reg_append_kernel<KB, QJL, VB, false, 1>), grid, dim3(kRegThreads), 0, stream, a);
   } else {
     if (aux)
-      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, true>), grid, dim3(kRegThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, true, 1>), grid, dim3(kRegThreads), 0, stream, a);
+    else if (a.groups == 2)   // one eight-wave workgroup per compute unit
+      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, false, 2>), grid, dim3(2 * kRegThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, false>), grid, dim3(kRegThreads), 0, stream, a);
+      hipLaunchKernelGGL((decode_reg_kernel<KB, QJL, VB, false, 1>), grid, dim3(kRegThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

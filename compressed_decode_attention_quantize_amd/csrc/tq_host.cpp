@@ -526,6 +526,14 @@ void set_split_ranges(const tq_config* c, int32_t max_seq_len, tq::DecodeArgs* a
   a->n_long = static_cast<int32_t>(n_long);
 }
 
+// Block groups per workgroup of the register-streamed decode: when the grid
+// holds at most one workgroup per compute unit, each workgroup takes eight
+// waves in two block groups (alternate blocks of its split, one query set-up),
+// so that two waves share each SIMD; otherwise two four-wave workgroups do.
+int reg_groups(const tq_config* c, int splits) {
+  return static_cast<int64_t>(splits) * split_units(c) <= tq::kComputeUnits ? 2 : 1;
+}
+
 // Largest split count of any call with lengths up to max_seq_len (the
 // automatic chunking is not monotonic in the length), for workspace sizing.
 int decode_splits_bound(const tq_config* c, int32_t max_seq_len) {
@@ -648,7 +656,7 @@ void fill_decode_args(const tq_config* cfg, const void* params, const void* k_ca
   a.chunk_blocks = decode_chunk_blocks(cfg, max_seq_len);
   a.n_splits = splits;
   set_split_ranges(cfg, max_seq_len, &a);
-  a.groups = mfma_path(cfg) ? mfma_groups(cfg, max_seq_len) : 1;
+  a.groups = mfma_path(cfg) ? mfma_groups(cfg, max_seq_len) : (reg_path(cfg) ? reg_groups(cfg, splits) : 1);
   a.k_codec = cfg->k_codec;
   a.k_bits = cfg->k_bits;
   a.v_codec = cfg->v_codec;

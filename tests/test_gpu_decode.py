@@ -44,7 +44,9 @@ def _oracle_cache(cfg, lens, seed, scale_heads=False):
     return spec, P, R, kc, vc, q
 
 
-def _gpu_decode(cfg, kc, vc, lens, q, max_seq_len=None):
+def _gpu_decode(cfg, kc, vc, lens, q, max_seq_len=None, want_logits=True):
+    """Decode on the GPU; with want_logits=False the plain variant (no logits
+    buffer: the kernel the benchmark times) and lg is None."""
     k_cache, v_cache = upload_cache(kc, vc, DEV)
     params = tq.init_params(cfg, DEV)
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
@@ -52,10 +54,10 @@ def _gpu_decode(cfg, kc, vc, lens, q, max_seq_len=None):
     ws = torch.zeros(tq.decode_workspace_bytes(cfg, msl), dtype=torch.uint8, device=DEV)
     qd = torch.from_numpy(np.ascontiguousarray(q, np.float32)).to(DEV)
     out = torch.empty_like(qd)
-    lg = torch.full((cfg.batch, cfg.n_q_heads, cfg.max_ctx), float("nan"), device=DEV)
+    lg = torch.full((cfg.batch, cfg.n_q_heads, cfg.max_ctx), float("nan"), device=DEV) if want_logits else None
     tq.decode_attention(cfg, params, k_cache, v_cache, seq, msl, qd, out, ws, lg)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), lg.cpu().numpy(), ws
+    return out.cpu().numpy(), (lg.cpu().numpy() if want_logits else None), ws
 
 
 @pytest.mark.parametrize("codec", list(CODECS))
@@ -71,16 +73,20 @@ def test_decode_matches_oracle(codec, heads):
     print(f"[decode] {codec} heads={heads}", flush=True)
     spec, P, R, kc, vc, q = _oracle_cache(cfg, lens, seed=list(CODECS).index(codec) + 10 * n_kv, scale_heads=True)
     out, lg, _ = _gpu_decode(cfg, kc, vc, lens, q)
+    # the plain variant (no logits requested): another kernel variant where
+    # the grid allows (two block groups per workgroup)
+    out_plain, _, _ = _gpu_decode(cfg, kc, vc, lens, q, want_logits=False)
     ref_out, ref_lg = oracle.decode(spec, P, R, lens, q, want_logits=True)
     G = n_q // n_kv
     for b, n in enumerate(lens):
         rows = slice(b * n_q, (b + 1) * n_q)
         check_out(out[b], ref_out[rows], f"{codec} b={b}")
+        check_out(out_plain[b], ref_out[rows], f"{codec} b={b} (no logits)")
         if n:
             check_logits(lg[b], ref_lg[rows], n, f"{codec} b={b}")
             assert np.all(np.isnan(lg[b][:, n:])), "logits written past the sequence"
         else:
-            assert np.all(out[b] == 0)
+            assert np.all(out[b] == 0) and np.all(out_plain[b] == 0)
 
 
 def test_raw_bypass_is_textbook_attention():

@@ -63,7 +63,7 @@ def _check_all_records(cfg, layer, k, v, lens, label):
     return tot
 
 
-def _check_pair(cfg, layer, k, v, q, lg, out, b, h, n, label):
+def _check_pair(cfg, layer, k, v, q, lg, out, b, h, n, label, out_plain=None):
     G = cfg.n_q_heads // cfg.n_kv_heads
     sub, Gr = _sub_records(cfg, layer, b, h, n)
     P = oracle.Params(sub, cfg.seed, cfg.layer)
@@ -79,6 +79,8 @@ def _check_pair(cfg, layer, k, v, q, lg, out, b, h, n, label):
         skip = np.repeat(differ[None], G, axis=0)
     worst = check_logits(lg[b, h * G:(h + 1) * G].cpu().numpy(), ref_lg, n, label, skip=skip)
     err = check_out(out[b, h * G:(h + 1) * G].cpu().numpy(), ref_out, label)
+    if out_plain is not None:   # the decode without logits (the launch the benchmark times)
+        err = max(err, check_out(out_plain[b, h * G:(h + 1) * G].cpu().numpy(), ref_out, label + " (no logits)"))
     print(f"{label}: records={st['records']} sign exceptions={st['sign_mismatch']}/{st['sign_total']} "
           f"worst logit rel={worst:.2e} max out err={err:.2e}", flush=True)
 
@@ -94,11 +96,12 @@ def test_full_size_prefill_then_decode(wi, wname):
     L.append(k, v)
     lg = torch.full((w.batch, w.n_q, w.ctx), float("nan"), device=DEV)
     out = L.decode(q, logits=lg)
+    out_plain = L.decode(q)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
+    assert torch.isfinite(out).all() and torch.isfinite(out_plain).all()
     rng = np.random.default_rng(wi)
     h = int(rng.integers(0, w.n_kv))
-    _check_pair(cfg, L, k, v, q, lg, out, 0, h, w.ctx, f"{wname} kv={h}")
+    _check_pair(cfg, L, k, v, q, lg, out, 0, h, w.ctx, f"{wname} kv={h}", out_plain=out_plain)
 
 
 @pytest.mark.parametrize("wi,wname", [(i, n) for i, n in enumerate(synth.ORDER) if n != "serving_b16_ctx8k"])
