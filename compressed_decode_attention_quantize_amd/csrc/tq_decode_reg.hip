@@ -391,22 +391,30 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
         sred[w][g][k1] = acc[g][1];
       }
     }
-    if (w < 4) {
-      // (head w's rotated query was written by this wave: no barrier)
-      const float4 xr = *reinterpret_cast<const float4*>(&qr[w][4 * dl.l]);
+    // The code sets' digits of head w & 3, two sets at a time.  With two groups
+    // and more than two code sets (the rotated queries are then in shared
+    // memory, past the barrier above), group gr takes the set pairs with
+    // (s2 / 2) % 2 == gr and waves 0..3 the sketch digits below; with two
+    // groups otherwise waves 0..3 take every code set and waves 4..7 the
+    // sketch digits.
+    constexpr bool kSplitCode = NG == 2 && QJL && NCS > 2;
+    if (kSplitCode || w < 4) {
+      const int hw = w & 3;
+      // (with one group head w's rotated query was written by this wave: no barrier)
+      const float4 xr = *reinterpret_cast<const float4*>(&qr[hw][4 * dl.l]);
 #pragma unroll
       for (int s2 = 0; s2 < NCS; s2 += 2) {
+        if (kSplitCode && ((s2 >> 1) & 1) != gr) continue;
         const int s = min(s2 + half, NCS - 1);   // (an odd last set is formed by both halves)
         const float coef = (KO::chain ? ((s == s2) ? ak[s2] : ak[min(s2 + 1, NCS - 1)]) : 1.0f) * kCodeScale;
-        write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, w, xr, coef, dl);
+        write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, hw, xr, coef, dl);
       }
     }
     if constexpr (QJL) {
       lds_barrier();   // every wave's sketch shares are in shared memory
-      // head hd's sketch digits: waves 0..3, or with two groups waves 4..7
-      // (while waves 0..3 form the code digits above)
-      const int hd = w - 4 * (NG - 1);
-      if (hd >= 0) {
+      // head hd's sketch digits
+      const int hd = kSplitCode ? w : w - 4 * (NG - 1);
+      if (hd >= 0 && hd < 4) {
         float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int c = 0; c < kWaves; ++c) {
@@ -811,7 +819,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     float avsum = 0.0f;
 #pragma unroll
     for (int T = 0; T < NTV; ++T) avsum += av[T];
-    const float voff = avsum * 0.5f * (accO[0] + __shfl_xor(accO[0], 32, 64));
+    const float voff = avsum * 0.5f * (accO[0] + lane_xor<32>(accO[0]));
     float v[2][4];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -820,8 +828,8 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
         float s = -voff;
 #pragma unroll
         for (int T = 0; T < NTV; ++T) s = fmaf(av[T], accV[r][T][i], s);
-        s += __shfl_xor(s, 1, 64);   // the 4 digit columns of head hc
-        s += __shfl_xor(s, 2, 64);
+        s += lane_xor<1>(s);   // the 4 digit columns of head hc
+        s += lane_xor<2>(s);
         v[r][i] = s;
       }
     // result row 4 g4 + i of pass r is coordinate 32 wl + 8 g4 + 2 i + r

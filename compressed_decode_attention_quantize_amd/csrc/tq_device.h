@@ -60,7 +60,7 @@ __device__ __forceinline__ float row_sum16(float x) {
 // Value of lane (l ^ H) for lane l, by the cheapest cross-lane route: DPP
 // within 16-lane rows (xor 1, 2 as quad permutations; xor 4 = xor 3 then
 // xor 7; xor 8 = xor 7 then xor 15 via the half-row and row mirrors), the
-// 32-lane swizzle for xor 16, a permute for xor 32.
+// 32-lane swizzle for xor 16, a 32-lane swap for xor 32.
 template <int H>
 __device__ __forceinline__ int lane_xor_i(int v) {
   if constexpr (H == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
@@ -74,7 +74,10 @@ __device__ __forceinline__ int lane_xor_i(int v) {
     return __builtin_amdgcn_update_dpp(0, u, 0x140, 0xF, 0xF, false);
   }
   if constexpr (H == 16) return __builtin_amdgcn_ds_swizzle(v, 0x401F);
-  if constexpr (H == 32) return __shfl_xor(v, 32, 64);
+  if constexpr (H == 32) {   // one swap of the register with itself, then each half takes the other's copy
+    const auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+    return static_cast<int>((__lane_id() & 32) ? r[0] : r[1]);
+  }
   return v;
 }
 template <int H>
