@@ -225,6 +225,8 @@ def serve_steps(args, w, layers, q, dev, tq, synth, seed, bytes_per_launch):
                 tq.decode_attention(L.cfg, L.params, L.k_cache, L.v_cache, lens[s + 1], w.ctx + s + 1, q, out,
                                     L.workspace)
 
+    if args.settle_ms > 0:   # plain decodes (they leave the caches as they are)
+        settle(layers, q, args.settle_ms / 1e3)
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -340,10 +342,34 @@ def time_prefill(layers, k, v, stream):
     return e0.elapsed_time(e1) / 1e3 / max(1, len(layers) - 1)
 
 
-def time_decode(layers, q, steps, warmup, stream):
-    """Decode passes over the layer stack: `warmup` untimed, then `steps`
-    timed with HIP events on the launch stream.  Returns (mean ms per step,
-    sorted per-step ms, wall seconds)."""
+SETTLE_S = 0.15
+
+
+def settle(layers, q, seconds):
+    """Untimed decode passes over the layer stack for `seconds` of wall time.
+    The GPU enters a run at its top clock and within a few ms of sustained
+    decode drops under its power limit, then recovers over the next ~20 ms
+    (1M context: ~175 us per launch for the first dozen launches, up to
+    ~240 us, then ~186-195 us): the timed steps measure the sustained state,
+    whatever the warm-up count."""
+    import torch
+    out = torch.empty_like(q)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for L in layers:
+            L.decode(q, out=out)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
+
+
+def time_decode(layers, q, steps, warmup, stream, settle_s=SETTLE_S):
+    """Decode passes over the layer stack: a settling phase (see settle), then
+    `warmup` untimed, then `steps` timed with HIP events on the launch stream.
+    Returns (mean ms per step, sorted per-step ms, wall seconds)."""
     import torch
     outs = [torch.empty_like(q) for _ in layers]
 
@@ -351,6 +377,8 @@ def time_decode(layers, q, steps, warmup, stream):
         for i, L in enumerate(layers):
             L.decode(q, out=outs[i])
 
+    if settle_s > 0:
+        settle(layers, q, settle_s)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -392,7 +420,7 @@ def measure_config(name, args, dev, tq, synth):
            "append_tokens_per_s": round(pos_s, 1), "append_ms_per_layer": round(app_s * 1e3, 4),
            "append_roofline": append_roofline(w, pos_s, krec, vrec)}
     if w.steps:
-        sargs = argparse.Namespace(steps=steps, warmup=args.warmup, serve="fused")
+        sargs = argparse.Namespace(steps=steps, warmup=args.warmup, serve="fused", settle_ms=args.settle_ms)
         sv = serve_steps(sargs, w, layers, q, dev, tq, synth, seed, nbytes)["serve"]
         us = sv["us_per_layer_step"]
         # the decode of a step attends ctx + warmup + s + 1 positions, s = 0 .. steps - 1
@@ -405,7 +433,7 @@ def measure_config(name, args, dev, tq, synth):
                     "gbs": round(gbs, 2), "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "tokens_per_s": sv["tokens_per_s"], "ms_per_step_all_layers": sv["ms_per_step_all_layers"]})
     else:
-        step_ms, per_step, _ = time_decode(layers, q, args.steps, args.warmup, stream)
+        step_ms, per_step, _ = time_decode(layers, q, args.steps, args.warmup, stream, args.settle_ms / 1e3)
         us = step_ms * 1e3 / n_layers
         gbs = nbytes / (us * 1e-6) / 1e9
         res.update({"mode": "decode (tq_decode_attention, one launch per layer)", "steps": args.steps,
@@ -424,6 +452,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first (the clocks and caches settle within a few tens of ms)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_S * 1e3,
+                    help="untimed decode work before the warm-up steps, in ms of wall time (the GPU's clocks "
+                         "swing under its power limit for the first ~20 ms of sustained decode)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--layers", type=int, default=0, help="layer caches to cycle (0 = workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -498,7 +529,7 @@ def main():
     if policy is not None:   # mean over the stack's layers
         per_layer = [algorithmic_decode_bytes(w, L.cfg, tq, lens)[0] for L in layers]
         bytes_per_launch = sum(per_layer) // n_layers
-    step_ms, per_step, wall = time_decode(layers, q, args.steps, args.warmup, stream)
+    step_ms, per_step, wall = time_decode(layers, q, args.steps, args.warmup, stream, args.settle_ms / 1e3)
     ceiling = read_ceiling(tq, dev)
 
     # average duration of one decode launch: the timed region (HIP events on
@@ -514,6 +545,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -77,7 +77,7 @@ def _tree_mismatches(spec, D, bits, Gc, Rc, sel, x, label):
     band of a decision boundary (checked on the oracle's own margins)."""
     diff = (Gc != Rc) & sel[:, None]
     n_bad = int(diff.sum())
-    assert n_bad <= SIGN_FRACTION * int(sel.sum()) * spec.d + 1, f"{label}: {n_bad} angle codes differ"
+    assert n_bad <= int(SIGN_FRACTION * int(sel.sum()) * spec.d), f"{label}: {n_bad} angle codes differ"
     if n_bad:
         assert x is not None, f"{label}: angle codes differ and no inputs to check the band"
         T = oracle.tree_tables(bits, spec.d)
