@@ -571,7 +571,9 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       const int tok = pos_of_slot(32 * wl + 2 * t + c);
       const float nk = h2f(c ? (Bk.kn >> 16) : Bk.kn);
       const float rho = QJL ? h2f(c ? (Bk.kr >> 16) : Bk.kr) : 0.0f;
-      float l2 = fmaf(nk, code2[c], QJL ? __fmul_rn(rho, qj2[c]) : 0.0f);
+      // (rho * qj as an fma with a zero addend: one mixed-precision instruction
+      // takes the fp16 rho as it is)
+      float l2 = fmaf(nk, code2[c], QJL ? fmaf(rho, qj2[c], 0.0f) : 0.0f);
       // computed on every lane: used only where valid, the products feeding it
       // would otherwise be sunk into a divergent branch
       asm volatile("" : "+v"(l2));
