@@ -134,7 +134,9 @@ struct PairCopier {
       const bool isv = !isk && q < F::kChunks + F::vChunks;
       const int stride = isk ? F::kBytes : (isv ? F::vBytes : 0);   // uniform
       uint8_t* dst = (isk || isv) ? slot + 1024 * q : junk;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, (lds_void_t*)(dst), 16, lo[j] + b0 * stride, 0, 0, 0);
+      // (the block's base in the scalar offset: no per-lane add)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, (lds_void_t*)(dst), 16, lo[j],
+                                               __builtin_amdgcn_readfirstlane(b0 * stride), 0, 0);
     }
   }
 };
@@ -241,6 +243,12 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   const int n_iter = max(0, (blk1 - blk0 + NG - 1) / NG);   // steps of NG blocks
   const int64_t slot0_idx = (static_cast<int64_t>(b) * a.n_kv + h) * a.n_blocks;
   const float inv_sqrt_d = 0.08838834764831845f;
+  // The optional logits go through a buffer over this (sequence, head
+  // group)'s rows, range-checked by the hardware: a lane with no logit to
+  // store takes an offset past its end (no branch in the step)
+  const __amdgpu_buffer_rsrc_t rlg = __builtin_amdgcn_make_buffer_rsrc(
+      a.logits != nullptr ? a.logits + (static_cast<int64_t>(b) * a.n_q + hq0) * a.max_ctx : a.logits,
+      static_cast<short>(0), a.logits != nullptr ? G * a.max_ctx * 4 : 0, 0x00020000);
 
   float av[NTV];
 #pragma unroll
@@ -397,7 +405,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
       const int hh = t >> 2, dd = t & 3;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) A8[cb] = (dd < 3) ? *reinterpret_cast<const long*>(&qdig[hh][dd][32 * cb + 8 * g4]) : 0;
-      qsc8 = __builtin_amdgcn_ldexpf(kLog2e * inv_sqrt_d, qexp8[g4]);
+      qsc8 = __builtin_amdgcn_ldexpf(kLog2e * inv_sqrt_d, qexp8[g4] - 7);   // (the digit sums come in units of 2^-7)
     } else {
       const uint4 lo = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 16 * g4]);
       const uint4 hi = *reinterpret_cast<const uint4*>(&alimb[0][t * 128 + 64 + 16 * g4]);
@@ -449,7 +457,10 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
       float lg2[2];
       if constexpr (KQ8) {
         // q8: per 32-coordinate block cb, exact int32 sums of q digits times
-        // k8, combined as D0 + D1 2^-7 + D2 2^-14 and scaled by the block's s16
+        // k8, combined as (D0 2^7 + D1) + D2 2^-7 (the first two in integer
+        // arithmetic: |D0|, |D1| <= 64 * 127 * 32 < 2^18, so the int32 is exact
+        // and its conversion rounds below 2^-24 of it) and scaled by the
+        // block's s16
         v4i dI[2][4];
         uint2 sc[2];
         int tok2[2];
@@ -470,16 +481,17 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
           float code = 0.0f;
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            float v = fmaf(static_cast<float>(dI[c][cb][1]), 0.0078125f, static_cast<float>(dI[c][cb][0]));
-            v = fmaf(static_cast<float>(dI[c][cb][2]), 6.103515625e-05f, v);
+            const int d01 = dI[c][cb][0] * 128 + dI[c][cb][1];
+            const float v = fmaf(static_cast<float>(dI[c][cb][2]), 0.0078125f, static_cast<float>(d01));
             const uint32_t sw = (cb < 2) ? sc[c].x : sc[c].y;
             code = fmaf(h2f((cb & 1) ? (sw >> 16) : sw), v, code);
           }
           const int tok = tok2[c];
           const float l2 = __fmul_rn(qsc8, code);
           const bool valid = (tok < n_t) && (g4 < G);
-          if (a.logits != nullptr && valid)
-            a.logits[(static_cast<int64_t>(b) * a.n_q + hq0 + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
+          // (no logits: an empty buffer, every store dropped; -1: past its end)
+          const int lo = valid ? (g4 * a.max_ctx + blk * kBlock + tok) * 4 : -1;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fmul_rn(l2, kLn2)), rlg, lo, 0, 0);
           lg2[c] = valid ? l2 : -INFINITY;
         }
       } else {
@@ -514,8 +526,8 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
         // explicit roundings: every unrolled copy of the step computes the same bits
         const float l2 = fmaf(__fmul_rn(alpha2, nk), code, QJL ? __fmul_rn(__fmul_rn(beta2, rho), qj) : 0.0f);
         const bool valid = (tok < n_t) && (g4 < G);
-        if (a.logits != nullptr && valid)
-          a.logits[(static_cast<int64_t>(b) * a.n_q + hq0 + g4) * a.max_ctx + blk * kBlock + tok] = __fmul_rn(l2, kLn2);
+        const int lo = valid ? (g4 * a.max_ctx + blk * kBlock + tok) * 4 : -1;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(__fmul_rn(l2, kLn2)), rlg, lo, 0, 0);
         lg2[c] = valid ? l2 : -INFINITY;
       }
       }
@@ -795,6 +807,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int64_t span = (static_cast<int64_t>(a.n_blocks) + 2 * kRing + 4) * std::max(a.k_block_bytes, a.v_block_bytes);
   if (span >= (int64_t{1} << 31) || static_cast<int64_t>(a.n_splits) * kPartialStride * 4 >= (int64_t{1} << 31))
     return hipErrorNotSupported;
+  // the logits of four heads of one sequence are addressed with 32-bit offsets
+  if (a.logits != nullptr && int64_t{16} * a.max_ctx >= (int64_t{1} << 31)) return hipErrorNotSupported;
   if (a.k_codec == Q8_BLOCK32) return launch_v<8, false>(a, stream);
   if (a.k_codec == POLAR_QJL) {
     switch (a.k_bits) {
