@@ -33,6 +33,7 @@ UNITS = [
     ("tq_decode.hip", []),
     ("tq_decode_mfma.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
     ("tq_decode_reg.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
+    ("tq_decode_q8.hip", ["-fno-honor-nans", "-ffp-contract=off"]),
     ("tq_dequant.hip", []),
     ("tq_stream.hip", []),
     ("tq_scratch.hip", []),

@@ -442,9 +442,15 @@ bool reg_path(const tq_config* c) {
   return tq::decode_reg_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
 }
 
+// q8 keys with more than four query heads per KV head: one workgroup serves
+// every head group of its KV head from one shared-memory ring.
+bool q8_path(const tq_config* c) {
+  return tq::decode_q8_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads, c->v_bits);
+}
+
 // Ring-staged matrix-core decode: the other codecs it serves (q8 keys).
 bool mfma_path(const tq_config* c) {
-  return !reg_path(c) && tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
+  return !reg_path(c) && !q8_path(c) && tq::decode_mfma_applies(c->k_codec, c->v_codec, c->n_q_heads / c->n_kv_heads);
 }
 
 // Independent (sequence, KV head, head group) units the splits multiply: the
@@ -489,6 +495,7 @@ int mfma_groups(const tq_config* c, int32_t max_seq_len) {
 
 int64_t target_workgroups(const tq_config* c, int32_t max_seq_len) {
   if (reg_path(c)) return tq::kRegWorkgroups;
+  if (q8_path(c)) return tq::kComputeUnits;   // one eight- or twelve-wave workgroup per compute unit
   return mfma_path(c) ? tq::kMfmaUnitWorkgroups / mfma_groups(c, max_seq_len) : tq::kValuWorkgroups;
 }
 
@@ -766,6 +773,7 @@ tq_status tq_decode_attention(const tq_config* cfg, const void* params, const vo
                                       workspace_bytes, &a);
   if (st != TQ_OK) return st;
   hipError_t e = tq::launch_decode_reg(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) e = tq::launch_decode_q8(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) e = tq::launch_decode_mfma(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) e = tq::launch_decode(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
@@ -789,6 +797,7 @@ tq_status tq_decode_attention_noalloc(const tq_config* cfg, const void* params, 
   fill_decode_args(cfg, params, k_cache, v_cache, seq_lens, max_seq_len, q, out, logits,
                    reinterpret_cast<uint32_t*>(base), base + tq::kScratchCounterBytes, &a);
   hipError_t e = tq::launch_decode_reg(a, s);
+  if (e == hipErrorNotSupported) e = tq::launch_decode_q8(a, s);
   if (e == hipErrorNotSupported) e = tq::launch_decode_mfma(a, s);
   if (e == hipErrorNotSupported) e = tq::launch_decode(a, s);
   return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
@@ -806,11 +815,13 @@ tq_status tq_append_decode(const tq_config* cfg, const void* params, void* k_cac
   if (st != TQ_OK) return st;
   a.len_add = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (reg_path(cfg) || mfma_path(cfg)) {
+  if (reg_path(cfg) || q8_path(cfg) || mfma_path(cfg)) {
     a.k_new = k_new;
     a.v_new = v_new;
     a.in_dtype = in_dtype;
-    hipError_t e = reg_path(cfg) ? tq::launch_decode_reg(a, s) : tq::launch_decode_mfma(a, s);
+    hipError_t e = reg_path(cfg) ? tq::launch_decode_reg(a, s) : hipErrorNotSupported;
+    if (e == hipErrorNotSupported) e = tq::launch_decode_q8(a, s);
+    if (e == hipErrorNotSupported) e = tq::launch_decode_mfma(a, s);
     if (e != hipErrorNotSupported) return e == hipSuccess ? TQ_OK : TQ_EDEVICE;
     a.k_new = a.v_new = nullptr;
   }

@@ -149,6 +149,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // values and G <= 16; hipErrorNotSupported otherwise.
 bool decode_reg_applies(int k_codec, int v_codec, int group);
 hipError_t launch_decode_reg(const DecodeArgs& a, hipStream_t stream);
+// q8 keys with POLAR values and more than four query heads per KV head: one
+// workgroup per (split, KV head, sequence) serving every head group from one
+// shared-memory ring; hipErrorNotSupported for other configurations.
+bool decode_q8_applies(int k_codec, int v_codec, int group, int v_bits);
+hipError_t launch_decode_q8(const DecodeArgs& a, hipStream_t stream);
 // Block groups (of four wavefronts) per workgroup of the matrix-core decode
 // kernel for a key codec: with one group two independent workgroups share a
 // compute unit, with two groups one workgroup of eight wavefronts fills it.

@@ -23,6 +23,11 @@ bool decode_reg_applies(int k_codec, int v_codec, int group) {
   return v_codec == POLAR && group <= kMaxGroup && (k_codec == POLAR || k_codec == POLAR_QJL);
 }
 hipError_t launch_decode_reg(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
+bool decode_q8_applies(int k_codec, int v_codec, int group, int v_bits) {
+  return k_codec == Q8_BLOCK32 && v_codec == POLAR && group > 4 &&
+         ((group + 3) / 4 == 2 ? (v_bits >= 2 && v_bits <= 4) : ((group + 3) / 4 == 3 && v_bits == 2));
+}
+hipError_t launch_decode_q8(const DecodeArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_dequantize(const DequantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_quantize_tree(const QuantArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_stream_read(const void*, uint64_t, uint32_t*, hipStream_t) { return hipErrorNotSupported; }
