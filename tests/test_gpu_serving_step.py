@@ -17,6 +17,7 @@ CODECS = {   # name -> (k_codec, k_bits, v_codec, v_bits)
     "qjl4_v4": (tq.POLAR_QJL, 4, tq.POLAR, 4),
     "qjl2_v3": (tq.POLAR_QJL, 2, tq.POLAR, 3),
     "q8_v4": (tq.Q8_BLOCK32, 8, tq.POLAR, 4),
+    "q8_v2": (tq.Q8_BLOCK32, 8, tq.POLAR, 2),            # G = 12: one workgroup for the three head groups
     "polar2_v2": (tq.POLAR, 2, tq.POLAR, 2),
     "raw_raw": (tq.RAW_F32, 32, tq.RAW_F32, 32),        # two launches
     "tree3_tree2": (tq.POLAR_TREE, 3, tq.POLAR_TREE, 2),  # two launches
