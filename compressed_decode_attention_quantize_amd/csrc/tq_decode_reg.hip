@@ -261,11 +261,18 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   const float* qp = a.q + (static_cast<int64_t>(b) * a.n_q + hq0 + min(w, G - 1)) * kD;
   const float pq0 = (w < G) ? qp[lane] : 0.0f, pq1 = (w < G) ? qp[lane + 64] : 0.0f;
   const float pdk0 = a.tb.dk[lane], pdk1 = a.tb.dk[lane + 64];
-  constexpr int kCpw = kD / kWaves;   // sketch-table coordinates per wave
+  // Two block groups with a sketch: waves 0..3 rotate and form the code
+  // digits while waves 4..7 form the sketch (32 table coordinates each); one
+  // group: every wave takes 32 coordinates of the sketch.
+  constexpr bool kPar = NG == 2 && QJL;
+  constexpr int kCpw = kPar ? 32 : kD / kWaves;   // sketch-table coordinates per sketch wave
+  const int cw = kPar ? w - 4 : w;                // this wave's coordinate slice (< 0: none)
   float2 st2[QJL ? kCpw : 1];
   if constexpr (QJL) {
+    if (cw >= 0) {
 #pragma unroll
-    for (int c = 0; c < kCpw; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * w + c) * kM + 2 * lane);
+      for (int c = 0; c < kCpw; ++c) st2[c] = *reinterpret_cast<const float2*>(a.tb.shd + (kCpw * cw + c) * kM + 2 * lane);
+    }
   }
 
   // ------------------------------------------------------------- streaming
@@ -351,21 +358,24 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       const int pb = o / (4 * (kPRow / 4)), rg = (o / (kPRow / 4)) % 4, dw = o % (kPRow / 4);
       reinterpret_cast<uint32_t*>(&plimb[pb / kSets][pb % kSets][(4 * rg + 3) * kPRow])[dw] = 0u;
     }
-    if (w < 4) {   // waves 0..3: head w
-      float lo = pq0 * pdk0, hi = pq1 * pdk1;
-      const float q0 = pq0, q1 = pq1;
-      if constexpr (QJL) {
-        qs[w][lane] = q0;
-        qs[w][lane + 64] = q1;
-      }
-      wave_fwht128(lo, hi, lane);
-      qr[w][slot_of(lane)] = lo;
-      qr[w][slot_of(lane + 64)] = hi;
-    }
     const DigitLane dl = digit_lane(lane);
     const int half = lane >> 5;
-    if constexpr (QJL) {
-      lds_barrier();   // every head's query is in shared memory (the cache loads stay in flight)
+    // the code sets' digits of head hw from its rotated query xr, set pairs
+    // s2 = 2 p0, 2 p0 + 2, ... below 2 p1 (two sets at a time, one per half)
+    auto code_digits = [&](int hw, const float4& xr, int p0, int p1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s2 = 0; s2 < NCS; s2 += 2) {
+        if ((s2 >> 1) < p0 || (s2 >> 1) >= p1) continue;
+        const int s = min(s2 + half, NCS - 1);   // (an odd last set is formed by both halves)
+        const float coef = (KO::chain ? ((s == s2) ? ak[s2] : ak[min(s2 + 1, NCS - 1)]) : 1.0f) * kCodeScale;
+        write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, hw, xr, coef, dl);
+      }
+    };
+    // this wave's share of (S H D_K / sqrt d) q for the four heads: table
+    // coordinates kCpw cw .. kCpw cw + kCpw - 1, sketch rows 2 lane, 2 lane + 1
+    auto sketch_share = [&]() __attribute__((always_inline)) {
+      if constexpr (!QJL) return;
+      else {
       float acc[4][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[g][0] = acc[g][1] = 0.0f;
@@ -373,7 +383,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       for (int c4 = 0; c4 < kCpw; c4 += 4) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 x = *reinterpret_cast<const float4*>(&qs[g][kCpw * w + c4]);
+          const float4 x = *reinterpret_cast<const float4*>(&qs[g][kCpw * cw + c4]);
           acc[g][0] = fmaf(st2[c4].x, x.x, acc[g][0]);
           acc[g][1] = fmaf(st2[c4].y, x.x, acc[g][1]);
           acc[g][0] = fmaf(st2[c4 + 1].x, x.y, acc[g][0]);
@@ -387,44 +397,79 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       const int k0 = slot_of(2 * lane), k1 = slot_of(2 * lane + 1);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        sred[w][g][k0] = acc[g][0];
-        sred[w][g][k1] = acc[g][1];
+        sred[cw][g][k0] = acc[g][0];
+        sred[cw][g][k1] = acc[g][1];
       }
-    }
-    // The code sets' digits of head w & 3, two sets at a time.  With two groups
-    // and more than two code sets (the rotated queries are then in shared
-    // memory, past the barrier above), group gr takes the set pairs with
-    // (s2 / 2) % 2 == gr and waves 0..3 the sketch digits below; with two
-    // groups otherwise waves 0..3 take every code set and waves 4..7 the
-    // sketch digits.
-    constexpr bool kSplitCode = NG == 2 && QJL && NCS > 2;
-    if (kSplitCode || w < 4) {
-      const int hw = w & 3;
-      // (with one group head w's rotated query was written by this wave: no barrier)
-      const float4 xr = *reinterpret_cast<const float4*>(&qr[hw][4 * dl.l]);
-#pragma unroll
-      for (int s2 = 0; s2 < NCS; s2 += 2) {
-        if (kSplitCode && ((s2 >> 1) & 1) != gr) continue;
-        const int s = min(s2 + half, NCS - 1);   // (an odd last set is formed by both halves)
-        const float coef = (KO::chain ? ((s == s2) ? ak[s2] : ak[min(s2 + 1, NCS - 1)]) : 1.0f) * kCodeScale;
-        write_digits(&alimb[0][0] + s * (16 * kARow), &aexp[0][0] + s * 64, &cconst[0][0] + 4 * s, hw, xr, coef, dl);
       }
-    }
-    if constexpr (QJL) {
-      lds_barrier();   // every wave's sketch shares are in shared memory
-      // head hd's sketch digits
-      const int hd = kSplitCode ? w : w - 4 * (NG - 1);
-      if (hd >= 0 && hd < 4) {
-        float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    };
+    // head hd's sketch digits from the kD / kCpw shares
+    auto sketch_digits = [&](int hd) __attribute__((always_inline)) {
+      if constexpr (!QJL) return;
+      else {
+      float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-        for (int c = 0; c < kWaves; ++c) {
-          const float4 y = *reinterpret_cast<const float4*>(&sred[c][hd][4 * dl.l]);
-          u.x += y.x;
-          u.y += y.y;
-          u.z += y.z;
-          u.w += y.w;
+      for (int c = 0; c < kD / kCpw; ++c) {
+        const float4 y = *reinterpret_cast<const float4*>(&sred[c][hd][4 * dl.l]);
+        u.x += y.x;
+        u.y += y.y;
+        u.z += y.z;
+        u.w += y.w;
+      }
+      write_digits(alimb[NCS], aexp[NCS], cconst[NCS], hd, u, kSketchScale, dl);   // (both halves: the same job)
+      }
+    };
+    constexpr int kPairs = (NCS + 1) / 2;
+    if constexpr (kPar) {
+      // waves 0..3: head w's query into shared memory for the sketch waves;
+      // after the barrier they rotate it and form the first code set pair
+      // while waves 4..7 form the sketch shares; after the next barrier the
+      // other code pairs and, on waves 4..7, the sketch digits
+      if (w < 4) {
+        qs[w][lane] = pq0;
+        qs[w][lane + 64] = pq1;
+      }
+      lds_barrier();   // every head's query is in shared memory (the cache loads stay in flight)
+      float4 xr = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (w < 4) {
+        float lo = pq0 * pdk0, hi = pq1 * pdk1;
+        wave_fwht128(lo, hi, lane);
+        qr[w][slot_of(lane)] = lo;
+        qr[w][slot_of(lane + 64)] = hi;
+        // (this wave's own rotated query: no barrier)
+        xr = *reinterpret_cast<const float4*>(&qr[w][4 * dl.l]);
+        code_digits(w, xr, 0, 1);
+      } else {
+        sketch_share();
+      }
+      lds_barrier();   // the sketch shares are in shared memory
+      if (w < 4) {
+        code_digits(w, xr, 1, kPairs);
+      } else {
+        sketch_digits(w - 4);
+      }
+    } else {
+      if (w < 4) {   // waves 0..3: head w
+        float lo = pq0 * pdk0, hi = pq1 * pdk1;
+        if constexpr (QJL) {
+          qs[w][lane] = pq0;
+          qs[w][lane + 64] = pq1;
         }
-        write_digits(alimb[NCS], aexp[NCS], cconst[NCS], hd, u, kSketchScale, dl);   // (both halves: the same job)
+        wave_fwht128(lo, hi, lane);
+        qr[w][slot_of(lane)] = lo;
+        qr[w][slot_of(lane + 64)] = hi;
+      }
+      if constexpr (QJL) {
+        lds_barrier();   // every head's query is in shared memory (the cache loads stay in flight)
+        sketch_share();
+      }
+      if (w < 4) {
+        // (head w's rotated query was written by this wave: no barrier)
+        const float4 xr = *reinterpret_cast<const float4*>(&qr[w][4 * dl.l]);
+        code_digits(w, xr, 0, kPairs);
+      }
+      if constexpr (QJL) {
+        lds_barrier();   // every wave's sketch shares are in shared memory
+        if (w < 4) sketch_digits(w);
       }
     }
   }
