@@ -267,13 +267,16 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       uint8_t* const pe = &pexp[hgl][par][0][0];
       const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
       const float rw = (mloc == -INFINITY) ? -INFINITY : ceilf(mloc);
-      if (t == 0) rwb[par][w][g4] = rw;
+      rwb[par][w][g4] = rw;   // every lane of the row stores the same value (no branch)
       // probabilities and base-32 digits of p * value radius (3 digits, ~14 bits)
       const uint32_t vn = *reinterpret_cast<const uint32_t*>(vb + 2048 * VB + sn);
       const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - rw);
       const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - rw);
-      float r0 = (p0 > 0.0f) ? p0 * h2f(vn) : 0.0f;
-      float r1 = (p1 > 0.0f) ? p1 * h2f(vn >> 16) : 0.0f;
+      // p * radius, 0 for p = 0 whatever the radius bits (slots past the length
+      // hold arbitrary bytes): 0 x inf and 0 x NaN give a quiet NaN, which the
+      // maximum with 0 drops (IEEE maxNum, the kernel's IEEE mode)
+      float r0 = __builtin_fmaxf(p0 * h2f(vn), 0.0f);
+      float r1 = __builtin_fmaxf(p1 * h2f(vn >> 16), 0.0f);
       const float pm = row_max16(fmaxf(r0, r1));
       const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
       // k-slots 32 wl + 2 t + c meet the sign field of the affine value operand
@@ -294,7 +297,7 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
         ebytes |= static_cast<uint32_t>(min(max(s0 - 5 * j + 127, 1), 254)) << (8 * j);
         *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
       }
-      if (t == 0) *reinterpret_cast<uint32_t*>(&pe[16 * wl + 4 * g4]) = ebytes;
+      *reinterpret_cast<uint32_t*>(&pe[16 * wl + 4 * g4]) = ebytes;   // the same from every lane of the row
       rw_out = rw;
       ps_out = p0 + p1;
     };
