@@ -83,6 +83,14 @@ struct Q8Copier {
   }
 };
 
+// A running or step reference with no valid position behind it: finite, so
+// that differences and exponentials of it need no special case (it converts
+// to a huge negative shift, 2^shift = 0).
+constexpr float kQ8NoRef = -1e30f;
+// float -> int of a shift that is at most a few units above zero, clamped
+// below (an absent reference gives a large negative value)
+__device__ __forceinline__ int q8_shift(float x) { return static_cast<int>(fmaxf(x, -1073741824.0f)); }
+
 // LG: logits requested (each step stores them through a range-checked
 // buffer); the plain variant stores nothing in its loop.
 template <int VB, int HG, bool FUSED, bool LG>
@@ -150,7 +158,7 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       LG ? a.logits + (static_cast<int64_t>(b) * a.n_q + hq0) * a.max_ctx : a.logits, static_cast<short>(0),
       LG ? G * a.max_ctx * 4 : 0, 0x00020000);
 
-  float m_a = -INFINITY, m_b = -INFINITY;   // running reference (log2) of head g4 / head t / 4
+  float m_a = kQ8NoRef, m_b = kQ8NoRef;   // running reference (log2) of head g4 / head t / 4
   float m_top = -INFINITY;                  // Sparse-V: largest step reference of head t / 4 so far
   const bool sparse_v = a.sparse_v > 0;
   const float tau_v = static_cast<float>(a.sparse_v);
@@ -266,12 +274,12 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       uint8_t* const pl = &plimb[hgl][par][0];
       uint8_t* const pe = &pexp[hgl][par][0][0];
       const float mloc = row_max16(fmaxf(lg2[0], lg2[1]));
-      const float rw = (mloc == -INFINITY) ? -INFINITY : ceilf(mloc);
+      const float rw = fmaxf(ceilf(mloc), kQ8NoRef);   // (no valid position: the finite no-reference)
       rwb[par][w][g4] = rw;   // every lane of the row stores the same value (no branch)
       // probabilities and base-32 digits of p * value radius (3 digits, ~14 bits)
       const uint32_t vn = *reinterpret_cast<const uint32_t*>(vb + 2048 * VB + sn);
-      const float p0 = (lg2[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[0] - rw);
-      const float p1 = (lg2[1] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg2[1] - rw);
+      const float p0 = __builtin_amdgcn_exp2f(lg2[0] - rw);   // exp2(-inf) = 0 for slots without a logit
+      const float p1 = __builtin_amdgcn_exp2f(lg2[1] - rw);
       // p * radius, 0 for p = 0 whatever the radius bits (slots past the length
       // hold arbitrary bytes): 0 x inf and 0 x NaN give a quiet NaN, which the
       // maximum with 0 drops (IEEE maxNum, the kernel's IEEE mode)
@@ -320,9 +328,9 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       }
       const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
       const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
-      const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_a - mn_a));
-      const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_b - mn_b));
-      lsum = lsum * fh + ((rw == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(ps, static_cast<int>(rw - mn_a)));
+      const float fh = __builtin_amdgcn_ldexpf(1.0f, q8_shift(m_a - mn_a));
+      const float fv = __builtin_amdgcn_ldexpf(1.0f, q8_shift(m_b - mn_b));
+      lsum = fmaf(lsum, fh, __builtin_amdgcn_ldexpf(ps, q8_shift(rw - mn_a)));
       m_a = mn_a;
       m_b = mn_b;
       if (__any(fv != 1.0f)) {   // rescale only when some head's reference moved
@@ -336,7 +344,7 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       // far for every head of the group: its value work is skipped
       if (sparse_v) {
         m_top = fmaxf(m_top, rb);
-        if (__all((rb == -INFINITY) || (rb < m_top - tau_v))) return;
+        if (__all(rb < m_top - tau_v)) return;   // (a block with no position: rb = kQ8NoRef, not skipped, p = 0)
       }
       v8i Pv;
       {
@@ -347,7 +355,7 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       // k-block g4 holds the positions of wave g4 of the group: its digits
       // carry 2^(its reference - the running one)
       const float rk_ = rg[g4][hb];
-      const int adj = (rk_ == -INFINITY) ? 0 : static_cast<int>(rk_ - m_b);
+      const int adj = q8_shift(rk_ - m_b);   // an empty k-block gives the smallest scale (its digits are 0)
       const int scp = min(max(static_cast<int>(pe[16 * g4 + t]) + adj, 1), 254);
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
@@ -402,7 +410,7 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
   {
     const float ls = row_sum16(lsum);
     if (t == 0) wred[w][g4] = ls;
-    if (wl == 0 && t == 0) mrun[hgl][g4] = m_a;
+    if (wl == 0 && t == 0) mrun[hgl][g4] = (m_a == kQ8NoRef) ? -INFINITY : m_a;
     const int hc = t >> 2;
     float avsum = 0.0f;
 #pragma unroll
