@@ -517,7 +517,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     for (int T = 0; T < NTV; ++T) accV[r][T] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   v4f accO = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const Fp4Fill kf = fp4_fill();
-  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u, kf);
+  const v8i aoff = expand_fp4_affine_v(t < 8 ? 0xffffffffu : 0u, kf);
   float lgp[2] = {-INFINITY, -INFINITY};   // this lane's two logits of the block before
 
   // ---- the pieces of a step
@@ -589,9 +589,9 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
     // r 2^-s0 < 16; s0 in [-103, 124] (pm < 2^128; pm below 2^-100 is taken
     // as 2^-100), so every digit's E8M0 byte s0 - 5 j + 127 lies in [14, 251]
     const int s0 = max(exponent_of(pm), -100) - 3;
-    const float sgn = (t >= 12) ? -1.0f : 1.0f;   // k-slots on the value operand's sign field
-    r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
-    r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
+    // (the value operand's sign field takes the complemented bit: no sign flip here)
+    r0 = __builtin_amdgcn_ldexpf(r0, -s0);
+    r1 = __builtin_amdgcn_ldexpf(r1, -s0);
     int pk = static_cast<int>(vn);   // (the high half of each packed word is not stored)
 #pragma unroll
     for (int j = 0; j < 3; ++j) {   // (the fourth digit row is zero from the start)
@@ -683,7 +683,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       for (int p = 0; p < VB; ++p) vw[p] = rr ? Bv.vp[p].y : Bv.vp[p].x;
 #pragma unroll
       for (int T = 0; T < NTV; ++T)
-        accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
+        accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine_v(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
     }
     accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
   };

@@ -75,6 +75,20 @@ __device__ __forceinline__ v8i expand_fp4_affine(uint32_t w, const Fp4Fill& k) {
   return r;
 }
 
+// The same for the value operand, with the sign field taken from the
+// complemented bit: element 8 * 3 + n is +s instead of -s, so the operand on
+// the other side (the probability digits) needs no sign flip on those
+// k-slots; fields 0..2 as above.
+__device__ __forceinline__ v8i expand_fp4_affine_v(uint32_t w, const Fp4Fill& k) {
+  v8i r;
+  r[0] = static_cast<int>((w & k.m0) | k.c0);
+  r[1] = static_cast<int>((w & k.m1) | k.c1);
+  r[2] = static_cast<int>(w & 0x44444444u);
+  r[3] = static_cast<int>((~w & k.m3) | k.c3);
+  r[4] = r[5] = r[6] = r[7] = 0;
+  return r;
+}
+
 __device__ __forceinline__ int exponent_of(float x) {   // floor(log2 x), x > 0 normal
   return static_cast<int>((__float_as_uint(x) >> 23) & 0xffu) - 127;
 }
