@@ -273,7 +273,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
   // is what every value row carries on top of its signed sum.
   v4f accO = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const Fp4Fill kf = fp4_fill();
-  const v8i aoff = expand_fp4_affine(t < 8 ? 0xffffffffu : 0u, kf);
+  const v8i aoff = expand_fp4_affine_v(t < 8 ? 0xffffffffu : 0u, kf);
 
   {
     // The query set-up and the ring's first copies do not wait for the
@@ -553,11 +553,9 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
       float r1 = (p1 > 0.0f) ? p1 * h2f(vn >> 16) : 0.0f;
       const float pm = row_max16(fmaxf(r0, r1));
       const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
-      // k-slots 32wl + 2t + c meet the sign field of the affine value operand
-      // when t / 4 == 3: those digits carry the opposite sign
-      const float sgn = (t >= 12) ? -1.0f : 1.0f;
-      r0 = sgn * __builtin_amdgcn_ldexpf(r0, -s0);
-      r1 = sgn * __builtin_amdgcn_ldexpf(r1, -s0);
+      // (the value operand's sign field takes the complemented bit: no sign flip here)
+      r0 = __builtin_amdgcn_ldexpf(r0, -s0);
+      r1 = __builtin_amdgcn_ldexpf(r1, -s0);
       uint32_t ebytes = 127u << 24;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -640,7 +638,7 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
           vw[p] = *reinterpret_cast<const uint32_t*>(vb + 4 * (p * 4 * kD + g4 * kD + 32 * wl + 16 * rr + t));
 #pragma unroll
         for (int T = 0; T < NTV; ++T)
-          accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
+          accV[rr][T] = mfma_fp4_fp8(expand_fp4_affine_v(term_word<VB>(vw, T), kf), Pv, accV[rr][T], scp);
       }
       accO = mfma_fp4_fp8(aoff, Pv, accO, scp);
     };
