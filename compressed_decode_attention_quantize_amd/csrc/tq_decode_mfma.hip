@@ -556,7 +556,6 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
       // (the value operand's sign field takes the complemented bit: no sign flip here)
       r0 = __builtin_amdgcn_ldexpf(r0, -s0);
       r1 = __builtin_amdgcn_ldexpf(r1, -s0);
-      uint32_t ebytes = 127u << 24;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int pk = 0;   // the fourth digit row stays zero
@@ -567,10 +566,13 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
             r0 = (r0 - d0) * 32.0f;
             r1 = (r1 - d1) * 32.0f;
           }
-          ebytes |= static_cast<uint32_t>(min(max(s0 - 5 * j + 127, 1), 254)) << (8 * j);
         }
         *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
       }
+      // bytes s0 + 127, s0 + 122, s0 + 117, 127: s0 lies in [-102, 125] (pm is
+      // 0, a normal float of at least 1e-30 or at most +inf), so every byte
+      // lies in [15, 252] and none carries into the next
+      const uint32_t ebytes = static_cast<uint32_t>(s0 * 0x010101 + (0x7f000000 + 127 + (122 << 8) + (117 << 16)));
       if (t == 0) *reinterpret_cast<uint32_t*>(&pe[16 * wl + 4 * g4]) = ebytes;
       rw_out = rw;
       ps_out = p0 + p1;
