@@ -159,6 +159,7 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       LG ? G * a.max_ctx * 4 : 0, 0x00020000);
 
   float m_a = kQ8NoRef, m_b = kQ8NoRef;   // running reference (log2) of head g4 / head t / 4
+  const int ref_src = 16 * g4;             // byte address of lane 4 g4 (whose t / 4 is g4) for a lane permute
   float m_top = -INFINITY;                  // Sparse-V: largest step reference of head t / 4 so far
   const bool sparse_v = a.sparse_v > 0;
   const float tau_v = static_cast<float>(a.sparse_v);
@@ -320,16 +321,15 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       const uint8_t* const pe = &pexp[hgl][par][0][0];
       const int hb = t >> 2;
       const float(*rg)[4] = &rwb[par][4 * hgl];   // the group's four waves
-      float ra = rg[0][g4], rb = rg[0][hb];
+      float rb = rg[0][hb];
 #pragma unroll
-      for (int u = 1; u < 4; ++u) {
-        ra = fmaxf(ra, rg[u][g4]);
-        rb = fmaxf(rb, rg[u][hb]);
-      }
-      const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
+      for (int u = 1; u < 4; ++u) rb = fmaxf(rb, rg[u][hb]);
       const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
-      const float fh = __builtin_amdgcn_ldexpf(1.0f, q8_shift(m_a - mn_a));
       const float fv = __builtin_amdgcn_ldexpf(1.0f, q8_shift(m_b - mn_b));
+      // head g4's reference and factor: every lane whose t / 4 is g4 holds them
+      // (the same recurrence over the same wave references), lane 4 g4 among them
+      const float mn_a = __int_as_float(__builtin_amdgcn_ds_bpermute(ref_src, __float_as_int(mn_b)));
+      const float fh = __int_as_float(__builtin_amdgcn_ds_bpermute(ref_src, __float_as_int(fv)));
       lsum = fmaf(lsum, fh, __builtin_amdgcn_ldexpf(ps, q8_shift(rw - mn_a)));
       m_a = mn_a;
       m_b = mn_b;

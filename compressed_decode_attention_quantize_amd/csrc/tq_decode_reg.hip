@@ -507,6 +507,7 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
       static_cast<short>(0), a.logits != nullptr ? G * a.max_ctx * 4 : 0, 0x00020000);
 
   float m_a = kNoRef, m_b = kNoRef;   // running reference of head g4 (denominator) / head t / 4 (column)
+  const int ref_src = 16 * g4;         // byte address of lane 4 g4 (whose t / 4 is g4) for a lane permute
   float m_top = -INFINITY;                  // Sparse-V: largest step reference of head t / 4 so far
   const float tau_v = static_cast<float>(a.sparse_v);
   float lsum = 0.0f;
@@ -635,16 +636,15 @@ __device__ __forceinline__ void decode_reg_body(const DecodeArgs& a) {
   // wave within the group); returns the block's reference of head t / 4
   auto merge_refs = [&](const float (*rwr)[4], float rw, float ps) __attribute__((always_inline)) {
     const int hb = t >> 2;
-    float ra = rwr[0][g4], rb = rwr[0][hb];
+    float rb = rwr[0][hb];
 #pragma unroll
-    for (int u = 1; u < 4; ++u) {
-      ra = fmaxf(ra, rwr[u][g4]);
-      rb = fmaxf(rb, rwr[u][hb]);
-    }
-    const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
+    for (int u = 1; u < 4; ++u) rb = fmaxf(rb, rwr[u][hb]);
     const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
-    const float fh = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_a - mn_a));
     const float fv = __builtin_amdgcn_ldexpf(1.0f, shift_of(m_b - mn_b));
+    // head g4's reference and factor: every lane whose t / 4 is g4 holds them
+    // (the same recurrence over the same wave references), lane 4 g4 among them
+    const float mn_a = __int_as_float(__builtin_amdgcn_ds_bpermute(ref_src, __float_as_int(mn_b)));
+    const float fh = __int_as_float(__builtin_amdgcn_ds_bpermute(ref_src, __float_as_int(fv)));
     lsum = fmaf(lsum, fh, __builtin_amdgcn_ldexpf(ps, shift_of(rw - mn_a)));
     m_a = mn_a;
     m_b = mn_b;
