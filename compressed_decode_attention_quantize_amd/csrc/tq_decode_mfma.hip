@@ -588,16 +588,15 @@ __device__ __forceinline__ void decode_mfma_body(const DecodeArgs& a) {
       const uint8_t* const pe = (par ? pexp1 : pexp0) + gr * 64;
       // running references of head g4 (denominator) and head t / 4 (result column)
       const int hb = t >> 2;
-      float ra = rwb[par][0][g4], rb = rwb[par][0][hb];
+      float rb = rwb[par][0][hb];
 #pragma unroll
-      for (int u = 1; u < kWaves; ++u) {
-        ra = fmaxf(ra, rwb[par][u][g4]);
-        rb = fmaxf(rb, rwb[par][u][hb]);
-      }
-      const float mn_a = (ra > m_a + 8.0f) ? ra : m_a;
+      for (int u = 1; u < kWaves; ++u) rb = fmaxf(rb, rwb[par][u][hb]);
       const float mn_b = (rb > m_b + 8.0f) ? rb : m_b;
-      const float fh = (m_a == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_a - mn_a));
       const float fv = (m_b == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(m_b - mn_b));
+      // head g4's: every lane whose t / 4 is g4 holds them (the same recurrence
+      // over the same wave references), lane 4 g4 among them
+      const float mn_a = __int_as_float(__builtin_amdgcn_ds_bpermute(16 * g4, __float_as_int(mn_b)));
+      const float fh = __int_as_float(__builtin_amdgcn_ds_bpermute(16 * g4, __float_as_int(fv)));
       lsum = lsum * fh + ((rw == -INFINITY) ? 0.0f : __builtin_amdgcn_ldexpf(ps, static_cast<int>(rw - mn_a)));
       m_a = mn_a;
       m_b = mn_b;
