@@ -284,8 +284,9 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       // p * radius, 0 for p = 0 whatever the radius bits (slots past the length
       // hold arbitrary bytes): 0 x inf and 0 x NaN give a quiet NaN, which the
       // maximum with 0 drops (IEEE maxNum, the kernel's IEEE mode)
-      float r0 = __builtin_fmaxf(p0 * h2f(vn), 0.0f);
-      float r1 = __builtin_fmaxf(p1 * h2f(vn >> 16), 0.0f);
+      // (an fma with a zero addend: one mixed-precision instruction takes the fp16 radius)
+      float r0 = __builtin_fmaxf(fmaf(p0, h2f(vn), 0.0f), 0.0f);
+      float r1 = __builtin_fmaxf(fmaf(p1, h2f(vn >> 16), 0.0f), 0.0f);
       const float pm = row_max16(fmaxf(r0, r1));
       const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
       // (the value operand's sign field takes the complemented bit: no sign flip here)

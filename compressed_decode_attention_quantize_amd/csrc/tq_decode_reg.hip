@@ -52,8 +52,10 @@ constexpr float kNoRef = -1e30f;
 // a * b for a >= 0 and b an fp16 radius, 0 for a = 0 whatever b (the cache
 // words of slots past the length are arbitrary): 0 x inf and 0 x NaN give a
 // quiet NaN, which the maximum with 0 drops (IEEE maxNum, the kernel's IEEE
-// mode); negative garbage gives 0 as well
-__device__ __forceinline__ float mul_zero_wins(float a, float b) { return __builtin_fmaxf(a * b, 0.0f); }
+// mode); negative garbage gives 0 as well.  Written as an fma with a zero
+// addend (the same rounding as the product) so that one mixed-precision
+// instruction takes the fp16 radius as it is.
+__device__ __forceinline__ float mul_zero_wins(float a, float b) { return __builtin_fmaxf(fmaf(a, b, 0.0f), 0.0f); }
 // float -> int of a shift that is at most a few units above zero, clamped
 // below (an absent reference gives a large negative value)
 __device__ __forceinline__ int shift_of(float x) { return static_cast<int>(fmaxf(x, -1073741824.0f)); }
