@@ -262,7 +262,10 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
             code = fmaf(h2f((cb & 1) ? (sw >> 16) : sw), v, code);
           }
           const int tok = tok2[c];
-          const float l2 = __fmul_rn(qsc8, code);
+          float l2 = __fmul_rn(qsc8, code);
+          // computed on every lane: used only where valid, the arithmetic
+          // feeding it would otherwise be sunk into a divergent branch
+          asm volatile("" : "+v"(l2));
           const bool valid = (tok < n_t) && (g4 < G);
           if constexpr (LG) {   // -1: past the buffer's end, the store is dropped
             const int lo = valid ? (g4 * a.max_ctx + blk * kBlock + tok) * 4 : -1;
