@@ -291,7 +291,8 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
       float r0 = __builtin_fmaxf(fmaf(p0, h2f(vn), 0.0f), 0.0f);
       float r1 = __builtin_fmaxf(fmaf(p1, h2f(vn >> 16), 0.0f), 0.0f);
       const float pm = row_max16(fmaxf(r0, r1));
-      const int s0 = (pm >= 1e-30f) ? exponent_of(pm) - 3 : 0;   // r 2^-s0 < 16
+      // r 2^-s0 < 16; pm below 2^-100 (0 included) is taken as 2^-100
+      const int s0 = max(exponent_of(pm), -100) - 3;
       // (the value operand's sign field takes the complemented bit: no sign flip here)
       r0 = __builtin_amdgcn_ldexpf(r0, -s0);
       r1 = __builtin_amdgcn_ldexpf(r1, -s0);
@@ -306,9 +307,9 @@ __device__ __forceinline__ void decode_q8_body(const DecodeArgs& a) {
         }
         *reinterpret_cast<uint16_t*>(&pl[(4 * g4 + j) * 128 + 32 * wl + 2 * t]) = static_cast<uint16_t>(pk & 0xffff);
       }
-      // bytes s0 + 127, s0 + 122, s0 + 117, 127: s0 lies in [-102, 124] (pm is
-      // 0 or a normal float of at least 1e-30), so every byte lies in [15, 251]
-      // and none carries into the next
+      // bytes s0 + 127, s0 + 122, s0 + 117, 127: s0 lies in [-103, 124] (pm is
+      // a finite float), so every byte lies in [14, 251] and none carries into
+      // the next
       const uint32_t ebytes = static_cast<uint32_t>(s0 * 0x010101 + (0x7f000000 + 127 + (122 << 8) + (117 << 16)));
       *reinterpret_cast<uint32_t*>(&pe[16 * wl + 4 * g4]) = ebytes;   // the same from every lane of the row
       rw_out = rw;
